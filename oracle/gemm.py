@@ -1,0 +1,84 @@
+"""CPU oracle: the backward contractions, in fp64.
+
+TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this module; the library never does.
+
+* "Add Autograd Backward Support for FP4 GEMM Custom Ops", Implementation
+  Method: with the saved operands dequantized to BF16,
+  grad_X = grad_output @ W_bf16 and grad_W = grad_output.T @ X_bf16.
+* "Train adapters on top of FP8 weights", `FP8LinearFunction.backward`: a
+  frozen weight returns only grad_X; `FP8GroupedMatmulFunction.backward`:
+  grad_output rows of group g (cumulative int32 end offsets, the first group
+  starting at 0) multiply that group's (output_dim, input_dim) weight; the
+  EP-sentinel comment in `fp8_grouped_mm_experts_forward`: rows past the last
+  offset are not written.
+
+The inputs are bf16 values (bit patterns) that the format oracle produced;
+every bf16 x bf16 product is exact in fp64 and the sums are fp64 (numpy's
+float64 matmul).  Grouped weight gradients of an empty group are the empty
+sum, zero.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .formats import bf16_bits_to_f64
+
+
+def _f64(bits) -> np.ndarray:
+    return bf16_bits_to_f64(bits)
+
+
+def linear_dx(grad_bits: np.ndarray, w_bits: np.ndarray) -> np.ndarray:
+    """grad_X[m,k] = sum_n grad[m,n] * W[n,k]; grad [M,N], W [N,K]."""
+    return _f64(grad_bits) @ _f64(w_bits)
+
+
+def linear_dw(grad_bits: np.ndarray, x_bits: np.ndarray) -> np.ndarray:
+    """grad_W[n,k] = sum_m grad[m,n] * X[m,k]; grad [M,N], X [M,K]."""
+    return _f64(grad_bits).T @ _f64(x_bits)
+
+
+def group_bounds(offsets) -> list[tuple[int, int]]:
+    """(start, end) rows of each group from cumulative end offsets."""
+    ends = [int(o) for o in np.asarray(offsets).reshape(-1)]
+    starts = [0] + ends[:-1]
+    return list(zip(starts, ends))
+
+
+def grouped_dx(grad_bits: np.ndarray, w_bits: np.ndarray, offsets) -> tuple[np.ndarray, int]:
+    """Per group g: grad_X[rows of g] = grad[rows of g] @ W[g].
+
+    Returns (dX [M,K] fp64, rows_written): rows at or past the last offset are
+    left as NaN here, standing for "not written"."""
+    G = _f64(grad_bits)
+    W = _f64(w_bits)
+    M, K = G.shape[0], W.shape[-1]
+    out = np.full((M, K), np.nan)
+    for g, (s, e) in enumerate(group_bounds(offsets)):
+        if e > s:
+            out[s:e] = G[s:e] @ W[g]
+    return out, group_bounds(offsets)[-1][1] if len(offsets) else 0
+
+
+def grouped_dw(grad_bits: np.ndarray, x_bits: np.ndarray, offsets) -> np.ndarray:
+    """Per group g: grad_W[g] = grad[rows of g].T @ X[rows of g]; zero when the
+    group is empty.  Returns [G, N, K] fp64."""
+    G = _f64(grad_bits)
+    X = _f64(x_bits)
+    bounds = group_bounds(offsets)
+    out = np.zeros((len(bounds), G.shape[1], X.shape[1]))
+    for g, (s, e) in enumerate(bounds):
+        if e > s:
+            out[g] = G[s:e].T @ X[s:e]
+    return out
+
+
+def rows_dx(grad_bits: np.ndarray, w_bits: np.ndarray, rows) -> np.ndarray:
+    """Selected rows of grad_X = grad @ W (for sampled checks at full size)."""
+    return _f64(np.asarray(grad_bits)[rows]) @ _f64(w_bits)
+
+
+def rows_dw(grad_bits: np.ndarray, x_bits: np.ndarray, n_rows) -> np.ndarray:
+    """Selected rows n of grad_W = grad.T @ X."""
+    return _f64(np.asarray(grad_bits)[:, n_rows]).T @ _f64(x_bits)

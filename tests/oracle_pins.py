@@ -1,0 +1,410 @@
+"""Pins of the CPU oracle to things other than itself.
+
+Each `pin_*` function raises AssertionError when the oracle disagrees with
+the format definitions, an independent library (torch's CPU casts and
+ops), a closed form, a brute-force search or a structural invariant of the
+method.  `test_oracle_pins.py` runs them; `test_oracle_mutations.py` plants
+plausible mistakes in the oracle and checks that some pin fails.
+"""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+import torch
+
+import workloads as W
+from oracle import formats as F
+from oracle import gemm as O
+
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_constants.json")))
+
+
+def _bits_f32(u):
+    return np.asarray(u, dtype=np.uint32).view(np.float32)
+
+
+def _torch_bf16_bits(f32: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(f32, dtype=np.float32)).bfloat16() \
+        .view(torch.int16).numpy().view(np.uint16)
+
+
+def _same_bits_or_both_nan(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return np.all((a == b) & (np.signbit(a) == np.signbit(b)) | (np.isnan(a) & np.isnan(b)))
+
+
+# ------------------------------------------------------------------ element tables
+
+def pin_e4m3_table():
+    """All 256 E4M3 codes against torch's CPU float8_e4m3fn decode; max 448
+    (AstrAI FP8_MAX)."""
+    ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    assert _same_bits_or_both_nan(F.E4M3_TABLE, ref), "E4M3 table differs from torch"
+    assert np.nanmax(F.E4M3_TABLE) == GOLDEN["e4m3_max"]["value"]
+    assert F.E4M3_TABLE[0x7E] == 448.0 and np.isnan(F.E4M3_TABLE[0x7F]) and np.isnan(F.E4M3_TABLE[0xFF])
+    assert F.E4M3_TABLE[0x01] == 2.0 ** -9 and F.E4M3_TABLE[0x08] == 2.0 ** -6
+
+
+def pin_e8m0_table():
+    """All 256 E8M0 codes against torch's CPU float8_e8m0fnu decode."""
+    ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e8m0fnu).double().numpy()
+    assert _same_bits_or_both_nan(F.E8M0_TABLE, ref), "E8M0 table differs from torch"
+    assert F.E8M0_TABLE[127] == 1.0 and F.E8M0_TABLE[0] == 2.0 ** -127
+
+
+def pin_e2m1_table():
+    """The 16 E2M1 codes against the OCP value list; eight distinct
+    magnitudes, as the FP4 page states."""
+    ocp = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    expect = np.array(ocp + [-v for v in ocp])
+    assert _same_bits_or_both_nan(F.E2M1_TABLE, expect), "E2M1 table differs from the OCP list"
+    assert len(set(np.abs(F.E2M1_TABLE).tolist())) == GOLDEN["e2m1_magnitudes"]["value"]
+
+
+# ------------------------------------------------------------------ rounding
+
+def pin_bf16_rounding():
+    """fp32 -> bf16 RNE against torch's CPU cast on every high half with
+    low halves at and around the tie; NaN gives 0x7FC0 with the sign."""
+    hi = np.arange(1 << 16, dtype=np.uint32) << 16
+    lows = np.array([0, 1, 0x7FFF, 0x8000, 0x8001, 0xFFFF, 0x1234, 0xC000], dtype=np.uint32)
+    u = (hi[:, None] | lows[None, :]).reshape(-1)
+    f = _bits_f32(u)
+    ok = ~np.isnan(f)
+    got = F.f32_to_bf16_bits(f[ok])
+    ref = _torch_bf16_bits(f[ok])
+    assert np.array_equal(got, ref), "bf16 rounding differs from torch"
+    nan = F.f32_to_bf16_bits(np.array([np.nan, -np.nan], dtype=np.float32))
+    assert nan[0] in (0x7FC0, 0xFFC0) and (nan[0] & 0x7FFF) == 0x7FC0
+    signed = F.f32_to_bf16_bits(np.array([np.nan, np.nan], dtype=np.float32), nan_sign=np.array([0, 1]))
+    assert list(signed) == [0x7FC0, 0xFFC0]
+
+
+def _all_bf16_finite() -> np.ndarray:
+    b = np.arange(1 << 16, dtype=np.uint32) << 16
+    f = _bits_f32(b)
+    return f[np.isfinite(f)].astype(np.float64)
+
+
+def pin_e4m3_rounding():
+    """RNE onto the E4M3 grid against torch's float8_e4m3fn cast for every
+    finite bf16 value below 464 in magnitude (torch does not saturate beyond
+    that point); at and above 448 the oracle saturates to +-448."""
+    v = _all_bf16_finite()
+    small = np.abs(v) < 464
+    got = F.round_to_grid(v[small], "e4m3")
+    ref = torch.from_numpy(v[small].astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, ref), "E4M3 rounding differs from torch"
+    big = F.round_to_grid(v[~small], "e4m3")
+    assert np.all((big & 0x7F) == 0x7E), "E4M3 does not saturate to 448"
+    assert np.all((big >> 7) == np.signbit(v[~small]))
+
+
+def _brute_nearest(t: np.ndarray, table: np.ndarray, sign_bit: int) -> np.ndarray:
+    """Brute force: distance to every finite non-negative grid point, the
+    nearest wins, a tie goes to the code with a clear last bit."""
+    codes = np.array([c for c in range(sign_bit) if np.isfinite(table[c])])
+    vals = table[codes]
+    a = np.abs(t)[:, None]
+    d = np.abs(a - vals[None, :])
+    dmin = d.min(axis=1, keepdims=True)
+    cand = d == dmin
+    even = cand & (codes[None, :] % 2 == 0)
+    pick = np.where(even.any(axis=1), np.argmax(even, axis=1), np.argmax(cand, axis=1))
+    top = np.argmax(vals)
+    pick = np.where(np.abs(t) >= vals[top], top, pick)
+    out = codes[pick]
+    return np.where(np.signbit(t), out | sign_bit, out).astype(np.uint8)
+
+
+def pin_e2m1_rounding():
+    """RNE onto the E2M1 grid against a brute-force nearest search over a
+    dense set of points including every midpoint, and the tie table
+    0.25->0, 0.75->1, 1.25->1, 1.75->2, 2.5->2, 3.5->4, 5->4, 7->6."""
+    t = np.concatenate([np.arange(-8, 8, 1 / 64), np.arange(0, 8, 0.25) + 1 / 1024, [1e30, -1e30]])
+    got = F.round_to_grid(t, "e2m1")
+    ref = _brute_nearest(t, F.E2M1_TABLE, 0x8)
+    assert np.array_equal(got, ref), "E2M1 rounding differs from brute force"
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 7.0])
+    expect = [0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0, 6.0]
+    assert F.E2M1_TABLE[F.round_to_grid(ties, "e2m1")].tolist() == expect
+
+
+def pin_e4m3_brute():
+    """E4M3 rounding against brute force, including values far past the
+    saturation point and subnormal midpoints."""
+    t = np.concatenate([np.arange(0, 16, 2.0 ** -10), np.linspace(-600, 600, 4001), [1e9, -1e9]])
+    assert np.array_equal(F.round_to_grid(t, "e4m3"), _brute_nearest(t, F.E4M3_TABLE, 0x80))
+
+
+# ------------------------------------------------------------------ dequant
+
+def _torch_decode_e4m3(codes_u8: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(codes_u8)).view(torch.float8_e4m3fn).float()
+
+
+def _torch_decode_e8m0(codes_u8: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(codes_u8)).view(torch.float8_e8m0fnu).float()
+
+
+def _bits_equal_nan_aware(a: np.ndarray, b: np.ndarray) -> bool:
+    a = np.asarray(a, np.uint16)
+    b = np.asarray(b, np.uint16)
+    an = ((a & 0x7F80) == 0x7F80) & ((a & 0x7F) != 0)
+    bn = ((b & 0x7F80) == 0x7F80) & ((b & 0x7F) != 0)
+    return bool(np.all(np.where(an | bn, an & bn, a == b)))
+
+
+def pin_fp8_b128_dequant():
+    """FP8 block dequant as the FP8-adapter page's own test writes it:
+    weight.float() * scale repeated over 128x128 blocks (cut at the edge),
+    in fp32 torch ops, then torch's bf16 cast; partial blocks included."""
+    g = W.rng(90, "w")
+    R, C = 300, 200
+    codes = g.integers(0, 256, size=(R, C), dtype=np.uint8)
+    codes[codes & 0x7F == 0x7F] = 0x10
+    scale = (g.random((3, 2), dtype=np.float32) * 2 + 0.5).astype(np.float32)
+    got = F.dequant(F.FMT_FP8_B128, codes, scale)[0]
+    s = torch.from_numpy(scale).repeat_interleave(128, dim=0)[:R].repeat_interleave(128, dim=1)[:, :C]
+    ref = (_torch_decode_e4m3(codes) * s).bfloat16().view(torch.int16).numpy().view(np.uint16)
+    assert _bits_equal_nan_aware(got, ref), "FP8 block dequant differs from the page's formulation"
+
+
+def pin_fp8_b128_page_rounding():
+    """The page's implementation rounds the scale to bf16 before a bf16
+    multiply; the reading taken (one fp32 multiply, then bf16) stays within
+    two bf16 ulps of it."""
+    g = W.rng(91, "w")
+    codes = g.integers(0, 0x7E, size=(256, 256), dtype=np.uint8)
+    scale = (g.random((2, 2), dtype=np.float32) + 0.5).astype(np.float32)
+    ours = F.bf16_bits_to_f64(F.dequant(F.FMT_FP8_B128, codes, scale)[0])
+    s = torch.from_numpy(scale).bfloat16().repeat_interleave(128, 0).repeat_interleave(128, 1)
+    page = (_torch_decode_e4m3(codes).bfloat16() * s).double().numpy()
+    ulp = np.maximum(np.abs(page), 2.0 ** -126) * 2.0 ** -7
+    assert np.all(np.abs(ours - page) <= 2 * ulp)
+
+
+def pin_mxfp8_dequant():
+    """MXFP8 dequant against torch: float8_e4m3fn x float8_e8m0fnu in fp32,
+    then bf16; both scale axes."""
+    g = W.rng(92, "w")
+    R, C = 64, 96
+    codes = g.integers(0, 256, size=(R, C), dtype=np.uint8)
+    for axis in (-1, -2):
+        shape = (R, C // 32) if axis == -1 else (R // 32, C)
+        sc = g.integers(100, 150, size=shape, dtype=np.uint8)
+        sc.flat[0] = 0xFF
+        got = F.dequant(F.FMT_MXFP8, codes, sc, axis=axis)[0]
+        s = _torch_decode_e8m0(sc)
+        s = s.repeat_interleave(32, dim=1) if axis == -1 else s.repeat_interleave(32, dim=0)
+        ref = (_torch_decode_e4m3(codes) * s).bfloat16().view(torch.int16).numpy().view(np.uint16)
+        assert _bits_equal_nan_aware(got, ref), f"MXFP8 axis {axis} differs from torch"
+
+
+def pin_fp4_dequant_closed_forms():
+    """Hand-built packed blocks: byte 0x21 is [0.5, 1.0] (low nibble first);
+    MXFP4 scale byte 130 multiplies by 8; NVFP4 code 1.0 with block scale
+    E4M3 2.0 (0x40) and tensor scale 0.25 is 0.5; an E8M0 NaN scale makes
+    NaN."""
+    codes = np.zeros((1, 16), dtype=np.uint8)
+    codes[0, 0] = 0x21
+    codes[0, 1] = 0xF7                                      # [6, -6]
+    mx = F.bf16_bits_to_f64(F.dequant(F.FMT_MXFP4, codes, np.array([[127]], np.uint8))[0])
+    assert mx[0, :4].tolist() == [0.5, 1.0, 6.0, -6.0]
+    mx8 = F.bf16_bits_to_f64(F.dequant(F.FMT_MXFP4, codes, np.array([[130]], np.uint8))[0])
+    assert mx8[0, :4].tolist() == [4.0, 8.0, 48.0, -48.0]
+    nan = F.dequant(F.FMT_MXFP4, codes, np.array([[255]], np.uint8))[0]
+    assert np.all((nan & 0x7FFF) == 0x7FC0)
+    nv_codes = np.full((1, 8), 0x22, dtype=np.uint8)       # all 1.0
+    nv_scale = np.array([[0x40]], dtype=np.uint8)          # E4M3 2.0
+    nv = F.bf16_bits_to_f64(F.dequant(F.FMT_NVFP4, nv_codes, nv_scale, np.float32(0.25))[0])
+    assert np.all(nv == 0.5)
+
+
+def pin_nvfp4_dequant_torch():
+    """NVFP4 dequant against torch ops: the block scale (torch E4M3 decode)
+    times the tensor scale in fp32, times the E2M1 value (OCP list) in fp32,
+    then bf16."""
+    g = W.rng(93, "w")
+    R, C = 32, 64
+    packed = g.integers(0, 256, size=(R, C // 2), dtype=np.uint8)
+    sc = g.integers(0, 0x7F, size=(R, C // 16), dtype=np.uint8)
+    ts = np.float32(0.0173)
+    got = F.dequant(F.FMT_NVFP4, packed, sc, ts)[0]
+    ocp = torch.tensor([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0,
+                        -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0])
+    p = torch.from_numpy(packed).long()
+    vals = torch.stack([ocp[p & 15], ocp[p >> 4]], dim=-1).reshape(R, C)
+    S = (_torch_decode_e4m3(sc) * torch.tensor(ts)).repeat_interleave(16, dim=1)
+    ref = (vals * S).bfloat16().view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, ref), "NVFP4 dequant differs from torch"
+
+
+# ------------------------------------------------------------------ MX quant
+
+def pin_mx_scale_rule():
+    """A block whose amax is exactly 448 * 2^5 (E4M3) or 6 * 2^5 (E2M1) gets
+    scale byte 127 + 5 and its codes back unchanged."""
+    g = W.rng(94, "x")
+    for elem, table, top in (("e4m3", F.E4M3_TABLE, 0x7E), ("e2m1", F.E2M1_TABLE, 0x7)):
+        n = 256 if elem == "e4m3" else 16
+        pool = np.array([c for c in range(n) if np.isfinite(table[c])])
+        codes = g.choice(pool, size=32).astype(np.uint8)
+        codes[3] = top
+        vals = (table[codes] * 32.0).astype(np.float32)
+        q, s = F.mx_quant(W.bf16_bits(vals[None, :]), -1, elem)
+        assert s.reshape(-1)[0] == 132, (elem, s)
+        qc = F.unpack_e2m1(q)[0, 0] if elem == "e2m1" else q[0, 0]
+        assert np.array_equal(table[qc], table[codes])
+
+
+def pin_mx_invariants():
+    """For random blocks across magnitudes (bf16 subnormals included): the
+    scaled amax lies in [2^emax, 2^(emax+1)) unless clamped; quantizing the
+    dequantized result returns the same bytes; the error is within half a
+    grid step of the top binade, or the clipped excess for saturated elements;
+    axis -2 equals axis -1 on the transpose."""
+    g = W.rng(95, "x")
+    mags = np.exp2(g.integers(-140, 120, size=(64, 1))).astype(np.float32)
+    x = (g.standard_normal((64, 64)).astype(np.float32) * mags)
+    bits = W.bf16_bits(x)
+    v = F.bf16_bits_to_f64(bits)
+    for elem, emax, fmt in (("e4m3", 8, F.FMT_MXFP8), ("e2m1", 2, F.FMT_MXFP4)):
+        q, s = F.mx_quant(bits, -1, elem)
+        amax = np.abs(v.reshape(64, 2, 32)).max(-1)
+        e = s[0].astype(np.int64) - 127
+        scaled = amax / np.exp2(e.astype(np.float64))
+        ok = (e > -127) & (amax > 0)
+        assert np.all((scaled[ok] >= 2.0 ** emax) & (scaled[ok] < 2.0 ** (emax + 1)))
+        deq = F.dequant(fmt, q, s, axis=-1)
+        q2, s2 = F.mx_quant(deq, -1, elem)
+        assert np.array_equal(q, q2) and np.array_equal(s, s2), f"{elem} not idempotent"
+        dv = F.bf16_bits_to_f64(deq[0])
+        step = np.exp2(e.astype(np.float64))[:, :, None] * (2.0 ** (emax - 3 if elem == "e4m3" else emax - 1))
+        err = np.abs(dv - v).reshape(64, 2, 32)
+        top = 448.0 if elem == "e4m3" else 6.0
+        sat = np.abs(v).reshape(64, 2, 32) - top * np.exp2(e.astype(np.float64))[:, :, None]
+        bound = np.maximum(step / 2, sat) * (1 + 1e-12) + 2.0 ** -133
+        assert np.all(err[ok] <= bound[ok])
+        qT, sT = F.mx_quant(np.ascontiguousarray(bits.T), -2, elem)
+        if elem == "e4m3":
+            assert np.array_equal(qT[0].T, q[0]) and np.array_equal(sT[0].T, s[0])
+        else:
+            assert np.array_equal(sT[0].T, s[0])
+
+
+def pin_mx_special_blocks():
+    """All-zero block -> scale 0 and signed zero codes; a NaN or an infinity
+    -> scale 0xFF and NaN codes (E4M3); a block of bf16 subnormals clamps the
+    exponent at -127."""
+    z = np.zeros((1, 32), np.float32)
+    z[0, 1] = -0.0
+    q, s = F.mx_quant(W.bf16_bits(z), -1, "e4m3")
+    assert s[0, 0, 0] == 0 and q[0, 0, 0] == 0 and q[0, 0, 1] == 0x80
+    n = np.ones((1, 32), np.float32)
+    n[0, 5] = np.nan
+    n[0, 6] = -1
+    q, s = F.mx_quant(W.bf16_bits(n), -1, "e4m3")
+    assert s[0, 0, 0] == 0xFF and q[0, 0, 0] == 0x7F and q[0, 0, 6] == 0xFF
+    i = np.ones((1, 32), np.float32)
+    i[0, 0] = np.inf
+    assert F.mx_quant(W.bf16_bits(i), -1, "e2m1")[1][0, 0, 0] == 0xFF
+    tiny = np.full((1, 32), 2.0 ** -130, np.float32)
+    q, s = F.mx_quant(W.bf16_bits(tiny), -1, "e4m3")
+    assert s[0, 0, 0] == 0
+    assert F.E4M3_TABLE[q[0, 0, 0]] * 2.0 ** -127 == 2.0 ** -130
+
+
+# ------------------------------------------------------------------ contractions
+
+def _tiny_bf16(number, tensor, shape):
+    return W.bf16_bits(W.normal_f32(number, tensor, shape, 1.0))
+
+
+def pin_gemm_brute_force():
+    """dX and dW against pure-Python triple loops on tiny shapes."""
+    M, N, K = 5, 7, 3
+    g = _tiny_bf16(96, "grad", (M, N))
+    w = _tiny_bf16(96, "w", (N, K))
+    x = _tiny_bf16(96, "x", (M, K))
+    gv, wv, xv = (F.bf16_bits_to_f64(a).tolist() for a in (g, w, x))
+    dx = [[sum(gv[m][n] * wv[n][k] for n in range(N)) for k in range(K)] for m in range(M)]
+    dw = [[sum(gv[m][n] * xv[m][k] for m in range(M)) for k in range(K)] for n in range(N)]
+    assert np.allclose(O.linear_dx(g, w), dx, rtol=1e-13, atol=0)
+    assert np.allclose(O.linear_dw(g, x), dw, rtol=1e-13, atol=0)
+
+
+def pin_gemm_transpose_identity():
+    """dW(grad, X) equals dX(grad^T, X): the two contractions agree on which
+    operand is transposed."""
+    g = _tiny_bf16(97, "grad", (33, 17))
+    x = _tiny_bf16(97, "x", (33, 9))
+    assert np.allclose(O.linear_dw(g, x), O.linear_dx(np.ascontiguousarray(g.T), x), rtol=1e-13)
+
+
+def _page_fp8_weight(number, rows, cols, grid, low):
+    g = W.rng(number, "w")
+    w = torch.from_numpy(g.standard_normal((rows, cols)).astype(np.float32)).to(torch.float8_e4m3fn)
+    scale = torch.from_numpy(g.random(grid).astype(np.float32) + np.float32(low))
+    return w.view(torch.uint8).numpy(), scale.numpy()
+
+
+def pin_fp8_adapter_linear_closed_form():
+    """The FP8-adapter page's linear test: with grad_out all ones, every row
+    of grad_X equals ones @ (W.float() * scale) within rtol 1e-2, atol 1e-1."""
+    c = GOLDEN["fp8_linear_test"]
+    codes, scale = _page_fp8_weight(98, c["out_features"], c["in_features"], tuple(c["scale_grid"]), c["scale_low"])
+    wd = F.dequant(F.FMT_FP8_B128, codes, scale)[0]
+    ones = W.bf16_bits(np.ones((c["tokens"], c["out_features"]), np.float32))
+    got = O.linear_dx(ones, wd)
+    s = torch.from_numpy(scale).repeat_interleave(128, 0).repeat_interleave(128, 1)
+    expected = torch.ones(c["tokens"], c["out_features"]) @ (_torch_decode_e4m3(codes) * s)
+    torch.testing.assert_close(torch.from_numpy(got).float(), expected, rtol=c["rtol"], atol=c["atol"])
+
+
+def pin_fp8_adapter_grouped_closed_form():
+    """The FP8-adapter page's grouped test: 2 groups of 3 tokens, W 512x256
+    viewed as 2 x 256 x 256; with ones as grad_out each token's grad_X is
+    ones @ W_deq[its group]."""
+    c = GOLDEN["fp8_grouped_test"]
+    G, tpg = c["groups"], c["tokens_per_group"]
+    codes, scale = _page_fp8_weight(99, c["out_features"], c["in_features"], tuple(c["scale_grid"]), c["scale_low"])
+    per = c["out_features"] // G
+    wd = np.stack([F.dequant(F.FMT_FP8_B128, codes[g * per:(g + 1) * per],
+                             scale[g * per // 128:(g + 1) * per // 128])[0] for g in range(G)])
+    offsets = np.arange(1, G + 1, dtype=np.int32) * tpg
+    ones = W.bf16_bits(np.ones((G * tpg, per), np.float32))
+    got, _ = O.grouped_dx(ones, wd, offsets)
+    s = torch.from_numpy(scale).repeat_interleave(128, 0).repeat_interleave(128, 1)
+    weight = (_torch_decode_e4m3(codes) * s).view(G, per, c["in_features"])
+    expected = (torch.ones(tpg, G, 1, per) @ weight).squeeze(2)      # [token, group, K]
+    expected = expected.permute(1, 0, 2).reshape(G * tpg, -1)
+    torch.testing.assert_close(torch.from_numpy(got).float(), expected, rtol=c["rtol"], atol=c["atol"])
+
+
+def pin_grouped_equals_dense():
+    """Grouped dX / dW equal the per-group dense results stacked; an empty
+    group gets dW = 0; rows past the last offset are not written; one group
+    spanning all rows equals the linear backward."""
+    M, N, K, G = 40, 24, 16, 4
+    g = _tiny_bf16(100, "grad", (M, N))
+    x = _tiny_bf16(100, "x", (M, K))
+    w = _tiny_bf16(100, "w", (G, N, K))
+    offsets = np.array([7, 7, 30, 36], dtype=np.int32)      # group 1 empty, rows 36.. untouched
+    dx, end = O.grouped_dx(g, w, offsets)
+    dw = O.grouped_dw(g, x, offsets)
+    assert end == 36 and np.all(np.isnan(dx[36:]))
+    bounds = [(0, 7), (7, 7), (7, 30), (30, 36)]
+    for gi, (s, e) in enumerate(bounds):
+        if e > s:
+            assert np.allclose(dx[s:e], O.linear_dx(g[s:e], w[gi]), rtol=1e-13)
+            assert np.allclose(dw[gi], O.linear_dw(g[s:e], x[s:e]), rtol=1e-13)
+    assert np.all(dw[1] == 0)
+    one_dx, _ = O.grouped_dx(g, w[:1], np.array([M], np.int32))
+    assert np.allclose(one_dx, O.linear_dx(g, w[0]), rtol=1e-13)
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

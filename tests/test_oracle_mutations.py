@@ -1,0 +1,118 @@
+"""Mutation check of the oracle's pins (CPU only).
+
+The FP4 backward page validates its tests by planting an error in the code
+under test and counting the tests that fail.  Here each plausible mistake is
+planted in the oracle (never in the GPU path) and at least one pin must
+fail; a mutation that no pin catches means the pins are vacuous for it.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+sys.path.insert(0, os.path.dirname(__file__))
+
+import oracle_pins  # noqa: E402
+from oracle import formats as F  # noqa: E402
+from oracle import gemm as O  # noqa: E402
+
+
+def _swap_nibbles(packed):
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (p.shape[-1] * 2,), dtype=np.uint8)
+    out[..., 0::2] = p >> 4
+    out[..., 1::2] = p & 0x0F
+    return out
+
+
+def _truncating_bf16(f, nan_sign=None):
+    u = np.ascontiguousarray(f, dtype=np.float32).view(np.uint32)
+    return (u >> 16).astype(np.uint16)
+
+
+_orig_round = F.round_to_grid
+
+
+def _ties_up(t, elem):
+    # nudge every value up by a hair so that ties round away from zero
+    return _orig_round(np.asarray(t) * (1 + 2.0 ** -40), elem)
+
+
+_orig_nv = F.dequant_nvfp4
+
+
+def _nv_without_tensor_scale(codes, scales, tensor_scale):
+    return _orig_nv(codes, scales, np.float32(1.0))
+
+
+_orig_expand = F.expand_scales
+
+
+def _expand_block64(scales, rows, cols, br, bc):
+    if br == 128:
+        s = _orig_expand(scales, rows, cols, 64, 64)
+        pad = [(0, 0)] * (s.ndim - 2) + [(0, rows - s.shape[-2]), (0, cols - s.shape[-1])]
+        return np.pad(s, pad, mode="edge")
+    return _orig_expand(scales, rows, cols, br, bc)
+
+
+def _expand_rows_off_by_one_block(scales, rows, cols, br, bc):
+    if (br, bc) == (F.MX_BLOCK, 1):
+        return _orig_expand(np.roll(scales, 1, axis=-2), rows, cols, br, bc)
+    return _orig_expand(scales, rows, cols, br, bc)
+
+
+def _dw_wrong_operand(grad_bits, x_bits):
+    return O._f64(grad_bits).T @ O._f64(x_bits)[::-1]
+
+
+_orig_bounds = O.group_bounds
+
+
+def _bounds_shifted(offsets):
+    b = _orig_bounds(offsets)
+    return [(s, e) for (s, e) in b[1:]] + [b[0]]
+
+
+def _no_f32_step(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+MUTATIONS = {
+    "nibble order swapped": (F, "unpack_e2m1", _swap_nibbles),
+    "bf16 truncation instead of RNE": (F, "f32_to_bf16_bits", _truncating_bf16),
+    "ties away from zero": (F, "round_to_grid", _ties_up),
+    "NVFP4 tensor scale dropped": (F, "dequant_nvfp4", _nv_without_tensor_scale),
+    "FP8 block 64 instead of 128": (F, "expand_scales", _expand_block64),
+    "MX axis -2 scale rows off by one block": (F, "expand_scales", _expand_rows_off_by_one_block),
+    "E4M3 MX emax 7": (F, "ELEM_EMAX", {"e4m3": 7, "e2m1": 2}),
+    "E2M1 MX emax 3": (F, "ELEM_EMAX", {"e4m3": 8, "e2m1": 3}),
+    "E4M3 bias 8": (F, "E4M3_TABLE", F.E4M3_TABLE / 2),
+    "E2M1 subnormal 0.25": (F, "E2M1_TABLE", np.where(np.abs(F.E2M1_TABLE) == 0.5, F.E2M1_TABLE / 2, F.E2M1_TABLE)),
+    "E8M0 bias 128": (F, "E8M0_TABLE", F.E8M0_TABLE / 2),
+    "dW operand rows reversed": (O, "linear_dw", _dw_wrong_operand),
+    "group bounds shifted": (O, "group_bounds", _bounds_shifted),
+}
+
+
+def _failing_pins():
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin()
+        except Exception:  # noqa: BLE001 - any failure counts as caught
+            failed.append(pin.__name__)
+    return failed
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name, monkeypatch):
+    module, attr, value = MUTATIONS[name]
+    monkeypatch.setattr(module, attr, value)
+    failed = _failing_pins()
+    assert failed, f"no pin catches the planted mistake: {name}"
+
+
+def test_unmutated_oracle_passes_every_pin():
+    assert _failing_pins() == []
