@@ -1,0 +1,190 @@
+"""Backward of block-scaled low-precision linear and grouped matmuls on MI355X.
+
+A thin Python binding over the C-ABI library `liblp.so` (declared in
+`include/lp.h`).  The functions below keep the C names; they only marshal
+torch tensors (device memory) and the current HIP stream into the C calls.
+Every step of the computation runs in the library's HIP kernels; there is no
+fallback, and importing this package fails if the library is not built
+(`python -m fp8_gemm_backward_amd.build`).
+
+Formats (see include/lp.h): "bf16", "mxfp4", "nvfp4", "fp8_b128", "mxfp8".
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+import re
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liblp.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "lp.h")
+
+FMT = {"bf16": 0, "mxfp4": 1, "nvfp4": 2, "fp8_b128": 3, "mxfp8": 4}
+STATUS = {0: "LP_OK", 1: "LP_ERR_NULL", 2: "LP_ERR_SHAPE", 3: "LP_ERR_FORMAT", 4: "LP_ERR_ALIGN",
+          5: "LP_ERR_HIP"}
+
+
+class LpError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)}")
+
+
+class _QTensorC(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int32), ("scale_axis", ctypes.c_int32), ("batch", ctypes.c_int64),
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("codes", ctypes.c_void_p),
+                ("scales", ctypes.c_void_p), ("tensor_scale", ctypes.c_void_p)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m fp8_gemm_backward_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER(_QTensorC)
+    v = ctypes.c_void_p
+    i64, i32 = ctypes.c_int64, ctypes.c_int32
+    lib.lp_dequant.argtypes = [P, v, v]
+    lib.lp_mx_quant.argtypes = [v, i64, i64, i64, i32, i32, v, v, v]
+    lib.lp_linear_bwd.argtypes = [P, P, P, v, v, v]
+    lib.lp_grouped_bwd.argtypes = [P, P, P, v, i64, v, v, v]
+    lib.lp_status_string.argtypes = [i32]
+    lib.lp_status_string.restype = ctypes.c_char_p
+    for f in ("lp_dequant", "lp_mx_quant", "lp_linear_bwd", "lp_grouped_bwd"):
+        getattr(lib, f).restype = ctypes.c_int32
+    return lib
+
+
+lib = _load()
+
+
+def header_functions() -> list[str]:
+    """Names of the functions declared in include/lp.h."""
+    text = open(HEADER_PATH).read()
+    return re.findall(r"^\s*(?:lp_status|const char\*)\s+(lp_\w+)\s*\(", text, re.M)
+
+
+@dataclasses.dataclass
+class QTensor:
+    """A (possibly block-scaled) tensor of logical shape [batch, rows, cols].
+
+    codes: bf16 values (fmt "bf16"), uint8 E4M3 codes, or uint8 packed E2M1
+    pairs; scales: uint8 E8M0 / E4M3 bytes or float32 block scales; for
+    NVFP4 `tensor_scale` is a one-element float32 device tensor.
+    """
+    fmt: str
+    codes: torch.Tensor
+    scales: Optional[torch.Tensor] = None
+    tensor_scale: Optional[torch.Tensor] = None
+    shape: tuple = ()
+    axis: int = -1
+
+    def __post_init__(self):
+        if not self.shape:
+            s = tuple(self.codes.shape)
+            cols = s[-1] * (2 if self.fmt in ("mxfp4", "nvfp4") else 1)
+            self.shape = (s[0] if len(s) == 3 else 1, s[-2], cols)
+        if len(self.shape) == 2:
+            self.shape = (1,) + tuple(self.shape)
+
+    @property
+    def rows(self) -> int:
+        return self.shape[1]
+
+    @property
+    def cols(self) -> int:
+        return self.shape[2]
+
+    def c(self) -> _QTensorC:
+        def ptr(t):
+            return None if t is None else t.data_ptr()
+        return _QTensorC(FMT[self.fmt], self.axis, self.shape[0], self.shape[1], self.shape[2],
+                         ptr(self.codes), ptr(self.scales), ptr(self.tensor_scale))
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _check(st: int, where: str):
+    if st != 0:
+        raise LpError(st, where)
+
+
+def lp_dequant(src: QTensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Decode `src` to bf16 [batch, rows, cols] (bit-exact)."""
+    if out is None:
+        out = torch.empty(src.shape, dtype=torch.bfloat16, device=src.codes.device)
+    q = src.c()
+    _check(lib.lp_dequant(ctypes.byref(q), out.data_ptr(), _stream(stream)), "lp_dequant")
+    return out
+
+
+def lp_mx_quant(src: torch.Tensor, axis: int, fmt: str = "mxfp8", codes: Optional[torch.Tensor] = None,
+                scales: Optional[torch.Tensor] = None, stream=None) -> QTensor:
+    """MX-quantize a bf16 tensor [batch, rows, cols] (or [rows, cols]) along
+    `axis` (-1 or -2) to "mxfp8" or "mxfp4"."""
+    shape = tuple(src.shape) if src.dim() == 3 else (1,) + tuple(src.shape)
+    b, r, c = shape
+    dev = src.device
+    if codes is None:
+        codes = torch.empty((b, r, c if fmt == "mxfp8" else c // 2), dtype=torch.uint8, device=dev)
+    if scales is None:
+        sshape = (b, r, c // 32) if axis == -1 else (b, r // 32, c)
+        scales = torch.empty(sshape, dtype=torch.uint8, device=dev)
+    _check(lib.lp_mx_quant(src.data_ptr(), b, r, c, axis, FMT[fmt], codes.data_ptr(), scales.data_ptr(),
+                           _stream(stream)), "lp_mx_quant")
+    return QTensor(fmt, codes, scales, None, shape, axis)
+
+
+def lp_linear_bwd(grad_out: QTensor, x: Optional[QTensor], w: Optional[QTensor], need_dx: bool = True,
+                  need_dw: bool = True, grad_x: Optional[torch.Tensor] = None,
+                  grad_w: Optional[torch.Tensor] = None, stream=None):
+    """(grad_X [M,K] or None, grad_W [N,K] or None) of a linear layer."""
+    M, N = grad_out.rows, grad_out.cols
+    K = (w if need_dx else x).cols
+    dev = grad_out.codes.device
+    if need_dx and grad_x is None:
+        grad_x = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    if need_dw and grad_w is None:
+        grad_w = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    g = grad_out.c()
+    xc = x.c() if x is not None else None
+    wc = w.c() if w is not None else None
+    st = lib.lp_linear_bwd(ctypes.byref(g), ctypes.byref(xc) if xc else None, ctypes.byref(wc) if wc else None,
+                           grad_x.data_ptr() if need_dx else None, grad_w.data_ptr() if need_dw else None,
+                           _stream(stream))
+    _check(st, "lp_linear_bwd")
+    return (grad_x if need_dx else None), (grad_w if need_dw else None)
+
+
+def lp_grouped_bwd(grad_out: QTensor, x: Optional[QTensor], w: Optional[QTensor], offsets: torch.Tensor,
+                   need_dx: bool = True, need_dw: bool = True, grad_x: Optional[torch.Tensor] = None,
+                   grad_w: Optional[torch.Tensor] = None, stream=None):
+    """(grad_X [M,K] or None, grad_W [G,N,K] or None) of a grouped matmul.
+    Rows of grad_X at or past offsets[-1] are left as they were in `grad_x`."""
+    M, N = grad_out.rows, grad_out.cols
+    G = offsets.numel()
+    K = (w if need_dx else x).cols
+    dev = grad_out.codes.device
+    if need_dx and grad_x is None:
+        grad_x = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    if need_dw and grad_w is None:
+        grad_w = torch.empty((G, N, K), dtype=torch.bfloat16, device=dev)
+    g = grad_out.c()
+    xc = x.c() if x is not None else None
+    wc = w.c() if w is not None else None
+    st = lib.lp_grouped_bwd(ctypes.byref(g), ctypes.byref(xc) if xc else None, ctypes.byref(wc) if wc else None,
+                            offsets.data_ptr(), G, grad_x.data_ptr() if need_dx else None,
+                            grad_w.data_ptr() if need_dw else None, _stream(stream))
+    _check(st, "lp_grouped_bwd")
+    return (grad_x if need_dx else None), (grad_w if need_dw else None)
+
+
+def lp_status_string(status: int) -> str:
+    return lib.lp_status_string(status).decode()

@@ -1,0 +1,151 @@
+// C-ABI entry points: argument checking, then one launch per contraction.
+// Every rule checked here is stated next to the entry point in lp.h.
+#include <stdint.h>
+
+#include "lp_internal.hpp"
+
+namespace {
+
+constexpr int64_t kMaxChunks = (int64_t)1 << 31;   // kernels index 16-byte chunks in 32 bits
+constexpr int64_t kMaxDim = ((int64_t)1 << 31) - 1;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool is_fp4(int f) { return f == LP_MXFP4 || f == LP_NVFP4; }
+
+// Shape, pointer and alignment checks of one operand tensor.
+lp_status check_tensor(const lp_qtensor* t) {
+  if (t == nullptr) return LP_ERR_NULL;
+  if (t->fmt < LP_BF16 || t->fmt > LP_MXFP8) return LP_ERR_FORMAT;
+  if (t->batch < 0 || t->rows < 0 || t->cols < 0) return LP_ERR_SHAPE;
+  if (t->rows > kMaxDim || t->cols > kMaxDim || t->batch > kMaxDim) return LP_ERR_SHAPE;
+  const int axis = t->fmt == LP_BF16 ? -1 : t->scale_axis;
+  if (axis != -1 && axis != -2) return LP_ERR_FORMAT;
+  if (axis == -2 && t->fmt != LP_MXFP8) return LP_ERR_FORMAT;
+  if (t->cols % 16) return LP_ERR_SHAPE;
+  if ((t->fmt == LP_MXFP4 || (t->fmt == LP_MXFP8 && axis == -1)) && t->cols % 32) return LP_ERR_SHAPE;
+  if (t->fmt == LP_MXFP8 && axis == -2 && t->rows % 32) return LP_ERR_SHAPE;
+  const int64_t n = t->batch * t->rows * t->cols;
+  if (n / 16 >= kMaxChunks) return LP_ERR_SHAPE;
+  if (n == 0) return LP_OK;
+  if (t->codes == nullptr) return LP_ERR_NULL;
+  if (t->fmt != LP_BF16 && t->scales == nullptr) return LP_ERR_NULL;
+  if (t->fmt == LP_NVFP4 && t->tensor_scale == nullptr) return LP_ERR_NULL;
+  if (!aligned(t->codes, 16)) return LP_ERR_ALIGN;
+  if (t->fmt != LP_BF16 && !aligned(t->scales, 16)) return LP_ERR_ALIGN;
+  if (t->fmt == LP_NVFP4 && !aligned(t->tensor_scale, 4)) return LP_ERR_ALIGN;
+  return LP_OK;
+}
+
+lp_status hip_status(hipError_t e) { return e == hipSuccess ? LP_OK : LP_ERR_HIP; }
+
+// Checks shared by the linear and grouped backward.  `groups` is 0 for the
+// dense linear (then w->batch must be 1).
+lp_status check_bwd(const lp_qtensor* grad, const lp_qtensor* x, const lp_qtensor* w, void* grad_x, void* grad_w,
+                    int64_t groups) {
+  lp_status st = check_tensor(grad);
+  if (st != LP_OK) return st;
+  if (grad->batch != 1) return LP_ERR_SHAPE;
+  if (grad->fmt != LP_BF16 && !(grad->fmt == LP_MXFP8 && grad->scale_axis == -1)) return LP_ERR_FORMAT;
+  const int64_t M = grad->rows, N = grad->cols;
+  int64_t K = -1;
+  if (grad_x != nullptr) {
+    if ((st = check_tensor(w)) != LP_OK) return st;
+    if (w->batch != (groups ? groups : 1) || w->rows != N) return LP_ERR_SHAPE;
+    K = w->cols;
+  }
+  if (grad_w != nullptr) {
+    if (grad->fmt != LP_BF16) return LP_ERR_FORMAT;   // dW contracts grad over rows: bf16 only
+    if ((st = check_tensor(x)) != LP_OK) return st;
+    if (x->batch != 1 || x->rows != M) return LP_ERR_SHAPE;
+    if (K >= 0 && x->cols != K) return LP_ERR_SHAPE;
+    K = x->cols;
+  }
+  for (const lp_qtensor* t : {grad_x ? w : nullptr, grad_w ? x : nullptr}) {
+    if (t != nullptr && is_fp4(t->fmt) && t->cols % 32) return LP_ERR_SHAPE;
+  }
+  if (grad_x != nullptr && M * K > 0 && !aligned(grad_x, 16)) return LP_ERR_ALIGN;
+  if (grad_w != nullptr && N * K > 0 && !aligned(grad_w, 16)) return LP_ERR_ALIGN;
+  return LP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+lp_status lp_dequant(const lp_qtensor* src, void* dst, void* stream) {
+  lp_status st = check_tensor(src);
+  if (st != LP_OK) return st;
+  if (src->fmt == LP_BF16) return LP_ERR_FORMAT;
+  if (src->batch * src->rows * src->cols == 0) return LP_OK;
+  if (dst == nullptr) return LP_ERR_NULL;
+  if (!aligned(dst, 16)) return LP_ERR_ALIGN;
+  return hip_status(lp::launch_dequant(*src, dst, static_cast<hipStream_t>(stream)));
+}
+
+lp_status lp_mx_quant(const void* src, int64_t batch, int64_t rows, int64_t cols, int32_t axis, int32_t dst_fmt,
+                      void* codes, void* scales, void* stream) {
+  if (batch < 0 || rows < 0 || cols < 0 || batch > kMaxDim || rows > kMaxDim || cols > kMaxDim) return LP_ERR_SHAPE;
+  if (axis != -1 && axis != -2) return LP_ERR_FORMAT;
+  if (dst_fmt != LP_MXFP8 && dst_fmt != LP_MXFP4) return LP_ERR_FORMAT;
+  if (axis == -1 && cols % 32) return LP_ERR_SHAPE;
+  if (axis == -2 && (rows % 32 || cols % 8)) return LP_ERR_SHAPE;
+  const int64_t n = batch * rows * cols;
+  if (n / 16 >= kMaxChunks) return LP_ERR_SHAPE;
+  if (n == 0) return LP_OK;
+  if (src == nullptr || codes == nullptr || scales == nullptr) return LP_ERR_NULL;
+  if (!aligned(src, 16) || !aligned(codes, 16) || !aligned(scales, 16)) return LP_ERR_ALIGN;
+  return hip_status(lp::launch_mx_quant(src, batch, rows, cols, axis, dst_fmt, codes, scales,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+static lp_status run_bwd(const lp_qtensor* grad, const lp_qtensor* x, const lp_qtensor* w, const int32_t* offsets,
+                         int64_t groups, void* grad_x, void* grad_w, void* stream) {
+  const int64_t M = grad->rows, N = grad->cols;
+  const int64_t K = grad_x ? w->cols : x->cols;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (grad_x != nullptr && M * K > 0) {
+    lp::GemmCall c{false, grad, w, offsets, (int32_t)(groups ? groups : 1), M, N, K, grad_x};
+    hipError_t e = lp::launch_gemm(c, s);
+    if (e != hipSuccess) return LP_ERR_HIP;
+  }
+  if (grad_w != nullptr && N * K > 0) {
+    lp::GemmCall c{true, grad, x, offsets, (int32_t)(groups ? groups : 1), M, N, K, grad_w};
+    hipError_t e = lp::launch_gemm(c, s);
+    if (e != hipSuccess) return LP_ERR_HIP;
+  }
+  return LP_OK;
+}
+
+lp_status lp_linear_bwd(const lp_qtensor* grad_out, const lp_qtensor* x, const lp_qtensor* w, void* grad_x,
+                        void* grad_w, void* stream) {
+  if (grad_x == nullptr && grad_w == nullptr) return LP_OK;
+  lp_status st = check_bwd(grad_out, x, w, grad_x, grad_w, 0);
+  if (st != LP_OK) return st;
+  return run_bwd(grad_out, x, w, nullptr, 0, grad_x, grad_w, stream);
+}
+
+lp_status lp_grouped_bwd(const lp_qtensor* grad_out, const lp_qtensor* x, const lp_qtensor* w,
+                         const int32_t* offsets, int64_t groups, void* grad_x, void* grad_w, void* stream) {
+  if (grad_x == nullptr && grad_w == nullptr) return LP_OK;
+  if (groups < 1 || groups > 1024) return LP_ERR_SHAPE;
+  lp_status st = check_bwd(grad_out, x, w, grad_x, grad_w, groups);
+  if (st != LP_OK) return st;
+  if (offsets == nullptr) return LP_ERR_NULL;
+  if (!aligned(offsets, 4)) return LP_ERR_ALIGN;
+  return run_bwd(grad_out, x, w, offsets, groups, grad_x, grad_w, stream);
+}
+
+const char* lp_status_string(int32_t s) {
+  switch (s) {
+    case LP_OK: return "ok";
+    case LP_ERR_NULL: return "a required pointer is NULL";
+    case LP_ERR_SHAPE: return "operand sizes are invalid or disagree";
+    case LP_ERR_FORMAT: return "unsupported format or scale axis for this call";
+    case LP_ERR_ALIGN: return "a pointer breaks the alignment rule";
+    case LP_ERR_HIP: return "the HIP runtime reported a launch error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,55 @@
+// Internal interface between the C-ABI layer (lp_api.hip) and the kernel
+// translation units.  Not installed; callers use include/lp.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lp.h"
+
+namespace lp {
+
+// Unsigned division by a divisor fixed at launch (Granlund & Montgomery,
+// "Division by invariant integers using multiplication", round-up variant):
+// q = (umulhi(n, magic) + n) >> shift, exact for n, d < 2^31.
+struct FastDiv {
+  uint32_t d, magic, shift;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  FastDiv f;
+  f.d = d;
+  uint32_t s = 0;
+  while ((1ull << s) < d) ++s;
+  f.shift = s;
+  f.magic = (uint32_t)(((1ull << 32) * ((1ull << s) - d)) / d + 1);
+  return f;
+}
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
+  uint32_t t = __umulhi(n, f.magic);
+  return (t + n) >> f.shift;
+}
+
+// Launchers; each returns hipSuccess or the launch error.  Arguments were
+// validated by the caller.
+hipError_t launch_dequant(const lp_qtensor& src, void* dst, hipStream_t stream);
+hipError_t launch_mx_quant(const void* src, int64_t batch, int64_t rows, int64_t cols, int axis,
+                           int dst_fmt, void* codes, void* scales, hipStream_t stream);
+
+// One backward contraction (grad_X or grad_W) over `groups` groups.
+//   dx: C[m][k] = sum_n grad[m][n] * W[g][n][k]  (groups partition the rows m)
+//   dw: C[g][n][k] = sum_m grad[m][n] * X[m][k]  (groups partition the sum over m)
+// offsets == nullptr means one group spanning all M rows.
+struct GemmCall {
+  bool dw;
+  const lp_qtensor* grad;
+  const lp_qtensor* other;  // W for dx, X for dw
+  const int32_t* offsets;
+  int32_t groups;
+  int64_t M, N, K;
+  void* out;
+};
+hipError_t launch_gemm(const GemmCall& call, hipStream_t stream);
+
+}  // namespace lp

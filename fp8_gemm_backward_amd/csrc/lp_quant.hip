@@ -1,0 +1,218 @@
+// Dynamic MX quantization of bf16 (HBM-bound, bit-exact).
+//
+// "perf: defer mxfp8 backward quantization", MXFP8GMMFunction.op_dx and
+// MXFP8MatMul.backward: the backward re-quantizes the gradient along its
+// last axis and the weight along its reduction axis, one E8M0 scale per 32
+// elements (group_sizes [1, 1, 32]).
+//
+// Per block of 32: amax over |v| is taken on the bf16 bit patterns (integer
+// max of the magnitude bits, which also flags NaN / infinity as >= 0x7F80);
+// e = floor(log2 amax) - emax, clamped to [-127, 127], comes exactly from
+// the exponent field (or the leading mantissa bit of a subnormal); each
+// element is multiplied by 2^-e (exact), clamped to the format's maximum
+// (saturation) and rounded to nearest even by the hardware conversion.
+#include "lp_device.hpp"
+#include "lp_internal.hpp"
+
+namespace lp {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+// floor(log2 |v|) of a non-zero finite bf16 magnitude (bits & 0x7FFF).
+__device__ __forceinline__ int floor_log2_bf16(uint32_t mag) {
+  uint32_t e = mag >> 7;
+  return e ? (int)e - 127 : (31 - __builtin_clz(mag)) - 133;
+}
+
+struct BlockScale {
+  uint32_t byte;   // E8M0 scale byte
+  float inv;       // 2^-e as fp32 (exact)
+  bool bad;        // NaN or infinity in the block
+};
+
+template <bool kFp4>
+__device__ __forceinline__ BlockScale block_scale(uint32_t amax_mag) {
+  constexpr int kEmax = kFp4 ? 2 : 8;
+  BlockScale s;
+  s.bad = amax_mag >= 0x7F80u;
+  int e = (amax_mag == 0u || s.bad) ? -127 : floor_log2_bf16(amax_mag) - kEmax;
+  e = e < -127 ? -127 : (e > 127 ? 127 : e);
+  s.byte = s.bad ? 0xFFu : (uint32_t)(e + 127);
+  s.inv = __builtin_bit_cast(float, (uint32_t)(127 - e) << 23);   // 127-e in [8, 254]
+  return s;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
+
+// Two scaled values -> two E4M3 codes (low byte first) in a 16-bit result.
+__device__ __forceinline__ uint32_t to_e4m3x2(float a, float b) {
+  a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+  b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+  i16x2 old = {0, 0};
+  i16x2 r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(old, a, b, 1.0f, false);
+  return (uint32_t)(uint16_t)r[0];
+}
+
+// Two scaled values -> one byte of two E2M1 codes (first in the low nibble).
+__device__ __forceinline__ uint32_t to_e2m1x2(float a, float b) {
+  a = __builtin_amdgcn_fmed3f(a, -6.0f, 6.0f);
+  b = __builtin_amdgcn_fmed3f(b, -6.0f, 6.0f);
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a, b, 1.0f, 0) & 0xFFu;
+}
+
+// NaN codes of a bad block: E4M3 0x7F with each element's sign; E2M1 0.
+__device__ __forceinline__ uint32_t nan_e4m3x2(uint32_t w) {
+  return 0x7F7Fu | ((w >> 8) & 0x80u) | ((w >> 16) & 0x8000u);
+}
+
+// Axis -1: thread i quantizes block i = elements [32i, 32i+32).
+template <bool kFp4>
+__global__ __launch_bounds__(kThreads) void mx_quant_cols(const u32x4* __restrict__ src,
+                                                          u32x4* __restrict__ codes,
+                                                          uint8_t* __restrict__ scales, uint32_t nblocks) {
+  uint32_t i = blockIdx.x * kThreads + threadIdx.x;
+  if (i >= nblocks) return;
+  u32x4 v[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) v[j] = __builtin_nontemporal_load(src + 4 * (size_t)i + j);
+  uint32_t amax = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t w = v[j][k] & 0x7FFF7FFFu;
+      amax = umax(amax, umax(w & 0xFFFFu, w >> 16));
+    }
+  BlockScale s = block_scale<kFp4>(amax);
+  scales[i] = (uint8_t)s.byte;
+  if constexpr (!kFp4) {
+    uint32_t o[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int k = 0; k < 4; k += 2) {
+        uint32_t w0 = v[j][k], w1 = v[j][k + 1];
+        uint32_t lo = s.bad ? nan_e4m3x2(w0) : to_e4m3x2(bf16_lo(w0) * s.inv, bf16_hi(w0) * s.inv);
+        uint32_t hi = s.bad ? nan_e4m3x2(w1) : to_e4m3x2(bf16_lo(w1) * s.inv, bf16_hi(w1) * s.inv);
+        o[2 * j + k / 2] = lo | (hi << 16);
+      }
+    codes[2 * (size_t)i] = u32x4{o[0], o[1], o[2], o[3]};
+    codes[2 * (size_t)i + 1] = u32x4{o[4], o[5], o[6], o[7]};
+  } else {
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t b0 = to_e2m1x2(bf16_lo(v[j][0]) * s.inv, bf16_hi(v[j][0]) * s.inv);
+      uint32_t b1 = to_e2m1x2(bf16_lo(v[j][1]) * s.inv, bf16_hi(v[j][1]) * s.inv);
+      uint32_t b2 = to_e2m1x2(bf16_lo(v[j][2]) * s.inv, bf16_hi(v[j][2]) * s.inv);
+      uint32_t b3 = to_e2m1x2(bf16_lo(v[j][3]) * s.inv, bf16_hi(v[j][3]) * s.inv);
+      o[j] = s.bad ? 0u : (b0 | (b1 << 8) | (b2 << 16) | (b3 << 24));
+    }
+    codes[i] = u32x4{o[0], o[1], o[2], o[3]};
+  }
+}
+
+// Axis -2: thread i owns a strip of 32 rows x 8 columns; every column is its
+// own scale block, so the amax is lane-local and consecutive lanes read
+// consecutive 16-byte column chunks of each row.
+template <bool kFp4>
+__global__ __launch_bounds__(kThreads) void mx_quant_rows(const uint16_t* __restrict__ src,
+                                                          uint8_t* __restrict__ codes,
+                                                          uint8_t* __restrict__ scales, uint32_t nstrips,
+                                                          FastDiv strips_per_row, uint32_t cols) {
+  uint32_t i = blockIdx.x * kThreads + threadIdx.x;
+  if (i >= nstrips) return;
+  uint32_t rb = fdiv(i, strips_per_row);                 // block of 32 rows over batch*rows
+  uint32_t c0 = (i - rb * strips_per_row.d) * 8u;
+  const uint16_t* base = src + (size_t)rb * 32u * cols + c0;
+  u32x4 v[32];
+#pragma unroll
+  for (int r = 0; r < 32; ++r) v[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (size_t)r * cols));
+  uint32_t amax[4] = {0, 0, 0, 0};   // packed pairs of column maxima
+#pragma unroll
+  for (int r = 0; r < 32; ++r)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t w = v[r][k] & 0x7FFF7FFFu;
+      amax[k] = umax(amax[k] & 0xFFFFu, w & 0xFFFFu) | (umax(amax[k] >> 16, w >> 16) << 16);
+    }
+  BlockScale s[8];
+  uint32_t sbytes[2] = {0, 0};
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    s[c] = block_scale<kFp4>((amax[c >> 1] >> (16 * (c & 1))) & 0xFFFFu);
+    sbytes[c >> 2] |= s[c].byte << (8 * (c & 3));
+  }
+  *reinterpret_cast<u32x2*>(scales + (size_t)rb * cols + c0) = u32x2{sbytes[0], sbytes[1]};
+  uint8_t* out = codes + (size_t)rb * 32u * (kFp4 ? cols / 2 : cols) + (kFp4 ? c0 / 2 : c0);
+#pragma unroll
+  for (int r = 0; r < 32; ++r) {
+    if constexpr (!kFp4) {
+      uint32_t o[2];
+#pragma unroll
+      for (int k = 0; k < 4; k += 2) {
+        uint32_t w0 = v[r][k], w1 = v[r][k + 1];
+        int c = 2 * k;
+        uint32_t p0 = to_e4m3x2(bf16_lo(w0) * s[c].inv, bf16_hi(w0) * s[c + 1].inv);
+        uint32_t p1 = to_e4m3x2(bf16_lo(w1) * s[c + 2].inv, bf16_hi(w1) * s[c + 3].inv);
+        uint32_t b0 = s[c].bad ? (0x7Fu | ((w0 >> 8) & 0x80u)) : (p0 & 0xFFu);
+        uint32_t b1 = s[c + 1].bad ? (0x7Fu | ((w0 >> 24) & 0x80u)) : (p0 >> 8);
+        uint32_t b2 = s[c + 2].bad ? (0x7Fu | ((w1 >> 8) & 0x80u)) : (p1 & 0xFFu);
+        uint32_t b3 = s[c + 3].bad ? (0x7Fu | ((w1 >> 24) & 0x80u)) : (p1 >> 8);
+        o[k / 2] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+      }
+      *reinterpret_cast<u32x2*>(out + (size_t)r * cols) = u32x2{o[0], o[1]};
+    } else {
+      uint32_t o = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        uint32_t w = v[r][k];
+        int c = 2 * k;
+        uint32_t b = to_e2m1x2(bf16_lo(w) * s[c].inv, bf16_hi(w) * s[c + 1].inv);
+        uint32_t lo = s[c].bad ? 0u : (b & 0xFu);
+        uint32_t hi = s[c + 1].bad ? 0u : (b >> 4);
+        o |= (lo | (hi << 4)) << (8 * k);
+      }
+      *reinterpret_cast<uint32_t*>(out + (size_t)r * (cols / 2)) = o;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_mx_quant(const void* src, int64_t batch, int64_t rows, int64_t cols, int axis, int dst_fmt,
+                           void* codes, void* scales, hipStream_t stream) {
+  const int64_t n = batch * rows * cols;
+  if (n == 0) return hipSuccess;
+  const bool fp4 = dst_fmt == LP_MXFP4;
+  if (axis == -1) {
+    const uint32_t nblocks = (uint32_t)(n / 32);
+    const dim3 grid((nblocks + kThreads - 1) / kThreads), block(kThreads);
+    auto s = static_cast<const u32x4*>(src);
+    auto c = static_cast<u32x4*>(codes);
+    auto sc = static_cast<uint8_t*>(scales);
+    if (fp4)
+      mx_quant_cols<true><<<grid, block, 0, stream>>>(s, c, sc, nblocks);
+    else
+      mx_quant_cols<false><<<grid, block, 0, stream>>>(s, c, sc, nblocks);
+  } else {
+    const uint32_t spr = (uint32_t)(cols / 8);
+    const uint32_t nstrips = (uint32_t)(batch * (rows / 32) * spr);
+    const dim3 grid((nstrips + kThreads - 1) / kThreads), block(kThreads);
+    auto s = static_cast<const uint16_t*>(src);
+    auto c = static_cast<uint8_t*>(codes);
+    auto sc = static_cast<uint8_t*>(scales);
+    if (fp4)
+      mx_quant_rows<true><<<grid, block, 0, stream>>>(s, c, sc, nstrips, make_fastdiv(spr), (uint32_t)cols);
+    else
+      mx_quant_rows<false><<<grid, block, 0, stream>>>(s, c, sc, nstrips, make_fastdiv(spr), (uint32_t)cols);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace lp

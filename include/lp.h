@@ -1,0 +1,207 @@
+/*
+ * lp.h - backward pass of block-scaled low-precision linear and grouped
+ * (per-expert) matmuls on AMD Instinct MI355X (gfx950).
+ *
+ * The saved forward operands are block-scaled low-precision tensors; the
+ * backward dequantizes them to bf16 and computes, in bf16 x bf16 -> fp32
+ * contractions:
+ *
+ *     grad_X = grad_out @ W          [M,N] x [N,K] -> [M,K]
+ *     grad_W = grad_out^T @ X        [N,M] x [M,K] -> [N,K]
+ *
+ * ("Add Autograd Backward Support for FP4 GEMM Custom Ops", Implementation
+ * Method: dequantize-then-compute in BF16; "Train adapters on top of FP8
+ * weights", FP8LinearFunction.backward and FP8GroupedMatmulFunction.backward;
+ * "perf: defer mxfp8 backward quantization", MXFP8GMMFunction.op_dx.)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every pointer to tensor data is a DEVICE pointer.  The caller allocates
+ *   and owns every buffer; the library allocates nothing, frees nothing and
+ *   keeps no pointer after a call returns.  It holds no state between calls
+ *   and is safe to call from several host threads.
+ * - Work is enqueued on `stream` (a hipStream_t; NULL is the default
+ *   stream) and runs asynchronously.  The status covers argument checking
+ *   and the launch only.  On any error nothing is enqueued and no output
+ *   is written.
+ * - Tensors are dense and row-major.  Element (b, r, c) of a [batch][rows][cols]
+ *   tensor is at offset (b*rows + r)*cols + c, in units of elements.
+ * - Codes, scales and outputs must be 16-byte aligned; an NVFP4 tensor scale
+ *   4-byte aligned.  A pointer may be NULL only when its tensor is empty.
+ *
+ * Formats (lp_fmt)
+ * ----------------
+ *   LP_BF16      bf16 values, 2 bytes each.  No scales.
+ *   LP_MXFP4     E2M1 codes packed two per byte along cols (element 2j in
+ *                the low nibble, 2j+1 in the high nibble), one E8M0 scale
+ *                byte per 32 elements along cols: scales[batch][rows][cols/32].
+ *   LP_NVFP4     E2M1 codes packed as LP_MXFP4; one E4M3 scale byte per 16
+ *                along cols: scales[batch][rows][cols/16]; plus one fp32
+ *                tensor scale (a decode multiplier, read from device memory).
+ *   LP_FP8_B128  E4M3 codes, one byte each; fp32 inverse scales (decode
+ *                multipliers) per 128x128 block:
+ *                scales[batch][ceil(rows/128)][ceil(cols/128)], blocks cut at
+ *                the tensor edge ("Train adapters on top of FP8 weights",
+ *                _dequantize_fp8_weight).
+ *   LP_MXFP8     E4M3 codes, one byte each; one E8M0 scale byte per 32
+ *                elements along `scale_axis`: -1 -> scales[batch][rows][cols/32],
+ *                -2 -> scales[batch][rows/32][cols] ("perf: defer mxfp8
+ *                backward quantization", npu_dynamic_mx_quant axis argument
+ *                and group_sizes [1, 1, 32]).
+ *
+ * Element values: E2M1 (1 sign, 2 exponent bits with bias 1, 1 mantissa bit:
+ * 0, 0.5, 1, 1.5, 2, 3, 4, 6), E4M3 (bias 7, max 448, no infinities,
+ * S.1111.111 = NaN), E8M0 (2^(byte-127), 0xFF = NaN).
+ *
+ * Decoded value: bf16_rne(fp32_rne(code_value * S)) where S is the fp32
+ * block multiplier (NVFP4: S = fp32_rne(E4M3(block byte) * tensor_scale)).
+ * A NaN result is 0x7FC0 carrying the code's sign bit.
+ */
+#ifndef LP_H
+#define LP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LP_OK = 0,
+  LP_ERR_NULL = 1,    /* a required pointer is NULL                              */
+  LP_ERR_SHAPE = 2,   /* negative size, operand sizes disagree, or a block or
+                         packing divisibility rule is broken                    */
+  LP_ERR_FORMAT = 3,  /* a format / scale-axis combination this call does not
+                         support                                                */
+  LP_ERR_ALIGN = 4,   /* a pointer breaks the alignment rule                     */
+  LP_ERR_HIP = 5      /* the HIP runtime reported an error at launch             */
+} lp_status;
+
+typedef enum {
+  LP_BF16 = 0,
+  LP_MXFP4 = 1,
+  LP_NVFP4 = 2,
+  LP_FP8_B128 = 3,
+  LP_MXFP8 = 4
+} lp_fmt;
+
+/* A (possibly block-scaled) tensor of logical shape [batch][rows][cols]. */
+typedef struct {
+  int32_t fmt;               /* lp_fmt                                          */
+  int32_t scale_axis;        /* -1: scale blocks run along cols; -2: along rows
+                                (LP_MXFP8 only; ignored for LP_BF16)            */
+  int64_t batch;             /* groups for a grouped weight, else 1             */
+  int64_t rows;
+  int64_t cols;              /* logical elements (not packed bytes)             */
+  const void* codes;         /* device pointer, layout per format above          */
+  const void* scales;        /* device pointer, NULL for LP_BF16                 */
+  const float* tensor_scale; /* device pointer to one fp32, LP_NVFP4 only       */
+} lp_qtensor;
+
+/*
+ * lp_dequant - decode a block-scaled tensor to bf16.
+ *
+ * Cites: "Add Autograd Backward Support for FP4 GEMM Custom Ops" (the backward
+ * dequantizes the saved packed FP4 inputs to BF16); "Train adapters on top of
+ * FP8 weights", _dequantize_fp8_weight (E4M3 times its 128x128-block inverse
+ * scale).
+ *
+ * src       any format except LP_BF16.  Divisibility: cols % 32 == 0 for
+ *           LP_MXFP4 and for LP_MXFP8 with scale_axis -1; rows % 32 == 0 and
+ *           cols % 16 == 0 for LP_MXFP8 with scale_axis -2; cols % 16 == 0 for
+ *           LP_NVFP4 and LP_FP8_B128 (rows arbitrary; partial 128-blocks are
+ *           cut at the edge).
+ * dst_bf16  device bf16 output [batch][rows][cols].
+ * Result is bit-exact: the rule in the header comment above.
+ */
+lp_status lp_dequant(const lp_qtensor* src, void* dst_bf16, void* stream);
+
+/*
+ * lp_mx_quant - dynamic MX quantization of a bf16 tensor along one axis.
+ *
+ * Cites: "perf: defer mxfp8 backward quantization", MXFP8GMMFunction.op_dx and
+ * MXFP8MatMul.backward (npu_dynamic_mx_quant of the gradient along -1 and of
+ * the weight along its reduction axis; E8M0 scale per 32).
+ *
+ * src_bf16    device bf16 [batch][rows][cols].
+ * axis        -1: blocks of 32 along cols (cols % 32 == 0);
+ *             -2: blocks of 32 along rows (rows % 32 == 0, cols % 8 == 0).
+ * dst_fmt     LP_MXFP8 (E4M3 elements) or LP_MXFP4 (E2M1, packed along cols;
+ *             cols must be even).
+ * dst_codes   device [batch][rows][cols] bytes (LP_MXFP8) or [batch][rows][cols/2].
+ * dst_scales  device E8M0 bytes [batch][rows][cols/32] (axis -1) or
+ *             [batch][rows/32][cols] (axis -2).
+ * Per block: amax = max |v|; e = floor(log2 amax) - emax (8 for E4M3, 2 for
+ * E2M1) clamped to [-127, 127]; scale byte = e + 127; each element is
+ * v * 2^-e rounded to nearest (ties to even) on the element grid, saturated
+ * to +-448 / +-6, sign kept.  A block holding a NaN or an infinity gets
+ * scale 0xFF and NaN codes (E4M3 0x7F | sign; E2M1 codes 0); an all-zero
+ * block gets scale 0 and signed-zero codes.  Bit-exact.
+ */
+lp_status lp_mx_quant(const void* src_bf16, int64_t batch, int64_t rows, int64_t cols,
+                      int32_t axis, int32_t dst_fmt, void* dst_codes, void* dst_scales,
+                      void* stream);
+
+/*
+ * lp_linear_bwd - backward of a linear layer y = x @ W^T with saved
+ * block-scaled operands.
+ *
+ * Cites: "Add Autograd Backward Support for FP4 GEMM Custom Ops",
+ * Implementation Method (grad_X = grad_output @ W_bf16, grad_W =
+ * grad_output.T @ X_bf16); "Train adapters on top of FP8 weights",
+ * FP8LinearFunction.backward (frozen weight: grad_X only); "AstrAI fp8.py",
+ * _LinearFp8.backward (each output is computed only when it is needed).
+ *
+ * grad_out  [M][N]: LP_BF16, or LP_MXFP8 with scale_axis -1 (needs grad_w == NULL).
+ * x         [M][K] saved input, or NULL when grad_w == NULL.
+ * w         [N][K] saved weight, or NULL when grad_x == NULL.
+ *           x and w: LP_BF16, LP_MXFP4, LP_NVFP4 (scale_axis -1), LP_FP8_B128,
+ *           or LP_MXFP8 (scale_axis -1 or -2).
+ * grad_x    device bf16 [M][K], or NULL to skip grad_X.
+ * grad_w    device bf16 [N][K], or NULL to skip grad_W.
+ * Sizes: M >= 0 arbitrary; N % 16 == 0, K % 16 == 0, plus each operand's
+ * block rule (K % 32 for FP4 and MX along K; N % 32 for MXFP8 grad_out and
+ * for MXFP8 w with scale_axis -2; M % 32 for MXFP8 x with scale_axis -2).
+ * Accumulation is fp32; outputs are rounded to bf16 (nearest even).
+ */
+lp_status lp_linear_bwd(const lp_qtensor* grad_out, const lp_qtensor* x, const lp_qtensor* w,
+                        void* grad_x, void* grad_w, void* stream);
+
+/*
+ * lp_grouped_bwd - backward of a grouped (per-expert) matmul.
+ *
+ * Cites: "Train adapters on top of FP8 weights", FP8GroupedMatmulFunction.
+ * backward ((S, output_dim) @ grouped (num_experts, output_dim, input_dim)
+ * -> (S, input_dim)) and FP8GroupedLinear.forward (int32 cumulative end
+ * offsets); the EP-sentinel comment of fp8_grouped_mm_experts_forward (rows
+ * past offsets[G-1] are skipped and left unwritten); "perf: defer mxfp8
+ * backward quantization", MXFP8GMMFunction.op_dx.
+ *
+ * offsets   device int32 [groups], cumulative END row of each group; group g
+ *           owns rows [offsets[g-1], offsets[g]) with offsets[-1] = 0.  The
+ *           caller guarantees 0 <= offsets[0] <= ... <= offsets[G-1] <= M.  The
+ *           kernels use end_g = clamp(offsets[g], end_{g-1}, M) (end_{-1} = 0),
+ *           which equals offsets[g] for a valid array and keeps a bad one from
+ *           making them read or write out of bounds.  Offsets are never read
+ *           on the host (no synchronisation).
+ * grad_out  [M][N] as for lp_linear_bwd.
+ * x         [M][K] (rows grouped like grad_out), or NULL when grad_w == NULL.
+ * w         [groups][N][K] (batch == groups), or NULL when grad_x == NULL.
+ * grad_x    device bf16 [M][K] or NULL.  Rows at or past offsets[G-1] are NOT
+ *           written.
+ * grad_w    device bf16 [groups][N][K] or NULL.  An empty group's slice is
+ *           written with zeros (the empty sum).
+ * Size and format rules as for lp_linear_bwd; 1 <= groups <= 1024.
+ */
+lp_status lp_grouped_bwd(const lp_qtensor* grad_out, const lp_qtensor* x, const lp_qtensor* w,
+                         const int32_t* offsets, int64_t groups, void* grad_x, void* grad_w,
+                         void* stream);
+
+/* A static, human-readable name for a status code. */
+const char* lp_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LP_H */

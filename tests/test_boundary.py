@@ -1,0 +1,105 @@
+"""The C-ABI library on the host: it loads, exports every function that
+include/lp.h declares, and rejects bad arguments with the documented status
+before touching the GPU (CPU only; no kernel is launched)."""
+import ctypes
+
+import pytest
+
+import fp8_gemm_backward_amd as lp
+from fp8_gemm_backward_amd import _QTensorC
+
+OK, NULL, SHAPE, FORMAT, ALIGN = 0, 1, 2, 3, 4
+FAKE = 0x10000          # 16-byte aligned stand-in pointer; never dereferenced here
+
+
+def test_library_exports_every_header_function():
+    names = lp.header_functions()
+    assert set(names) == {"lp_dequant", "lp_mx_quant", "lp_linear_bwd", "lp_grouped_bwd", "lp_status_string"}
+    for n in names:
+        assert hasattr(lp.lib, n), n
+
+
+def test_status_strings():
+    assert lp.lp_status_string(0) == "ok"
+    for s in range(1, 6):
+        assert lp.lp_status_string(s) not in ("ok", "unknown status")
+    assert lp.lp_status_string(99) == "unknown status"
+
+
+def q(fmt, rows, cols, batch=1, axis=-1, codes=FAKE, scales=FAKE, ts=FAKE):
+    return _QTensorC(lp.FMT[fmt], axis, batch, rows, cols, codes, scales, ts)
+
+
+def dq(t, dst=FAKE):
+    return lp.lib.lp_dequant(ctypes.byref(t) if t is not None else None, dst, None)
+
+
+@pytest.mark.parametrize("t,dst,expect", [
+    (None, FAKE, NULL),
+    (q("mxfp4", 4, 64, codes=None), FAKE, NULL),
+    (q("mxfp4", 4, 64, scales=None), FAKE, NULL),
+    (q("nvfp4", 4, 64, ts=None), FAKE, NULL),
+    (q("mxfp4", 4, 64), None, NULL),
+    (q("mxfp4", 4, 48), FAKE, SHAPE),            # MX blocks of 32 along cols
+    (q("fp8_b128", 4, 40), FAKE, SHAPE),         # cols % 16
+    (q("mxfp8", 40, 64, axis=-2), FAKE, SHAPE),  # rows % 32 along rows
+    (q("mxfp8", -1, 64), FAKE, SHAPE),
+    (q("bf16", 4, 64), FAKE, FORMAT),            # nothing to decode
+    (q("mxfp4", 32, 64, axis=-2), FAKE, FORMAT),  # only MXFP8 scales along rows
+    (_QTensorC(9, -1, 1, 4, 64, FAKE, FAKE, FAKE), FAKE, FORMAT),
+    (q("mxfp4", 4, 64, codes=FAKE + 8), FAKE, ALIGN),
+    (q("mxfp4", 4, 64, scales=FAKE + 4), FAKE, ALIGN),
+    (q("mxfp4", 4, 64), FAKE + 2, ALIGN),
+    (q("mxfp4", 0, 64, codes=None, scales=None), None, OK),   # empty: nothing to do
+])
+def test_dequant_rejects(t, dst, expect):
+    assert dq(t, dst) == expect
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((None, 1, 32, 32, -1, lp.FMT["mxfp8"], FAKE, FAKE), NULL),
+    ((FAKE, 1, 32, 48, -1, lp.FMT["mxfp8"], FAKE, FAKE), SHAPE),
+    ((FAKE, 1, 48, 32, -2, lp.FMT["mxfp8"], FAKE, FAKE), SHAPE),
+    ((FAKE, 1, 32, 36, -2, lp.FMT["mxfp8"], FAKE, FAKE), SHAPE),
+    ((FAKE, 1, 32, 32, 0, lp.FMT["mxfp8"], FAKE, FAKE), FORMAT),
+    ((FAKE, 1, 32, 32, -1, lp.FMT["nvfp4"], FAKE, FAKE), FORMAT),
+    ((FAKE + 8, 1, 32, 32, -1, lp.FMT["mxfp8"], FAKE, FAKE), ALIGN),
+    ((None, 1, 0, 32, -1, lp.FMT["mxfp8"], None, None), OK),
+])
+def test_mx_quant_rejects(args, expect):
+    assert lp.lib.lp_mx_quant(*args, None) == expect
+
+
+def lin(g, x, w, dx=FAKE, dw=FAKE):
+    ref = lambda t: ctypes.byref(t) if t is not None else None  # noqa: E731
+    return lp.lib.lp_linear_bwd(ref(g), ref(x), ref(w), dx, dw, None)
+
+
+@pytest.mark.parametrize("g,x,w,dx,dw,expect", [
+    (q("bf16", 64, 128), q("mxfp4", 64, 128), q("mxfp4", 128, 128), None, None, OK),   # nothing asked
+    (None, q("mxfp4", 64, 128), q("mxfp4", 128, 128), FAKE, FAKE, NULL),
+    (q("bf16", 64, 128), None, q("mxfp4", 128, 128), FAKE, FAKE, NULL),        # dW needs x
+    (q("bf16", 64, 128), q("mxfp4", 64, 128), None, FAKE, FAKE, NULL),         # dX needs w
+    (q("bf16", 64, 128), q("mxfp4", 64, 128), q("mxfp4", 64, 128), FAKE, None, SHAPE),   # w rows != N
+    (q("bf16", 64, 128), q("mxfp4", 32, 128), q("mxfp4", 128, 128), None, FAKE, SHAPE),  # x rows != M
+    (q("bf16", 64, 128), q("mxfp4", 64, 96), q("mxfp4", 128, 128), FAKE, FAKE, SHAPE),   # K disagrees
+    (q("bf16", 64, 120), q("mxfp4", 64, 128), q("mxfp4", 120, 128), FAKE, FAKE, SHAPE),  # N % 16
+    (q("nvfp4", 64, 128), q("mxfp4", 64, 128), q("mxfp4", 128, 128), FAKE, None, FORMAT),  # grad format
+    (q("mxfp8", 64, 128), q("mxfp4", 64, 128), q("mxfp4", 128, 128), None, FAKE, FORMAT),  # MXFP8 grad, dW
+    (q("bf16", 64, 128), q("mxfp4", 64, 128), q("nvfp4", 128, 48), FAKE, None, SHAPE),   # FP4 K % 32
+    (q("bf16", 64, 128), q("mxfp4", 64, 128), q("mxfp4", 128, 128, batch=2), FAKE, None, SHAPE),
+    (q("bf16", 64, 128), q("mxfp4", 64, 128), q("mxfp4", 128, 128), FAKE + 8, None, ALIGN),
+])
+def test_linear_bwd_rejects(g, x, w, dx, dw, expect):
+    assert lin(g, x, w, dx, dw) == expect
+
+
+def test_grouped_bwd_rejects():
+    g, x, w = q("bf16", 64, 128), q("mxfp4", 64, 128), q("mxfp4", 128, 128, batch=4)
+    call = lambda off, G, w=w: lp.lib.lp_grouped_bwd(  # noqa: E731
+        ctypes.byref(g), ctypes.byref(x), ctypes.byref(w), off, G, FAKE, FAKE, None)
+    assert call(FAKE, 0) == SHAPE
+    assert call(FAKE, 1025) == SHAPE
+    assert call(None, 4) == NULL
+    assert call(FAKE + 2, 4) == ALIGN
+    assert call(FAKE, 3) == SHAPE          # w batch must equal groups

@@ -1,0 +1,223 @@
+"""lp_linear_bwd / lp_grouped_bwd against the fp64 oracle (GPU).
+
+Tolerance on every output tensor: relative Frobenius error <= 5e-3 and
+max |error| <= 1e-2 * max |reference|; both sides consume the same
+quantized operands, so the bound covers only accumulation order and the
+final bf16 rounding (about 1e-3 relative on its own).
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from gpu_util import assert_bits_equal, assert_close, bf16_dev, bits_host, quantize
+from oracle import formats as F
+from oracle import gemm as O
+
+pytestmark = pytest.mark.gpu
+
+FORMATS = [("bf16", -1), ("mxfp4", -1), ("nvfp4", -1), ("fp8_b128", -1), ("mxfp8", -1), ("mxfp8", -2)]
+
+
+def _grad(lp, number, M, N, fmt="bf16"):
+    bits = W.bf16_bits(W.normal_f32(number, "grad", (M, N), 1.0))
+    if fmt == "bf16":
+        return lp.QTensor("bf16", bf16_dev(bits), shape=(1, M, N)), bits
+    q, deq = quantize(lp, "mxfp8", F.bf16_bits_to_f64(bits).astype(np.float32)[None], axis=-1)
+    return q, deq[0]
+
+
+def _operand(lp, number, tensor, shape, fmt, axis, sigma=1.0):
+    vals = W.normal_f32(number, tensor, shape, sigma)
+    q, deq = quantize(lp, fmt, vals, axis)
+    return q, deq
+
+
+@pytest.mark.parametrize("fmt,axis", FORMATS)
+def test_linear_small_ragged(lp, fmt, axis):
+    """M = 300 (ragged), N = 320, K = 288: several tiles, partial tiles in
+    every dimension, the narrow-tile configuration."""
+    M, N, K = 300, 320, 288
+    if fmt == "mxfp8" and axis == -2:
+        M = 320                       # X scales along rows need M % 32
+    g, gb = _grad(lp, 31, M, N)
+    x, xd = _operand(lp, 31, "x", (M, K), fmt, axis)
+    w, wd = _operand(lp, 31, "w", (N, K), fmt, axis)
+    dx, dw = lp.lp_linear_bwd(g, x, w)
+    torch.cuda.synchronize()
+    assert_close(dx, O.linear_dx(gb, wd[0]), f"{fmt}{axis} dX")
+    assert_close(dw, O.linear_dw(gb, xd[0]), f"{fmt}{axis} dW")
+
+
+@pytest.mark.parametrize("fmt,axis", FORMATS)
+def test_linear_wide_tiles(lp, fmt, axis):
+    """Shapes that select the 256x256 configuration for both products:
+    dX 4100 x 4096 (ragged M) over N = 272; dW 4096 x 4096 over M = 160."""
+    g, gb = _grad(lp, 32, 4100, 272)
+    w, wd = _operand(lp, 32, "w", (272, 4096), fmt, -1 if axis == -2 else axis)
+    dx, _ = lp.lp_linear_bwd(g, None, w, need_dw=False)
+    g2, gb2 = _grad(lp, 33, 160, 4096)
+    x, xd = _operand(lp, 33, "x", (160, 4096), fmt, axis)
+    _, dw = lp.lp_linear_bwd(g2, x, None, need_dx=False)
+    torch.cuda.synchronize()
+    assert_close(dx, O.linear_dx(gb, wd[0]), f"{fmt} dX")
+    assert_close(dw, O.linear_dw(gb2, xd[0]), f"{fmt}{axis} dW")
+
+
+def test_linear_mxfp8_grad(lp):
+    """MX-quantized gradient (along its last axis) times an MXFP8 weight
+    quantized along its reduction axis, as in the deferred backward."""
+    M, N, K = 520, 384, 448
+    g, gd = _grad(lp, 34, M, N, fmt="mxfp8")
+    w, wd = _operand(lp, 34, "w", (N, K), "mxfp8", -2, sigma=0.02)
+    dx, _ = lp.lp_linear_bwd(g, None, w, need_dw=False)
+    torch.cuda.synchronize()
+    assert_close(dx, O.linear_dx(gd, wd[0]), "mxfp8 x mxfp8 dX")
+
+
+def _sentinel(shape):
+    return torch.full(shape, -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)   # 0xFFFF (NaN)
+
+
+@pytest.mark.parametrize("fmt,axis", [("mxfp4", -1), ("fp8_b128", -1), ("nvfp4", -1), ("mxfp8", -2)])
+def test_grouped_edges(lp, fmt, axis):
+    """Five groups: an empty one, one smaller than a tile, ragged ends, and
+    rows past the last offset that must keep their sentinel value."""
+    M, N, K, G = 700, 256, 320, 5
+    sizes = [130, 0, 17, 300, 203]            # sum 650 < M: rows 650.. untouched
+    offsets = W.cumulative_ends(sizes)
+    g, gb = _grad(lp, 35, M, N)
+    x, xd = _operand(lp, 35, "x", (M, K), fmt, -1 if axis == -2 else axis)
+    w, wd = _operand(lp, 35, "w", (G, N, K), fmt, axis)
+    off = torch.from_numpy(offsets).cuda()
+    dx0 = _sentinel((M, K))
+    dw0 = _sentinel((G, N, K))
+    dx, dw = lp.lp_grouped_bwd(g, x, w, off, grad_x=dx0, grad_w=dw0)
+    torch.cuda.synchronize()
+    ref_dx, end = O.grouped_dx(gb, wd, offsets)
+    ref_dw = O.grouped_dw(gb, xd[0], offsets)
+    assert_close(dx[:end], ref_dx[:end], f"{fmt} grouped dX")
+    assert np.all(bits_host(dx[end:]) == 0xFFFF), "rows past the last offset were written"
+    assert_close(dw, ref_dw, f"{fmt} grouped dW")
+    assert np.all(bits_host(dw[1]) == 0), "empty group's dW is not zero"
+
+
+def test_grouped_one_group_equals_linear(lp):
+    """One group spanning all rows gives bit-identical results to the linear
+    backward (same kernels, same tile order)."""
+    M, N, K = 600, 256, 512
+    g, _ = _grad(lp, 36, M, N)
+    x, _ = _operand(lp, 36, "x", (M, K), "mxfp4", -1)
+    w, _ = _operand(lp, 36, "w", (1, N, K), "mxfp4", -1)
+    off = torch.tensor([M], dtype=torch.int32, device="cuda")
+    dx1, dw1 = lp.lp_grouped_bwd(g, x, w, off)
+    dx2, dw2 = lp.lp_linear_bwd(g, x, w)
+    torch.cuda.synchronize()
+    assert_bits_equal(bits_host(dx1), bits_host(dx2), "dX")
+    assert_bits_equal(bits_host(dw1)[0], bits_host(dw2), "dW")
+
+
+def test_grouped_bad_offsets_are_clamped(lp):
+    """Offsets out of order or past M are clamped (end_g = clamp(o_g,
+    end_{g-1}, M)): the kernels stay in bounds and compute those groups."""
+    M, N, K, G = 256, 128, 256, 4
+    offsets = np.array([100, 40, 9999, 300], dtype=np.int32)   # -> ends 100, 100, 256, 256
+    g, gb = _grad(lp, 37, M, N)
+    x, xd = _operand(lp, 37, "x", (M, K), "bf16", -1)
+    w, wd = _operand(lp, 37, "w", (G, N, K), "bf16", -1)
+    dx, dw = lp.lp_grouped_bwd(g, x, w, torch.from_numpy(offsets).cuda())
+    torch.cuda.synchronize()
+    clamped = np.array([100, 100, 256, 256], dtype=np.int32)
+    assert_close(dx, O.grouped_dx(gb, wd, clamped)[0], "dX")
+    assert_close(dw, O.grouped_dw(gb, xd[0], clamped), "dW")
+
+
+def test_empty_tokens(lp):
+    g = lp.QTensor("bf16", torch.empty((0, 128), dtype=torch.bfloat16, device="cuda"), shape=(1, 0, 128))
+    w, _ = _operand(lp, 38, "w", (128, 64), "mxfp4", -1)
+    dx, _ = lp.lp_linear_bwd(g, None, w, need_dw=False)
+    assert dx.shape == (0, 64)
+
+
+# ------------------------------------------------------------------ full sizes, sampled
+
+def _sample_rows(n, k, seed):
+    return np.sort(W.rng(seed, "x").choice(n, size=min(k, n), replace=False))
+
+
+def test_fp8_frozen_full_size(lp):
+    """4096 x 8192 grad, 8192 x 2048 E4M3 weight: dX, 64 sampled rows."""
+    w = W.WORKLOADS["fp8_frozen"]
+    X, Wt, G = W.dense_inputs(w)
+    wq, wd = quantize(lp, "fp8_b128", Wt)
+    g = lp.QTensor("bf16", bf16_dev(G), shape=(1, w.M, w.N))
+    dx, _ = lp.lp_linear_bwd(g, None, wq, need_dw=False)
+    torch.cuda.synchronize()
+    rows = _sample_rows(w.M, 64, 40)
+    assert_close(dx[torch.from_numpy(rows).cuda()], O.rows_dx(G, wd[0], rows), "fp8 frozen dX")
+
+
+def test_nvfp4_linear_full_size(lp):
+    """8192 x 4096 NVFP4 X and 4096 x 4096 NVFP4 W: dX and dW, sampled rows."""
+    w = W.WORKLOADS["nvfp4_linear"]
+    X, Wt, G = W.dense_inputs(w)
+    xq, xd = quantize(lp, "nvfp4", X)
+    wq, wd = quantize(lp, "nvfp4", Wt)
+    g = lp.QTensor("bf16", bf16_dev(G), shape=(1, w.M, w.N))
+    dx, dw = lp.lp_linear_bwd(g, xq, wq)
+    torch.cuda.synchronize()
+    rows = _sample_rows(w.M, 48, 41)
+    assert_close(dx[torch.from_numpy(rows).cuda()], O.rows_dx(G, wd[0], rows), "nvfp4 dX")
+    nrows = _sample_rows(w.N, 48, 42)
+    assert_close(dw[torch.from_numpy(nrows).cuda()], O.rows_dw(G, xd[0], nrows), "nvfp4 dW")
+
+
+def test_mxfp4_grouped_full_size(lp):
+    """8 experts, 16384 tokens routed by Dirichlet(1): grouped dX and dW,
+    sampled rows of every group."""
+    w = W.WORKLOADS["mxfp4_grouped"]
+    X, Wt, G = W.dense_inputs(w)
+    offsets = W.cumulative_ends(W.group_sizes(w))
+    xq, xd = quantize(lp, "mxfp4", X)
+    wq, wd = quantize(lp, "mxfp4", Wt)
+    g = lp.QTensor("bf16", bf16_dev(G), shape=(1, w.M, w.N))
+    dx, dw = lp.lp_grouped_bwd(g, xq, wq, torch.from_numpy(offsets).cuda())
+    torch.cuda.synchronize()
+    for gi, (s, e) in enumerate(O.group_bounds(offsets)):
+        if e == s:
+            continue
+        rows = s + _sample_rows(e - s, 8, 43 + gi)
+        assert_close(dx[torch.from_numpy(rows).cuda()], O.rows_dx(G, wd[gi], rows), f"group {gi} dX")
+        nrows = _sample_rows(w.N, 6, 60 + gi)
+        ref = O.rows_dw(G[s:e], xd[0][s:e], nrows)
+        assert_close(dw[gi][torch.from_numpy(nrows).cuda()], ref, f"group {gi} dW")
+
+
+def test_mxfp8_deferred_full_size(lp):
+    """64 experts, 32768 tokens with Zipf(1.1) sizes: the GPU quantizes grad
+    (along -1) and W (along the reduction axis) and runs grouped dX; sampled
+    rows are checked against the oracle's own quantization of the same bf16
+    inputs."""
+    w = W.WORKLOADS["mxfp8_deferred"]
+    offsets = W.cumulative_ends(W.group_sizes(w))
+    Wt = W.torch_normal_bf16((w.groups, w.N, w.K), w.w_sigma, seed=5005, device="cuda")
+    Gt = W.torch_normal_bf16((w.M, w.N), 1.0, seed=5006, device="cuda")
+    gq = lp.lp_mx_quant(Gt, -1, "mxfp8")
+    wq = lp.lp_mx_quant(Wt, -2, "mxfp8")
+    gq.shape = (1, w.M, w.N)
+    dx, _ = lp.lp_grouped_bwd(gq, None, wq, torch.from_numpy(offsets).cuda(), need_dw=False)
+    torch.cuda.synchronize()
+    bounds = O.group_bounds(offsets)
+    experts = [int(np.argmax(np.diff([0] + list(offsets))))] + [int(e) for e in W.rng(44, "x").choice(w.groups, 3)]
+    for gi in experts:
+        s, e = bounds[gi]
+        if e == s:
+            continue
+        rows = s + _sample_rows(e - s, 8, 45 + gi)
+        gbits = Gt[torch.from_numpy(rows).cuda()].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        gc, gs = F.mx_quant(gbits[None], -1, "e4m3")
+        g_deq = F.dequant("mxfp8", gc, gs, axis=-1)[0]
+        wbits = Wt[gi].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        wc, ws = F.mx_quant(wbits[None], -2, "e4m3")
+        w_deq = F.dequant("mxfp8", wc, ws, axis=-2)[0]
+        assert_close(dx[torch.from_numpy(rows).cuda()], O.linear_dx(g_deq, w_deq), f"expert {gi} dX")
