@@ -1,0 +1,375 @@
+"""Benchmark of the block-scaled backward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+
+A step is one pass of the workload's whole backward path over one batch of
+synthetic input already resident in HBM:
+  fp8_frozen      lp_linear_bwd: dX of a frozen FP8 128x128-block weight (default)
+  nvfp4_linear    lp_linear_bwd: dX and dW, NVFP4 X and W
+  mxfp4_grouped   lp_grouped_bwd: dX and dW over 8 experts, MXFP4 X and W
+  mxfp8_deferred  lp_mx_quant(grad, -1) + lp_mx_quant(W, -2) + lp_grouped_bwd dX
+  mxfp4_tiny      lp_linear_bwd: dX and dW, 64 x 128 x 128
+Input sets are rotated through about 1 GB so that the 256 MiB Infinity Cache
+cannot serve a repeated step.  Prints one JSON line (rank 0).
+
+Inputs are drawn on the GPU by torch and quantized there: FP8 blocks and
+NVFP4 with plain torch ops (input preparation only), MXFP4 with the
+library's own lp_mx_quant.  The CPU-baseline leg runs the CPU oracle on a
+bounded sample of the same workload (its inputs drawn with numpy).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+METRIC = "backward TFLOP/s (dX+dW) and % BF16 MFMA peak; dequant/quant GB/s vs HBM"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+ROTATE_BYTES = 1 << 30
+
+
+# ------------------------------------------------------------------ input preparation (torch, GPU)
+
+def _randn(shape, sigma, seed):
+    return W.torch_normal_bf16(shape, sigma, seed, "cuda").float()
+
+
+def fp8_b128_quant_torch(w: torch.Tensor):
+    """FP8 block inputs: s = amax/448 per 128x128 block, codes = E4M3(w / s)."""
+    R, C = w.shape[-2:]
+    lead = w.shape[:-2]
+    wb = w.reshape(*lead, R // 128, 128, C // 128, 128)
+    amax = wb.abs().amax(dim=(-3, -1))
+    s = (amax / 448.0).clamp_min(1e-30)
+    t = wb / s[..., :, None, :, None]
+    codes = t.to(torch.float8_e4m3fn).view(torch.uint8).reshape(*lead, R, C)
+    return codes.contiguous(), s.float().contiguous()
+
+
+_E2M1 = torch.tensor([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def nvfp4_quant_torch(x: torch.Tensor):
+    """NVFP4 inputs (two-level recipe): tensor scale amax/(6*448), E4M3 block
+    scale per 16, E2M1 codes by nearest magnitude."""
+    st = (x.abs().amax() / (6.0 * 448.0)).clamp_min(1e-30).float()
+    R, C = x.shape[-2:]
+    xb = x.reshape(R, C // 16, 16)
+    sb = (xb.abs().amax(-1) / 6.0 / st).to(torch.float8_e4m3fn)
+    S = sb.float() * st
+    t = (xb / S.clamp_min(1e-30)[..., None]).reshape(R, C)
+    grid = _E2M1.to(x.device)
+    mag = (t.abs()[..., None] - grid).abs().argmin(-1).to(torch.uint8)
+    code = mag | ((t < 0).to(torch.uint8) << 3)
+    packed = (code[:, 0::2] | (code[:, 1::2] << 4)).contiguous()
+    return packed, sb.view(torch.uint8).contiguous(), st.reshape(1).contiguous()
+
+
+# ------------------------------------------------------------------ workload runners
+
+class Phase:
+    """One library call of a step, timed with HIP events on the launch stream."""
+
+    def __init__(self, name, kernel, flops=0.0, nbytes=0.0):
+        self.name, self.kernel, self.flops, self.nbytes = name, kernel, flops, nbytes
+        self.ms = []
+
+
+def build(lp, name: str):
+    w = W.WORKLOADS[name]
+    M, N, K = w.M, w.N, w.K
+    sets = []
+    phases = []
+    if name in ("fp8_frozen", "nvfp4_linear", "mxfp4_tiny"):
+        per_set = M * N * 2 + N * K * (1 if w.fmt == "fp8_b128" else 0.5) * (1 if name == "fp8_frozen" else 2)
+        nsets = max(1, min(16, math.ceil(ROTATE_BYTES / per_set)))
+        for i in range(nsets):
+            g = W.torch_normal_bf16((M, N), 1.0, 7000 + i, "cuda")
+            wt = _randn((N, K), w.w_sigma, 7100 + i)
+            gq = lp.QTensor("bf16", g, shape=(1, M, N))
+            if w.fmt == "fp8_b128":
+                c, s = fp8_b128_quant_torch(wt)
+                wq, xq = lp.QTensor("fp8_b128", c, s, shape=(1, N, K)), None
+            elif w.fmt == "nvfp4":
+                xt = _randn((M, K), 1.0, 7200 + i)
+                c, s, ts = nvfp4_quant_torch(wt)
+                wq = lp.QTensor("nvfp4", c, s, ts, shape=(1, N, K))
+                c, s, ts = nvfp4_quant_torch(xt)
+                xq = lp.QTensor("nvfp4", c, s, ts, shape=(1, M, K))
+            else:
+                xt = _randn((M, K), 1.0, 7200 + i).to(torch.bfloat16)
+                wq = lp.lp_mx_quant(wt.to(torch.bfloat16), -1, "mxfp4")
+                xq = lp.lp_mx_quant(xt, -1, "mxfp4")
+            dx = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+            dw = torch.empty((N, K), dtype=torch.bfloat16, device="cuda") if w.need_dw else None
+            sets.append((gq, xq, wq, dx, dw))
+        flops = 2.0 * M * N * K * (2 if w.need_dw else 1)
+        phases.append(Phase("linear_bwd", "gemm_kernel", flops=flops))
+
+        def step(i, stream):
+            gq, xq, wq, dx, dw = sets[i % len(sets)]
+            ev = _events(stream)
+            lp.lp_linear_bwd(gq, xq, wq, need_dw=w.need_dw, grad_x=dx, grad_w=dw, stream=stream)
+            return [ev.stop(stream)]
+        standalone = [("W", sets[0][2])] + ([("X", sets[0][1])] if sets[0][1] is not None else [])
+    elif name == "mxfp4_grouped":
+        offsets = torch.from_numpy(W.cumulative_ends(W.group_sizes(w))).cuda()
+        per_set = M * N * 2 + (M * K + w.groups * N * K) * 0.53125
+        nsets = max(1, min(8, math.ceil(ROTATE_BYTES / per_set)))
+        for i in range(nsets):
+            g = W.torch_normal_bf16((M, N), 1.0, 7300 + i, "cuda")
+            xq = lp.lp_mx_quant(W.torch_normal_bf16((M, K), 1.0, 7400 + i, "cuda"), -1, "mxfp4")
+            wq = lp.lp_mx_quant(W.torch_normal_bf16((w.groups, N, K), 1.0, 7500 + i, "cuda"), -1, "mxfp4")
+            dx = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+            dw = torch.empty((w.groups, N, K), dtype=torch.bfloat16, device="cuda")
+            sets.append((lp.QTensor("bf16", g, shape=(1, M, N)), xq, wq, dx, dw))
+        phases.append(Phase("grouped_bwd", "gemm_kernel", flops=4.0 * M * N * K))
+
+        def step(i, stream):
+            gq, xq, wq, dx, dw = sets[i % len(sets)]
+            ev = _events(stream)
+            lp.lp_grouped_bwd(gq, xq, wq, offsets, grad_x=dx, grad_w=dw, stream=stream)
+            return [ev.stop(stream)]
+        standalone = [("X", sets[0][1]), ("W", sets[0][2])]
+    elif name == "mxfp8_deferred":
+        offsets = torch.from_numpy(W.cumulative_ends(W.group_sizes(w))).cuda()
+        g = W.torch_normal_bf16((M, N), 1.0, 7600, "cuda")
+        wt = W.torch_normal_bf16((w.groups, N, K), w.w_sigma, 7601, "cuda")
+        gq = lp.lp_mx_quant(g, -1, "mxfp8")
+        wq = lp.lp_mx_quant(wt, -2, "mxfp8")
+        dx = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+        sets.append((g, wt, gq, wq, dx))
+        phases.append(Phase("mx_quant grad", "mx_quant_cols", nbytes=M * N * (2 + 1 + 1 / 32)))
+        phases.append(Phase("mx_quant W", "mx_quant_rows", nbytes=w.groups * N * K * (2 + 1 + 1 / 32)))
+        phases.append(Phase("grouped_bwd dX", "gemm_kernel", flops=2.0 * M * N * K))
+
+        def step(i, stream):
+            g, wt, gq, wq, dx = sets[0]
+            ev = _events(stream)
+            lp.lp_mx_quant(g, -1, "mxfp8", codes=gq.codes, scales=gq.scales, stream=stream)
+            t0 = ev.stop(stream)
+            ev = _events(stream)
+            lp.lp_mx_quant(wt, -2, "mxfp8", codes=wq.codes, scales=wq.scales, stream=stream)
+            t1 = ev.stop(stream)
+            ev = _events(stream)
+            gq.shape = (1, M, N)
+            lp.lp_grouped_bwd(gq, None, wq, offsets, need_dw=False, grad_x=dx, stream=stream)
+            return [t0, t1, ev.stop(stream)]
+        standalone = []
+    else:
+        raise SystemExit(f"unknown workload {name}")
+    return w, phases, step, standalone
+
+
+class _events:
+    def __init__(self, stream):
+        self.a = torch.cuda.Event(enable_timing=True)
+        self.b = torch.cuda.Event(enable_timing=True)
+        self.a.record(stream)
+
+    def stop(self, stream):
+        self.b.record(stream)
+        return (self.a, self.b)
+
+
+def dequant_bytes(q) -> float:
+    n = q.shape[0] * q.shape[1] * q.shape[2]
+    per = {"mxfp4": 0.5 + 1 / 32, "nvfp4": 0.5 + 1 / 16, "fp8_b128": 1.0 + 4 / (128 * 128), "mxfp8": 1 + 1 / 32}
+    return n * (per[q.fmt] + 2.0)
+
+
+def time_standalone(lp, stream, q, reps=20):
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
+    for _ in range(3):
+        lp.lp_dequant(q, out, stream=stream)
+    evs = []
+    for _ in range(reps):
+        ev = _events(stream)
+        lp.lp_dequant(q, out, stream=stream)
+        evs.append(ev.stop(stream))
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
+    gbs = dequant_bytes(q) / (ms * 1e-3) / 1e9
+    return {"ms": round(ms, 5), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+
+
+# ------------------------------------------------------------------ HBM traffic from committed counters
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "fp8_gemm_backward_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel from profiles/, or None if
+    absent or taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_sources") != kernel_source_digest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# ------------------------------------------------------------------ CPU baseline (oracle)
+
+def cpu_baseline(name: str, budget_s: float = 12.0):
+    """The oracle on a bounded sample of the workload: decode of the saved
+    operands the sample needs plus the fp64 contraction of sampled rows,
+    extrapolated linearly to the whole step."""
+    from oracle import formats as F
+    from oracle import gemm as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [os.cpu_count()])
+    except Exception:  # noqa: BLE001
+        cores = os.cpu_count()
+    w = W.WORKLOADS[name]
+    M, N, K = w.M, w.N, w.K
+    if name == "mxfp8_deferred":
+        # one expert: quantize its weight along -2 and a slab of gradient rows
+        # along -1, decode both, contract.
+        rows = 256
+        gb = W.bf16_bits(W.normal_f32(w.number, "grad", (rows, N), 1.0))
+        wb = W.bf16_bits(W.normal_f32(w.number, "w", (N, K), w.w_sigma))
+        t0 = time.perf_counter()
+        gc, gs = F.mx_quant(gb[None], -1, "e4m3")
+        wc, ws = F.mx_quant(wb[None], -2, "e4m3")
+        gd = F.dequant("mxfp8", gc, gs, axis=-1)[0]
+        wd = F.dequant("mxfp8", wc, ws, axis=-2)[0]
+        t_w = time.perf_counter() - t0
+        t1 = time.perf_counter()
+        O.linear_dx(gd, wd)
+        t_rows = time.perf_counter() - t1
+        total = t_w * w.groups + t_rows * (M / rows)
+        flops = 2.0 * M * N * K
+        sample = f"1 of {w.groups} experts' weight quantized+decoded, {rows} grad rows quantized+decoded+contracted; extrapolated"
+    else:
+        X, Wt, G = W.dense_inputs(w)
+        fmt = w.fmt
+        quant = {"fp8_b128": F.quant_fp8_b128, "nvfp4": lambda a: F.quant_nvfp4(a),
+                 "mxfp4": F.quant_mxfp4_f32}[fmt]
+        wq = quant(Wt)
+        xq = quant(X) if X is not None else None
+
+        def deq(q):
+            if fmt == "nvfp4":
+                return F.dequant(fmt, q[0], q[1], q[2])
+            return F.dequant(fmt, q[0], q[1])
+        t0 = time.perf_counter()
+        wd = deq(wq)
+        xd = deq(xq)[0] if xq is not None else None
+        t_dec = time.perf_counter() - t0
+        rows = min(M, 64)
+        while True:
+            t1 = time.perf_counter()
+            O.rows_dx(G, wd[0] if not w.grouped else wd[0], np.arange(rows))
+            if xd is not None:
+                O.rows_dw(G[:rows], xd[:rows], np.arange(N))
+            t_rows = time.perf_counter() - t1
+            if t_rows > budget_s / 4 or rows >= M:
+                break
+            rows = min(M, rows * 4)
+        total = t_dec + t_rows * (M / rows)
+        flops = 2.0 * M * N * K * (2 if w.need_dw else 1)
+        sample = (f"whole-operand decode, then dX{' and dW' if w.need_dw else ''} over {rows} of {M} token rows "
+                  f"(fp64), time extrapolated to all rows")
+    return {"value": round(flops / total / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": sample, "seconds": round(total, 3)}
+
+
+# ------------------------------------------------------------------ main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="fp8_frozen", choices=sorted(W.WORKLOADS))
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
+    a = ap.parse_args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import fp8_gemm_backward_amd as lp
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        w, phases, step, standalone = build(lp, a.workload)
+    torch.cuda.synchronize()
+
+    for i in range(a.warmup):
+        step(i, stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    recs = []
+    for i in range(a.steps):
+        recs.append(step(a.warmup + i, stream))
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    for r in recs:
+        for ph, (e0, e1) in zip(phases, r):
+            ph.ms.append(e0.elapsed_time(e1))
+
+    ms_step = elapsed / a.steps * 1e3
+    flops = sum(p.flops for p in phases)
+    value = flops / (ms_step * 1e-3) / 1e12
+    dom = max(phases, key=lambda p: np.mean(p.ms))
+    dom_ms = float(np.mean(dom.ms))
+    if dom.flops:
+        achieved = dom.flops / (dom_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+    else:
+        achieved = dom.nbytes / (dom_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    roof["traffic"] = committed_traffic(a.workload)
+    roof["kernel"] = dom.kernel
+    roof["launch_ms"] = round(dom_ms, 5)
+
+    phase_rec = {}
+    for p in phases:
+        m = float(np.mean(p.ms))
+        rec = {"ms": round(m, 5)}
+        if p.flops:
+            rec["TFLOP/s"] = round(p.flops / (m * 1e-3) / 1e12, 2)
+            rec["frac_mfma"] = round(p.flops / (m * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+        if p.nbytes:
+            rec["GB/s"] = round(p.nbytes / (m * 1e-3) / 1e9, 1)
+            rec["frac_hbm"] = round(p.nbytes / (m * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+        phase_rec[p.name] = rec
+    hbm = {f"dequant {n}": time_standalone(lp, stream, q) for n, q in standalone}
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "format": w.fmt, "M": w.M, "N": w.N, "K": w.K, "groups": w.groups,
+                   "grad_x": w.need_dx, "grad_w": w.need_dw, "global_batch": w.M, "parallelism": "none (1 GPU)"},
+        "roofline": roof, "phases": phase_rec, "standalone_hbm": hbm,
+    }
+    if not a.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(w.name)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

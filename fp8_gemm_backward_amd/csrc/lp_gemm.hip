@@ -29,6 +29,8 @@
 //
 // The MFMA is issued as D = Qfrag x Pfrag so that each lane's accumulator
 // holds four consecutive output columns, stored as one 8-byte write.
+#include <type_traits>
+
 #include "lp_device.hpp"
 #include "lp_internal.hpp"
 
@@ -46,11 +48,12 @@ struct Op {
   const uint8_t* codes;
   const uint8_t* scales;
   const float* tensor_scale;
-  int64_t code_batch;    // bytes between groups (grouped weight), else 0
+  int64_t code_batch;    // bytes between groups' codes (grouped weight)
   int64_t scale_batch;   // bytes between groups' scale grids
+  int64_t scale_bytes;   // bytes of one group's scale grid
   int32_t code_ld;       // bytes per row of codes
-  int32_t scale_ld;      // scale entries per row of the scale grid
-  int32_t cols;          // logical columns (bounds of the mn index)
+  int32_t scale_ld;      // bytes per row of the scale grid
+  int32_t rows;          // rows per group
 };
 
 struct Params {
@@ -67,16 +70,30 @@ struct Params {
   int32_t ntiles;        // grid size
 };
 
-template <int kBP, int kBQ, int kNWP, int kNWQ>
+template <int kBP, int kBQ, int kNWP, int kNWQ, bool kPP>
 struct Cfg {
   static constexpr int BP = kBP, BQ = kBQ, NWP = kNWP, NWQ = kNWQ;
+  static constexpr bool PINGPONG = kPP;                // two alternating wave groups
   static constexpr int NT = 64 * NWP * NWQ;
   static constexpr int WP = BP / NWP, WQ = BQ / NWQ;   // wave tile
   static constexpr int FP = WP / 32, FQ = WQ / 32;     // 32x32 MFMA blocks per wave
-  static constexpr int PK = BK + 8;                    // k-major LDS pitch (bf16)
-  static constexpr int PMP = BP + 32;                  // mn-major LDS pitch for P
-  static constexpr int PMQ = BQ + 32;                  // mn-major LDS pitch for Q
 };
+
+// ---------------------------------------------------------------- buffer loads
+// Every global read goes through a buffer resource whose range ends where the
+// valid data ends; reads past it return zero without touching memory.  This
+// zero-fills contraction tails and out-of-range rows without branches.
+
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr int32_t kOOB = (int32_t)0x80000000;   // an offset beyond any range
+
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, int64_t bytes) {
+  bytes = bytes < 0 ? 0 : (bytes > 0x7FFFFFFF ? 0x7FFFFFFF : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload16(Rsrc r, int32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
 
 // Codes per 16-byte chunk.
 template <int F>
@@ -84,63 +101,40 @@ constexpr int elems_per_chunk() {
   return F == BF16 ? 8 : ((F == MXFP4 || F == NVFP4) ? 32 : 16);
 }
 
-// Raw (undecoded) contents of one chunk: 16 code bytes plus its scale
-// information.  `s` holds up to 16 scale bytes (MXFP8 along rows) or one
-// fp32 / E8M0 / pair of E4M3 scales in s[0].
-struct Raw {
-  u32x4 c;
-  u32x4 s;
-};
-
-// Load the raw chunk at (row gk, column gm) of an operand; zero when out of
-// range.  Zero codes with zero scales decode to +0.
+// Undecoded contents of one chunk: 16 code bytes and its scale data (one
+// E8M0 byte, a pair of E4M3 bytes, one fp32, or 16 E8M0 bytes for MXFP8 with
+// scales along the rows).
 template <int F, int A>
-__device__ __forceinline__ Raw load_chunk(const Op& op, int64_t cbase, int64_t sbase, int gk, int gm, bool valid) {
-  Raw r;
-  r.c = u32x4{0, 0, 0, 0};
-  r.s = u32x4{0, 0, 0, 0};
-  if (!valid) return r;
-  constexpr int bytes_num = (F == BF16) ? 2 : 1;   // bytes per element = num/den
-  constexpr int bytes_den = (F == MXFP4 || F == NVFP4) ? 2 : 1;
-  const uint8_t* cp = op.codes + cbase + (int64_t)gk * op.code_ld + (int64_t)gm * bytes_num / bytes_den;
-  r.c = *reinterpret_cast<const u32x4*>(cp);
-  const uint8_t* sp = op.scales + sbase;
-  if constexpr (F == FP8_B128) {
-    r.s[0] = reinterpret_cast<const uint32_t*>(sp)[(int64_t)(gk >> 7) * op.scale_ld + (gm >> 7)];
-  } else if constexpr (F == MXFP4 || (F == MXFP8 && A == -1)) {
-    r.s[0] = sp[(int64_t)gk * op.scale_ld + (gm >> 5)];
-  } else if constexpr (F == NVFP4) {
-    r.s[0] = *reinterpret_cast<const uint16_t*>(sp + (int64_t)gk * op.scale_ld + (gm >> 4));
-  } else if constexpr (F == MXFP8 && A == -2) {
-    r.s = *reinterpret_cast<const u32x4*>(sp + (int64_t)(gk >> 5) * op.scale_ld + gm);
-  }
-  return r;
-}
+struct Raw {
+  using S = std::conditional_t<(F == MXFP8 && A == -2), u32x4, uint32_t>;
+  u32x4 c;
+  S s;
+};
 
 // Decode a raw chunk to bf16 (EPC/2 dwords).  Values equal the standalone
 // dequantization except that NaN payloads are left as the hardware makes them.
 template <int F, int A>
-__device__ __forceinline__ void decode_chunk(const Raw& r, float ts, uint32_t* o) {
+__device__ __forceinline__ void decode_chunk(const Raw<F, A>& r, float ts, uint32_t* o) {
   if constexpr (F == BF16) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) o[j] = r.c[j];
   } else if constexpr (F == MXFP4) {
-    float cs = e8m0_to_cvt_scale(r.s[0]);
+    float cs = e8m0_to_cvt_scale(r.s);   // the byte load zero-extends
 #pragma unroll
     for (int j = 0; j < 4; ++j) fp4x8_to_bf16_pow2(r.c[j], cs, o + 4 * j);
   } else if constexpr (F == NVFP4) {
-    f32x2 sv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(r.s[0], 1.0f, false);
+    f32x2 sv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(r.s, 1.0f, false);
     float S0 = sv[0] * ts, S1 = sv[1] * ts;
     fp4x8_to_bf16_mul(r.c[0], S0, o + 0);
     fp4x8_to_bf16_mul(r.c[1], S0, o + 4);
     fp4x8_to_bf16_mul(r.c[2], S1, o + 8);
     fp4x8_to_bf16_mul(r.c[3], S1, o + 12);
   } else if constexpr (F == FP8_B128) {
-    float S = __builtin_bit_cast(float, r.s[0]);
+    float S = __builtin_bit_cast(float, r.s);
 #pragma unroll
     for (int j = 0; j < 4; ++j) fp8x4_to_bf16_mul(r.c[j], S, o + 2 * j);
   } else if constexpr (F == MXFP8 && A == -1) {
-    float cs = e8m0_to_cvt_scale(r.s[0]);
+    float cs = e8m0_to_cvt_scale(r.s);
 #pragma unroll
     for (int j = 0; j < 4; ++j) fp8x4_to_bf16_pow2(r.c[j], cs, o + 2 * j);
   } else {  // MXFP8 along rows: one scale byte per column
@@ -161,52 +155,153 @@ __device__ __forceinline__ void decode_chunk(const Raw& r, float ts, uint32_t* o
   }
 }
 
-// Operand tile loader.  kKMajor: tile is R=BMN rows (mn) x BK columns (k) of
-// the tensor; otherwise BK rows (k) x BMN columns (mn).
-template <int F, int A, bool kKMajor, int BMN, int NT>
+// Operand tile loader.  kKMajor: the tile is BMN rows (mn) x BK columns (the
+// contraction runs along the tensor's columns); otherwise BK rows (the
+// contraction runs along its rows) x BMN columns.  Per-thread chunk
+// positions are fixed for the whole k loop; only the window moves.
+//
+// NT threads share the work; with NSPLIT > 1 the tile's chunks are split into
+// NSPLIT contiguous parts and this loader's threads own part `split`.
+template <int F, int A, bool kKMajor, int BMN, int NT, int NSPLIT = 1>
 struct Loader {
   static constexpr int EPC = elems_per_chunk<F>();
   static constexpr int CPR = kKMajor ? BK / EPC : BMN / EPC;        // chunks per tile row
   static constexpr int CHUNKS = kKMajor ? BMN * CPR : BK * CPR;
-  static constexpr int PER = CHUNKS / NT;
-  static_assert(CHUNKS % NT == 0, "tile not evenly divided among threads");
+  static constexpr int PER = CHUNKS / (NT * NSPLIT);
+  static_assert(CHUNKS % (NT * NSPLIT) == 0, "tile not evenly divided among threads");
   static constexpr int PITCH = kKMajor ? BK + 8 : BMN + 32;        // LDS pitch in bf16
   static constexpr int LDS_ELEMS = kKMajor ? BMN * PITCH : BK * PITCH;
+  static constexpr int BPE2 = F == BF16 ? 4 : ((F == MXFP4 || F == NVFP4) ? 1 : 2);  // 2 x bytes per element
 
-  Raw raw[PER];
+  using Stage = Raw<F, A>[PER];
+
+  int32_t voff[PER];     // code byte offset of each chunk inside the window
+  int32_t row[PER];      // chunk's row in the tile
+  int32_t lds[PER];      // chunk's LDS offset (bf16 elements)
+  int32_t mnc[PER];      // chunk's global mn index (mn-major) / column in the tile (k-major)
+  const uint8_t* cbase;  // codes of this tile's group (and rows, k-major)
+  const uint8_t* sbase;
+  int64_t crows_bytes;   // k-major: bytes from cbase to the end of the tensor
   float ts;
 
-  // k0: first contraction index of the slab; kend: end of the contraction
-  // range; mn0 / mnend: the tile's mn range.
-  __device__ __forceinline__ void load(const Op& op, int64_t cbase, int64_t sbase, int k0, int kend, int mn0,
-                                       int mnend) {
+  __device__ __forceinline__ void init(const Op& op, int g, int mn0, int mnend_rows, int t, int split) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      int c = threadIdx.x + i * NT;
-      int row = c / CPR, col = (c % CPR) * EPC;
+      const int c = split * (CHUNKS / NSPLIT) + t + i * NT;
+      const int r = c / CPR, col = (c % CPR) * EPC;
+      row[i] = r;
+      lds[i] = r * PITCH + col;
       if constexpr (kKMajor) {
-        int gm = mn0 + row, gk = k0 + col;
-        raw[i] = load_chunk<F, A>(op, cbase, sbase, gm, gk, gm < mnend && gk < kend);
+        mnc[i] = col;
+        voff[i] = r * op.code_ld + col * BPE2 / 2;
       } else {
-        int gk = k0 + row, gm = mn0 + col;
-        raw[i] = load_chunk<F, A>(op, cbase, sbase, gk, gm, gk < kend && gm < mnend);
+        mnc[i] = mn0 + col;
+        voff[i] = r * op.code_ld + (mn0 + col) * BPE2 / 2;
+      }
+    }
+    if constexpr (kKMajor) {
+      cbase = op.codes + (int64_t)mn0 * op.code_ld;
+      sbase = op.scales + (int64_t)mn0 * op.scale_ld;
+      crows_bytes = (int64_t)(mnend_rows - mn0) * op.code_ld;
+    } else {
+      cbase = op.codes + (int64_t)g * op.code_batch;
+      sbase = op.scales + (int64_t)g * op.scale_batch;
+      crows_bytes = 0;
+    }
+    if constexpr (F == NVFP4) ts = *op.tensor_scale; else ts = 0.0f;
+  }
+
+  // Issue the loads of the slab starting at contraction index k0 (reads
+  // beyond kend come back as zero).  Never branches.
+  __device__ __forceinline__ void load(Stage& st, const Op& op, int k0, int kend) const {
+    if constexpr (kKMajor) {
+      // window: this tile's rows, from column k0 on; columns >= kend masked.
+      const Rsrc cr = make_rsrc(cbase + (int64_t)k0 * BPE2 / 2, crows_bytes - (int64_t)k0 * BPE2 / 2);
+      const bool tail = k0 + BK > kend;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int off = (tail && k0 + mnc[i] >= kend) ? kOOB : voff[i];
+        st[i].c = bload16(cr, off);
+        if constexpr (F == MXFP8) {
+          const Rsrc sr = make_rsrc(sbase + (k0 >> 5), crows_bytes / op.code_ld * op.scale_ld - (k0 >> 5));
+          const int so = (tail && k0 + mnc[i] >= kend) ? kOOB : row[i] * op.scale_ld + (mnc[i] >> 5);
+          st[i].s = __builtin_amdgcn_raw_buffer_load_b8(sr, so, 0, 0);
+        }
+      }
+    } else {
+      // window: rows [k0, kend) of this group's tensor.
+      const int nrows = kend - k0;
+      const Rsrc cr = make_rsrc(cbase + (int64_t)k0 * op.code_ld, (int64_t)nrows * op.code_ld);
+#pragma unroll
+      for (int i = 0; i < PER; ++i) st[i].c = bload16(cr, voff[i]);
+      if constexpr (F == MXFP4 || (F == MXFP8 && A == -1) || F == NVFP4) {
+        const Rsrc sr = make_rsrc(sbase + (int64_t)k0 * op.scale_ld, (int64_t)nrows * op.scale_ld);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+          const int so = row[i] * op.scale_ld + (F == NVFP4 ? (mnc[i] >> 4) : (mnc[i] >> 5));
+          if constexpr (F == NVFP4)
+            st[i].s = __builtin_amdgcn_raw_buffer_load_b16(sr, so, 0, 0);
+          else
+            st[i].s = __builtin_amdgcn_raw_buffer_load_b8(sr, so, 0, 0);
+        }
+      } else if constexpr (F == FP8_B128 || F == MXFP8) {
+        const Rsrc sr = make_rsrc(sbase, op.scale_bytes);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+          const int gk = k0 + row[i];
+          if constexpr (F == FP8_B128) {
+            const int so = gk < kend ? ((gk >> 7) * op.scale_ld + (mnc[i] >> 7) * 4) : kOOB;
+            st[i].s = __builtin_amdgcn_raw_buffer_load_b32(sr, so, 0, 0);
+          } else {
+            const int so = gk < kend ? ((gk >> 5) * op.scale_ld + mnc[i]) : kOOB;
+            st[i].s = bload16(sr, so);
+          }
+        }
       }
     }
   }
 
-  __device__ __forceinline__ void store(uint16_t* lds) const {
+  // Decode and write the chunks i with i % NPARTS == PART (the store is
+  // split so that its parts can be interleaved with a slab's MFMAs).
+  template <int PART, int NPARTS>
+  __device__ __forceinline__ void store_part(const Stage& st, uint16_t* buf) const {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      int c = threadIdx.x + i * NT;
-      int row = c / CPR, col = (c % CPR) * EPC;
+    for (int i = PART; i < PER; i += NPARTS) {
       uint32_t o[EPC / 2];
-      decode_chunk<F, A>(raw[i], ts, o);
-      u32x4* dst = reinterpret_cast<u32x4*>(lds + row * PITCH + col);
+      decode_chunk<F, A>(st[i], ts, o);
+      u32x4* dst = reinterpret_cast<u32x4*>(buf + lds[i]);
 #pragma unroll
       for (int j = 0; j < EPC / 8; ++j) dst[j] = u32x4{o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]};
     }
   }
+  __device__ __forceinline__ void store(const Stage& st, uint16_t* buf) const { store_part<0, 1>(st, buf); }
+
+  // LDS writes issued by store_part<PART, NPARTS>.
+  static constexpr int writes(int part, int nparts) {
+    int n = 0;
+    for (int i = part; i < PER; i += nparts) n += EPC / 8;
+    return n;
+  }
+  // Global loads issued by load().
+  static constexpr int loads() {
+    return PER * ((F == BF16) ? 1 : ((F == MXFP8 && A == -2) ? 2 : 2));
+  }
 };
+
+// Scheduling pattern of one k-substep: N MFMAs, each followed by up to one
+// LDS read, one global load, NV vector-ALU instructions and one LDS write,
+// so that the fragment reads of the next substep and the decode of the next
+// slab fill the issue slots while the matrix cores work.
+template <int I, int N, int NDSR, int NVMEM, int NV, int NDSW>
+__device__ __forceinline__ void interleave() {
+  if constexpr (I < N) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                         // MFMA
+    if constexpr (I < NDSR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    if constexpr (I < NVMEM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); // VMEM read
+    if constexpr (I < NDSW) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+    interleave<I + 1, N, NDSR, NVMEM, NV, NDSW>();
+  }
+}
 
 // k-major fragment: lane holds row (mn) `base + lane%32`, k = kk + (lane/32)*8 .. +7.
 template <int PITCH>
@@ -239,145 +334,87 @@ __device__ __forceinline__ int xcd_remap(int hw, int n) {
   return x < rem ? x * (per + 1) + j : rem * (per + 1) + (x - rem) * per + j;
 }
 
-template <class C, int PF, int PA, int QF, int QA, bool kDW>
-__global__ __launch_bounds__(C::NT) void gemm_kernel(Params p) {
-  using LP = Loader<PF, PA, !kDW, C::BP, C::NT>;
-  using LQ = Loader<QF, QA, false, C::BQ, C::NT>;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (LP::LDS_ELEMS + LQ::LDS_ELEMS)];
-  __shared__ int32_t s_ends[kMaxGroups];
+// The output tile, group and contraction range of one workgroup.
+struct Tile {
+  int g, p0, pend, q0, kbeg, kend;
+  bool valid;
+};
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wp = wave / C::NWQ, wq = wave % C::NWQ;
+// Map the workgroup to its tile.  s_ends: LDS for the group offsets.
+template <class C, bool kDW>
+__device__ __forceinline__ Tile select_tile(const Params& p, int32_t* s_ends) {
+  const int tid = threadIdx.x;
   const int tile = xcd_remap(blockIdx.x, p.ntiles);
-
-  // ---- which output tile, group and contraction range
-  int g = 0, p0, pend, q0, kbeg = 0, kend = p.Ktot;
+  Tile t{0, 0, 0, 0, 0, p.Ktot, true};
+  if (p.offsets != nullptr) {
+    for (int i = tid; i < p.groups; i += C::NT) s_ends[i] = p.offsets[i];
+    __syncthreads();
+  }
   if constexpr (!kDW) {
     // Groups partition the output rows; tiles never straddle a group.
-    int pidx = tile / p.nq;
-    q0 = (tile % p.nq) * C::BQ;
+    const int pidx = tile / p.nq;
+    t.q0 = (tile % p.nq) * C::BQ;
     if (p.offsets == nullptr) {
-      p0 = pidx * C::BP;
-      pend = p.Ptot;
+      t.p0 = pidx * C::BP;
+      t.pend = p.Ptot;
     } else {
-      for (int i = tid; i < p.groups; i += C::NT) s_ends[i] = p.offsets[i];
-      __syncthreads();
       int start = 0, seen = 0;
-      p0 = -1;
-      pend = 0;
+      t.p0 = -1;
       for (int gi = 0; gi < p.groups; ++gi) {
         int e = s_ends[gi];
-        e = e < start ? start : (e > p.Ptot ? p.Ptot : e);        // clamp into [start, M]
-        int t = (e - start + C::BP - 1) / C::BP;
-        if (pidx < seen + t) {
-          g = gi;
-          p0 = start + (pidx - seen) * C::BP;
-          pend = e;
+        e = e < start ? start : (e > p.Ptot ? p.Ptot : e);        // end_g = clamp(o_g, end_{g-1}, M)
+        const int n = (e - start + C::BP - 1) / C::BP;
+        if (pidx < seen + n) {
+          t.g = gi;
+          t.p0 = start + (pidx - seen) * C::BP;
+          t.pend = e;
           break;
         }
-        seen += t;
+        seen += n;
         start = e;
       }
-      if (p0 < 0) return;                                        // past the last tile
     }
-    if (p0 >= pend) return;
+    t.valid = t.p0 >= 0 && t.p0 < t.pend;
   } else {
-    // Groups partition the contraction; every group has np x nq tiles.
-    const int per_group = p.np * p.nq;
-    g = tile / per_group;
-    int t = tile % per_group;
-    p0 = (t / p.nq) * C::BP;
-    q0 = (t % p.nq) * C::BQ;
-    pend = p.Ptot;
+    // Groups partition the contraction; every group has np x nq tiles, whose
+    // cost grows with the group's size.  Tiles are dealt round-robin over the
+    // groups so that each XCD's contiguous range holds an equal share of
+    // every group (dealing whole groups to XCDs would leave the XCD with the
+    // largest group running long after the others).
+    t.g = tile % p.groups;
+    const int r = tile / p.groups;
+    t.p0 = (r / p.nq) * C::BP;
+    t.q0 = (r % p.nq) * C::BQ;
+    t.pend = p.Ptot;
     if (p.offsets != nullptr) {
-      // The same clamped chain as for dx: end_g = clamp(offsets[g], end_{g-1}, M).
-      for (int i = tid; i < p.groups; i += C::NT) s_ends[i] = p.offsets[i];
-      __syncthreads();
       int start = 0, e = 0;
-      for (int gi = 0; gi <= g; ++gi) {
+      for (int gi = 0; gi <= t.g; ++gi) {
         e = s_ends[gi];
         e = e < start ? start : (e > p.Ktot ? p.Ktot : e);
-        if (gi < g) start = e;
+        if (gi < t.g) start = e;
       }
-      kbeg = start;
-      kend = e;
+      t.kbeg = start;
+      t.kend = e;
     }
   }
+  return t;
+}
 
-  // ---- operand bases
-  const int64_t pcb = kDW ? 0 : 0, psb = 0;
-  const int64_t qcb = kDW ? 0 : (int64_t)g * p.Q.code_batch;
-  const int64_t qsb = kDW ? 0 : (int64_t)g * p.Q.scale_batch;
-
-  LP lp;
-  LQ lq;
-  if constexpr (PF == NVFP4) lp.ts = *p.P.tensor_scale; else lp.ts = 0.0f;
-  if constexpr (QF == NVFP4) lq.ts = *p.Q.tensor_scale; else lq.ts = 0.0f;
-
-  // Stage s: P tile at smem + s*STAGE, Q tile right after it.
-  constexpr int STAGE = LP::LDS_ELEMS + LQ::LDS_ELEMS;
-
-  f32x16 acc[C::FP][C::FQ];
-#pragma unroll
-  for (int i = 0; i < C::FP; ++i)
-#pragma unroll
-    for (int j = 0; j < C::FQ; ++j) acc[i][j] = f32x16{};
-
-  const int nk = (kend - kbeg + BK - 1) / BK;
-  // P's mn range: output rows [p0, pend); Q's mn range: columns [q0, Qtot).
-  if (nk > 0) {
-    lp.load(p.P, pcb, psb, kbeg, kend, p0, pend);
-    lq.load(p.Q, qcb, qsb, kbeg, kend, q0, p.Qtot);
-    lp.store(smem);
-    lq.store(smem + LP::LDS_ELEMS);
-    __syncthreads();
-  }
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      const int k0 = kbeg + (kt + 1) * BK;
-      lp.load(p.P, pcb, psb, k0, kend, p0, pend);
-      lq.load(p.Q, qcb, qsb, k0, kend, q0, p.Qtot);
-    }
-    const uint16_t* sp = smem + cur * STAGE;
-    const uint16_t* sq = sp + LP::LDS_ELEMS;
-#pragma unroll
-    for (int kk = 0; kk < BK; kk += 16) {
-      bf16x8 pf[C::FP], qf[C::FQ];
-#pragma unroll
-      for (int i = 0; i < C::FP; ++i) {
-        if constexpr (!kDW)
-          pf[i] = frag_kmajor<LP::PITCH>(sp, wp * C::WP + i * 32, kk, lane);
-        else
-          pf[i] = frag_mnmajor<LP::PITCH>(sp, wp * C::WP + i * 32, kk, lane);
-      }
-#pragma unroll
-      for (int j = 0; j < C::FQ; ++j) qf[j] = frag_mnmajor<LQ::PITCH>(sq, wq * C::WQ + j * 32, kk, lane);
-#pragma unroll
-      for (int i = 0; i < C::FP; ++i)
-#pragma unroll
-        for (int j = 0; j < C::FQ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[j], pf[i], acc[i][j], 0, 0, 0);
-    }
-    if (more) {
-      lp.store(smem + (cur ^ 1) * STAGE);
-      lq.store(smem + (cur ^ 1) * STAGE + LP::LDS_ELEMS);
-    }
-    __syncthreads();
-  }
-
-  // ---- epilogue: fp32 -> bf16 (nearest even), masked 8-byte stores
-  uint16_t* out = p.C + (kDW ? (int64_t)g * p.c_batch : 0);
+// fp32 -> bf16 (nearest even) and masked 8-byte stores of one wave's
+// FP x FQ accumulator blocks (lane holds 4 consecutive output columns).
+template <class C, bool kDW>
+__device__ __forceinline__ void store_acc(const Params& p, const Tile& t, f32x16 (&acc)[C::FP][C::FQ], int wp,
+                                          int wq, int lane) {
+  uint16_t* out = p.C + (kDW ? (int64_t)t.g * p.c_batch : 0);
 #pragma unroll
   for (int i = 0; i < C::FP; ++i) {
-    const int row = p0 + wp * C::WP + i * 32 + (lane & 31);
-    if (row >= pend) continue;
+    const int row = t.p0 + wp * C::WP + i * 32 + (lane & 31);
+    if (row >= t.pend) continue;
 #pragma unroll
     for (int j = 0; j < C::FQ; ++j) {
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const int col = q0 + wq * C::WQ + j * 32 + 8 * r4 + 4 * (lane >> 5);
+        const int col = t.q0 + wq * C::WQ + j * 32 + 8 * r4 + 4 * (lane >> 5);
         if (col < p.Qtot) {
           u32x2 v = {pack_bf16x2(acc[i][j][4 * r4], acc[i][j][4 * r4 + 1]),
                      pack_bf16x2(acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3])};
@@ -388,6 +425,202 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(Params p) {
   }
 }
 
+// Fragments of one 16-deep k-substep and the MFMAs on them.
+template <class C, bool kDW, int PPITCH, int QPITCH, int PELEMS>
+struct Mma {
+  bf16x8 p[C::FP];
+  bf16x8 q[C::FQ];
+  __device__ __forceinline__ void load(const uint16_t* sp, int kk, int wp, int wq, int lane) {
+    const uint16_t* sq = sp + PELEMS;
+#pragma unroll
+    for (int i = 0; i < C::FP; ++i) {
+      if constexpr (!kDW)
+        p[i] = frag_kmajor<PPITCH>(sp, wp * C::WP + i * 32, kk, lane);
+      else
+        p[i] = frag_mnmajor<PPITCH>(sp, wp * C::WP + i * 32, kk, lane);
+    }
+#pragma unroll
+    for (int j = 0; j < C::FQ; ++j) q[j] = frag_mnmajor<QPITCH>(sq, wq * C::WQ + j * 32, kk, lane);
+  }
+  __device__ __forceinline__ void run(f32x16 (&acc)[C::FP][C::FQ]) const {
+#pragma unroll
+    for (int i = 0; i < C::FP; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FQ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q[j], p[i], acc[i][j], 0, 0, 0);
+  }
+};
+
+// Single wave per SIMD: every wave multiplies, loads and decodes; slab k+2
+// in flight and slab k+1 decoded into LDS (interleaved with the MFMAs by
+// scheduling groups) while slab k is multiplied.
+template <class C, int PF, int PA, int QF, int QA, bool kDW>
+__global__ __launch_bounds__(C::NT) void gemm_kernel(Params p) {
+  using LP = Loader<PF, PA, !kDW, C::BP, C::NT>;
+  using LQ = Loader<QF, QA, false, C::BQ, C::NT>;
+  using M = Mma<C, kDW, LP::PITCH, LQ::PITCH, LP::LDS_ELEMS>;
+  constexpr int STAGE = LP::LDS_ELEMS + LQ::LDS_ELEMS;   // P tile, then Q tile
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+  __shared__ int32_t s_ends[kMaxGroups];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wp = wave / C::NWQ, wq = wave % C::NWQ;
+  const Tile t = select_tile<C, kDW>(p, s_ends);
+  if (!t.valid) return;
+  const int kend = t.kend, kbeg = t.kbeg;
+
+  LP lp;
+  LQ lq;
+  // dx: P = grad rows [p0, pend) (k-major), Q = W[g] columns from q0.
+  // dw: P = grad columns from p0, Q = X columns from q0, rows [kbeg, kend).
+  lp.init(p.P, 0, t.p0, kDW ? 0 : p.P.rows, tid, 0);
+  lq.init(p.Q, kDW ? 0 : t.g, t.q0, 0, tid, 0);
+
+  f32x16 acc[C::FP][C::FQ];
+#pragma unroll
+  for (int i = 0; i < C::FP; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FQ; ++j) acc[i][j] = f32x16{};
+
+  constexpr int NM = C::FP * C::FQ;                                   // MFMAs per substep
+  constexpr int NR = (kDW ? 2 * C::FP : C::FP) + 2 * C::FQ;          // fragment reads per substep
+  constexpr int NL = LP::loads() + LQ::loads();                       // global loads per slab
+  auto kstep = [&](typename LP::Stage& ldp, typename LQ::Stage& ldq, int kload, const typename LP::Stage& stp,
+                   const typename LQ::Stage& stq, const uint16_t* cur, uint16_t* nxt) {
+    M fa, fb;
+    fa.load(cur, 0, wp, wq, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    lp.load(ldp, p.P, kload, kend);
+    lq.load(ldq, p.Q, kload, kend);
+    fb.load(cur, 16, wp, wq, lane);
+    lp.template store_part<0, 4>(stp, nxt);
+    lq.template store_part<0, 4>(stq, nxt + LP::LDS_ELEMS);
+    fa.run(acc);
+    interleave<0, NM, NR, NL, 0, LP::writes(0, 4) + LQ::writes(0, 4)>();
+    __builtin_amdgcn_sched_barrier(0);
+    fa.load(cur, 32, wp, wq, lane);
+    lp.template store_part<1, 4>(stp, nxt);
+    lq.template store_part<1, 4>(stq, nxt + LP::LDS_ELEMS);
+    fb.run(acc);
+    interleave<0, NM, NR, 0, 0, LP::writes(1, 4) + LQ::writes(1, 4)>();
+    __builtin_amdgcn_sched_barrier(0);
+    fb.load(cur, 48, wp, wq, lane);
+    lp.template store_part<2, 4>(stp, nxt);
+    lq.template store_part<2, 4>(stq, nxt + LP::LDS_ELEMS);
+    fa.run(acc);
+    interleave<0, NM, NR, 0, 0, LP::writes(2, 4) + LQ::writes(2, 4)>();
+    __builtin_amdgcn_sched_barrier(0);
+    lp.template store_part<3, 4>(stp, nxt);
+    lq.template store_part<3, 4>(stq, nxt + LP::LDS_ELEMS);
+    fb.run(acc);
+    interleave<0, NM, 0, 0, 0, LP::writes(3, 4) + LQ::writes(3, 4)>();
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+  };
+
+  // Two register stages (A, B) and two LDS buffers; the slab count is
+  // rounded up to even so the body has no branch (slabs past the
+  // contraction end load as zeros and add nothing).
+  const int nk = (kend - kbeg + BK - 1) / BK;
+  const int nk2 = (nk + 1) & ~1;
+  typename LP::Stage pa, pb;
+  typename LQ::Stage qa, qb;
+  uint16_t* buf0 = smem;
+  uint16_t* buf1 = smem + STAGE;
+  if (nk > 0) {
+    lp.load(pa, p.P, kbeg, kend);
+    lq.load(qa, p.Q, kbeg, kend);
+    lp.load(pb, p.P, kbeg + BK, kend);
+    lq.load(qb, p.Q, kbeg + BK, kend);
+    lp.store(pa, buf0);
+    lq.store(qa, buf0 + LP::LDS_ELEMS);
+    __syncthreads();
+  }
+  for (int kt = 0; kt < nk2; kt += 2) {
+    kstep(pa, qa, kbeg + (kt + 2) * BK, pb, qb, buf0, buf1);
+    kstep(pb, qb, kbeg + (kt + 3) * BK, pa, qa, buf1, buf0);
+  }
+  store_acc<C, kDW>(p, t, acc, wp, wq, lane);
+}
+
+// Two waves per SIMD in two groups that alternate ("ping-pong"): in each
+// half of a slab one group multiplies while the other decodes its half of
+// the next slab into LDS and issues the loads of the slab after, so every
+// SIMD always has a wave feeding its matrix core.  Waves w and w + NT/128
+// share a SIMD (waves are dealt to the four SIMDs round-robin).
+template <class C, int PF, int PA, int QF, int QA, bool kDW>
+__global__ __launch_bounds__(C::NT) void gemm_pingpong(Params p) {
+  constexpr int GT = C::NT / 2;                                 // threads per group
+  using LP = Loader<PF, PA, !kDW, C::BP, GT, 2>;
+  using LQ = Loader<QF, QA, false, C::BQ, GT, 2>;
+  using M = Mma<C, kDW, LP::PITCH, LQ::PITCH, LP::LDS_ELEMS>;
+  constexpr int STAGE = LP::LDS_ELEMS + LQ::LDS_ELEMS;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+  __shared__ int32_t s_ends[kMaxGroups];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wp = wave / C::NWQ, wq = wave % C::NWQ;
+  const int grp = tid / GT;                                     // 0: multiplies first
+  const Tile t = select_tile<C, kDW>(p, s_ends);
+  if (!t.valid) return;
+  const int kend = t.kend, kbeg = t.kbeg;
+
+  LP lp;
+  LQ lq;
+  lp.init(p.P, 0, t.p0, kDW ? 0 : p.P.rows, tid % GT, grp);
+  lq.init(p.Q, kDW ? 0 : t.g, t.q0, 0, tid % GT, grp);
+
+  f32x16 acc[C::FP][C::FQ];
+#pragma unroll
+  for (int i = 0; i < C::FP; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FQ; ++j) acc[i][j] = f32x16{};
+
+  auto multiply = [&](const uint16_t* cur) {
+    M fa, fb;
+    fa.load(cur, 0, wp, wq, lane);
+    fb.load(cur, 16, wp, wq, lane);
+    fa.run(acc);
+    fa.load(cur, 32, wp, wq, lane);
+    fb.run(acc);
+    fb.load(cur, 48, wp, wq, lane);
+    fa.run(acc);
+    fb.run(acc);
+  };
+
+  const int nk = (kend - kbeg + BK - 1) / BK;
+  typename LP::Stage ps;
+  typename LQ::Stage qs;
+  // prologue: slab 0 into LDS buffer 0, slab 1 into registers
+  if (nk > 0) {
+    lp.load(ps, p.P, kbeg, kend);
+    lq.load(qs, p.Q, kbeg, kend);
+    lp.store(ps, smem);
+    lq.store(qs, smem + LP::LDS_ELEMS);
+    lp.load(ps, p.P, kbeg + BK, kend);
+    lq.load(qs, p.Q, kbeg + BK, kend);
+    __syncthreads();
+  }
+  for (int kt = 0; kt < nk; ++kt) {
+    const uint16_t* cur = smem + (kt & 1) * STAGE;
+    uint16_t* nxt = smem + ((kt + 1) & 1) * STAGE;
+    const int kload = kbeg + (kt + 2) * BK;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      if (half == grp) {
+        multiply(cur);
+      } else {
+        lp.store(ps, nxt);
+        lq.store(qs, nxt + LP::LDS_ELEMS);
+        lp.load(ps, p.P, kload, kend);
+        lq.load(qs, p.Q, kload, kend);
+      }
+      __syncthreads();
+    }
+  }
+  store_acc<C, kDW>(p, t, acc, wp, wq, lane);
+}
+
 // ---------------------------------------------------------------- host side
 
 Op make_op(const lp_qtensor& t) {
@@ -395,50 +628,50 @@ Op make_op(const lp_qtensor& t) {
   o.codes = static_cast<const uint8_t*>(t.codes);
   o.scales = static_cast<const uint8_t*>(t.scales);
   o.tensor_scale = t.tensor_scale;
-  o.cols = (int32_t)t.cols;
+  o.rows = (int32_t)t.rows;
   const int64_t R = t.rows, Cc = t.cols;
   switch (t.fmt) {
     case LP_BF16:
       o.code_ld = (int32_t)(Cc * 2);
-      o.code_batch = R * Cc * 2;
       break;
     case LP_MXFP4:
       o.code_ld = (int32_t)(Cc / 2);
-      o.code_batch = R * Cc / 2;
       o.scale_ld = (int32_t)(Cc / 32);
-      o.scale_batch = R * (Cc / 32);
+      o.scale_bytes = R * (Cc / 32);
       break;
     case LP_NVFP4:
       o.code_ld = (int32_t)(Cc / 2);
-      o.code_batch = R * Cc / 2;
       o.scale_ld = (int32_t)(Cc / 16);
-      o.scale_batch = R * (Cc / 16);
+      o.scale_bytes = R * (Cc / 16);
       break;
     case LP_FP8_B128:
       o.code_ld = (int32_t)Cc;
-      o.code_batch = R * Cc;
-      o.scale_ld = (int32_t)((Cc + 127) / 128);
-      o.scale_batch = ((R + 127) / 128) * ((Cc + 127) / 128) * 4;
+      o.scale_ld = (int32_t)(((Cc + 127) / 128) * 4);
+      o.scale_bytes = ((R + 127) / 128) * ((Cc + 127) / 128) * 4;
       break;
     case LP_MXFP8:
       o.code_ld = (int32_t)Cc;
-      o.code_batch = R * Cc;
       if (t.scale_axis == -1) {
         o.scale_ld = (int32_t)(Cc / 32);
-        o.scale_batch = R * (Cc / 32);
+        o.scale_bytes = R * (Cc / 32);
       } else {
         o.scale_ld = (int32_t)Cc;
-        o.scale_batch = (R / 32) * Cc;
+        o.scale_bytes = (R / 32) * Cc;
       }
       break;
   }
+  o.code_batch = R * o.code_ld;
+  o.scale_batch = o.scale_bytes;
   return o;
 }
 
 template <class C, int PF, int PA, int QF, int QA, bool kDW>
 hipError_t run(const Params& prm, hipStream_t stream) {
   if (prm.ntiles <= 0) return hipSuccess;
-  gemm_kernel<C, PF, PA, QF, QA, kDW><<<dim3(prm.ntiles), dim3(C::NT), 0, stream>>>(prm);
+  if constexpr (C::PINGPONG)
+    gemm_pingpong<C, PF, PA, QF, QA, kDW><<<dim3(prm.ntiles), dim3(C::NT), 0, stream>>>(prm);
+  else
+    gemm_kernel<C, PF, PA, QF, QA, kDW><<<dim3(prm.ntiles), dim3(C::NT), 0, stream>>>(prm);
   return hipGetLastError();
 }
 
@@ -471,8 +704,8 @@ hipError_t launch_cfg(const GemmCall& call, Params prm, hipStream_t stream) {
   return dispatch_q<C, BF16, -1, true>(*call.other, prm, stream);
 }
 
-using Big = Cfg<256, 256, 2, 4>;     // 512 threads, wave tile 128 x 64
-using Narrow = Cfg<256, 128, 2, 2>;  // 256 threads, wave tile 128 x 64
+using Big = Cfg<256, 256, 2, 4, true>;      // 512 threads, two groups of 4 waves, wave tile 128 x 64
+using Narrow = Cfg<256, 128, 2, 2, false>;  // 256 threads (one wave per SIMD), wave tile 128 x 64
 
 }  // namespace
 
