@@ -23,9 +23,20 @@
 // LDS layouts: an operand whose contraction index is contiguous in memory
 // (grad in dx, "k-major") is stored [mn][k] and read with ds_read_b128; an
 // operand whose contraction runs along its rows (W in dx, grad and X in dw,
-// "mn-major") is stored [k][mn] exactly as loaded and read with
-// ds_read_b64_tr_b16, which hands lane i of each 16-lane group column i of
-// four consecutive rows, i.e. the MFMA operand layout.
+// "mn-major") is stored [k][mn] and read with ds_read_b64_tr_b16, which hands
+// lane i of each 16-lane group column i of four consecutive rows, i.e. the
+// MFMA operand layout.
+//
+// Bank rules of the gfx950 LDS (measured): a 16-byte write serves 8 lanes per
+// cycle and is conflict-free when their 16-byte slots differ modulo 128 bytes;
+// a 16-byte read serves 16 lanes per cycle (slots distinct modulo 256 bytes);
+// the transposing 8-byte read serves 32 lanes, i.e. four rows of 64 bytes,
+// which must fall in distinct quarters of 256 bytes.  The k-major tile uses a
+// 144-byte row pitch (both directions conflict-free).  The mn-major tile uses
+// a pitch of 64 mod 256 bytes (rows land in distinct quarters for the
+// transposing read) and XORs the low two bits of the 16-byte chunk index
+// with bits 1..2 of the row; eight consecutive lanes decode the same columns
+// of eight consecutive rows, so their writes hit eight distinct slots.
 //
 // The MFMA is issued as D = Qfrag x Pfrag so that each lane's accumulator
 // holds four consecutive output columns, stored as one 8-byte write.
@@ -175,9 +186,11 @@ struct Loader {
 
   using Stage = Raw<F, A>[PER];
 
+  static constexpr int PIECES = EPC / 8;                            // 16-byte LDS writes per chunk
+
   int32_t voff[PER];     // code byte offset of each chunk inside the window
   int32_t row[PER];      // chunk's row in the tile
-  int32_t lds[PER];      // chunk's LDS offset (bf16 elements)
+  int32_t lds[PER][PIECES];  // LDS offset (bf16 elements) of each 16-byte piece of the chunk
   int32_t mnc[PER];      // chunk's global mn index (mn-major) / column in the tile (k-major)
   const uint8_t* cbase;  // codes of this tile's group (and rows, k-major)
   const uint8_t* sbase;
@@ -188,9 +201,20 @@ struct Loader {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int c = split * (CHUNKS / NSPLIT) + t + i * NT;
-      const int r = c / CPR, col = (c % CPR) * EPC;
+      // k-major: consecutive chunks run along a row.  mn-major: groups of
+      // eight consecutive chunks run down eight rows at the same columns.
+      const int r = kKMajor ? c / CPR : (c / (8 * CPR)) * 8 + (c & 7);
+      const int col = kKMajor ? (c % CPR) * EPC : ((c >> 3) % CPR) * EPC;
       row[i] = r;
-      lds[i] = r * PITCH + col;
+#pragma unroll
+      for (int j = 0; j < PIECES; ++j) {
+        if constexpr (kKMajor) {
+          lds[i][j] = r * PITCH + col + 8 * j;
+        } else {
+          const int q = col / 8 + j;                                  // logical 16-byte chunk
+          lds[i][j] = r * PITCH + 8 * ((q & ~3) | ((q & 3) ^ ((r >> 1) & 3)));
+        }
+      }
       if constexpr (kKMajor) {
         mnc[i] = col;
         voff[i] = r * op.code_ld + col * BPE2 / 2;
@@ -269,9 +293,9 @@ struct Loader {
     for (int i = PART; i < PER; i += NPARTS) {
       uint32_t o[EPC / 2];
       decode_chunk<F, A>(st[i], ts, o);
-      u32x4* dst = reinterpret_cast<u32x4*>(buf + lds[i]);
 #pragma unroll
-      for (int j = 0; j < EPC / 8; ++j) dst[j] = u32x4{o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]};
+      for (int j = 0; j < PIECES; ++j)
+        *reinterpret_cast<u32x4*>(buf + lds[i][j]) = u32x4{o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]};
     }
   }
   __device__ __forceinline__ void store(const Stage& st, uint16_t* buf) const { store_part<0, 1>(st, buf); }
@@ -310,16 +334,21 @@ __device__ __forceinline__ bf16x8 frag_kmajor(const uint16_t* lds, int base, int
   return *reinterpret_cast<const bf16x8*>(p);
 }
 
-// mn-major fragment (LDS [k][mn]): lane holds column `base + lane%32` at the
-// same k's, assembled from two transposing reads of four rows each.
+// mn-major fragment (LDS [k][mn], swizzled as the loader stores it): lane
+// holds column `base + lane%32` at the same k's, assembled from two
+// transposing reads of four rows each.  base is a multiple of 32 and kk of
+// 16, so the row's swizzle term depends on the lane only.
 template <int PITCH>
 __device__ __forceinline__ bf16x8 frag_mnmajor(const uint16_t* lds, int base, int kk, int lane) {
-  int i16 = lane & 15, grp = lane >> 4;
-  int row = kk + (grp >> 1) * 8 + (i16 >> 2);
-  int col = base + (grp & 1) * 16 + (i16 & 3) * 4;
-  const uint16_t* p = lds + row * PITCH + col;
-  i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
-  i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * PITCH));
+  const int i16 = lane & 15, grp = lane >> 4;
+  const int row = kk + (grp >> 1) * 8 + (i16 >> 2);              // row % 8 == i16 / 4
+  const int lc = (grp & 1) * 2 + ((i16 & 3) >> 1);                 // logical chunk in the fragment
+  const int half = (i16 & 1) * 4;
+  const int ha = (i16 >> 3) & 1, hb = 2 + ((i16 >> 3) & 1);        // ((row >> 1) & 3) for rows r, r + 4
+  const uint16_t* pa = lds + row * PITCH + base + 8 * (lc ^ ha) + half;
+  const uint16_t* pb = lds + (row + 4) * PITCH + base + 8 * (lc ^ hb) + half;
+  i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(pa));
+  i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(pb));
   typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8;
   i16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
   return __builtin_bit_cast(bf16x8, v);
