@@ -1,0 +1,817 @@
+// Fused dequantize + bf16 MFMA backward contractions (dense and grouped):
+// kernel templates, shared by the per-format translation units.
+//
+// "Add Autograd Backward Support for FP4 GEMM Custom Ops", Implementation
+// Method: grad_X = grad_output @ W_bf16 and grad_W = grad_output.T @ X_bf16
+// after dequantizing the saved operands; "Train adapters on top of FP8
+// weights", FP8GroupedMatmulFunction.backward: the rows of each group
+// (int32 cumulative end offsets) multiply that group's weight, rows past the
+// last offset are skipped; "perf: defer mxfp8 backward quantization",
+// MXFP8GMMFunction.op_dx: the same contraction with MX-quantized operands.
+//
+// Notation: the output tile is P x Q (P = rows of the output, Q = its
+// columns, always the layer input dim K); the contraction runs over "k".
+//   dx: out[m][q] = sum_n grad[m][n] * W[g][n][q]   P = m, k = n
+//   dw: out[g][n][q] = sum_m grad[m][n] * X[m][q]   P = n, k = m (group rows)
+//
+// Each workgroup owns one BP x BQ output tile and runs four waves, one per
+// SIMD, each owning a (BP/2) x (BQ/2) quarter held in accumulation registers.
+// The contraction advances in BK = 64 slabs:
+// * the bf16 gradient (P) goes from global memory straight into LDS
+//   (buffer_load_dwordx4 ... lds), three LDS buffers deep, issued two slabs
+//   ahead;
+// * a quantized operand is loaded into registers three slabs ahead (two when
+//   no operand is loaded straight into LDS) and decoded into a bf16 LDS tile
+//   one slab ahead (two LDS buffers), once for the whole workgroup;
+// * the MFMAs of slab k (v_mfma_f32_32x32x16_bf16, four 16-deep substeps)
+//   run from register fragments read from LDS one substep ahead.
+// Every MFMA is followed by a fixed share of the other work (fragment reads
+// of the next substep, load issues, a quarter of a decoded piece), and
+// scheduling fences keep that order, so the matrix core is fed while the
+// rest proceeds: a wave issues in order, so work bunched behind one MFMA
+// leaves the matrix core idle.  One barrier per slab, inside its last
+// substep, publishes slab k+1.
+//
+// LDS layouts.  An operand whose contraction index is contiguous in memory
+// (grad in dx, "k-major") is stored [mn][k] and read with ds_read_b128; an
+// operand whose contraction runs along its rows (W in dx, grad and X in dw,
+// "mn-major") is stored [k][mn] and read with ds_read_b64_tr_b16, which hands
+// lane i of each 16-lane group column i of four consecutive rows, i.e. the
+// MFMA operand layout.  Bank rules of the gfx950 LDS (measured): a 16-byte
+// write serves 8 lanes per cycle, conflict-free when their 16-byte slots
+// differ modulo 128 bytes; a 16-byte read serves 16 lanes per cycle (slots
+// distinct modulo 256 bytes); the transposing 8-byte read serves 32 lanes,
+// i.e. four rows of 64 bytes, which must fall in distinct quarters of 256
+// bytes.  Rows are unpadded and 16-byte chunks are XOR-swizzled by row:
+// * mn-major: chunk q of row r at q ^ (4 (r & 3) | ((r >> 1) & 3)); eight
+//   consecutive lanes decode the same columns of eight consecutive rows;
+// * k-major (direct): chunk c of row r at c ^ ((r >> 1) & 7);
+// * k-major decoded (MXFP8 grad): 144-byte pitch, no swizzle.
+//
+// The MFMA is issued as D = Qfrag x Pfrag so that each lane's accumulator
+// holds four consecutive output columns, stored as one 8-byte write.
+#pragma once
+
+#include <type_traits>
+#include <utility>
+
+#include "lp_device.hpp"
+#include "lp_internal.hpp"
+
+namespace lp {
+namespace gk {
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short i16x8v __attribute__((ext_vector_type(8)));
+
+constexpr int BK = 64;
+constexpr int NT = 256;                 // four waves, one per SIMD
+constexpr int kMaxGroups = 1024;
+constexpr int kMaxLds = 160 * 1024;
+
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N-1>) in order.
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+// One operand as the kernel sees it.
+struct Op {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const float* tensor_scale;
+  int64_t code_batch;    // bytes between groups' codes (grouped weight)
+  int64_t scale_batch;   // bytes between groups' scale grids
+  int64_t scale_bytes;   // bytes of one group's scale grid
+  int32_t code_ld;       // bytes per row of codes
+  int32_t scale_ld;      // bytes per row of the scale grid
+  int32_t rows;          // rows per group
+};
+
+struct Params {
+  Op P, Q;
+  uint16_t* C;
+  int64_t c_batch;       // elements between output groups (dw), else 0
+  int32_t ldc;           // = Qtot
+  int32_t Ptot;          // output rows: M (dx) or N (dw)
+  int32_t Qtot;          // output columns: K
+  int32_t Ktot;          // contraction length: N (dx) or M (dw)
+  const int32_t* offsets;
+  int32_t groups;
+  int32_t nq;            // Q-tiles
+  int32_t ntiles;        // grid size
+};
+
+template <int kBP, int kBQ>
+struct Cfg {
+  static constexpr int BP = kBP, BQ = kBQ;
+  static constexpr int WP = BP / 2, WQ = BQ / 2;       // 2 x 2 waves
+  static constexpr int FP = WP / 32, FQ = WQ / 32;     // 32x32 MFMA blocks per wave
+};
+
+// ---------------------------------------------------------------- buffer loads
+// Every global read goes through a buffer resource whose range ends where the
+// valid data ends; reads past it return zero without touching memory.  This
+// zero-fills contraction tails and out-of-range rows without branches.
+
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr int32_t kOOB = (int32_t)0x80000000;   // an offset beyond any range
+
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, int64_t bytes) {
+  bytes = bytes < 0 ? 0 : (bytes > 0x7FFFFFFF ? 0x7FFFFFFF : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload16(Rsrc r, int32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// 16 bytes per lane from a buffer straight into LDS: lane i writes bytes
+// [16i, 16i+16) after `lds` (wave-uniform).
+__device__ __forceinline__ void lds_load16(Rsrc r, uint8_t* lds, int32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, off, 0, 0, 0);
+}
+
+// 16-byte chunk swizzles (see the header).
+__device__ __forceinline__ constexpr int swz_mn(int r) { return ((r & 3) << 2) | ((r >> 1) & 3); }
+__device__ __forceinline__ constexpr int swz_k(int r) { return (r >> 1) & 7; }
+
+// Codes per 16-byte chunk.
+template <int F>
+constexpr int elems_per_chunk() {
+  return F == BF16 ? 8 : ((F == MXFP4 || F == NVFP4) ? 32 : 16);
+}
+
+// Undecoded contents of one chunk: 16 code bytes and its scale data (one
+// E8M0 byte, a pair of E4M3 bytes, one fp32, or 16 E8M0 bytes for MXFP8 with
+// scales along the rows).  Scales keep the exact type their load returns: a
+// widening at the load would be a separate instruction that the compiler
+// may hoist to the loop back edge, where it waits for the load to land.
+template <int F, int A>
+struct Raw {
+  using S = std::conditional_t<
+      (F == MXFP8 && A == -2), u32x4,
+      std::conditional_t<F == NVFP4, uint16_t, std::conditional_t<F == FP8_B128, uint32_t, uint8_t>>>;
+  u32x4 c;
+  S s;
+};
+
+// Decode quarter Q (two elements, one output dword) of 16-byte piece J
+// (eight elements) of a raw chunk to bf16.  The quarters of a piece are
+// decoded in order; quarter 0 leaves the piece's scale factor in `sc` for the
+// others, so that the work of a piece can be spread over several MFMAs.
+// Values equal the standalone dequantization except that NaN payloads are
+// left as the hardware makes them.
+template <int F, int A, int J, int Q>
+__device__ __forceinline__ uint32_t decode_quarter(const Raw<F, A>& r, float ts, float& sc) {
+  if constexpr (F == BF16) {
+    return r.c[Q];
+  } else if constexpr (F == MXFP4) {
+    if constexpr (Q == 0) sc = e8m0_to_cvt_scale(r.s);
+    return bf16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(r.c[J], sc, Q));
+  } else if constexpr (F == NVFP4) {
+    if constexpr (Q == 0) {
+      const f32x2 sv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((uint32_t)r.s, 1.0f, false);
+      sc = sv[J / 2] * ts;                                   // scale of elements 16 (J/2) .. +15
+    }
+    const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.c[J], 1.0f, Q);
+    return pack_bf16x2(v[0] * sc, v[1] * sc);
+  } else if constexpr (F == FP8_B128) {
+    const float S = __builtin_bit_cast(float, r.s);
+    const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(r.c[2 * J + Q / 2], 1.0f, Q % 2 == 1);
+    return pack_bf16x2(v[0] * S, v[1] * S);
+  } else if constexpr (F == MXFP8 && A == -1) {
+    if constexpr (Q == 0) sc = e8m0_to_cvt_scale(r.s);
+    return bf16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.c[2 * J + Q / 2], sc, Q % 2 == 1));
+  } else {  // MXFP8 along rows: one scale byte per column (elements 2h, 2h+1 of the word)
+    constexpr bool hi = Q % 2 == 1;
+    const uint32_t w = r.c[2 * J + Q / 2], sw = r.s[2 * J + Q / 2];
+    const uint32_t s0 = hi ? (sw >> 16) & 0xFFu : sw & 0xFFu;
+    const uint32_t s1 = hi ? sw >> 24 : (sw >> 8) & 0xFFu;
+    const uint32_t x = bf16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, e8m0_to_cvt_scale(s0), hi));
+    const uint32_t y = bf16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, e8m0_to_cvt_scale(s1), hi));
+    return (x & 0xFFFFu) | (y & 0xFFFF0000u);
+  }
+}
+
+// Decoding state of the piece in progress.
+struct DecState {
+  float sc;
+  uint32_t o[4];
+};
+
+// ---------------------------------------------------------------- operand tiles
+// Quantized operand: loaded into registers, decoded into an LDS tile.
+// kKMajor: the tile is BMN rows (mn) x BK columns (the contraction runs
+// along the tensor's columns); otherwise BK rows x BMN columns.  Per-thread
+// chunk positions are fixed for the whole k loop; only the window moves.
+template <int F, int A, bool kKMajor, int BMN>
+struct Decoded {
+  static constexpr bool kDirect = false;
+  static constexpr int EPC = elems_per_chunk<F>();
+  static constexpr int CPR = kKMajor ? BK / EPC : BMN / EPC;        // chunks per tile row
+  static constexpr int CHUNKS = kKMajor ? BMN * CPR : BK * CPR;
+  static constexpr int PER = CHUNKS / NT;                            // chunks per thread
+  static_assert(CHUNKS % NT == 0, "tile not evenly divided among threads");
+  static constexpr int PIECES = EPC / 8;                             // 16-byte LDS writes per chunk
+  static constexpr int PITCH = kKMajor ? BK + 8 : BMN;               // LDS row pitch, bf16 elements
+  static constexpr int BUF_BYTES = (kKMajor ? BMN : BK) * PITCH * 2;
+  static constexpr int BPE2 = F == BF16 ? 4 : ((F == MXFP4 || F == NVFP4) ? 1 : 2);  // 2 x bytes per element
+  static constexpr bool kScale = F != BF16;
+  static constexpr int ITEMS = PER;                                  // load items per slab
+  static constexpr int VMEM = PER * (kScale ? 2 : 1);                // vector-memory loads per slab
+  static constexpr int QUARTERS = F == BF16 ? 1 : 4;                 // decode items per piece
+  static constexpr int DECODES = PER * PIECES * QUARTERS;            // decode items per slab
+  static_assert(kKMajor ? (F == MXFP8) : true, "k-major decode is for MXFP8 only");
+
+  using Stage = Raw<F, A>[PER];
+
+  int32_t voff[PER];         // code byte offset of each chunk inside the window
+  int32_t row[PER];          // chunk's row in the tile
+  int32_t mnc[PER];          // chunk's global mn index (mn-major) / column in the tile (k-major)
+  int32_t lds[PER][PIECES];  // byte offset of each 16-byte piece inside an LDS buffer
+  const uint8_t* cbase;
+  const uint8_t* sbase;
+  int64_t crows_bytes;       // k-major: bytes from cbase to the end of the tensor
+  float ts;
+
+  struct Win {
+    Rsrc cr, sr;
+    int k0, kend;
+    bool tail;
+  };
+
+  __device__ __forceinline__ void init(const Op& op, int g, int mn0, int mnend_rows, int t) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = t + i * NT;
+      // k-major: consecutive chunks run along a row.  mn-major: groups of
+      // eight consecutive chunks run down eight rows at the same columns.
+      const int r = kKMajor ? c / CPR : (c / (8 * CPR)) * 8 + (c & 7);
+      const int col = kKMajor ? (c % CPR) * EPC : ((c >> 3) % CPR) * EPC;
+      row[i] = r;
+#pragma unroll
+      for (int j = 0; j < PIECES; ++j) {
+        const int q = col / 8 + j;                                   // logical 16-byte chunk
+        lds[i][j] = 2 * r * PITCH + 16 * (kKMajor ? q : (q ^ swz_mn(r)));
+      }
+      if constexpr (kKMajor) {
+        mnc[i] = col;
+        voff[i] = r * op.code_ld + col * BPE2 / 2;
+      } else {
+        mnc[i] = mn0 + col;
+        voff[i] = r * op.code_ld + (mn0 + col) * BPE2 / 2;
+      }
+    }
+    if constexpr (kKMajor) {
+      cbase = op.codes + (int64_t)mn0 * op.code_ld;
+      sbase = op.scales + (int64_t)mn0 * op.scale_ld;
+      crows_bytes = (int64_t)(mnend_rows - mn0) * op.code_ld;
+    } else {
+      cbase = op.codes + (int64_t)g * op.code_batch;
+      sbase = op.scales + (int64_t)g * op.scale_batch;
+      crows_bytes = 0;
+    }
+    if constexpr (F == NVFP4) ts = *op.tensor_scale; else ts = 0.0f;
+  }
+
+  // Buffer windows of the slab starting at contraction index k0 (reads at or
+  // beyond kend come back as zero).
+  __device__ __forceinline__ Win window(const Op& op, int k0, int kend) const {
+    Win w;
+    w.k0 = k0;
+    w.kend = kend;
+    w.tail = k0 + BK > kend;
+    if constexpr (kKMajor) {
+      w.cr = make_rsrc(cbase + (int64_t)k0 * BPE2 / 2, crows_bytes - (int64_t)k0 * BPE2 / 2);
+      w.sr = make_rsrc(sbase + (k0 >> 5), crows_bytes / op.code_ld * op.scale_ld - (k0 >> 5));
+    } else {
+      const int64_t nrows = kend - k0;
+      w.cr = make_rsrc(cbase + (int64_t)k0 * op.code_ld, nrows * op.code_ld);
+      if constexpr (F == MXFP4 || (F == MXFP8 && A == -1) || F == NVFP4)
+        w.sr = make_rsrc(sbase + (int64_t)k0 * op.scale_ld, nrows * op.scale_ld);
+      else
+        w.sr = make_rsrc(sbase, op.scale_bytes);
+    }
+    return w;
+  }
+
+  // Loads of chunk I (codes, then its scale data).
+  template <int I>
+  __device__ __forceinline__ void load(Stage& st, const Win& w, const Op& op) const {
+    if constexpr (kKMajor) {
+      const bool out = w.tail && w.k0 + mnc[I] >= w.kend;
+      st[I].c = bload16(w.cr, out ? kOOB : voff[I]);
+      st[I].s = __builtin_amdgcn_raw_buffer_load_b8(w.sr, out ? kOOB : row[I] * op.scale_ld + (mnc[I] >> 5), 0, 0);
+    } else {
+      st[I].c = bload16(w.cr, voff[I]);
+      if constexpr (F == MXFP4 || (F == MXFP8 && A == -1)) {
+        st[I].s = __builtin_amdgcn_raw_buffer_load_b8(w.sr, row[I] * op.scale_ld + (mnc[I] >> 5), 0, 0);
+      } else if constexpr (F == NVFP4) {
+        st[I].s = __builtin_amdgcn_raw_buffer_load_b16(w.sr, row[I] * op.scale_ld + (mnc[I] >> 4), 0, 0);
+      } else if constexpr (F == FP8_B128) {
+        const int gk = w.k0 + row[I];
+        const int so = gk < w.kend ? ((gk >> 7) * op.scale_ld + (mnc[I] >> 7) * 4) : kOOB;
+        st[I].s = __builtin_amdgcn_raw_buffer_load_b32(w.sr, so, 0, 0);
+      } else if constexpr (F == MXFP8) {
+        const int gk = w.k0 + row[I];
+        st[I].s = bload16(w.sr, gk < w.kend ? ((gk >> 5) * op.scale_ld + mnc[I]) : kOOB);
+      }
+    }
+  }
+
+  // Decode item Q (a quarter, or the whole piece for bf16) of piece J of
+  // chunk I; the last one writes the piece to the LDS buffer.
+  template <int I, int J, int Q>
+  __device__ __forceinline__ void decode(const Stage& st, uint8_t* buf, DecState& d) const {
+    if constexpr (F == BF16) {
+      *reinterpret_cast<u32x4*>(buf + lds[I][J]) = st[I].c;
+    } else {
+      d.o[Q] = decode_quarter<F, A, J, Q>(st[I], ts, d.sc);
+      if constexpr (Q == 3) *reinterpret_cast<u32x4*>(buf + lds[I][J]) = u32x4{d.o[0], d.o[1], d.o[2], d.o[3]};
+    }
+  }
+};
+
+// bf16 operand: global memory straight into LDS.  One buffer_load_dwordx4
+// ... lds moves 1 KiB, lane i filling bytes [16i, 16i+16) of the block, so
+// the (swizzled) layout is set by which global chunk each lane fetches.  The
+// four waves issue PER blocks each.
+template <bool kKMajor, int BMN>
+struct Direct {
+  static constexpr bool kDirect = true;
+  static constexpr int BUF_BYTES = BMN * BK * 2;
+  static constexpr int BLOCKS = BUF_BYTES / 1024;
+  static constexpr int PER = BLOCKS / 4;                             // blocks per wave
+  static constexpr int RPB = kKMajor ? 8 : 1024 / (2 * BMN);         // tile rows per block
+  static constexpr int LPR = 64 / RPB;                               // lanes per tile row
+  static constexpr int ITEMS = PER;
+  static constexpr int VMEM = PER;
+  static constexpr int DECODES = 0;
+  static constexpr int PIECES = 1;
+  struct Stage {};
+  struct Win {
+    Rsrc r;
+    int k0, kend;
+    bool tail;
+  };
+
+  int32_t voff[PER];   // lane's byte offset inside the window
+  int32_t colk[PER];   // k-major: lane's first column inside the slab (tail mask)
+  int32_t lds0;        // byte offset of the wave's first block inside a buffer
+  const uint8_t* base;
+  int64_t rows_bytes;  // k-major: bytes from base to the end of the tensor
+  int32_t ld;
+
+  __device__ __forceinline__ void init(const Op& op, int g, int mn0, int mnend_rows, int wave, int lane) {
+    ld = op.code_ld;
+    lds0 = wave * PER * 1024;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int row = RPB * (wave * PER + i) + lane / LPR;
+      const int pc = lane % LPR;                                     // physical chunk in the row
+      if constexpr (kKMajor) {
+        const int q = pc ^ swz_k(row);
+        voff[i] = row * ld + 16 * q;
+        colk[i] = 8 * q;
+      } else {
+        const int q = pc ^ swz_mn(row);
+        voff[i] = row * ld + 2 * mn0 + 16 * q;
+        colk[i] = 0;
+      }
+    }
+    if constexpr (kKMajor) {
+      base = op.codes + (int64_t)mn0 * ld;
+      rows_bytes = (int64_t)(mnend_rows - mn0) * ld;
+    } else {
+      base = op.codes + (int64_t)g * op.code_batch;
+      rows_bytes = 0;
+    }
+  }
+
+  __device__ __forceinline__ Win window(const Op&, int k0, int kend) const {
+    Win w;
+    w.k0 = k0;
+    w.kend = kend;
+    w.tail = k0 + BK > kend;
+    if constexpr (kKMajor)
+      w.r = make_rsrc(base + 2 * (int64_t)k0, rows_bytes - 2 * (int64_t)k0);
+    else
+      w.r = make_rsrc(base + (int64_t)k0 * ld, (int64_t)(kend - k0) * ld);
+    return w;
+  }
+
+  template <int I>
+  __device__ __forceinline__ void load(uint8_t* buf, const Win& w) const {
+    int32_t off = voff[I];
+    if constexpr (kKMajor) off = (w.tail && w.k0 + colk[I] >= w.kend) ? kOOB : off;
+    lds_load16(w.r, buf + lds0 + 1024 * I, off);
+  }
+};
+
+// ---------------------------------------------------------------- fragments
+// Per-lane LDS byte addresses of one wave's MFMA fragments; substep s adds a
+// constant (or, for direct k-major tiles, has its own address).
+//
+// k-major tile: lane holds row (mn) `base + lane%32`, k = 16 s + (lane/32)*8 .. +7.
+// mn-major tile: lane holds column `base + lane%32` at the same k's, from two
+// transposing reads (rows r and r + 4 of each 8-row half).
+template <bool kKMajor, bool kDirect, int BMN, int NF>
+struct FragAddr {
+  static constexpr int PITCH = kKMajor ? (kDirect ? BK : BK + 8) : BMN;   // bf16 elements
+  static constexpr int NREAD = kKMajor ? 1 : 2;                           // reads per fragment
+  static constexpr int SUB = kKMajor ? 32 : 16 * 2 * BMN;                 // bytes between substeps
+  static constexpr int NA = kKMajor ? (kDirect ? 4 : 1) : NF;
+  static constexpr int NB = kKMajor ? 1 : NF;
+  int32_t a[NA];
+  int32_t b[NB];
+
+  __device__ __forceinline__ void init(int mn_base, int lane) {
+    if constexpr (kKMajor) {
+      const int r = lane & 31;                                        // (mn_base is a multiple of 32)
+      if constexpr (kDirect) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) a[s] = 2 * (mn_base + r) * PITCH + 16 * ((2 * s + (lane >> 5)) ^ swz_k(r));
+      } else {
+        a[0] = 2 * (mn_base + r) * PITCH + 16 * (lane >> 5);
+      }
+      b[0] = 0;
+    } else {
+      const int i16 = lane & 15, grp = lane >> 4;
+      const int row = (grp >> 1) * 8 + (i16 >> 2);                   // plus 16 s; row % 8 == i16 / 4
+      const int lc = (grp & 1) * 2 + ((i16 & 3) >> 1);               // logical chunk in the 4-chunk group
+      const int half = (i16 & 1) * 8;                                 // bytes
+      const int s4 = row & 3, ha = (row >> 1) & 3, hb = ((row + 4) >> 1) & 3;
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const int m = mn_base / 32 + f;                                // 4-chunk group of the fragment
+        a[f] = 2 * row * PITCH + 16 * (4 * (m ^ s4) + (lc ^ ha)) + half;
+        b[f] = 2 * (row + 4) * PITCH + 16 * (4 * (m ^ s4) + (lc ^ hb)) + half;
+      }
+    }
+  }
+
+  // Read R (0 .. NREAD-1) of fragment f at substep S into dst.
+  template <int S, int R, int f>
+  __device__ __forceinline__ void read(const uint8_t* buf, i16x8v& dst) const {
+    if constexpr (kKMajor) {
+      const int off = (kDirect ? a[S] : a[0] + S * SUB) + f * 32 * 2 * PITCH;
+      dst = __builtin_bit_cast(i16x8v, *reinterpret_cast<const u32x4*>(buf + off));
+    } else {
+      const uint8_t* p = buf + (R == 0 ? a[f] : b[f]) + S * SUB;
+      const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+      typedef short i16x4v __attribute__((ext_vector_type(4)));
+      if constexpr (R == 0)
+        dst.lo = __builtin_bit_cast(i16x4v, v);
+      else
+        dst.hi = __builtin_bit_cast(i16x4v, v);
+    }
+  }
+};
+
+// Map the hardware workgroup id so that each XCD (workgroups are dealt to
+// the 8 XCDs round-robin) receives a contiguous range of logical tiles.
+__device__ __forceinline__ int xcd_remap(int hw, int n) {
+  constexpr int X = 8;
+  int per = n / X, rem = n % X;
+  int x = hw % X, j = hw / X;
+  return x < rem ? x * (per + 1) + j : rem * (per + 1) + (x - rem) * per + j;
+}
+
+// The output tile, group and contraction range of one workgroup.
+struct Tile {
+  int g, p0, pend, q0, kbeg, kend;
+  bool valid;
+};
+
+// Map the workgroup to its tile.  s_ends: LDS for the group offsets.
+template <class C, bool kDW>
+__device__ __forceinline__ Tile select_tile(const Params& p, int32_t* s_ends) {
+  const int tid = threadIdx.x;
+  const int tile = xcd_remap(blockIdx.x, p.ntiles);
+  Tile t{0, 0, 0, 0, 0, p.Ktot, true};
+  if (p.offsets != nullptr) {
+    for (int i = tid; i < p.groups; i += NT) s_ends[i] = p.offsets[i];
+    __syncthreads();
+  }
+  if constexpr (!kDW) {
+    // Groups partition the output rows; tiles never straddle a group.
+    const int pidx = tile / p.nq;
+    t.q0 = (tile % p.nq) * C::BQ;
+    if (p.offsets == nullptr) {
+      t.p0 = pidx * C::BP;
+      t.pend = p.Ptot;
+    } else {
+      int start = 0, seen = 0;
+      t.p0 = -1;
+      for (int gi = 0; gi < p.groups; ++gi) {
+        int e = s_ends[gi];
+        e = e < start ? start : (e > p.Ptot ? p.Ptot : e);        // end_g = clamp(o_g, end_{g-1}, M)
+        const int n = (e - start + C::BP - 1) / C::BP;
+        if (pidx < seen + n) {
+          t.g = gi;
+          t.p0 = start + (pidx - seen) * C::BP;
+          t.pend = e;
+          break;
+        }
+        seen += n;
+        start = e;
+      }
+    }
+    t.valid = t.p0 >= 0 && t.p0 < t.pend;
+  } else {
+    // Groups partition the contraction; every group has np x nq tiles, whose
+    // cost grows with the group's size.  Tiles are dealt round-robin over the
+    // groups so that each XCD's contiguous range holds an equal share of
+    // every group (dealing whole groups to XCDs would leave the XCD with the
+    // largest group running long after the others).
+    t.g = tile % p.groups;
+    const int r = tile / p.groups;
+    t.p0 = (r / p.nq) * C::BP;
+    t.q0 = (r % p.nq) * C::BQ;
+    t.pend = p.Ptot;
+    if (p.offsets != nullptr) {
+      int start = 0, e = 0;
+      for (int gi = 0; gi <= t.g; ++gi) {
+        e = s_ends[gi];
+        e = e < start ? start : (e > p.Ktot ? p.Ktot : e);
+        if (gi < t.g) start = e;
+      }
+      t.kbeg = start;
+      t.kend = e;
+    }
+  }
+  return t;
+}
+
+// fp32 -> bf16 (nearest even) and masked 8-byte stores of one wave's
+// FP x FQ accumulator blocks (lane holds 4 consecutive output columns).
+template <class C, bool kDW>
+__device__ __forceinline__ void store_acc(const Params& p, const Tile& t, f32x16 (&acc)[C::FP][C::FQ], int wp,
+                                          int wq, int lane) {
+  uint16_t* out = p.C + (kDW ? (int64_t)t.g * p.c_batch : 0);
+#pragma unroll
+  for (int i = 0; i < C::FP; ++i) {
+    const int row = t.p0 + wp * C::WP + i * 32 + (lane & 31);
+    if (row >= t.pend) continue;
+#pragma unroll
+    for (int j = 0; j < C::FQ; ++j) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int col = t.q0 + wq * C::WQ + j * 32 + 8 * r4 + 4 * (lane >> 5);
+        if (col < p.Qtot) {
+          u32x2 v = {pack_bf16x2(acc[i][j][4 * r4], acc[i][j][4 * r4 + 1]),
+                     pack_bf16x2(acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3])};
+          *reinterpret_cast<u32x2*>(out + (int64_t)row * p.ldc + col) = v;
+        }
+      }
+    }
+  }
+}
+
+// s_waitcnt vmcnt(N) lgkmcnt(0), then s_barrier.  Written out because the
+// compiler's workgroup barrier waits for every outstanding load (direct LDS
+// loads count as LDS writes), which would drain the prefetch each slab.
+template <int N>
+__device__ __forceinline__ void barrier_vm() {
+  static_assert(N >= 0 && N <= 63, "vmcnt out of range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// The bf16 P operand lands in three LDS buffers that are separate variables,
+// so that the compiler can tell the buffer being read from the two being
+// filled by direct loads and waits only for the load that filled it.  This
+// needs the buffer of each slab fixed at compile time: the main loop covers
+// three slabs, and decoded operands use three register stages to match.
+template <class C, int PF, int PA, int QF, int QA, bool kDW>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_kernel(Params p) {
+  constexpr bool PK = !kDW;                                      // P k-major in dx, mn-major in dw
+  constexpr bool PD = PF == BF16;                                // P loaded straight into LDS
+  using LP = std::conditional_t<PD, Direct<PK, C::BP>, Decoded<PF, PA, PK, C::BP>>;
+  using LQ = Decoded<QF, QA, false, C::BQ>;
+  constexpr int PERIOD = PD ? 3 : 2;                             // slabs per iteration = register stages
+  constexpr int PBUF = LP::BUF_BYTES, QBUF = LQ::BUF_BYTES;
+  static_assert((PD ? 3 * PBUF : 2 * PBUF) + 2 * QBUF <= kMaxLds, "LDS budget");
+  static_assert(kMaxGroups * 4 <= PBUF, "group ends alias P buffer 0");
+  __shared__ __attribute__((aligned(1024))) uint8_t sp0[PD ? PBUF : 2 * PBUF];
+  __shared__ __attribute__((aligned(1024))) uint8_t sp1[PD ? PBUF : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t sp2[PD ? PBUF : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t sq[2 * QBUF];
+
+  // Per slab, in issue order: direct P loads, register loads (P, then Q).
+  constexpr int nDP = PD ? LP::VMEM : 0;
+  constexpr int nL = (PD ? 0 : LP::VMEM) + LQ::VMEM;
+  constexpr int NIS = LP::ITEMS + LQ::ITEMS;
+  constexpr int ND = LP::DECODES + LQ::DECODES;
+  constexpr int DS0 = C::FP * C::FQ / 2;                         // first decode slot
+  constexpr int FP = C::FP, FQ = C::FQ, NM = FP * FQ;
+  using FAP = FragAddr<PK, PD, C::BP, FP>;
+  using FAQ = FragAddr<false, false, C::BQ, FQ>;
+  constexpr int NRP = FAP::NREAD, NR = FP * NRP + 2 * FQ;
+  // The barrier of slab k needs this wave's direct loads of slab k+1 (issued
+  // at the start of slab k-1); vmcnt lets the loads issued after them stay
+  // outstanding (loads complete in order).
+  constexpr int NV_LOOP = PD ? nDP + 2 * nL : 63;
+  constexpr int NV_PRO = PD ? nDP + (PERIOD - 1) * nL : 63;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wp = wave >> 1, wq = wave & 1;
+  const Tile t = select_tile<C, kDW>(p, reinterpret_cast<int32_t*>(sp0));
+  if (!t.valid) return;
+  __syncthreads();                                               // group ends read; buffer 0 reusable
+  const int kend = t.kend, kbeg = t.kbeg;
+
+  // dx: P = grad rows [p0, pend) (k-major), Q = W[g] columns from q0.
+  // dw: P = grad columns from p0, Q = X columns from q0, rows [kbeg, kend).
+  LP lp;
+  LQ lq;
+  if constexpr (PD) lp.init(p.P, 0, t.p0, kDW ? 0 : p.P.rows, wave, lane);
+  else lp.init(p.P, 0, t.p0, kDW ? 0 : p.P.rows, tid);
+  lq.init(p.Q, kDW ? 0 : t.g, t.q0, 0, tid);
+  FAP fap;
+  FAQ faq;
+  fap.init(wp * C::WP, lane);
+  faq.init(wq * C::WQ, lane);
+
+  // P buffer of slab k (B = k mod 3 when direct, else k's parity at run time).
+  auto pbuf = [&](auto bi, int k) -> uint8_t* {
+    constexpr int B = decltype(bi)::value % 3;
+    if constexpr (!PD) return sp0 + (k & 1) * PBUF;
+    else if constexpr (B == 0) return sp0;
+    else if constexpr (B == 1) return sp1;
+    else return sp2;
+  };
+  auto qbuf = [&](int k) -> uint8_t* { return sq + (k & 1) * QBUF; };
+
+  f32x16 acc[FP][FQ];
+#pragma unroll
+  for (int i = 0; i < FP; ++i)
+#pragma unroll
+    for (int j = 0; j < FQ; ++j) acc[i][j] = f32x16{};
+
+  i16x8v fr[2][FP + FQ];             // two fragment sets: P fragments, then Q fragments
+  typename LP::Stage ps[PERIOD];
+  typename LQ::Stage qs[PERIOD];
+
+  // Load item n into register stage ST (direct P items: into LDS buffer pb).
+  auto issue = [&](auto ni, auto sti, const typename LP::Win& pw, const typename LQ::Win& qw, uint8_t* pb) {
+    constexpr int n = decltype(ni)::value, ST = decltype(sti)::value;
+    if constexpr (n < LP::ITEMS) {
+      if constexpr (PD) lp.template load<n>(pb, pw);
+      else lp.template load<n>(ps[ST], pw, p.P);
+    } else {
+      lq.template load<n - LP::ITEMS>(qs[ST], qw, p.Q);
+    }
+  };
+  // Decode item n of register stage ST into LDS buffers pb / qb.
+  DecState dst;
+  auto decode = [&](auto ni, auto sti, uint8_t* pb, uint8_t* qb) {
+    constexpr int n = decltype(ni)::value, ST = decltype(sti)::value;
+    if constexpr (n < LP::DECODES) {
+      if constexpr (!PD) {
+        constexpr int QU = LP::QUARTERS, piece = n / QU;
+        lp.template decode<piece / LP::PIECES, piece % LP::PIECES, n % QU>(ps[ST], pb, dst);
+      }
+    } else {
+      constexpr int m = n - LP::DECODES, QU = LQ::QUARTERS, piece = m / QU;
+      lq.template decode<piece / LQ::PIECES, piece % LQ::PIECES, m % QU>(qs[ST], qb, dst);
+    }
+  };
+  // Fragment read r of substep S into fragment set SET, in the order the
+  // MFMAs consume them: P0, Q0 .. Q(FQ-1), P1 .. P(FP-1).
+  auto read = [&](auto ri, auto si, auto seti, const uint8_t* pb, const uint8_t* qb) {
+    constexpr int r = decltype(ri)::value, S = decltype(si)::value, SET = decltype(seti)::value;
+    if constexpr (r < NRP) {
+      fap.template read<S, r, 0>(pb, fr[SET][0]);
+    } else if constexpr (r < NRP + 2 * FQ) {
+      constexpr int j = (r - NRP) / 2, h = (r - NRP) % 2;
+      faq.template read<S, h, j>(qb, fr[SET][FP + j]);
+    } else {
+      constexpr int i = 1 + (r - NRP - 2 * FQ) / NRP, h = (r - NRP - 2 * FQ) % NRP;
+      fap.template read<S, h, i>(pb, fr[SET][i]);
+    }
+  };
+  auto mfma = [&](auto mi, auto seti) {
+    constexpr int m = decltype(mi)::value, SET = decltype(seti)::value;
+    constexpr int i = m / FQ, j = m % FQ;
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fr[SET][FP + j]),
+                                                        __builtin_bit_cast(bf16x8, fr[SET][i]), acc[i][j], 0, 0, 0);
+  };
+
+  const int nk = (kend - kbeg + BK - 1) / BK;
+  if (nk > 0) {
+    // Prologue: register loads of slabs 0 .. PERIOD-1 and direct loads of
+    // slabs 0 and 1 issued; slab 0 decoded; substep-0 fragments read.  The
+    // order (register loads of slab s, then direct loads of slab s) repeats
+    // the loop's (direct loads of k+2, register loads of k+3), so that the
+    // compiler's wait counts agree on both ways into the loop.
+    static_for<PERIOD>([&](auto si) {
+      constexpr int s = decltype(si)::value;
+      const auto pw = lp.window(p.P, kbeg + s * BK, kend);
+      const auto qw = lq.window(p.Q, kbeg + s * BK, kend);
+      static_for<NIS>([&](auto n) {
+        constexpr int v = decltype(n)::value;
+        constexpr int item = PD ? (v + LP::ITEMS) % NIS : v;         // direct items last
+        if constexpr (!(PD && item < LP::ITEMS && s >= 2)) issue(IC<item>{}, si, pw, qw, pbuf(si, s));
+      });
+    });
+    static_for<ND>([&](auto n) { decode(n, IC<0>{}, pbuf(IC<0>{}, 0), qbuf(0)); });
+    barrier_vm<NV_PRO>();
+    static_for<NR>([&](auto r) { read(r, IC<0>{}, IC<0>{}, pbuf(IC<0>{}, 0), qbuf(0)); });
+  }
+
+  // Slab k = kt + J: multiply P buffer (k) and Q buffer (k); issue the
+  // register loads of slab k + PERIOD into stage J and the direct loads of
+  // slab k + 2; decode slab k + 1 from stage (J + 1) % PERIOD.
+  auto slab = [&](auto ji, int k) {
+    constexpr int J = decltype(ji)::value;
+    constexpr int JN = (J + 1) % PERIOD;
+    const uint8_t* const pcur = pbuf(ji, k);
+    const uint8_t* const qcur = qbuf(k);
+    uint8_t* const pnxt = pbuf(IC<J + 1>{}, k + 1);
+    uint8_t* const qnxt = qbuf(k + 1);
+    uint8_t* const pdst = pbuf(IC<J + 2>{}, k + 2);
+    const auto pw = lp.window(p.P, kbeg + (k + (PD ? 2 : PERIOD)) * BK, kend);
+    const auto qw = lq.window(p.Q, kbeg + (k + PERIOD) * BK, kend);
+
+    static_for<4>([&](auto si) {
+      constexpr int S = decltype(si)::value;
+      constexpr int CUR = S & 1, NXT = CUR ^ 1;
+      static_for<NM>([&](auto mi) {
+        constexpr int m = decltype(mi)::value;
+        mfma(mi, IC<CUR>{});
+        if constexpr (S == 3 && m == 0) barrier_vm<NV_LOOP>();
+        if constexpr (S < 3) {
+          static_for<NR>([&](auto ri) {                              // reads spread over the substep
+            if constexpr (decltype(ri)::value * NM / NR == m) read(ri, IC<S + 1>{}, IC<NXT>{}, pcur, qcur);
+          });
+        } else if constexpr (m > 0) {
+          static_for<NR>([&](auto ri) {                              // next slab's substep 0
+            if constexpr (1 + decltype(ri)::value * (NM - 1) / NR == m) read(ri, IC<0>{}, IC<0>{}, pnxt, qnxt);
+          });
+        }
+        if constexpr (S == 0) {
+          static_for<NIS>([&](auto ni) {
+            if constexpr (decltype(ni)::value * NM / NIS == m) issue(ni, ji, pw, qw, pdst);
+          });
+        }
+        if constexpr (S < 3) {                                       // decode from mid substep 0 on
+          static_for<ND>([&](auto di) {
+            if constexpr (DS0 + decltype(di)::value * (3 * NM - DS0) / ND == S * NM + m) decode(di, IC<JN>{}, pnxt, qnxt);
+          });
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    });
+  };
+
+  for (int kt = 0; kt < nk; kt += PERIOD) {
+    static_for<PERIOD>([&](auto ji) { slab(ji, kt + decltype(ji)::value); });
+  }
+  // No direct load may still be writing LDS when the workgroup ends.
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  store_acc<C, kDW>(p, t, acc, wp, wq, lane);
+}
+
+template <class C, int PF, int PA, int QF, int QA, bool kDW>
+inline hipError_t run(const Params& prm, hipStream_t stream) {
+  if (prm.ntiles <= 0) return hipSuccess;
+  gemm_kernel<C, PF, PA, QF, QA, kDW><<<dim3(prm.ntiles), dim3(NT), 0, stream>>>(prm);
+  return hipGetLastError();
+}
+
+// Q-operand format dispatch.
+template <class C, int PF, int PA, bool kDW>
+inline hipError_t dispatch_q(const lp_qtensor& q, const Params& prm, hipStream_t s) {
+  switch (q.fmt) {
+    case LP_BF16: return run<C, PF, PA, BF16, -1, kDW>(prm, s);
+    case LP_MXFP4: return run<C, PF, PA, MXFP4, -1, kDW>(prm, s);
+    case LP_NVFP4: return run<C, PF, PA, NVFP4, -1, kDW>(prm, s);
+    case LP_FP8_B128: return run<C, PF, PA, FP8_B128, -1, kDW>(prm, s);
+    case LP_MXFP8:
+      return q.scale_axis == -1 ? run<C, PF, PA, MXFP8, -1, kDW>(prm, s) : run<C, PF, PA, MXFP8, -2, kDW>(prm, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+// Launch of one operand-format combination; each is instantiated in its own
+// translation unit (lp_gemm_<dx|dw>_<tile>[_<grad format>].hip).
+using Big = Cfg<256, 256>;      // wave tile 128 x 128
+using Narrow = Cfg<256, 128>;   // wave tile 128 x 64
+hipError_t dx_big_bf16(const lp_qtensor& q, const Params& prm, hipStream_t s);
+hipError_t dx_big_mxfp8(const lp_qtensor& q, const Params& prm, hipStream_t s);
+hipError_t dx_narrow_bf16(const lp_qtensor& q, const Params& prm, hipStream_t s);
+hipError_t dx_narrow_mxfp8(const lp_qtensor& q, const Params& prm, hipStream_t s);
+hipError_t dw_big(const lp_qtensor& q, const Params& prm, hipStream_t s);
+hipError_t dw_narrow(const lp_qtensor& q, const Params& prm, hipStream_t s);
+
+}  // namespace gk
+}  // namespace lp
