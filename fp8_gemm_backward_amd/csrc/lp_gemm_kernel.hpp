@@ -551,28 +551,48 @@ __device__ __forceinline__ Tile select_tile(const Params& p, int32_t* s_ends) {
   return t;
 }
 
-// fp32 -> bf16 (nearest even) and masked 8-byte stores of one wave's
-// FP x FQ accumulator blocks (lane holds 4 consecutive output columns).
+// Epilogue: fp32 -> bf16 (nearest even) through an LDS staging area of the
+// wave's own (`stage`, 128 x WQ bf16), so that the global stores are 16
+// bytes per lane and whole 256-byte row segments per 16 lanes.  A lane's
+// accumulator holds four consecutive columns of one row (8-byte pieces);
+// 8-byte slot s of row r is staged at s ^ (r & 15), which keeps both the
+// staging writes (rows 0..15 of one column) and the row-wise reads free of
+// bank conflicts.
 template <class C, bool kDW>
 __device__ __forceinline__ void store_acc(const Params& p, const Tile& t, f32x16 (&acc)[C::FP][C::FQ], int wp,
-                                          int wq, int lane) {
-  uint16_t* out = p.C + (kDW ? (int64_t)t.g * p.c_batch : 0);
+                                          int wq, int lane, uint8_t* stage) {
+  constexpr int ROWB = C::WQ * 2;                                  // staged row bytes
+  constexpr int SLOTS = ROWB / 8;                                  // 8-byte slots per row
+  static_assert(SLOTS >= 16, "swizzle needs 16 slots per row");
 #pragma unroll
   for (int i = 0; i < C::FP; ++i) {
-    const int row = t.p0 + wp * C::WP + i * 32 + (lane & 31);
-    if (row >= t.pend) continue;
+    const int r = i * 32 + (lane & 31);
 #pragma unroll
     for (int j = 0; j < C::FQ; ++j) {
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const int col = t.q0 + wq * C::WQ + j * 32 + 8 * r4 + 4 * (lane >> 5);
-        if (col < p.Qtot) {
-          u32x2 v = {pack_bf16x2(acc[i][j][4 * r4], acc[i][j][4 * r4 + 1]),
-                     pack_bf16x2(acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3])};
-          *reinterpret_cast<u32x2*>(out + (int64_t)row * p.ldc + col) = v;
-        }
+        const int slot = (j * 32 + 8 * r4 + 4 * (lane >> 5)) / 4;
+        const u32x2 v = {pack_bf16x2(acc[i][j][4 * r4], acc[i][j][4 * r4 + 1]),
+                         pack_bf16x2(acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3])};
+        *reinterpret_cast<u32x2*>(stage + r * ROWB + 8 * (slot ^ (r & 15))) = v;
       }
     }
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);                              // lgkmcnt(0): own staging writes done
+  uint16_t* out = p.C + (kDW ? (int64_t)t.g * p.c_batch : 0);
+  constexpr int LPR = ROWB / 16;                                   // lanes per staged row
+  constexpr int RPI = 64 / LPR;                                    // rows per instruction
+  const int c16 = lane % LPR;
+  const int col = t.q0 + wq * C::WQ + 8 * c16;
+#pragma unroll 4
+  for (int it = 0; it < C::WP / RPI; ++it) {
+    const int r = it * RPI + lane / LPR;
+    const uint8_t* src = stage + r * ROWB;
+    const u32x2 lo = *reinterpret_cast<const u32x2*>(src + 8 * ((2 * c16) ^ (r & 15)));
+    const u32x2 hi = *reinterpret_cast<const u32x2*>(src + 8 * ((2 * c16 + 1) ^ (r & 15)));
+    const int row = t.p0 + wp * C::WP + r;
+    if (row < t.pend && col < p.Qtot)
+      *reinterpret_cast<u32x4*>(out + (int64_t)row * p.ldc + col) = u32x4{lo[0], lo[1], hi[0], hi[1]};
   }
 }
 
@@ -616,8 +636,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   using FAQ = FragAddr<false, false, C::BQ, FQ>;
   constexpr int NRP = FAP::NREAD, NR = FP * NRP + 2 * FQ;
   // The barrier of slab k needs this wave's direct loads of slab k+1 (issued
-  // at the start of slab k-1); vmcnt lets the loads issued after them stay
-  // outstanding (loads complete in order).
+  // in slab k-1, ahead of its register loads); vmcnt lets the loads issued
+  // after them stay outstanding (loads complete in order).
   constexpr int NV_LOOP = PD ? nDP + 2 * nL : 63;
   constexpr int NV_PRO = PD ? nDP + (PERIOD - 1) * nL : 63;
 
@@ -758,9 +778,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
             if constexpr (1 + decltype(ri)::value * (NM - 1) / NR == m) read(ri, IC<0>{}, IC<0>{}, pnxt, qnxt);
           });
         }
-        if constexpr (S == 0) {
+        if constexpr (S < 3) {                                       // loads spread over substeps 0-2
           static_for<NIS>([&](auto ni) {
-            if constexpr (decltype(ni)::value * NM / NIS == m) issue(ni, ji, pw, qw, pdst);
+            if constexpr (decltype(ni)::value * 3 * NM / NIS == S * NM + m) issue(ni, ji, pw, qw, pdst);
           });
         }
         if constexpr (S < 3) {                                       // decode from mid substep 0 on
@@ -776,9 +796,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   for (int kt = 0; kt < nk; kt += PERIOD) {
     static_for<PERIOD>([&](auto ji) { slab(ji, kt + decltype(ji)::value); });
   }
-  // No direct load may still be writing LDS when the workgroup ends.
+  // No direct load may still be writing LDS when the workgroup ends, and no
+  // wave may still read a buffer the staging below overwrites.
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-  store_acc<C, kDW>(p, t, acc, wp, wq, lane);
+  __syncthreads();
+  constexpr int SB = C::WP * C::WQ * 2;                          // staging bytes per wave
+  static_assert(PD ? (PBUF >= SB && 2 * QBUF >= SB) : (2 * PBUF >= 2 * SB && 2 * QBUF >= 2 * SB), "staging fits");
+  uint8_t* stage = PD ? (wave == 0 ? sp0 : wave == 1 ? sp1 : wave == 2 ? sp2 : sq)
+                      : (wave < 2 ? sp0 + wave * SB : sq + (wave - 2) * SB);
+  store_acc<C, kDW>(p, t, acc, wp, wq, lane, stage);
 }
 
 template <class C, int PF, int PA, int QF, int QA, bool kDW>
