@@ -5,7 +5,7 @@ A thin Python binding over the C-ABI library `liblp.so` (declared in
 torch tensors (device memory) and the current HIP stream into the C calls.
 Every step of the computation runs in the library's HIP kernels; there is no
 fallback, and importing this package fails if the library is not built
-(`python -m fp8_gemm_backward_amd.build`).
+(`python fp8_gemm_backward_amd/build.py`).
 
 Formats (see include/lp.h): "bf16", "mxfp4", "nvfp4", "fp8_b128", "mxfp8".
 """
@@ -42,7 +42,7 @@ class _QTensorC(ctypes.Structure):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m fp8_gemm_backward_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python fp8_gemm_backward_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.POINTER(_QTensorC)
     v = ctypes.c_void_p

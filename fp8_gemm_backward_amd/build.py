@@ -1,4 +1,4 @@
-"""Build the lp HIP library for gfx950: `python -m fp8_gemm_backward_amd.build`.
+"""Build the lp HIP library for gfx950: `python fp8_gemm_backward_amd/build.py`.
 
 Compiles every `csrc/*.hip` with hipcc into objects under `_build/` at the
 repository root (in parallel) and links them into
