@@ -209,10 +209,12 @@ def time_standalone(lp, stream, q, reps=20):
 # ------------------------------------------------------------------ HBM traffic from committed counters
 
 def kernel_source_digest() -> str:
+    """Digest of the sources the fused GEMM kernels are built from."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "fp8_gemm_backward_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        h.update(open(os.path.join(csrc, f), "rb").read())
+        if f.startswith("lp_gemm") or f in ("lp_device.hpp", "lp_internal.hpp"):
+            h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 

@@ -6,7 +6,7 @@
 
 namespace {
 
-constexpr int64_t kMaxChunks = (int64_t)1 << 31;   // kernels index 16-byte chunks in 32 bits
+constexpr int64_t kMaxUnits = (int64_t)1 << 31;    // kernels index 8-element units in 32 bits
 constexpr int64_t kMaxDim = ((int64_t)1 << 31) - 1;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -26,7 +26,7 @@ lp_status check_tensor(const lp_qtensor* t) {
   if ((t->fmt == LP_MXFP4 || (t->fmt == LP_MXFP8 && axis == -1)) && t->cols % 32) return LP_ERR_SHAPE;
   if (t->fmt == LP_MXFP8 && axis == -2 && t->rows % 32) return LP_ERR_SHAPE;
   const int64_t n = t->batch * t->rows * t->cols;
-  if (n / 16 >= kMaxChunks) return LP_ERR_SHAPE;
+  if (n / 8 >= kMaxUnits) return LP_ERR_SHAPE;
   if (n == 0) return LP_OK;
   if (t->codes == nullptr) return LP_ERR_NULL;
   if (t->fmt != LP_BF16 && t->scales == nullptr) return LP_ERR_NULL;
@@ -91,7 +91,7 @@ lp_status lp_mx_quant(const void* src, int64_t batch, int64_t rows, int64_t cols
   if (axis == -1 && cols % 32) return LP_ERR_SHAPE;
   if (axis == -2 && (rows % 32 || cols % 8)) return LP_ERR_SHAPE;
   const int64_t n = batch * rows * cols;
-  if (n / 16 >= kMaxChunks) return LP_ERR_SHAPE;
+  if (n / 8 >= kMaxUnits) return LP_ERR_SHAPE;
   if (n == 0) return LP_OK;
   if (src == nullptr || codes == nullptr || scales == nullptr) return LP_ERR_NULL;
   if (!aligned(src, 16) || !aligned(codes, 16) || !aligned(scales, 16)) return LP_ERR_ALIGN;

@@ -11,6 +11,8 @@
 // the exponent field (or the leading mantissa bit of a subnormal); each
 // element is multiplied by 2^-e (exact), clamped to the format's maximum
 // (saturation) and rounded to nearest even by the hardware conversion.
+#include <type_traits>
+
 #include "lp_device.hpp"
 #include "lp_internal.hpp"
 
@@ -70,50 +72,60 @@ __device__ __forceinline__ uint32_t nan_e4m3x2(uint32_t w) {
   return 0x7F7Fu | ((w >> 8) & 0x80u) | ((w >> 16) & 0x8000u);
 }
 
-// Axis -1: thread i quantizes block i = elements [32i, 32i+32).
+// Axis -1: the work unit is eight consecutive elements (16 bytes of bf16);
+// the four lanes of a quad hold one 32-element block and take its amax
+// with two DPP exchanges inside the quad.  Lane i of a wave takes unit
+// base + i, so every load and code store of a wave covers one contiguous
+// span; each thread handles kUnits units, spaced a workgroup apart, with
+// all loads issued first; codes are written with nontemporal stores.
+constexpr int kUnits = 4;
+constexpr int kSpan = kThreads * kUnits;
+
+__device__ __forceinline__ uint32_t quad_max(uint32_t v) {
+  v = umax(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  v = umax(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  return v;
+}
+
 template <bool kFp4>
 __global__ __launch_bounds__(kThreads) void mx_quant_cols(const u32x4* __restrict__ src,
-                                                          u32x4* __restrict__ codes,
-                                                          uint8_t* __restrict__ scales, uint32_t nblocks) {
-  uint32_t i = blockIdx.x * kThreads + threadIdx.x;
-  if (i >= nblocks) return;
-  u32x4 v[4];
+                                                          std::conditional_t<kFp4, uint32_t, u32x2>* __restrict__ codes,
+                                                          uint8_t* __restrict__ scales, uint32_t nunits) {
+  u32x4 v[kUnits];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) v[j] = __builtin_nontemporal_load(src + 4 * (size_t)i + j);
-  uint32_t amax = 0;
+  for (int j = 0; j < kUnits; ++j) {
+    const uint32_t u = blockIdx.x * kSpan + j * kThreads + threadIdx.x;
+    v[j] = u < nunits ? __builtin_nontemporal_load(src + u) : u32x4{0u, 0u, 0u, 0u};
+  }
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < kUnits; ++j) {
+    const uint32_t u = blockIdx.x * kSpan + j * kThreads + threadIdx.x;
+    uint32_t amax = 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      uint32_t w = v[j][k] & 0x7FFF7FFFu;
+      const uint32_t w = v[j][k] & 0x7FFF7FFFu;
       amax = umax(amax, umax(w & 0xFFFFu, w >> 16));
     }
-  BlockScale s = block_scale<kFp4>(amax);
-  scales[i] = (uint8_t)s.byte;
-  if constexpr (!kFp4) {
-    uint32_t o[8];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
+    amax = quad_max(amax);                                 // all four lanes of the quad agree
+    if (u >= nunits) continue;                             // whole quads drop out together
+    const BlockScale s = block_scale<kFp4>(amax);
+    if ((threadIdx.x & 3) == 0) scales[u >> 2] = (uint8_t)s.byte;
+    if constexpr (!kFp4) {
+      uint32_t o[2];
 #pragma unroll
       for (int k = 0; k < 4; k += 2) {
-        uint32_t w0 = v[j][k], w1 = v[j][k + 1];
-        uint32_t lo = s.bad ? nan_e4m3x2(w0) : to_e4m3x2(bf16_lo(w0) * s.inv, bf16_hi(w0) * s.inv);
-        uint32_t hi = s.bad ? nan_e4m3x2(w1) : to_e4m3x2(bf16_lo(w1) * s.inv, bf16_hi(w1) * s.inv);
-        o[2 * j + k / 2] = lo | (hi << 16);
+        const uint32_t w0 = v[j][k], w1 = v[j][k + 1];
+        const uint32_t lo = s.bad ? nan_e4m3x2(w0) : to_e4m3x2(bf16_lo(w0) * s.inv, bf16_hi(w0) * s.inv);
+        const uint32_t hi = s.bad ? nan_e4m3x2(w1) : to_e4m3x2(bf16_lo(w1) * s.inv, bf16_hi(w1) * s.inv);
+        o[k / 2] = lo | (hi << 16);
       }
-    codes[2 * (size_t)i] = u32x4{o[0], o[1], o[2], o[3]};
-    codes[2 * (size_t)i + 1] = u32x4{o[4], o[5], o[6], o[7]};
-  } else {
-    uint32_t o[4];
+      __builtin_nontemporal_store(u32x2{o[0], o[1]}, codes + u);
+    } else {
+      uint32_t o = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t b0 = to_e2m1x2(bf16_lo(v[j][0]) * s.inv, bf16_hi(v[j][0]) * s.inv);
-      uint32_t b1 = to_e2m1x2(bf16_lo(v[j][1]) * s.inv, bf16_hi(v[j][1]) * s.inv);
-      uint32_t b2 = to_e2m1x2(bf16_lo(v[j][2]) * s.inv, bf16_hi(v[j][2]) * s.inv);
-      uint32_t b3 = to_e2m1x2(bf16_lo(v[j][3]) * s.inv, bf16_hi(v[j][3]) * s.inv);
-      o[j] = s.bad ? 0u : (b0 | (b1 << 8) | (b2 << 16) | (b3 << 24));
+      for (int k = 0; k < 4; ++k) o |= to_e2m1x2(bf16_lo(v[j][k]) * s.inv, bf16_hi(v[j][k]) * s.inv) << (8 * k);
+      __builtin_nontemporal_store(s.bad ? 0u : o, codes + u);
     }
-    codes[i] = u32x4{o[0], o[1], o[2], o[3]};
   }
 }
 
@@ -191,15 +203,14 @@ hipError_t launch_mx_quant(const void* src, int64_t batch, int64_t rows, int64_t
   if (n == 0) return hipSuccess;
   const bool fp4 = dst_fmt == LP_MXFP4;
   if (axis == -1) {
-    const uint32_t nblocks = (uint32_t)(n / 32);
-    const dim3 grid((nblocks + kThreads - 1) / kThreads), block(kThreads);
+    const uint32_t nunits = (uint32_t)(n / 8);
+    const dim3 grid((nunits + kSpan - 1) / kSpan), block(kThreads);
     auto s = static_cast<const u32x4*>(src);
-    auto c = static_cast<u32x4*>(codes);
     auto sc = static_cast<uint8_t*>(scales);
     if (fp4)
-      mx_quant_cols<true><<<grid, block, 0, stream>>>(s, c, sc, nblocks);
+      mx_quant_cols<true><<<grid, block, 0, stream>>>(s, static_cast<uint32_t*>(codes), sc, nunits);
     else
-      mx_quant_cols<false><<<grid, block, 0, stream>>>(s, c, sc, nblocks);
+      mx_quant_cols<false><<<grid, block, 0, stream>>>(s, static_cast<u32x2*>(codes), sc, nunits);
   } else {
     const uint32_t spr = (uint32_t)(cols / 8);
     const uint32_t nstrips = (uint32_t)(batch * (rows / 32) * spr);

@@ -28,6 +28,8 @@
  *   tensor is at offset (b*rows + r)*cols + c, in units of elements.
  * - Codes, scales and outputs must be 16-byte aligned; an NVFP4 tensor scale
  *   4-byte aligned.  A pointer may be NULL only when its tensor is empty.
+ * - A tensor holds fewer than 2^34 elements and each of batch, rows, cols is
+ *   below 2^31 (LP_ERR_SHAPE otherwise).
  *
  * Formats (lp_fmt)
  * ----------------

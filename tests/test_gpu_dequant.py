@@ -93,3 +93,21 @@ def test_empty_is_noop(lp):
                    torch.empty((0, 1), dtype=torch.uint8, device="cuda"), shape=(1, 0, 32))
     out = lp.lp_dequant(q)
     assert out.shape == (1, 0, 32)
+
+
+@pytest.mark.parametrize("fmt,shape,axis", [
+    ("nvfp4", (1, 5, 16), -1),          # 80 elements: not a whole 32-element code chunk
+    ("nvfp4", (3, 37, 48), -1),         # ragged units of the last workgroup, batched
+    ("mxfp4", (1, 1027, 32), -1),
+    ("mxfp8", (2, 33, 96), -1),
+    ("mxfp8", (2, 64, 48), -2),
+    ("fp8_b128", (3, 129, 272), -1),
+])
+def test_ragged_sizes(lp, fmt, shape, axis):
+    """Element counts that leave the last workgroup partly empty and rows
+    as short as one scale block."""
+    vals = W.rng(12, "x").standard_normal(shape, dtype=np.float32)
+    q, ref = quantize(lp, fmt, vals, axis)
+    out = lp.lp_dequant(q)
+    torch.cuda.synchronize()
+    assert_bits_equal(bits_host(out), ref, f"{fmt} {shape}")

@@ -110,3 +110,13 @@ def test_mxfp4_grouped_operand_full_size(lp):
     w = W.WORKLOADS["mxfp4_grouped"]
     bits = W.bf16_bits(W.normal_f32(w.number, "x", (1, w.M, w.K), 1.0))
     _check(lp, bits, -1, "mxfp4", "X")
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4"])
+@pytest.mark.parametrize("shape", [(1, 1, 32), (1, 33, 64), (2, 1029, 32)])
+def test_ragged_sizes_along_cols(lp, fmt, shape):
+    """Block counts that leave the last workgroup partly empty, down to a
+    single 32-element block."""
+    g = W.rng(23, "x")
+    x = g.standard_normal(shape).astype(np.float32) * np.exp2(g.integers(-20, 20, size=shape[:-1] + (1,)))
+    _check(lp, W.bf16_bits(x.astype(np.float32)), -1, fmt, f"{fmt} {shape}")
