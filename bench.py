@@ -118,11 +118,15 @@ def build(lp, name: str):
             sets.append((gq, xq, wq, dx, dw))
         flops = 2.0 * M * N * K * (2 if w.need_dw else 1)
         phases.append(Phase("linear_bwd", "gemm_kernel", flops=flops))
+        # One workspace serves every input set: steps run in order on one stream.
+        gq, xq, wq = sets[0][:3]
+        nws = lp.lp_linear_bwd_workspace(gq, xq, wq, True, w.need_dw)
+        ws = torch.zeros(nws, dtype=torch.uint8, device="cuda") if nws else None
 
         def step(i, stream):
             gq, xq, wq, dx, dw = sets[i % len(sets)]
             ev = _events(stream)
-            lp.lp_linear_bwd(gq, xq, wq, need_dw=w.need_dw, grad_x=dx, grad_w=dw, stream=stream)
+            lp.lp_linear_bwd(gq, xq, wq, need_dw=w.need_dw, grad_x=dx, grad_w=dw, stream=stream, workspace=ws)
             return [ev.stop(stream)]
         standalone = [("W", sets[0][2])] + ([("X", sets[0][1])] if sets[0][1] is not None else [])
     elif name == "mxfp4_grouped":

@@ -51,9 +51,12 @@ def _load() -> ctypes.CDLL:
     lib.lp_mx_quant.argtypes = [v, i64, i64, i64, i32, i32, v, v, v]
     lib.lp_linear_bwd.argtypes = [P, P, P, v, v, v]
     lib.lp_grouped_bwd.argtypes = [P, P, P, v, i64, v, v, v]
+    lib.lp_linear_bwd_workspace.argtypes = [P, P, P, v, v, ctypes.POINTER(ctypes.c_size_t)]
+    lib.lp_linear_bwd_ws.argtypes = [P, P, P, v, v, v, ctypes.c_size_t, v]
     lib.lp_status_string.argtypes = [i32]
     lib.lp_status_string.restype = ctypes.c_char_p
-    for f in ("lp_dequant", "lp_mx_quant", "lp_linear_bwd", "lp_grouped_bwd"):
+    for f in ("lp_dequant", "lp_mx_quant", "lp_linear_bwd", "lp_grouped_bwd", "lp_linear_bwd_workspace",
+              "lp_linear_bwd_ws"):
         getattr(lib, f).restype = ctypes.c_int32
     return lib
 
@@ -144,8 +147,11 @@ def lp_mx_quant(src: torch.Tensor, axis: int, fmt: str = "mxfp8", codes: Optiona
 
 def lp_linear_bwd(grad_out: QTensor, x: Optional[QTensor], w: Optional[QTensor], need_dx: bool = True,
                   need_dw: bool = True, grad_x: Optional[torch.Tensor] = None,
-                  grad_w: Optional[torch.Tensor] = None, stream=None):
-    """(grad_X [M,K] or None, grad_W [N,K] or None) of a linear layer."""
+                  grad_w: Optional[torch.Tensor] = None, stream=None, workspace: Optional[torch.Tensor] = None):
+    """(grad_X [M,K] or None, grad_W [N,K] or None) of a linear layer.
+    `workspace`: a zero-filled uint8 device tensor of at least
+    lp_linear_bwd_workspace(...) bytes lets the call split its contraction
+    (lp_linear_bwd_ws); None calls lp_linear_bwd."""
     M, N = grad_out.rows, grad_out.cols
     K = (w if need_dx else x).cols
     dev = grad_out.codes.device
@@ -156,11 +162,30 @@ def lp_linear_bwd(grad_out: QTensor, x: Optional[QTensor], w: Optional[QTensor],
     g = grad_out.c()
     xc = x.c() if x is not None else None
     wc = w.c() if w is not None else None
-    st = lib.lp_linear_bwd(ctypes.byref(g), ctypes.byref(xc) if xc else None, ctypes.byref(wc) if wc else None,
-                           grad_x.data_ptr() if need_dx else None, grad_w.data_ptr() if need_dw else None,
-                           _stream(stream))
-    _check(st, "lp_linear_bwd")
+    args = (ctypes.byref(g), ctypes.byref(xc) if xc else None, ctypes.byref(wc) if wc else None,
+            grad_x.data_ptr() if need_dx else None, grad_w.data_ptr() if need_dw else None)
+    if workspace is None:
+        st = lib.lp_linear_bwd(*args, _stream(stream))
+        _check(st, "lp_linear_bwd")
+    else:
+        st = lib.lp_linear_bwd_ws(*args, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                  _stream(stream))
+        _check(st, "lp_linear_bwd_ws")
     return (grad_x if need_dx else None), (grad_w if need_dw else None)
+
+
+def lp_linear_bwd_workspace(grad_out: QTensor, x: Optional[QTensor], w: Optional[QTensor], need_dx: bool = True,
+                            need_dw: bool = True) -> int:
+    """Workspace bytes lp_linear_bwd_ws can use for this call (0: it does not split)."""
+    g = grad_out.c()
+    xc = x.c() if x is not None else None
+    wc = w.c() if w is not None else None
+    n = ctypes.c_size_t(0)
+    st = lib.lp_linear_bwd_workspace(ctypes.byref(g), ctypes.byref(xc) if xc else None,
+                                     ctypes.byref(wc) if wc else None, 1 if need_dx else None,
+                                     1 if need_dw else None, ctypes.byref(n))
+    _check(st, "lp_linear_bwd_workspace")
+    return n.value
 
 
 def lp_grouped_bwd(grad_out: QTensor, x: Optional[QTensor], w: Optional[QTensor], offsets: torch.Tensor,

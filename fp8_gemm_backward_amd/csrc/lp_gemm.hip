@@ -54,21 +54,69 @@ hipError_t launch_cfg(const GemmCall& call, Params prm, hipStream_t stream) {
   prm.nq = (int32_t)((prm.Qtot + C::BQ - 1) / C::BQ);
   if (!call.dw) {
     const int64_t ptiles = call.offsets ? (call.M / C::BP + call.groups) : (call.M + C::BP - 1) / C::BP;
-    prm.ntiles = (int32_t)(ptiles * prm.nq);
+    prm.ntiles = (int32_t)(ptiles * prm.nq * prm.splits);
     const bool mx = call.grad->fmt == LP_MXFP8;
     if constexpr (C::BQ == Big::BQ) return mx ? dx_big_mxfp8(*call.other, prm, stream) : dx_big_bf16(*call.other, prm, stream);
     else return mx ? dx_narrow_mxfp8(*call.other, prm, stream) : dx_narrow_bf16(*call.other, prm, stream);
   }
   const int64_t np = (prm.Ptot + C::BP - 1) / C::BP;
-  prm.ntiles = (int32_t)(np * prm.nq * call.groups);
+  prm.ntiles = (int32_t)(np * prm.nq * call.groups * prm.splits);
   if constexpr (C::BQ == Big::BQ) return dw_big(*call.other, prm, stream);
   else return dw_narrow(*call.other, prm, stream);
+}
+
+constexpr int kCUs = 256;
+constexpr int64_t kMinSplitSlabs = 16;     // contraction slabs per split, at least
+
+// Output tiles of the 256 x 256 configuration.
+int64_t big_tiles(const GemmCall& call) {
+  const int64_t p = call.dw ? call.groups * ((call.N + 255) / 256) : (call.M + 255) / 256;
+  return p * ((call.K + 255) / 256);
+}
+
+// Output tiles of the 256 x 128 configuration.
+int64_t narrow_tiles(const GemmCall& call) {
+  const int64_t p = call.dw ? call.groups * ((call.N + 255) / 256) : (call.M + 255) / 256;
+  return p * ((call.K + 127) / 128);
+}
+
+// Split plan of a dense contraction whose output tiles would leave most CUs
+// idle even at 256 x 128 (fewer than half as many tiles as CUs): as many
+// splits of 256 x 256 tiles as keep one workgroup per CU, each split at
+// least kMinSplitSlabs slabs long.  splits == 1: no split.  Measured on the
+// 4096 x 2048 output of an 8192-long contraction (128 big tiles, two
+// splits), the partials' write-back and re-read cost more than the narrower
+// tiles lose, hence the threshold.
+struct SplitPlan {
+  int32_t splits, split_len;
+  int64_t tiles;
+  size_t bytes;
+};
+
+SplitPlan split_plan(const GemmCall& call) {
+  SplitPlan sp{1, 0, big_tiles(call), 0};
+  if (call.offsets != nullptr || narrow_tiles(call) >= kCUs / 2 || sp.tiles == 0) return sp;
+  const int64_t ktot = call.dw ? call.M : call.N;
+  const int64_t nk = (ktot + BK - 1) / BK;
+  int64_t s = kCUs / sp.tiles;
+  if (s > nk / kMinSplitSlabs) s = nk / kMinSplitSlabs;
+  if (s < 2) return sp;
+  const int64_t per = (nk + s - 1) / s;                 // slabs per split
+  s = (nk + per - 1) / per;                             // no empty split
+  if (s < 2) return sp;
+  sp.splits = (int32_t)s;
+  sp.split_len = (int32_t)(per * BK);
+  const size_t counters = ((size_t)sp.tiles * 4 + 255) / 256 * 256;
+  sp.bytes = counters + (size_t)sp.tiles * s * Big::BP * Big::BQ * sizeof(float);
+  return sp;
 }
 
 }  // namespace
 }  // namespace gk
 
 using namespace gk;
+
+size_t gemm_workspace_bytes(const GemmCall& call) { return split_plan(call).bytes; }
 
 hipError_t launch_gemm(const GemmCall& call, hipStream_t stream) {
   Params prm{};
@@ -79,6 +127,7 @@ hipError_t launch_gemm(const GemmCall& call, hipStream_t stream) {
   prm.Qtot = (int32_t)call.K;
   prm.offsets = call.offsets;
   prm.groups = call.groups;
+  prm.splits = 1;
   if (!call.dw) {
     prm.Ptot = (int32_t)call.M;
     prm.Ktot = (int32_t)call.N;
@@ -88,12 +137,20 @@ hipError_t launch_gemm(const GemmCall& call, hipStream_t stream) {
     prm.Ktot = (int32_t)call.M;
     prm.c_batch = call.N * call.K;
   }
-  // Fewer than one full wave of 256-wide tiles across the 256 CUs: halve the
-  // tile width so that every CU gets work.
-  const int64_t big_tiles = (call.dw ? call.groups * ((call.N + 255) / 256) : (call.M + 255) / 256) *
-                            ((call.K + 255) / 256);
-  if (big_tiles < 256) return launch_cfg<Narrow>(call, prm, stream);
-  return launch_cfg<Big>(call, prm, stream);
+  if (big_tiles(call) >= kCUs) return launch_cfg<Big>(call, prm, stream);
+  // Fewer than one full wave of 256 x 256 tiles across the CUs: split the
+  // contraction when a large enough workspace is given, else halve the tile
+  // width so that every CU gets work.
+  const SplitPlan sp = split_plan(call);
+  if (sp.splits > 1 && call.ws != nullptr && call.ws_bytes >= sp.bytes) {
+    const size_t counters = ((size_t)sp.tiles * 4 + 255) / 256 * 256;
+    prm.splits = sp.splits;
+    prm.split_len = sp.split_len;
+    prm.cnt = static_cast<uint32_t*>(call.ws);
+    prm.ws = reinterpret_cast<float*>(static_cast<uint8_t*>(call.ws) + counters);
+    return launch_cfg<Big>(call, prm, stream);
+  }
+  return launch_cfg<Narrow>(call, prm, stream);
 }
 
 }  // namespace lp

@@ -107,7 +107,13 @@ struct Params {
   const int32_t* offsets;
   int32_t groups;
   int32_t nq;            // Q-tiles
-  int32_t ntiles;        // grid size
+  int32_t ntiles;        // grid size (output tiles x splits)
+  // Split contraction (dense calls only): `splits` workgroups share each
+  // output tile, split s covering contraction [s * split_len, (s+1) * split_len).
+  int32_t splits;        // 1: no split
+  int32_t split_len;     // multiple of BK
+  float* ws;             // fp32 partial tiles [tile][split][BP * BQ]
+  uint32_t* cnt;         // per-tile arrival counters, zero between calls
 };
 
 template <int kBP, int kBQ>
@@ -488,6 +494,7 @@ __device__ __forceinline__ int xcd_remap(int hw, int n) {
 // The output tile, group and contraction range of one workgroup.
 struct Tile {
   int g, p0, pend, q0, kbeg, kend;
+  int tile, split;       // output tile and contraction split (split calls)
   bool valid;
 };
 
@@ -495,8 +502,13 @@ struct Tile {
 template <class C, bool kDW>
 __device__ __forceinline__ Tile select_tile(const Params& p, int32_t* s_ends) {
   const int tid = threadIdx.x;
-  const int tile = xcd_remap(blockIdx.x, p.ntiles);
-  Tile t{0, 0, 0, 0, 0, p.Ktot, true};
+  int tile = xcd_remap(blockIdx.x, p.ntiles);
+  int split = 0;
+  if (p.splits > 1) {                                          // the splits of a tile are neighbours
+    split = tile % p.splits;
+    tile /= p.splits;
+  }
+  Tile t{0, 0, 0, 0, 0, p.Ktot, tile, split, true};
   if (p.offsets != nullptr) {
     for (int i = tid; i < p.groups; i += NT) s_ends[i] = p.offsets[i];
     __syncthreads();
@@ -548,6 +560,10 @@ __device__ __forceinline__ Tile select_tile(const Params& p, int32_t* s_ends) {
       t.kend = e;
     }
   }
+  if (p.splits > 1) {
+    t.kbeg = split * p.split_len;
+    t.kend = t.kbeg + p.split_len < p.Ktot ? t.kbeg + p.split_len : p.Ktot;
+  }
   return t;
 }
 
@@ -594,6 +610,65 @@ __device__ __forceinline__ void store_acc(const Params& p, const Tile& t, f32x16
     if (row < t.pend && col < p.Qtot)
       *reinterpret_cast<u32x4*>(out + (int64_t)row * p.ldc + col) = u32x4{lo[0], lo[1], hi[0], hi[1]};
   }
+}
+
+// Split contraction: every split writes its fp32 partial tile to the
+// workspace, then counts itself in at the tile's counter; the workgroup that
+// arrives last adds the partials of all splits in split order (its own from
+// registers) and goes on to the bf16 epilogue, the others end.  Nothing
+// waits on another workgroup.  The sum is the same whichever split arrives
+// last.  The last one clears the counter for the next call.  Partials are
+// laid out [wave][16-byte piece][lane] so that every access of a wave is one
+// contiguous KiB.  `flag` is LDS for broadcasting the arrival count.
+// Ordering: each wave waits for its own partial stores, the workgroup
+// barrier orders them before thread 0's device-scope acquire-release
+// increment (whose release writes the L2 back, whose acquire invalidates the
+// L2 and this CU's L1), and a second barrier orders that increment before
+// any wave of the last arriver reads the other partials.  One release and
+// one acquire per workgroup: issuing them from every wave costs a whole-L2
+// write-back each.
+template <class C>
+__device__ __forceinline__ bool reduce_split(const Params& p, const Tile& t, f32x16 (&acc)[C::FP][C::FQ], int wave,
+                                             int lane, uint32_t* flag) {
+  constexpr int NV = C::FP * C::FQ * 4;                          // 16-byte pieces per lane
+  constexpr size_t kTileFloats = (size_t)C::BP * C::BQ;
+  f32x4* const base = reinterpret_cast<f32x4*>(p.ws + (size_t)t.tile * p.splits * kTileFloats) +
+                      (size_t)wave * NV * 64 + lane;
+  constexpr size_t kSplitStride = kTileFloats / 4;               // f32x4 pieces per split
+  f32x4* const mine = base + (size_t)t.split * kSplitStride;
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const f32x16& a = acc[v / (4 * C::FQ)][(v / 4) % C::FQ];
+    const int r = v % 4;
+    __builtin_nontemporal_store(f32x4{a[4 * r], a[4 * r + 1], a[4 * r + 2], a[4 * r + 3]}, mine + v * 64);
+  }
+  __builtin_amdgcn_s_waitcnt(0);                                 // this wave's partial stores done
+  __syncthreads();
+  if (threadIdx.x == 0) *flag = __hip_atomic_fetch_add(p.cnt + t.tile, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const bool last = *flag == (uint32_t)(p.splits - 1);
+  __syncthreads();                                               // flag read before LDS is reused
+  if (!last) return false;
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    f32x16& a = acc[v / (4 * C::FQ)][(v / 4) % C::FQ];
+    const int r = v % 4;
+    const f32x4 own = {a[4 * r], a[4 * r + 1], a[4 * r + 2], a[4 * r + 3]};
+    f32x4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s = 0; s < p.splits; ++s) {
+      const f32x4 x = s == t.split ? own : __builtin_nontemporal_load(base + (size_t)s * kSplitStride + v * 64);
+      sum[0] += x[0];
+      sum[1] += x[1];
+      sum[2] += x[2];
+      sum[3] += x[3];
+    }
+    a[4 * r] = sum[0];
+    a[4 * r + 1] = sum[1];
+    a[4 * r + 2] = sum[2];
+    a[4 * r + 3] = sum[3];
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(p.cnt + t.tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
 }
 
 // s_waitcnt vmcnt(N) lgkmcnt(0), then s_barrier.  Written out because the
@@ -802,6 +877,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   __syncthreads();
   constexpr int SB = C::WP * C::WQ * 2;                          // staging bytes per wave
   static_assert(PD ? (PBUF >= SB && 2 * QBUF >= SB) : (2 * PBUF >= 2 * SB && 2 * QBUF >= 2 * SB), "staging fits");
+  if (p.splits > 1 && !reduce_split<C>(p, t, acc, wave, lane, reinterpret_cast<uint32_t*>(sq))) return;
   uint8_t* stage = PD ? (wave == 0 ? sp0 : wave == 1 ? sp1 : wave == 2 ? sp2 : sq)
                       : (wave < 2 ? sp0 + wave * SB : sq + (wave - 2) * SB);
   store_acc<C, kDW>(p, t, acc, wp, wq, lane, stage);

@@ -49,7 +49,13 @@ struct GemmCall {
   int32_t groups;
   int64_t M, N, K;
   void* out;
+  void* ws;                 // workspace for split contractions, or nullptr
+  size_t ws_bytes;
 };
 hipError_t launch_gemm(const GemmCall& call, hipStream_t stream);
+
+// Workspace bytes the contraction would use to split its contraction
+// (0: it does not split).
+size_t gemm_workspace_bytes(const GemmCall& call);
 
 }  // namespace lp

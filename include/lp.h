@@ -62,6 +62,7 @@
 #ifndef LP_H
 #define LP_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -168,6 +169,45 @@ lp_status lp_mx_quant(const void* src_bf16, int64_t batch, int64_t rows, int64_t
  */
 lp_status lp_linear_bwd(const lp_qtensor* grad_out, const lp_qtensor* x, const lp_qtensor* w,
                         void* grad_x, void* grad_w, void* stream);
+
+/*
+ * lp_linear_bwd_workspace - workspace bytes that lp_linear_bwd_ws can use to
+ * split the contraction of this call across workgroups.
+ *
+ * Arguments as for lp_linear_bwd; grad_x and grad_w only say which outputs
+ * are wanted (non-NULL) and are not dereferenced.  *bytes is 0 when the
+ * call does not split (its 256 x 256 output tiles already fill the GPU, or
+ * its contraction is short); otherwise it is the size of a workspace that
+ * lets lp_linear_bwd_ws split it.  Checks and errors as for lp_linear_bwd.
+ */
+lp_status lp_linear_bwd_workspace(const lp_qtensor* grad_out, const lp_qtensor* x, const lp_qtensor* w,
+                                  const void* grad_x, const void* grad_w, size_t* bytes);
+
+/*
+ * lp_linear_bwd_ws - lp_linear_bwd with a caller-owned workspace.
+ *
+ * Cites: as lp_linear_bwd (same operation, same results up to fp32
+ * summation order).
+ *
+ * When a contraction has fewer 256 x 256 output tiles than the GPU has
+ * compute units, the library splits its contraction over several
+ * workgroups per tile: each writes an fp32 partial tile into the workspace,
+ * and the last to finish sums the partials in a fixed order and writes the
+ * bf16 output.  The result does not depend on which workgroup finishes
+ * last.
+ *
+ * workspace        device memory, 256-byte aligned, or NULL (no splitting).
+ * workspace_bytes  its size; if smaller than lp_linear_bwd_workspace
+ *                  reports, the call does not split (still correct).
+ * The workspace must be zero-filled before its first use; every completed
+ * call leaves the part that must start at zero (per-tile counters) zero
+ * again.  Two calls that may run at the same time (other streams, other
+ * threads) must not share a workspace.  Other arguments, rules and errors
+ * as for lp_linear_bwd; LP_ERR_ALIGN for a misaligned workspace.
+ */
+lp_status lp_linear_bwd_ws(const lp_qtensor* grad_out, const lp_qtensor* x, const lp_qtensor* w,
+                           void* grad_x, void* grad_w, void* workspace, size_t workspace_bytes,
+                           void* stream);
 
 /*
  * lp_grouped_bwd - backward of a grouped (per-expert) matmul.

@@ -14,7 +14,8 @@ FAKE = 0x10000          # 16-byte aligned stand-in pointer; never dereferenced h
 
 def test_library_exports_every_header_function():
     names = lp.header_functions()
-    assert set(names) == {"lp_dequant", "lp_mx_quant", "lp_linear_bwd", "lp_grouped_bwd", "lp_status_string"}
+    assert set(names) == {"lp_dequant", "lp_mx_quant", "lp_linear_bwd", "lp_grouped_bwd", "lp_status_string",
+                          "lp_linear_bwd_workspace", "lp_linear_bwd_ws"}
     for n in names:
         assert hasattr(lp.lib, n), n
 
@@ -103,3 +104,42 @@ def test_grouped_bwd_rejects():
     assert call(None, 4) == NULL
     assert call(FAKE + 2, 4) == ALIGN
     assert call(FAKE, 3) == SHAPE          # w batch must equal groups
+
+
+def ws_bytes(g, x, w, dx=True, dw=True):
+    n = ctypes.c_size_t(123)
+    st = lp.lib.lp_linear_bwd_workspace(ctypes.byref(g), ctypes.byref(x) if x else None,
+                                        ctypes.byref(w) if w else None, 1 if dx else None, 1 if dw else None,
+                                        ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_size_rules():
+    # dX of the frozen FP8 weight: 256 tiles of 256 x 128 fill the CUs -> no split
+    g = q("bf16", 4096, 8192)
+    st, n = ws_bytes(g, None, q("fp8_b128", 8192, 2048), dw=False)
+    assert st == OK and n == 0
+    # dX with 2 x 3 tiles of 256 x 256 over N = 4096: 64 slabs -> 4 splits of 16 slabs,
+    # 6 per-tile counters (24 B, rounded to 256) + 6 x 4 fp32 tiles of 256 x 256
+    st, n = ws_bytes(q("bf16", 300, 4096), None, q("fp8_b128", 4096, 544), dw=False)
+    assert st == OK and n == 256 + 6 * 4 * 256 * 256 * 4
+    # enough tiles already: no split
+    st, n = ws_bytes(q("bf16", 8192, 4096), q("nvfp4", 8192, 4096), q("nvfp4", 4096, 4096))
+    assert st == OK and n == 0
+    # short contraction (2 slabs): no split
+    st, n = ws_bytes(q("bf16", 64, 128), q("mxfp4", 64, 128), q("mxfp4", 128, 128))
+    assert st == OK and n == 0
+    # dW over a long token axis: 1 x 2 tiles, 4096 / 64 = 64 slabs -> 4 splits of 16 slabs
+    st, n = ws_bytes(q("bf16", 4096, 256), q("bf16", 4096, 512), None, dx=False)
+    assert st == OK and n == 256 + 2 * 4 * 256 * 256 * 4
+    # argument errors as for lp_linear_bwd
+    st, n = ws_bytes(q("bf16", 64, 128), q("mxfp4", 63, 128), None, dx=False)
+    assert st == SHAPE and n == 0
+    assert lp.lib.lp_linear_bwd_workspace(ctypes.byref(g), None, None, 1, None, None) == NULL
+
+
+def test_linear_bwd_ws_rejects_misaligned_workspace():
+    g = q("bf16", 4096, 8192)
+    w = q("fp8_b128", 8192, 2048)
+    assert lp.lib.lp_linear_bwd_ws(ctypes.byref(g), None, ctypes.byref(w), FAKE, None, FAKE + 16, 1 << 30,
+                                   None) == ALIGN

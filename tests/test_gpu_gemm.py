@@ -75,6 +75,79 @@ def test_linear_mxfp8_grad(lp):
     assert_close(dx, O.linear_dx(gd, wd[0]), "mxfp8 x mxfp8 dX")
 
 
+def _workspace(lp, g, x, w, need_dx=True, need_dw=True):
+    n = lp.lp_linear_bwd_workspace(g, x, w, need_dx, need_dw)
+    assert n > 0, "shape expected to split its contraction"
+    return torch.zeros(n, dtype=torch.uint8, device="cuda")
+
+
+def _counters_zero(ws, tiles):
+    assert int(ws[: 4 * tiles].count_nonzero()) == 0, "per-tile counters not cleared"
+
+
+@pytest.mark.parametrize("fmt,axis", FORMATS)
+def test_split_dx(lp, fmt, axis):
+    """dX over a long contraction with few output tiles: M = 300 (ragged),
+    N = 4096, K = 544 -> 2 x 3 tiles of 256 x 256, four splits of 16 slabs.
+    Two calls in a row give the same bits (the sum does not depend on which
+    split finishes last) and leave the counters at zero."""
+    M, N, K = 300, 4096, 544
+    g, gb = _grad(lp, 35, M, N)
+    w, wd = _operand(lp, 35, "w", (N, K), fmt, axis)
+    ws = _workspace(lp, g, None, w, need_dw=False)
+    dx1, _ = lp.lp_linear_bwd(g, None, w, need_dw=False, workspace=ws)
+    dx2, _ = lp.lp_linear_bwd(g, None, w, need_dw=False, workspace=ws)
+    torch.cuda.synchronize()
+    _counters_zero(ws, 6)
+    assert_close(dx1, O.linear_dx(gb, wd[0]), f"{fmt}{axis} split dX")
+    assert_bits_equal(bits_host(dx2), bits_host(dx1), "second call")
+
+
+@pytest.mark.parametrize("fmt,axis", FORMATS)
+def test_split_dw(lp, fmt, axis):
+    """dW over a long, ragged token axis: M = 4100 (4128 for X scaled along
+    rows), N = 272, K = 544 -> 2 x 3 tiles, 65 slabs in four splits, the last
+    one short and ragged."""
+    M = 4128 if (fmt == "mxfp8" and axis == -2) else 4100
+    N, K = 272, 544
+    g, gb = _grad(lp, 36, M, N)
+    x, xd = _operand(lp, 36, "x", (M, K), fmt, axis)
+    ws = _workspace(lp, g, x, None, need_dx=False)
+    _, dw1 = lp.lp_linear_bwd(g, x, None, need_dx=False, workspace=ws)
+    _, dw2 = lp.lp_linear_bwd(g, x, None, need_dx=False, workspace=ws)
+    torch.cuda.synchronize()
+    _counters_zero(ws, 6)
+    assert_close(dw1, O.linear_dw(gb, xd[0]), f"{fmt}{axis} split dW")
+    assert_bits_equal(bits_host(dw2), bits_host(dw1), "second call")
+
+
+def test_split_mxfp8_grad(lp):
+    """Split dX with an MX-quantized gradient and an MXFP8 weight along its
+    reduction axis."""
+    M, N, K = 520, 4096, 448
+    g, gd = _grad(lp, 37, M, N, fmt="mxfp8")
+    w, wd = _operand(lp, 37, "w", (N, K), "mxfp8", -2, sigma=0.02)
+    ws = _workspace(lp, g, None, w, need_dw=False)
+    dx, _ = lp.lp_linear_bwd(g, None, w, need_dw=False, workspace=ws)
+    torch.cuda.synchronize()
+    _counters_zero(ws, 3 * 2)
+    assert_close(dx, O.linear_dx(gd, wd[0]), "mxfp8 x mxfp8 split dX")
+
+
+def test_split_workspace_too_small_falls_back(lp):
+    """A workspace smaller than reported: the call does not split, same result
+    within tolerance, workspace untouched."""
+    M, N, K = 300, 4096, 544
+    g, gb = _grad(lp, 38, M, N)
+    w, wd = _operand(lp, 38, "w", (N, K), "fp8_b128", -1)
+    n = lp.lp_linear_bwd_workspace(g, None, w, True, False)
+    ws = torch.zeros(n - 256, dtype=torch.uint8, device="cuda")
+    dx, _ = lp.lp_linear_bwd(g, None, w, need_dw=False, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(ws.count_nonzero()) == 0
+    assert_close(dx, O.linear_dx(gb, wd[0]), "fallback dX")
+
+
 def _sentinel(shape):
     return torch.full(shape, -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)   # 0xFFFF (NaN)
 
@@ -146,15 +219,32 @@ def _sample_rows(n, k, seed):
 
 
 def test_fp8_frozen_full_size(lp):
-    """4096 x 8192 grad, 8192 x 2048 E4M3 weight: dX, 64 sampled rows."""
+    """4096 x 8192 grad, 8192 x 2048 E4M3 weight: dX, 64 sampled rows (the
+    256 x 128 tiles fill the GPU, so no workspace is asked for)."""
     w = W.WORKLOADS["fp8_frozen"]
     X, Wt, G = W.dense_inputs(w)
     wq, wd = quantize(lp, "fp8_b128", Wt)
     g = lp.QTensor("bf16", bf16_dev(G), shape=(1, w.M, w.N))
+    assert lp.lp_linear_bwd_workspace(g, None, wq, True, False) == 0
     dx, _ = lp.lp_linear_bwd(g, None, wq, need_dw=False)
     torch.cuda.synchronize()
     rows = _sample_rows(w.M, 64, 40)
     assert_close(dx[torch.from_numpy(rows).cuda()], O.rows_dx(G, wd[0], rows), "fp8 frozen dX")
+
+
+def test_split_dw_full_contraction(lp):
+    """A low-rank-adapter-sized dW: N = 256, K = 512 over all 16384 tokens of
+    an NVFP4 input (two 256 x 256 tiles, 256 slabs in 16 splits); 32 sampled
+    rows of dW against the oracle."""
+    M, N, K = 16384, 256, 512
+    g, gb = _grad(lp, 39, M, N)
+    x, xd = _operand(lp, 39, "x", (M, K), "nvfp4", -1)
+    ws = _workspace(lp, g, x, None, need_dx=False)
+    _, dw = lp.lp_linear_bwd(g, x, None, need_dx=False, workspace=ws)
+    torch.cuda.synchronize()
+    _counters_zero(ws, 2)
+    nrows = _sample_rows(N, 32, 43)
+    assert_close(dw[torch.from_numpy(nrows).cuda()], O.rows_dw(gb, xd[0], nrows), "split dW 16384 tokens")
 
 
 def test_nvfp4_linear_full_size(lp):
