@@ -68,6 +68,7 @@ typedef short i16x8v __attribute__((ext_vector_type(8)));
 constexpr int BK = 64;
 constexpr int NT = 256;                 // four waves, one per SIMD
 constexpr int kMaxGroups = 1024;
+constexpr int kLptGroups = 256;         // grouped dW ranks groups by size up to this many
 constexpr int kMaxLds = 160 * 1024;
 
 template <class F, int... I>
@@ -513,7 +514,7 @@ __device__ __forceinline__ Tile select_tile(const Params& p, int32_t* s_ends) {
     for (int i = tid; i < p.groups; i += NT) s_ends[i] = p.offsets[i];
     __syncthreads();
   }
-  if constexpr (!kDW) {
+  if (!kDW) {
     // Groups partition the output rows; tiles never straddle a group.
     const int pidx = tile / p.nq;
     t.q0 = (tile % p.nq) * C::BQ;
@@ -538,12 +539,46 @@ __device__ __forceinline__ Tile select_tile(const Params& p, int32_t* s_ends) {
       }
     }
     t.valid = t.p0 >= 0 && t.p0 < t.pend;
-  } else {
+  } else if (p.offsets != nullptr && p.groups <= kLptGroups) {
     // Groups partition the contraction; every group has np x nq tiles, whose
-    // cost grows with the group's size.  Tiles are dealt round-robin over the
-    // groups so that each XCD's contiguous range holds an equal share of
-    // every group (dealing whole groups to XCDs would leave the XCD with the
-    // largest group running long after the others).
+    // cost grows with the group's size.  Longest first: the tiles are listed
+    // by group in decreasing size (ties by group index) and taken in
+    // hardware dispatch order, which deals consecutive tiles to the XCDs in
+    // turn, so every XCD starts on its share of the largest group and the
+    // short tiles fill in behind (longest-processing-time-first list
+    // scheduling).
+    int32_t* ends = s_ends + kMaxGroups / 2;                   // clamped ends (groups <= kLptGroups)
+    int32_t* pick = s_ends + kMaxGroups - 1;
+    for (int i = tid; i < p.groups; i += NT) {
+      int e = 0;                                               // end_i = min(max(0, o_0..o_i), M)
+      for (int j = 0; j <= i; ++j) e = s_ends[j] > e ? s_ends[j] : e;
+      ends[i] = e < p.Ktot ? e : p.Ktot;
+    }
+    __syncthreads();
+    const int per = p.ntiles / p.groups;                       // tiles per group
+    const int pos = blockIdx.x;
+    const int rank = pos / per;
+    for (int i = tid; i < p.groups; i += NT) {
+      const int si = ends[i] - (i ? ends[i - 1] : 0);
+      int r = 0;
+      for (int j = 0; j < p.groups; ++j) {
+        const int sj = ends[j] - (j ? ends[j - 1] : 0);
+        r += (sj > si || (sj == si && j < i)) ? 1 : 0;
+      }
+      if (r == rank) *pick = i;
+    }
+    __syncthreads();
+    t.g = *pick;
+    const int r = pos - rank * per;
+    t.p0 = (r / p.nq) * C::BP;
+    t.q0 = (r % p.nq) * C::BQ;
+    t.pend = p.Ptot;
+    t.kbeg = t.g ? ends[t.g - 1] : 0;
+    t.kend = ends[t.g];
+  } else {
+    // Dense dW, or too many groups to rank per workgroup: tiles are dealt
+    // round-robin over the groups so that each XCD's contiguous range holds
+    // an equal share of every group.
     t.g = tile % p.groups;
     const int r = tile / p.groups;
     t.p0 = (r / p.nq) * C::BP;

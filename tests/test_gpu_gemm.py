@@ -175,6 +175,32 @@ def test_grouped_edges(lp, fmt, axis):
     assert np.all(bits_host(dw[1]) == 0), "empty group's dW is not zero"
 
 
+@pytest.mark.parametrize("sizes_kind", ["ties", "many"])
+def test_grouped_orders(lp, sizes_kind):
+    """Grouped dW tile orders: equal group sizes (the size ranking breaks ties
+    by group index) and 300 groups (more than are ranked by size, so tiles
+    are dealt round-robin), with empty groups among them."""
+    if sizes_kind == "ties":
+        sizes = [96, 96, 0, 96, 96, 96, 0, 96]
+        M = 640
+    else:
+        g0 = W.rng(44, "route")
+        sizes = g0.integers(0, 9, size=300)
+        sizes[g0.choice(300, size=30, replace=False)] = 0
+        M = int(sizes.sum()) + 20
+    G = len(sizes)
+    N, K = 128, 256
+    offsets = W.cumulative_ends(np.asarray(sizes))
+    g, gb = _grad(lp, 44, M, N)
+    x, xd = _operand(lp, 44, "x", (M, K), "mxfp4", -1)
+    w, wd = _operand(lp, 44, "w", (G, N, K), "mxfp4", -1)
+    dx, dw = lp.lp_grouped_bwd(g, x, w, torch.from_numpy(offsets).cuda())
+    torch.cuda.synchronize()
+    ref_dx, end = O.grouped_dx(gb, wd, offsets)
+    assert_close(dx[:end], ref_dx[:end], f"{sizes_kind} grouped dX")
+    assert_close(dw, O.grouped_dw(gb, xd[0], offsets), f"{sizes_kind} grouped dW")
+
+
 def test_grouped_one_group_equals_linear(lp):
     """One group spanning all rows gives bit-identical results to the linear
     backward (same kernels, same tile order)."""
