@@ -93,9 +93,15 @@ struct SplitPlan {
   size_t bytes;
 };
 
+// dX of an MXFP8 gradient and an MXFP8 weight scaled along its rows: both
+// scales run along the contraction, so the block-scaled MFMA applies them.
+bool native_mx(const GemmCall& call) {
+  return !call.dw && call.grad->fmt == LP_MXFP8 && call.other->fmt == LP_MXFP8 && call.other->scale_axis == -2;
+}
+
 SplitPlan split_plan(const GemmCall& call) {
   SplitPlan sp{1, 0, big_tiles(call), 0};
-  if (call.offsets != nullptr || narrow_tiles(call) >= kCUs / 2 || sp.tiles == 0) return sp;
+  if (call.offsets != nullptr || native_mx(call) || narrow_tiles(call) >= kCUs / 2 || sp.tiles == 0) return sp;
   const int64_t ktot = call.dw ? call.M : call.N;
   const int64_t nk = (ktot + BK - 1) / BK;
   int64_t s = kCUs / sp.tiles;
@@ -136,6 +142,12 @@ hipError_t launch_gemm(const GemmCall& call, hipStream_t stream) {
     prm.Ptot = (int32_t)call.N;
     prm.Ktot = (int32_t)call.M;
     prm.c_batch = call.N * call.K;
+  }
+  if (native_mx(call)) {
+    prm.nq = (int32_t)((prm.Qtot + Big::BQ - 1) / Big::BQ);
+    const int64_t ptiles = call.offsets ? (call.M / Big::BP + call.groups) : (call.M + Big::BP - 1) / Big::BP;
+    prm.ntiles = (int32_t)(ptiles * prm.nq);
+    return dx_mx(prm, stream);
   }
   if (big_tiles(call) >= kCUs) return launch_cfg<Big>(call, prm, stream);
   // Fewer than one full wave of 256 x 256 tiles across the CUs: split the

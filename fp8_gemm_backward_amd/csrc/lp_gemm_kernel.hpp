@@ -949,6 +949,9 @@ hipError_t dx_narrow_bf16(const lp_qtensor& q, const Params& prm, hipStream_t s)
 hipError_t dx_narrow_mxfp8(const lp_qtensor& q, const Params& prm, hipStream_t s);
 hipError_t dw_big(const lp_qtensor& q, const Params& prm, hipStream_t s);
 hipError_t dw_narrow(const lp_qtensor& q, const Params& prm, hipStream_t s);
+// MXFP8 gradient x MXFP8 weight scaled along its rows, on the block-scaled MFMA
+// (256 x 256 tiles, no split).
+hipError_t dx_mx(const Params& prm, hipStream_t s);
 
 }  // namespace gk
 }  // namespace lp

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import workloads as W
-from gpu_util import assert_bits_equal, assert_close, bf16_dev, bits_host, quantize
+from gpu_util import assert_bits_equal, assert_close, bf16_dev, bits_host, dev, quantize
 from oracle import formats as F
 from oracle import gemm as O
 
@@ -122,16 +122,69 @@ def test_split_dw(lp, fmt, axis):
 
 
 def test_split_mxfp8_grad(lp):
-    """Split dX with an MX-quantized gradient and an MXFP8 weight along its
-    reduction axis."""
+    """Split dX with an MX-quantized gradient and an MXFP4 weight (decoded
+    to bf16 in the mainloop)."""
     M, N, K = 520, 4096, 448
     g, gd = _grad(lp, 37, M, N, fmt="mxfp8")
-    w, wd = _operand(lp, 37, "w", (N, K), "mxfp8", -2, sigma=0.02)
+    w, wd = _operand(lp, 37, "w", (N, K), "mxfp4", -1, sigma=0.02)
     ws = _workspace(lp, g, None, w, need_dw=False)
     dx, _ = lp.lp_linear_bwd(g, None, w, need_dw=False, workspace=ws)
     torch.cuda.synchronize()
     _counters_zero(ws, 3 * 2)
-    assert_close(dx, O.linear_dx(gd, wd[0]), "mxfp8 x mxfp8 split dX")
+    assert_close(dx, O.linear_dx(gd, wd[0]), "mxfp8 x mxfp4 split dX")
+
+
+def test_native_mx_needs_no_workspace(lp):
+    """MXFP8 gradient x MXFP8 weight along its reduction axis runs on the
+    block-scaled MFMA, which does not split."""
+    g, _ = _grad(lp, 45, 520, 4096, fmt="mxfp8")
+    w, _ = _operand(lp, 45, "w", (4096, 448), "mxfp8", -2, sigma=0.02)
+    assert lp.lp_linear_bwd_workspace(g, None, w, True, False) == 0
+
+
+@pytest.mark.parametrize("N", [288, 2048])
+def test_native_mx_grouped_edges(lp, N):
+    """Block-scaled MFMA path, grouped: an empty group, a group smaller than
+    a tile, ragged group ends, rows past the last offset kept, output width
+    336 (a partial 256-column tile) and, for N = 288, a contraction ending
+    half way through a 64-deep slab."""
+    M, K, G = 700, 336, 5
+    sizes = [130, 0, 17, 300, 203]
+    offsets = W.cumulative_ends(sizes)
+    g, gd = _grad(lp, 46, M, N, fmt="mxfp8")
+    w, wd = _operand(lp, 46, "w", (G, N, K), "mxfp8", -2, sigma=0.02)
+    dx0 = _sentinel((M, K))
+    dx, _ = lp.lp_grouped_bwd(g, None, w, torch.from_numpy(offsets).cuda(), need_dw=False, grad_x=dx0)
+    torch.cuda.synchronize()
+    ref, end = O.grouped_dx(gd, wd, offsets)
+    assert_close(dx[:end], ref[:end], f"native mx grouped dX N={N}")
+    assert np.all(bits_host(dx[end:]) == 0xFFFF), "rows past the last offset were written"
+
+
+def test_native_mx_matches_decode_path_with_nan_blocks(lp):
+    """The block-scaled MFMA and the decode-to-bf16 path agree: on finite
+    blocks within the tolerance, and a gradient block with scale 0xFF (NaN)
+    makes the same output rows NaN in both."""
+    M, N, K = 300, 512, 288
+    gbits = W.bf16_bits(W.normal_f32(47, "grad", (1, M, N), 1.0))
+    gc, gs = F.mx_quant(gbits, -1, "e4m3")
+    gs = gs.copy()
+    gs[0, 7, 3] = 0xFF                           # row 7, columns 96..127
+    gs[0, 200, 15] = 0xFF                        # row 200, columns 480..511
+    g = lp.QTensor("mxfp8", dev(gc[0]), dev(gs[0]), shape=(1, M, N), axis=-1)
+    w, wd = _operand(lp, 47, "w", (N, K), "mxfp8", -2, sigma=0.02)
+    dx_native, _ = lp.lp_linear_bwd(g, None, w, need_dw=False)
+    gbf = lp.lp_dequant(g)
+    gq = lp.QTensor("bf16", gbf.view(M, N), shape=(1, M, N))
+    dx_decode, _ = lp.lp_linear_bwd(gq, None, w, need_dw=False)
+    torch.cuda.synchronize()
+    a = dx_native.float().cpu().numpy()
+    b = dx_decode.float().cpu().numpy()
+    assert np.array_equal(np.isnan(a), np.isnan(b))
+    assert np.isnan(a[7]).all() and np.isnan(a[200]).all() and not np.isnan(np.delete(a, [7, 200], 0)).any()
+    fin = np.delete(np.arange(M), [7, 200])
+    ref = O.linear_dx(F.dequant("mxfp8", gc, gs, axis=-1)[0][fin], wd[0])
+    assert_close(dx_native[torch.from_numpy(fin).cuda()], ref, "native vs oracle, finite rows")
 
 
 def test_split_workspace_too_small_falls_back(lp):
