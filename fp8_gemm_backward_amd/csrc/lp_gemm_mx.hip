@@ -45,9 +45,10 @@ constexpr int XFP = 4, XFQ = 4;                 // 32 x 32 blocks per wave
 constexpr int XBK = 64;                         // contraction per slab
 constexpr int kPBytes = XBP * XBK;              // gradient codes per slab
 constexpr int kQBytes = XBK * XBQ;              // weight codes per slab
-constexpr int kSBytes = 4096;                   // scales, one dword each: grad [wp][256], weight [wq][256]
-constexpr int kStageBytes = kPBytes + kQBytes + kSBytes;
-constexpr int kVmPerSlab = 4 + 4 + 4;           // direct loads per wave and slab
+constexpr int kTileBytes = kPBytes + kQBytes;
+constexpr int kGatherBytes = 4096;              // gathered scales of one slab (byte-gather mode)
+constexpr int kChunkSlabs = 8;                  // slabs per scale chunk (chunk mode)
+constexpr int kChunkBytes = XBP * 16 + 16 * XBQ;  // grad [256 rows][16 blocks] + weight [16 blocks][256 cols]
 using XCfg = Cfg<XBP, XBQ>;
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -62,13 +63,37 @@ __device__ __forceinline__ int p_swz(int m) { return (m >> 2) & 3; }
 // distinct slots.
 __device__ __forceinline__ int q_swz(int n) { return 2 * (n & 7); }
 
+// Scale bytes reach LDS in one of two ways.
+// * Chunk mode (the gradient's scale rows are 16-byte aligned: N % 512 ==
+//   0): every eight slabs, one 16-byte load per gradient row (its next 16
+//   scale blocks) and 16 weight scale rows of 256 bytes, double-buffered;
+//   each slab a lane reads its eight scale bytes (four fragments of each
+//   operand) with byte reads.  Scale blocks at or past the end of the
+//   contraction are zeroed in registers (their codes are zero, and a NaN
+//   scale would turn the zero products into NaN).
+// * Byte-gather mode (any N % 32 == 0): every slab, 1-byte direct loads
+//   gather exactly the bytes each lane needs.  A 1- or 2-byte direct load
+//   writes each lane's value as a zero-extended dword at 4 i (measured),
+//   which is the form the MFMA's scale operand takes (opsel 0).  The 4 KiB
+//   block holds grad scales [wp][256] then weight scales [wq][256]; position
+//   x = 64 u + i of a region holds the scale of block x / 128 of row
+//   (column) 32 (i % 4) + 16 (u & 1) + i / 4 of that wave tile, so that one
+//   16-byte read gives a lane its four fragments' scales.  This issues one
+//   memory request per byte, which costs a quarter of the dense throughput.
+template <bool kChunk>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void mx_dx_kernel(Params p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t st0[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t st1[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t st2[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t st3[kStageBytes];
-  static_assert(kMaxGroups * 4 <= kStageBytes, "group ends alias stage 0");
-  static_assert(XWP * XWQ * 2 <= kStageBytes, "epilogue staging fits a stage");
+  constexpr int kStage = kChunk ? kTileBytes : kTileBytes + kGatherBytes;
+  constexpr int T = kChunk ? 8 : 12;                             // direct loads per wave and slab
+  constexpr int S = 2;                                           // chunk loads per wave
+  constexpr int UNROLL = kChunk ? 2 * kChunkSlabs : 4;           // stage, register set and chunk buffer fixed
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t st2[kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t st3[kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t sc0[kChunk ? kChunkBytes : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t sc1[kChunk ? kChunkBytes : 16];
+  static_assert(kMaxGroups * 4 <= kStage, "group ends alias stage 0");
+  static_assert(XWP * XWQ * 2 <= kStage, "epilogue staging fits a stage");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -89,6 +114,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   const int64_t psrow_bytes = (int64_t)(M - t.p0) * sldp;
   const uint8_t* qc = p.Q.codes + (int64_t)t.g * p.Q.code_batch;
   const Rsrc qs_r = make_rsrc(p.Q.scales + (int64_t)t.g * p.Q.scale_batch, p.Q.scale_bytes);
+  const Rsrc ps_r = make_rsrc(ps, psrow_bytes);
 
   // Per-lane parts of the direct loads, fixed for the whole loop; the parts
   // that differ between a wave's loads are uniform (scalar offsets).
@@ -105,34 +131,32 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   const int qc0 = (lane & 15) ^ (2 * (lane >> 4));
   const int32_t q_base = (16 * wave + lane / 16) * ldq + t.q0;   // + 4 u ldq
   const int32_t q_off_even = q_base + 16 * qc0, q_off_odd = q_base + 16 * (qc0 ^ 8);
-  // Scale bytes: a 1- or 2-byte direct load writes each lane's value as a
-  // zero-extended dword at 4 i (measured), which is the form the MFMA's scale
-  // operand takes (opsel 0).  The 4 KiB scale block holds grad scales
-  // [wp][256] then weight scales [wq][256], one dword each; waves 0, 1 gather
-  // the grad regions, waves 2, 3 the weight regions, 64 positions per load u.
-  // Position x = 64 u + i of a region holds (h, r, f) = (u / 2, 16 (u & 1) +
-  // i / 4, i % 4): the scale of block h of row (column) 32 f + r of that wave
-  // tile, so that one 16-byte read gives a lane its four fragments' scales.
+  // Byte-gather mode: waves 0, 1 gather the grad regions, waves 2, 3 the
+  // weight regions, 64 positions per load u.
   const bool s_grad = wave < 2;
-  const int s_region = wave & 1;
-  const int s_rc = s_region * 128 + 32 * (lane & 3) + lane / 4;  // + 16 (u & 1)
+  const int s_rc = (wave & 1) * 128 + 32 * (lane & 3) + lane / 4;   // + 16 (u & 1)
   const int32_t s_lane = s_grad ? s_rc * sldp : t.q0 + s_rc;
   const int32_t s_rstep = s_grad ? sldp : 1;                     // per row (column)
   const int32_t s_bstep = s_grad ? 1 : sldq;                     // per scale block
-  const Rsrc s_rsrc = s_grad ? make_rsrc(ps, psrow_bytes) : qs_r;
-  const int s_dst = kPBytes + kQBytes + 1024 * wave;
+  const Rsrc s_rsrc = s_grad ? ps_r : qs_r;
+  const int s_dst = kTileBytes + 1024 * wave;
 
   auto stage = [&](auto si) -> uint8_t* {
-    constexpr int S = decltype(si)::value % 4;
-    if constexpr (S == 0) return st0;
-    else if constexpr (S == 1) return st1;
-    else if constexpr (S == 2) return st2;
+    constexpr int I = decltype(si)::value % 4;
+    if constexpr (I == 0) return st0;
+    else if constexpr (I == 1) return st1;
+    else if constexpr (I == 2) return st2;
     else return st3;
+  };
+  auto chunkbuf = [&](auto ci) -> uint8_t* {
+    if constexpr (decltype(ci)::value % 2 == 0) return sc0;
+    else return sc1;
   };
 
   // Direct loads of the slab at contraction k0 into stage buffer `sb`,
-  // item u (0..11): gradient codes, weight codes, scale bytes.  Contraction
-  // index k0 + 32 and up is past the end only in the last slab (N % 32 == 0).
+  // item u: gradient codes (0..3), weight codes (4..7), gathered scale bytes
+  // (8..11, byte-gather mode).  Contraction index k0 + 32 and up is past the
+  // end only in the last slab (N % 32 == 0).
   auto issue = [&](auto ui, uint8_t* sb, int k0) {
     constexpr int u = decltype(ui)::value;
     if constexpr (u < 4) {
@@ -153,6 +177,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
                                                out ? kOOB : s_lane, so, 0, 0);
     }
   };
+  // Chunk mode: scale blocks [kb, kb + 16) of the tile, kb = k0 / 32 of the
+  // chunk's first slab.  Gradient: row 64 w + i, 16 bytes; weight: block row
+  // 4 w + i / 16, 16 bytes at column 16 (i % 16).
+  auto issue_chunk = [&](uint8_t* cb, int k0) {
+    const int kb = k0 >> 5;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ps_r, (lds_void*)(cb + 1024 * wave), 16, (64 * wave + lane) * sldp,
+                                             kb, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(qs_r, (lds_void*)(cb + XBP * 16 + 1024 * wave), 16,
+                                             (4 * wave + lane / 16) * sldq + t.q0 + 16 * (lane & 15), kb * sldq, 0, 0);
+  };
 
   // Fragment addresses inside a stage.  Gradient fragment f of lane l: row
   // m = wp 128 + 32 f + l % 32, chunks h and 2 + h (h = l / 32); the swizzle
@@ -172,34 +206,55 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 #pragma unroll
     for (int j = 0; j < XFQ; ++j) qa[j] = a0 ^ (32 * j);
   }
-  const int32_t psa = kPBytes + kQBytes + wp * 1024 + (hh * 32 + r32) * 16;
-  const int32_t qsa = kPBytes + kQBytes + 2048 + wq * 1024 + (hh * 32 + r32) * 16;
+  // Scale addresses: byte-gather mode, one 16-byte read per operand;
+  // chunk mode, fragment f's byte is at + 16 * 32 f (gradient) or + 32 f
+  // (weight), slab position s8 in the chunk adds 2 s8 (gradient) or
+  // 2 s8 * 256 (weight).
+  const int32_t psa = kChunk ? 16 * (wp * XWP + r32) + hh : kTileBytes + wp * 1024 + (hh * 32 + r32) * 16;
+  const int32_t qsa = kChunk ? XBP * 16 + hh * XBQ + wq * XWQ + r32
+                             : kTileBytes + 2048 + wq * 1024 + (hh * 32 + r32) * 16;
 
   i32x8 pf[2][XFP], qf[2][XFQ];
-  u32x4 psc[2], qsc[2];
-  // Read r (0..25) of a slab's fragments into set SET: gradient fragments
-  // (two 16-byte reads each), weight fragments (four transposing reads
-  // each), then the two scale words.
-  auto read = [&](auto ri, auto seti, const uint8_t* sb) {
-    constexpr int r = decltype(ri)::value, SET = decltype(seti)::value;
+  int32_t psc[2][XFP], qsc[2][XFQ];
+  // Read r of the fragments of the slab at contraction k0 (stage sb, slab
+  // position S8 in its scale chunk cb) into register set SET: gradient
+  // fragments (two 16-byte reads each), weight fragments (four transposing
+  // reads each), then the scales.
+  constexpr int NFRAG = 2 * XFP + 4 * XFQ;
+  constexpr int NREAD = NFRAG + (kChunk ? XFP + XFQ : 2);
+  auto read = [&](auto ri, auto seti, auto s8i, const uint8_t* sb, const uint8_t* cb, int k0) {
+    constexpr int r = decltype(ri)::value, SET = decltype(seti)::value, S8 = decltype(s8i)::value;
     if constexpr (r < 2 * XFP) {
       constexpr int f = r / 2, e = r % 2;
       const u32x4 v = *reinterpret_cast<const u32x4*>(sb + (e ? pa1 : pa0) + f * 32 * XBK);
 #pragma unroll
       for (int d = 0; d < 4; ++d) pf[SET][f][4 * e + d] = (int)v[d];
-    } else if constexpr (r < 2 * XFP + 4 * XFQ) {
+    } else if constexpr (r < NFRAG) {
       constexpr int j = (r - 2 * XFP) / 4, tt = (r - 2 * XFP) % 4;
       constexpr int toff = (32 * (tt / 2) + 8 * (tt % 2)) * XBQ;
       const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(sb + qa[j] + toff));
       qf[SET][j][2 * tt] = v[0];
       qf[SET][j][2 * tt + 1] = v[1];
-    } else if constexpr (r == 2 * XFP + 4 * XFQ) {
-      psc[SET] = *reinterpret_cast<const u32x4*>(sb + psa);
+    } else if constexpr (!kChunk) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(sb + (r == NFRAG ? psa : qsa));
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        if constexpr (r == NFRAG) psc[SET][f] = (int)v[f];
+        else qsc[SET][f] = (int)v[f];
+      }
     } else {
-      qsc[SET] = *reinterpret_cast<const u32x4*>(sb + qsa);
+      const bool valid = k0 + 32 * hh < kend;                    // this lane's scale block exists
+      if constexpr (r < NFRAG + XFP) {
+        constexpr int f = r - NFRAG;
+        const int b = cb[psa + 16 * 32 * f + 2 * S8];
+        psc[SET][f] = valid ? b : 0;
+      } else {
+        constexpr int j = r - NFRAG - XFP;
+        const int b = cb[qsa + 32 * j + 2 * S8 * XBQ];
+        qsc[SET][j] = valid ? b : 0;
+      }
     }
   };
-  constexpr int NREAD = 2 * XFP + 4 * XFQ + 2;
 
   f32x16 acc[XFP][XFQ];
 #pragma unroll
@@ -211,44 +266,56 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     constexpr int m = decltype(mi)::value, SET = decltype(seti)::value;
     constexpr int i = m / XFQ, j = m % XFQ;
     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qf[SET][j], pf[SET][i], acc[i][j], 0, 0, 0,
-                                                                 (int)qsc[SET][j], 0, (int)psc[SET][i]);
+                                                                 qsc[SET][j], 0, psc[SET][i]);
   };
   constexpr int NM = XFP * XFQ;
 
   const int nk = (kend - kbeg + XBK - 1) / XBK;
   if (nk > 0) {
-    // Prologue: slabs 0, 1, 2 in flight; slab 0 landed and published; its fragments read.
+    // Prologue: (chunk 0,) slabs 0, 1, 2 in flight; slab 0 landed and
+    // published; its fragments read.
+    if constexpr (kChunk) issue_chunk(chunkbuf(IC<0>{}), kbeg);
     static_for<3>([&](auto si) {
       constexpr int s = decltype(si)::value;
-      static_for<kVmPerSlab>([&](auto u) { issue(u, stage(si), kbeg + s * XBK); });
+      static_for<T>([&](auto u) { issue(u, stage(si), kbeg + s * XBK); });
     });
-    barrier_vm<2 * kVmPerSlab>();
-    static_for<NREAD>([&](auto r) { read(r, IC<0>{}, stage(IC<0>{})); });
+    barrier_vm<2 * T>();
+    static_for<NREAD>([&](auto r) { read(r, IC<0>{}, IC<0>{}, stage(IC<0>{}), chunkbuf(IC<0>{}), kbeg); });
   }
 
-  // Slab k = kt + J (stage J): publish slab k+1, issue slab k+3 into the
-  // stage of slab k-1, multiply slab k while reading slab k+1's fragments.
+  // Slab k = kt + J (stage J % 4): publish slab k+1, issue slab k+3 into the
+  // stage of slab k-1 (in chunk mode, first the next scale chunk at chunk
+  // position 4), multiply slab k while reading slab k+1's fragments.
   auto slab = [&](auto ji, int k) {
     constexpr int J = decltype(ji)::value;
     constexpr int CUR = J & 1, NXT = CUR ^ 1;
-    barrier_vm<kVmPerSlab>();
+    constexpr int S8 = J % kChunkSlabs, S8N = (J + 1) % kChunkSlabs;
+    // Loads issued after slab k+1's tiles: slab k+2's, plus a scale chunk
+    // issued at chunk position 4 of slab k-1.
+    barrier_vm<T + ((kChunk && S8 == 5) ? S : 0)>();
     uint8_t* const nxt = stage(IC<J + 1>{});
     uint8_t* const dst = stage(IC<J + 3>{});
+    const uint8_t* const cnxt = chunkbuf(IC<(J + 1) / kChunkSlabs>{});
     const int k3 = kbeg + (k + 3) * XBK;
+    const int k1 = kbeg + (k + 1) * XBK;
+    if constexpr (kChunk && S8 == 4) issue_chunk(chunkbuf(IC<J / kChunkSlabs + 1>{}), kbeg + (k + 4) * XBK);
     static_for<NM>([&](auto mi) {
       constexpr int m = decltype(mi)::value;
       mfma(mi, IC<CUR>{});
-      static_for<kVmPerSlab>([&](auto ui) {                          // loads over the first 12 MFMAs
+      static_for<T>([&](auto ui) {                                   // loads over the first MFMAs
         if constexpr (decltype(ui)::value == m) issue(ui, dst, k3);
       });
-      static_for<NREAD>([&](auto ri) {                               // reads over all 16
-        if constexpr (decltype(ri)::value * NM / NREAD == m) read(ri, IC<NXT>{}, nxt);
+      static_for<NREAD>([&](auto ri) {                               // reads over all of them
+        if constexpr (decltype(ri)::value * NM / NREAD == m) read(ri, IC<NXT>{}, IC<S8N>{}, nxt, cnxt, k1);
       });
       __builtin_amdgcn_sched_barrier(0);
     });
   };
-  for (int kt = 0; kt < nk; kt += 4) {
-    static_for<4>([&](auto ji) { slab(ji, kt + decltype(ji)::value); });
+  for (int kt = 0; kt < nk; kt += UNROLL) {
+    static_for<UNROLL>([&](auto ji) {
+      constexpr int J = decltype(ji)::value;
+      if (kt + J < nk) slab(ji, kt + J);
+    });
   }
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   __syncthreads();
@@ -260,7 +327,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 
 hipError_t dx_mx(const Params& prm, hipStream_t s) {
   if (prm.ntiles <= 0) return hipSuccess;
-  mx_dx_kernel<<<dim3(prm.ntiles), dim3(NT), 0, s>>>(prm);
+  // Chunk mode needs 16-byte aligned gradient scale rows (N % 512 == 0).
+  if (prm.P.scale_ld % 16 == 0)
+    mx_dx_kernel<true><<<dim3(prm.ntiles), dim3(NT), 0, s>>>(prm);
+  else
+    mx_dx_kernel<false><<<dim3(prm.ntiles), dim3(NT), 0, s>>>(prm);
   return hipGetLastError();
 }
 

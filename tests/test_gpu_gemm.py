@@ -142,12 +142,14 @@ def test_native_mx_needs_no_workspace(lp):
     assert lp.lp_linear_bwd_workspace(g, None, w, True, False) == 0
 
 
-@pytest.mark.parametrize("N", [288, 2048])
+@pytest.mark.parametrize("N", [288, 2048, 4608])
 def test_native_mx_grouped_edges(lp, N):
     """Block-scaled MFMA path, grouped: an empty group, a group smaller than
     a tile, ragged group ends, rows past the last offset kept, output width
-    336 (a partial 256-column tile) and, for N = 288, a contraction ending
-    half way through a 64-deep slab."""
+    336 (a partial 256-column tile).  N = 288: a contraction ending half way
+    through a 64-deep slab (scale bytes gathered per slab); N = 2048, 4608:
+    scale rows loaded in 512-deep chunks, 4608 ending mid-way through the
+    16-slab main-loop block."""
     M, K, G = 700, 336, 5
     sizes = [130, 0, 17, 300, 203]
     offsets = W.cumulative_ends(sizes)
