@@ -49,14 +49,15 @@ def _load() -> ctypes.CDLL:
     i64, i32 = ctypes.c_int64, ctypes.c_int32
     lib.lp_dequant.argtypes = [P, v, v]
     lib.lp_mx_quant.argtypes = [v, i64, i64, i64, i32, i32, v, v, v]
+    lib.lp_mx_quant_dual.argtypes = [v, i64, i64, i64, i32, v, v, v, v, v]
     lib.lp_linear_bwd.argtypes = [P, P, P, v, v, v]
     lib.lp_grouped_bwd.argtypes = [P, P, P, v, i64, v, v, v]
     lib.lp_linear_bwd_workspace.argtypes = [P, P, P, v, v, ctypes.POINTER(ctypes.c_size_t)]
     lib.lp_linear_bwd_ws.argtypes = [P, P, P, v, v, v, ctypes.c_size_t, v]
     lib.lp_status_string.argtypes = [i32]
     lib.lp_status_string.restype = ctypes.c_char_p
-    for f in ("lp_dequant", "lp_mx_quant", "lp_linear_bwd", "lp_grouped_bwd", "lp_linear_bwd_workspace",
-              "lp_linear_bwd_ws"):
+    for f in ("lp_dequant", "lp_mx_quant", "lp_mx_quant_dual", "lp_linear_bwd", "lp_grouped_bwd",
+              "lp_linear_bwd_workspace", "lp_linear_bwd_ws"):
         getattr(lib, f).restype = ctypes.c_int32
     return lib
 
@@ -143,6 +144,22 @@ def lp_mx_quant(src: torch.Tensor, axis: int, fmt: str = "mxfp8", codes: Optiona
     _check(lib.lp_mx_quant(src.data_ptr(), b, r, c, axis, FMT[fmt], codes.data_ptr(), scales.data_ptr(),
                            _stream(stream)), "lp_mx_quant")
     return QTensor(fmt, codes, scales, None, shape, axis)
+
+
+def lp_mx_quant_dual(src: torch.Tensor, fmt: str = "mxfp8", stream=None) -> tuple:
+    """MX-quantize a bf16 tensor [batch, rows, cols] (or [rows, cols]) along
+    both axes in one pass: (copy scaled along -1, copy scaled along -2)."""
+    shape = tuple(src.shape) if src.dim() == 3 else (1,) + tuple(src.shape)
+    b, r, c = shape
+    dev = src.device
+    cb = c if fmt == "mxfp8" else c // 2
+    codes_c = torch.empty((b, r, cb), dtype=torch.uint8, device=dev)
+    scales_c = torch.empty((b, r, c // 32), dtype=torch.uint8, device=dev)
+    codes_r = torch.empty((b, r, cb), dtype=torch.uint8, device=dev)
+    scales_r = torch.empty((b, r // 32, c), dtype=torch.uint8, device=dev)
+    _check(lib.lp_mx_quant_dual(src.data_ptr(), b, r, c, FMT[fmt], codes_c.data_ptr(), scales_c.data_ptr(),
+                                codes_r.data_ptr(), scales_r.data_ptr(), _stream(stream)), "lp_mx_quant_dual")
+    return QTensor(fmt, codes_c, scales_c, None, shape, -1), QTensor(fmt, codes_r, scales_r, None, shape, -2)
 
 
 def lp_linear_bwd(grad_out: QTensor, x: Optional[QTensor], w: Optional[QTensor], need_dx: bool = True,

@@ -46,7 +46,13 @@ lp_status check_bwd(const lp_qtensor* grad, const lp_qtensor* x, const lp_qtenso
   lp_status st = check_tensor(grad);
   if (st != LP_OK) return st;
   if (grad->batch != 1) return LP_ERR_SHAPE;
-  if (grad->fmt != LP_BF16 && !(grad->fmt == LP_MXFP8 && grad->scale_axis == -1)) return LP_ERR_FORMAT;
+  // grad_out: bf16 for every product; MXFP8 along its columns (the dX
+  // contraction) for dX only; MXFP8 along its rows (the dW contraction) for a
+  // dense dW of an MXFP8 input scaled along its rows, only.
+  const bool g_mx_cols = grad->fmt == LP_MXFP8 && grad->scale_axis == -1;
+  const bool g_mx_rows = grad->fmt == LP_MXFP8 && grad->scale_axis == -2;
+  if (grad->fmt != LP_BF16 && !g_mx_cols && !g_mx_rows) return LP_ERR_FORMAT;
+  if (g_mx_rows && (grad_x != nullptr || groups != 0)) return LP_ERR_FORMAT;
   const int64_t M = grad->rows, N = grad->cols;
   int64_t K = -1;
   if (grad_x != nullptr) {
@@ -55,8 +61,9 @@ lp_status check_bwd(const lp_qtensor* grad, const lp_qtensor* x, const lp_qtenso
     K = w->cols;
   }
   if (grad_w != nullptr) {
-    if (grad->fmt != LP_BF16) return LP_ERR_FORMAT;   // dW contracts grad over rows: bf16 only
+    if (g_mx_cols) return LP_ERR_FORMAT;              // its scales do not run along the dW contraction
     if ((st = check_tensor(x)) != LP_OK) return st;
+    if (g_mx_rows && !(x->fmt == LP_MXFP8 && x->scale_axis == -2)) return LP_ERR_FORMAT;
     if (x->batch != 1 || x->rows != M) return LP_ERR_SHAPE;
     if (K >= 0 && x->cols != K) return LP_ERR_SHAPE;
     K = x->cols;
@@ -97,6 +104,24 @@ lp_status lp_mx_quant(const void* src, int64_t batch, int64_t rows, int64_t cols
   if (!aligned(src, 16) || !aligned(codes, 16) || !aligned(scales, 16)) return LP_ERR_ALIGN;
   return hip_status(lp::launch_mx_quant(src, batch, rows, cols, axis, dst_fmt, codes, scales,
                                         static_cast<hipStream_t>(stream)));
+}
+
+lp_status lp_mx_quant_dual(const void* src, int64_t batch, int64_t rows, int64_t cols, int32_t dst_fmt,
+                           void* codes_cols, void* scales_cols, void* codes_rows, void* scales_rows, void* stream) {
+  if (batch < 0 || rows < 0 || cols < 0 || batch > kMaxDim || rows > kMaxDim || cols > kMaxDim) return LP_ERR_SHAPE;
+  if (dst_fmt != LP_MXFP8 && dst_fmt != LP_MXFP4) return LP_ERR_FORMAT;
+  if (rows % 32 || cols % 32) return LP_ERR_SHAPE;
+  const int64_t n = batch * rows * cols;
+  if (n / 8 >= kMaxUnits) return LP_ERR_SHAPE;
+  if (n == 0) return LP_OK;
+  if (src == nullptr || codes_cols == nullptr || scales_cols == nullptr || codes_rows == nullptr ||
+      scales_rows == nullptr)
+    return LP_ERR_NULL;
+  if (!aligned(src, 16) || !aligned(codes_cols, 16) || !aligned(scales_cols, 16) || !aligned(codes_rows, 16) ||
+      !aligned(scales_rows, 16))
+    return LP_ERR_ALIGN;
+  return hip_status(lp::launch_mx_quant_dual(src, batch, rows, cols, dst_fmt, codes_cols, scales_cols, codes_rows,
+                                             scales_rows, static_cast<hipStream_t>(stream)));
 }
 
 static lp_status run_bwd(const lp_qtensor* grad, const lp_qtensor* x, const lp_qtensor* w, const int32_t* offsets,

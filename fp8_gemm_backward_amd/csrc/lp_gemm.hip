@@ -95,8 +95,11 @@ struct SplitPlan {
 
 // dX of an MXFP8 gradient and an MXFP8 weight scaled along its rows: both
 // scales run along the contraction, so the block-scaled MFMA applies them.
+// Dense dW of an MXFP8 gradient and an MXFP8 input both scaled along their
+// rows (the token axis, the contraction) likewise.
 bool native_mx(const GemmCall& call) {
-  return !call.dw && call.grad->fmt == LP_MXFP8 && call.other->fmt == LP_MXFP8 && call.other->scale_axis == -2;
+  if (call.grad->fmt != LP_MXFP8 || call.other->fmt != LP_MXFP8 || call.other->scale_axis != -2) return false;
+  return !call.dw || (call.grad->scale_axis == -2 && call.offsets == nullptr);
 }
 
 SplitPlan split_plan(const GemmCall& call) {
@@ -145,6 +148,10 @@ hipError_t launch_gemm(const GemmCall& call, hipStream_t stream) {
   }
   if (native_mx(call)) {
     prm.nq = (int32_t)((prm.Qtot + Big::BQ - 1) / Big::BQ);
+    if (call.dw) {
+      prm.ntiles = (int32_t)(((call.N + Big::BP - 1) / Big::BP) * prm.nq);
+      return dw_mx(prm, stream);
+    }
     const int64_t ptiles = call.offsets ? (call.M / Big::BP + call.groups) : (call.M + Big::BP - 1) / Big::BP;
     prm.ntiles = (int32_t)(ptiles * prm.nq);
     return dx_mx(prm, stream);

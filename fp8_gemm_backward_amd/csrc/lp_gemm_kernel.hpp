@@ -952,6 +952,9 @@ hipError_t dw_narrow(const lp_qtensor& q, const Params& prm, hipStream_t s);
 // MXFP8 gradient x MXFP8 weight scaled along its rows, on the block-scaled MFMA
 // (256 x 256 tiles, no split).
 hipError_t dx_mx(const Params& prm, hipStream_t s);
+// Dense grad_W of an MXFP8 gradient and an MXFP8 input, both scaled along
+// their rows (the contraction), on the block-scaled MFMA.
+hipError_t dw_mx(const Params& prm, hipStream_t s);
 
 }  // namespace gk
 }  // namespace lp

@@ -12,7 +12,10 @@
 // is the contraction of the decoded operands up to fp32 summation order, as
 // in the decode-to-bf16 path, with no decode work and at the FP8 MFMA rate.
 //
-//   out[m][q] = sum_n grad[m][n] * W[g][n][q]      (rows m of group g)
+//   dX: out[m][q] = sum_n grad[m][n] * W[g][n][q]    (rows m of group g)
+//   dW: out[n][q] = sum_m grad[m][n] * X[m][q]       (dense; grad and X both
+//       MX-quantized along their rows, the Deferred-MXFP8 page's
+//       MXFP8MatMul.backward with dual-axis gradient quantization)
 //
 // Layout facts of the two gfx950 instructions used (checked on the hardware
 // with in-bounds probes):
@@ -26,13 +29,15 @@
 //   lane q addressing row n0 + q / 2 at byte 8 (q & 1) of a 16-column chunk,
 //   lane i receives column i of rows n0 .. n0 + 7: the weight's transpose.
 //
-// Tiles: 256 (grad rows) x 256 (output columns) per workgroup, four waves of
+// Tiles: 256 (output rows) x 256 (output columns) per workgroup, four waves of
 // 128 x 128, 64-deep slabs.  Everything a slab needs - 16 KiB of gradient
 // codes, 16 KiB of weight codes and the scale bytes gathered into the
 // order the lanes read them - goes from global memory straight into LDS
 // (buffer_load ... lds), four stages deep in separate LDS variables, issued
 // three slabs ahead.  A slab's fragments are read during the previous slab's
-// MFMAs.  One barrier per slab.
+// MFMAs.  One barrier per slab.  In dX the gradient tile is [m][64 B] (its
+// contraction contiguous, read with ds_read_b128); in dW both tiles are
+// [contraction][256 B] and both are read through the transposing read.
 #include "lp_gemm_kernel.hpp"
 
 namespace lp {
@@ -80,8 +85,9 @@ __device__ __forceinline__ int q_swz(int n) { return 2 * (n & 7); }
 //   (column) 32 (i % 4) + 16 (u & 1) + i / 4 of that wave tile, so that one
 //   16-byte read gives a lane its four fragments' scales.  This issues one
 //   memory request per byte, which costs a quarter of the dense throughput.
-template <bool kChunk>
+template <bool kDW, bool kChunk>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void mx_dx_kernel(Params p) {
+  static_assert(!kDW || kChunk, "dW scale rows (N or K bytes, multiples of 16) always load in chunks");
   constexpr int kStage = kChunk ? kTileBytes : kTileBytes + kGatherBytes;
   constexpr int T = kChunk ? 8 : 12;                             // direct loads per wave and slab
   constexpr int S = 2;                                           // chunk loads per wave
@@ -98,12 +104,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wp = wave >> 1, wq = wave & 1;
-  const Tile t = select_tile<XCfg, false>(p, reinterpret_cast<int32_t*>(st0));
+  const Tile t = select_tile<XCfg, kDW>(p, reinterpret_cast<int32_t*>(st0));
   if (!t.valid) return;
   __syncthreads();                                               // group ends read; stage 0 reusable
 
   const int ldp = p.P.code_ld;                                   // N bytes per gradient row
-  const int sldp = p.P.scale_ld;                                 // N / 32
+  const int sldp = p.P.scale_ld;                                 // dX: N / 32; dW: N (scales per 32 rows)
   const int ldq = p.Q.code_ld;                                   // K bytes per weight row
   const int sldq = p.Q.scale_ld;                                 // K scale bytes per 32 weight rows
   const int M = p.Ptot;
@@ -114,7 +120,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   const int64_t psrow_bytes = (int64_t)(M - t.p0) * sldp;
   const uint8_t* qc = p.Q.codes + (int64_t)t.g * p.Q.code_batch;
   const Rsrc qs_r = make_rsrc(p.Q.scales + (int64_t)t.g * p.Q.scale_batch, p.Q.scale_bytes);
-  const Rsrc ps_r = make_rsrc(ps, psrow_bytes);
+  const Rsrc ps_r = kDW ? make_rsrc(p.P.scales, p.P.scale_bytes) : make_rsrc(ps, psrow_bytes);
 
   // Per-lane parts of the direct loads, fixed for the whole loop; the parts
   // that differ between a wave's loads are uniform (scalar offsets).
@@ -131,6 +137,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   const int qc0 = (lane & 15) ^ (2 * (lane >> 4));
   const int32_t q_base = (16 * wave + lane / 16) * ldq + t.q0;   // + 4 u ldq
   const int32_t q_off_even = q_base + 16 * qc0, q_off_odd = q_base + 16 * (qc0 ^ 8);
+  // dW: the gradient tile is loaded like the weight tile, at columns p0.
+  const int32_t pq_base = (16 * wave + lane / 16) * ldp + t.p0;
+  const int32_t pq_off_even = pq_base + 16 * qc0, pq_off_odd = pq_base + 16 * (qc0 ^ 8);
   // Byte-gather mode: waves 0, 1 gather the grad regions, waves 2, 3 the
   // weight regions, 64 positions per load u.
   const bool s_grad = wave < 2;
@@ -159,7 +168,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   // end only in the last slab (N % 32 == 0).
   auto issue = [&](auto ui, uint8_t* sb, int k0) {
     constexpr int u = decltype(ui)::value;
-    if constexpr (u < 4) {
+    if constexpr (u < 4 && kDW) {
+      const Rsrc r = make_rsrc(p.P.codes + (int64_t)k0 * ldp, (int64_t)(kend - k0) * ldp);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(sb + 1024 * (4 * wave + u)), 16,
+                                               (u & 1) ? pq_off_odd : pq_off_even, 4 * u * ldp, 0, 0);
+    } else if constexpr (u < 4) {
       const Rsrc r = make_rsrc(pc + k0, prow_bytes - k0);
       const bool out = k0 + XBK > kend && (k0 >= kend || p_hi);    // kend - k0 is <= 0, 32 or >= 64
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(sb + 1024 * (4 * wave + u)), 16, out ? kOOB : p_off,
@@ -182,8 +195,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   // 4 w + i / 16, 16 bytes at column 16 (i % 16).
   auto issue_chunk = [&](uint8_t* cb, int k0) {
     const int kb = k0 >> 5;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ps_r, (lds_void*)(cb + 1024 * wave), 16, (64 * wave + lane) * sldp,
-                                             kb, 0, 0);
+    if constexpr (kDW)   // gradient scales [M / 32][N]: block row 4 w + i / 16, columns p0 + 16 (i % 16)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ps_r, (lds_void*)(cb + 1024 * wave), 16,
+                                               (4 * wave + lane / 16) * sldp + t.p0 + 16 * (lane & 15), kb * sldp, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ps_r, (lds_void*)(cb + 1024 * wave), 16, (64 * wave + lane) * sldp,
+                                               kb, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(qs_r, (lds_void*)(cb + XBP * 16 + 1024 * wave), 16,
                                              (4 * wave + lane / 16) * sldq + t.q0 + 16 * (lane & 15), kb * sldq, 0, 0);
   };
@@ -210,7 +227,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   // chunk mode, fragment f's byte is at + 16 * 32 f (gradient) or + 32 f
   // (weight), slab position s8 in the chunk adds 2 s8 (gradient) or
   // 2 s8 * 256 (weight).
-  const int32_t psa = kChunk ? 16 * (wp * XWP + r32) + hh : kTileBytes + wp * 1024 + (hh * 32 + r32) * 16;
+  int32_t pqa[XFP];                                              // dW: gradient fragments like the weight's
+  {
+    const int i16 = lane & 15, c16 = (lane >> 4) & 1;
+    const int n0 = 16 * hh + i16 / 2;
+    const int32_t a0 = n0 * XBQ + 16 * ((wp * (XWP / 16) + c16) ^ q_swz(n0)) + 8 * (i16 & 1);
+#pragma unroll
+    for (int f = 0; f < XFP; ++f) pqa[f] = a0 ^ (32 * f);
+  }
+  const int32_t psa = kDW ? hh * XBP + wp * XWP + r32
+                          : (kChunk ? 16 * (wp * XWP + r32) + hh : kTileBytes + wp * 1024 + (hh * 32 + r32) * 16);
   const int32_t qsa = kChunk ? XBP * 16 + hh * XBQ + wq * XWQ + r32
                              : kTileBytes + 2048 + wq * 1024 + (hh * 32 + r32) * 16;
 
@@ -224,7 +250,17 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   constexpr int NREAD = NFRAG + (kChunk ? XFP + XFQ : 2);
   auto read = [&](auto ri, auto seti, auto s8i, const uint8_t* sb, const uint8_t* cb, int k0) {
     constexpr int r = decltype(ri)::value, SET = decltype(seti)::value, S8 = decltype(s8i)::value;
-    if constexpr (r < 2 * XFP) {
+    if constexpr (r < 2 * XFP && kDW) {
+      constexpr int f = r / 2, e = r % 2;                        // two transposing reads per r
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int tt = 2 * e + h2;
+        const int toff = (32 * (tt / 2) + 8 * (tt % 2)) * XBQ;
+        const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(sb + pqa[f] + toff));
+        pf[SET][f][2 * tt] = v[0];
+        pf[SET][f][2 * tt + 1] = v[1];
+      }
+    } else if constexpr (r < 2 * XFP) {
       constexpr int f = r / 2, e = r % 2;
       const u32x4 v = *reinterpret_cast<const u32x4*>(sb + (e ? pa1 : pa0) + f * 32 * XBK);
 #pragma unroll
@@ -246,7 +282,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
       const bool valid = k0 + 32 * hh < kend;                    // this lane's scale block exists
       if constexpr (r < NFRAG + XFP) {
         constexpr int f = r - NFRAG;
-        const int b = cb[psa + 16 * 32 * f + 2 * S8];
+        const int b = kDW ? cb[psa + 32 * f + 2 * S8 * XBP] : cb[psa + 16 * 32 * f + 2 * S8];
         psc[SET][f] = valid ? b : 0;
       } else {
         constexpr int j = r - NFRAG - XFP;
@@ -320,7 +356,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   __syncthreads();
   uint8_t* stg = wave == 0 ? st0 : wave == 1 ? st1 : wave == 2 ? st2 : st3;
-  store_acc<XCfg, false>(p, t, acc, wp, wq, lane, stg);
+  store_acc<XCfg, kDW>(p, t, acc, wp, wq, lane, stg);
 }
 
 }  // namespace
@@ -329,9 +365,15 @@ hipError_t dx_mx(const Params& prm, hipStream_t s) {
   if (prm.ntiles <= 0) return hipSuccess;
   // Chunk mode needs 16-byte aligned gradient scale rows (N % 512 == 0).
   if (prm.P.scale_ld % 16 == 0)
-    mx_dx_kernel<true><<<dim3(prm.ntiles), dim3(NT), 0, s>>>(prm);
+    mx_dx_kernel<false, true><<<dim3(prm.ntiles), dim3(NT), 0, s>>>(prm);
   else
-    mx_dx_kernel<false><<<dim3(prm.ntiles), dim3(NT), 0, s>>>(prm);
+    mx_dx_kernel<false, false><<<dim3(prm.ntiles), dim3(NT), 0, s>>>(prm);
+  return hipGetLastError();
+}
+
+hipError_t dw_mx(const Params& prm, hipStream_t s) {
+  if (prm.ntiles <= 0) return hipSuccess;
+  mx_dx_kernel<true, true><<<dim3(prm.ntiles), dim3(NT), 0, s>>>(prm);
   return hipGetLastError();
 }
 

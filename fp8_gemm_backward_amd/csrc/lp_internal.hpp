@@ -36,6 +36,8 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
 hipError_t launch_dequant(const lp_qtensor& src, void* dst, hipStream_t stream);
 hipError_t launch_mx_quant(const void* src, int64_t batch, int64_t rows, int64_t cols, int axis,
                            int dst_fmt, void* codes, void* scales, hipStream_t stream);
+hipError_t launch_mx_quant_dual(const void* src, int64_t batch, int64_t rows, int64_t cols, int dst_fmt,
+                                void* codes_c, void* scales_c, void* codes_r, void* scales_r, hipStream_t stream);
 
 // One backward contraction (grad_X or grad_W) over `groups` groups.
 //   dx: C[m][k] = sum_n grad[m][n] * W[g][n][k]  (groups partition the rows m)

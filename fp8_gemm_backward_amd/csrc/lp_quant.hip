@@ -195,6 +195,98 @@ __global__ __launch_bounds__(kThreads) void mx_quant_rows(const uint16_t* __rest
   }
 }
 
+// Both axes at once ("perf: defer mxfp8 backward quantization",
+// MXFP8MatMul.backward, npu_dynamic_mx_quant_with_dual_axis): one read of
+// the bf16 tensor, two quantized copies.  Thread i owns a strip of 32 rows x
+// 8 columns as in mx_quant_rows, which gives the blocks along the rows
+// lane-locally; the four lanes of a quad hold 32 consecutive columns of the
+// same rows (cols % 32 == 0, so quads never straddle a row), and each row's
+// block along the columns takes its amax with two DPP exchanges.
+template <bool kFp4>
+__global__ __launch_bounds__(kThreads) void mx_quant_dual(const uint16_t* __restrict__ src,
+                                                          uint8_t* __restrict__ codes_c, uint8_t* __restrict__ scales_c,
+                                                          uint8_t* __restrict__ codes_r, uint8_t* __restrict__ scales_r,
+                                                          uint32_t nstrips, FastDiv strips_per_row, uint32_t cols) {
+  uint32_t i = blockIdx.x * kThreads + threadIdx.x;
+  if (i >= nstrips) return;                              // whole quads (nstrips % 4 == 0)
+  uint32_t rb = fdiv(i, strips_per_row);                 // block of 32 rows over batch*rows
+  uint32_t c0 = (i - rb * strips_per_row.d) * 8u;
+  const uint16_t* base = src + (size_t)rb * 32u * cols + c0;
+  u32x4 v[32];
+#pragma unroll
+  for (int r = 0; r < 32; ++r) v[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (size_t)r * cols));
+
+  // Blocks along the rows (axis -2): one per column of the strip.
+  uint32_t amax[4] = {0, 0, 0, 0};   // packed pairs of column maxima
+#pragma unroll
+  for (int r = 0; r < 32; ++r)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t w = v[r][k] & 0x7FFF7FFFu;
+      amax[k] = umax(amax[k] & 0xFFFFu, w & 0xFFFFu) | (umax(amax[k] >> 16, w >> 16) << 16);
+    }
+  BlockScale s[8];
+  uint32_t sbytes[2] = {0, 0};
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    s[c] = block_scale<kFp4>((amax[c >> 1] >> (16 * (c & 1))) & 0xFFFFu);
+    sbytes[c >> 2] |= s[c].byte << (8 * (c & 3));
+  }
+  *reinterpret_cast<u32x2*>(scales_r + (size_t)rb * cols + c0) = u32x2{sbytes[0], sbytes[1]};
+  const size_t row_bytes = kFp4 ? cols / 2 : cols;
+  uint8_t* out_r = codes_r + (size_t)rb * 32u * row_bytes + (kFp4 ? c0 / 2 : c0);
+  uint8_t* out_c = codes_c + (size_t)rb * 32u * row_bytes + (kFp4 ? c0 / 2 : c0);
+  const uint32_t sc_row = cols / 32;                     // column-block scales per row
+  uint8_t* sc_c = scales_c + (size_t)rb * 32u * sc_row + c0 / 32;
+  const bool leader = (threadIdx.x & 3) == 0;
+#pragma unroll
+  for (int r = 0; r < 32; ++r) {
+    // Block along the columns (axis -1) of row r: 32 columns over the quad.
+    uint32_t m = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t w = v[r][k] & 0x7FFF7FFFu;
+      m = umax(m, umax(w & 0xFFFFu, w >> 16));
+    }
+    const BlockScale sr = block_scale<kFp4>(quad_max(m));
+    if (leader) sc_c[(size_t)r * sc_row] = (uint8_t)sr.byte;
+    if constexpr (!kFp4) {
+      uint32_t oc[2], orr[2];
+#pragma unroll
+      for (int k = 0; k < 4; k += 2) {
+        const uint32_t w0 = v[r][k], w1 = v[r][k + 1];
+        const uint32_t lo = sr.bad ? nan_e4m3x2(w0) : to_e4m3x2(bf16_lo(w0) * sr.inv, bf16_hi(w0) * sr.inv);
+        const uint32_t hi = sr.bad ? nan_e4m3x2(w1) : to_e4m3x2(bf16_lo(w1) * sr.inv, bf16_hi(w1) * sr.inv);
+        oc[k / 2] = lo | (hi << 16);
+        const int c = 2 * k;
+        const uint32_t p0 = to_e4m3x2(bf16_lo(w0) * s[c].inv, bf16_hi(w0) * s[c + 1].inv);
+        const uint32_t p1 = to_e4m3x2(bf16_lo(w1) * s[c + 2].inv, bf16_hi(w1) * s[c + 3].inv);
+        const uint32_t b0 = s[c].bad ? (0x7Fu | ((w0 >> 8) & 0x80u)) : (p0 & 0xFFu);
+        const uint32_t b1 = s[c + 1].bad ? (0x7Fu | ((w0 >> 24) & 0x80u)) : (p0 >> 8);
+        const uint32_t b2 = s[c + 2].bad ? (0x7Fu | ((w1 >> 8) & 0x80u)) : (p1 & 0xFFu);
+        const uint32_t b3 = s[c + 3].bad ? (0x7Fu | ((w1 >> 24) & 0x80u)) : (p1 >> 8);
+        orr[k / 2] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+      }
+      *reinterpret_cast<u32x2*>(out_c + (size_t)r * cols) = u32x2{oc[0], oc[1]};
+      *reinterpret_cast<u32x2*>(out_r + (size_t)r * cols) = u32x2{orr[0], orr[1]};
+    } else {
+      uint32_t oc = 0, orr = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t w = v[r][k];
+        oc |= to_e2m1x2(bf16_lo(w) * sr.inv, bf16_hi(w) * sr.inv) << (8 * k);
+        const int c = 2 * k;
+        const uint32_t b = to_e2m1x2(bf16_lo(w) * s[c].inv, bf16_hi(w) * s[c + 1].inv);
+        const uint32_t lo = s[c].bad ? 0u : (b & 0xFu);
+        const uint32_t hi = s[c + 1].bad ? 0u : (b >> 4);
+        orr |= (lo | (hi << 4)) << (8 * k);
+      }
+      *reinterpret_cast<uint32_t*>(out_c + (size_t)r * (cols / 2)) = sr.bad ? 0u : oc;
+      *reinterpret_cast<uint32_t*>(out_r + (size_t)r * (cols / 2)) = orr;
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_mx_quant(const void* src, int64_t batch, int64_t rows, int64_t cols, int axis, int dst_fmt,
@@ -223,6 +315,25 @@ hipError_t launch_mx_quant(const void* src, int64_t batch, int64_t rows, int64_t
     else
       mx_quant_rows<false><<<grid, block, 0, stream>>>(s, c, sc, nstrips, make_fastdiv(spr), (uint32_t)cols);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_quant_dual(const void* src, int64_t batch, int64_t rows, int64_t cols, int dst_fmt,
+                                void* codes_c, void* scales_c, void* codes_r, void* scales_r, hipStream_t stream) {
+  const int64_t n = batch * rows * cols;
+  if (n == 0) return hipSuccess;
+  const uint32_t spr = (uint32_t)(cols / 8);
+  const uint32_t nstrips = (uint32_t)(batch * (rows / 32) * spr);
+  const dim3 grid((nstrips + kThreads - 1) / kThreads), block(kThreads);
+  auto s = static_cast<const uint16_t*>(src);
+  auto cc = static_cast<uint8_t*>(codes_c);
+  auto scc = static_cast<uint8_t*>(scales_c);
+  auto cr = static_cast<uint8_t*>(codes_r);
+  auto scr = static_cast<uint8_t*>(scales_r);
+  if (dst_fmt == LP_MXFP4)
+    mx_quant_dual<true><<<grid, block, 0, stream>>>(s, cc, scc, cr, scr, nstrips, make_fastdiv(spr), (uint32_t)cols);
+  else
+    mx_quant_dual<false><<<grid, block, 0, stream>>>(s, cc, scc, cr, scr, nstrips, make_fastdiv(spr), (uint32_t)cols);
   return hipGetLastError();
 }
 

@@ -146,6 +146,25 @@ lp_status lp_mx_quant(const void* src_bf16, int64_t batch, int64_t rows, int64_t
                       void* stream);
 
 /*
+ * lp_mx_quant_dual - dynamic MX quantization along both axes at once.
+ *
+ * Cites: "perf: defer mxfp8 backward quantization", MXFP8MatMul.backward
+ * (npu_dynamic_mx_quant_with_dual_axis of the gradient: one copy scaled
+ * along -1 for grad_X, one along -2 for grad_W).
+ *
+ * src_bf16     device bf16 [batch][rows][cols]; rows % 32 == 0, cols % 32 == 0.
+ * dst_fmt      LP_MXFP8 or LP_MXFP4.
+ * codes_cols, scales_cols   the copy with blocks along cols: exactly what
+ *              lp_mx_quant(src, ..., axis -1, ...) writes.
+ * codes_rows, scales_rows   the copy with blocks along rows: exactly what
+ *              lp_mx_quant(src, ..., axis -2, ...) writes.
+ * One read of src.  Bit-exact, with the rules of lp_mx_quant.
+ */
+lp_status lp_mx_quant_dual(const void* src_bf16, int64_t batch, int64_t rows, int64_t cols, int32_t dst_fmt,
+                           void* codes_cols, void* scales_cols, void* codes_rows, void* scales_rows,
+                           void* stream);
+
+/*
  * lp_linear_bwd - backward of a linear layer y = x @ W^T with saved
  * block-scaled operands.
  *
@@ -155,7 +174,12 @@ lp_status lp_mx_quant(const void* src_bf16, int64_t batch, int64_t rows, int64_t
  * FP8LinearFunction.backward (frozen weight: grad_X only); "AstrAI fp8.py",
  * _LinearFp8.backward (each output is computed only when it is needed).
  *
- * grad_out  [M][N]: LP_BF16, or LP_MXFP8 with scale_axis -1 (needs grad_w == NULL).
+ * grad_out  [M][N]: LP_BF16; or LP_MXFP8 with scale_axis -1 (its scales run
+ *           along the dX contraction; needs grad_w == NULL); or LP_MXFP8 with
+ *           scale_axis -2 (along the dW contraction; needs grad_x == NULL and x
+ *           LP_MXFP8 with scale_axis -2), as produced by lp_mx_quant_dual.
+ *           ("perf: defer mxfp8 backward quantization", MXFP8MatMul.backward:
+ *           the gradient is quantized along both axes, one copy per product.)
  * x         [M][K] saved input, or NULL when grad_w == NULL.
  * w         [N][K] saved weight, or NULL when grad_x == NULL.
  *           x and w: LP_BF16, LP_MXFP4, LP_NVFP4 (scale_axis -1), LP_FP8_B128,
@@ -166,6 +190,11 @@ lp_status lp_mx_quant(const void* src_bf16, int64_t batch, int64_t rows, int64_t
  * block rule (K % 32 for FP4 and MX along K; N % 32 for MXFP8 grad_out and
  * for MXFP8 w with scale_axis -2; M % 32 for MXFP8 x with scale_axis -2).
  * Accumulation is fp32; outputs are rounded to bf16 (nearest even).
+ * When both operands of a product are MXFP8 with their scales along its
+ * contraction (dX: grad_out -1, w -2; dW: grad_out -2, x -2), the product
+ * runs on the block-scaled FP8 MFMA: each code product times its two E8M0
+ * scales is exact, so the result equals the decode-then-bf16 route up to
+ * fp32 summation order.
  */
 lp_status lp_linear_bwd(const lp_qtensor* grad_out, const lp_qtensor* x, const lp_qtensor* w,
                         void* grad_x, void* grad_w, void* stream);
@@ -233,7 +262,9 @@ lp_status lp_linear_bwd_ws(const lp_qtensor* grad_out, const lp_qtensor* x, cons
  *           written.
  * grad_w    device bf16 [groups][N][K] or NULL.  An empty group's slice is
  *           written with zeros (the empty sum).
- * Size and format rules as for lp_linear_bwd; 1 <= groups <= 1024.
+ * Size and format rules as for lp_linear_bwd, except that grad_out scaled
+ * along its rows (-2) is not accepted (its 32-row blocks would straddle
+ * groups); 1 <= groups <= 1024.
  */
 lp_status lp_grouped_bwd(const lp_qtensor* grad_out, const lp_qtensor* x, const lp_qtensor* w,
                          const int32_t* offsets, int64_t groups, void* grad_x, void* grad_w,

@@ -15,7 +15,7 @@ FAKE = 0x10000          # 16-byte aligned stand-in pointer; never dereferenced h
 def test_library_exports_every_header_function():
     names = lp.header_functions()
     assert set(names) == {"lp_dequant", "lp_mx_quant", "lp_linear_bwd", "lp_grouped_bwd", "lp_status_string",
-                          "lp_linear_bwd_workspace", "lp_linear_bwd_ws"}
+                          "lp_linear_bwd_workspace", "lp_linear_bwd_ws", "lp_mx_quant_dual"}
     for n in names:
         assert hasattr(lp.lib, n), n
 
@@ -71,6 +71,24 @@ def test_mx_quant_rejects(args, expect):
     assert lp.lib.lp_mx_quant(*args, None) == expect
 
 
+@pytest.mark.parametrize("args,expect", [
+    ((None, 1, 32, 32, lp.FMT["mxfp8"], FAKE, FAKE, FAKE, FAKE), NULL),
+    ((FAKE, 1, 32, 32, lp.FMT["mxfp8"], FAKE, FAKE, None, FAKE), NULL),
+    ((FAKE, 1, 32, 48, lp.FMT["mxfp8"], FAKE, FAKE, FAKE, FAKE), SHAPE),      # cols % 32
+    ((FAKE, 1, 48, 32, lp.FMT["mxfp8"], FAKE, FAKE, FAKE, FAKE), SHAPE),      # rows % 32
+    ((FAKE, 1, 32, 32, lp.FMT["fp8_b128"], FAKE, FAKE, FAKE, FAKE), FORMAT),
+    ((FAKE, 1, 32, 32, lp.FMT["mxfp4"], FAKE, FAKE, FAKE, FAKE + 4), ALIGN),
+    ((None, 3, 0, 64, lp.FMT["mxfp8"], None, None, None, None), OK),
+])
+def test_mx_quant_dual_rejects(args, expect):
+    assert lp.lib.lp_mx_quant_dual(*args, None) == expect
+
+
+def test_grouped_rejects_row_scaled_grad():
+    g, x = q("mxfp8", 64, 128, axis=-2), q("mxfp8", 64, 128, axis=-2)
+    assert lp.lib.lp_grouped_bwd(ctypes.byref(g), ctypes.byref(x), None, FAKE, 2, None, FAKE, None) == FORMAT
+
+
 def lin(g, x, w, dx=FAKE, dw=FAKE):
     ref = lambda t: ctypes.byref(t) if t is not None else None  # noqa: E731
     return lp.lib.lp_linear_bwd(ref(g), ref(x), ref(w), dx, dw, None)
@@ -87,6 +105,9 @@ def lin(g, x, w, dx=FAKE, dw=FAKE):
     (q("bf16", 64, 120), q("mxfp4", 64, 128), q("mxfp4", 120, 128), FAKE, FAKE, SHAPE),  # N % 16
     (q("nvfp4", 64, 128), q("mxfp4", 64, 128), q("mxfp4", 128, 128), FAKE, None, FORMAT),  # grad format
     (q("mxfp8", 64, 128), q("mxfp4", 64, 128), q("mxfp4", 128, 128), None, FAKE, FORMAT),  # MXFP8 grad, dW
+    (q("mxfp8", 64, 128, axis=-2), None, q("mxfp8", 128, 128, axis=-2), FAKE, None, FORMAT),  # row-scaled grad, dX
+    (q("mxfp8", 64, 128, axis=-2), q("mxfp4", 64, 128), None, None, FAKE, FORMAT),   # row-scaled grad, X not MX rows
+    (q("mxfp8", 64, 128, axis=-2), q("mxfp8", 64, 128, axis=-1), None, None, FAKE, FORMAT),
     (q("bf16", 64, 128), q("mxfp4", 64, 128), q("nvfp4", 128, 48), FAKE, None, SHAPE),   # FP4 K % 32
     (q("bf16", 64, 128), q("mxfp4", 64, 128), q("mxfp4", 128, 128, batch=2), FAKE, None, SHAPE),
     (q("bf16", 64, 128), q("mxfp4", 64, 128), q("mxfp4", 128, 128), FAKE + 8, None, ALIGN),

@@ -203,6 +203,45 @@ def test_split_workspace_too_small_falls_back(lp):
     assert_close(dx, O.linear_dx(gb, wd[0]), "fallback dX")
 
 
+@pytest.mark.parametrize("M,N,K", [(4128, 272, 336), (2048, 512, 768)])
+def test_native_mx_dw(lp, M, N, K):
+    """Dense dW of an MXFP8 gradient and an MXFP8 input both scaled along
+    their rows (the token axis): the block-scaled MFMA's dW form.  4128
+    tokens end half way through a 64-deep slab; 272 x 336 leaves partial
+    256 x 256 tiles."""
+    gbits = W.bf16_bits(W.normal_f32(48, "grad", (1, M, N), 1.0))
+    gc, gs = F.mx_quant(gbits, -2, "e4m3")
+    g = lp.QTensor("mxfp8", dev(gc[0]), dev(gs[0]), shape=(1, M, N), axis=-2)
+    x, xd = _operand(lp, 48, "x", (M, K), "mxfp8", -2)
+    _, dw = lp.lp_linear_bwd(g, x, None, need_dx=False)
+    torch.cuda.synchronize()
+    gd = F.dequant("mxfp8", gc, gs, axis=-2)[0]
+    assert_close(dw, O.linear_dw(gd, xd[0]), f"native mx dW {M}x{N}x{K}")
+
+
+def test_native_mx_dw_matches_decode_path_with_nan_blocks(lp):
+    """A gradient block with scale 0xFF makes the same dW rows NaN
+    in the block-scaled path as in the decode path (grad decoded to bf16)."""
+    M, N, K = 512, 256, 288
+    gbits = W.bf16_bits(W.normal_f32(49, "grad", (1, M, N), 1.0))
+    gc, gs = F.mx_quant(gbits, -2, "e4m3")
+    gs = gs.copy()
+    gs[0, 3, 17] = 0xFF                          # rows 96..127 of grad column 17 -> dW row 17
+    g = lp.QTensor("mxfp8", dev(gc[0]), dev(gs[0]), shape=(1, M, N), axis=-2)
+    x, xd = _operand(lp, 49, "x", (M, K), "mxfp8", -2)
+    _, dw_native = lp.lp_linear_bwd(g, x, None, need_dx=False)
+    gq = lp.QTensor("bf16", lp.lp_dequant(g).view(M, N), shape=(1, M, N))
+    _, dw_decode = lp.lp_linear_bwd(gq, x, None, need_dx=False)
+    torch.cuda.synchronize()
+    a = dw_native.float().cpu().numpy()
+    b = dw_decode.float().cpu().numpy()
+    assert np.array_equal(np.isnan(a), np.isnan(b))
+    assert np.isnan(a[17]).all() and not np.isnan(np.delete(a, 17, 0)).any()
+    keep = np.delete(np.arange(N), 17)
+    gd = F.dequant("mxfp8", gc, gs, axis=-2)[0]
+    assert_close(dw_native[torch.from_numpy(keep).cuda()], O.rows_dw(gd, xd[0], keep), "native dW, finite rows")
+
+
 def _sentinel(shape):
     return torch.full(shape, -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)   # 0xFFFF (NaN)
 

@@ -120,3 +120,28 @@ def test_ragged_sizes_along_cols(lp, fmt, shape):
     g = W.rng(23, "x")
     x = g.standard_normal(shape).astype(np.float32) * np.exp2(g.integers(-20, 20, size=shape[:-1] + (1,)))
     _check(lp, W.bf16_bits(x.astype(np.float32)), -1, fmt, f"{fmt} {shape}")
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4"])
+@pytest.mark.parametrize("data", ["every_bf16", "random_batched"])
+def test_dual_axis_equals_single_axis(lp, fmt, data):
+    """lp_mx_quant_dual writes exactly the two copies lp_mx_quant writes along
+    -1 and along -2, which the oracle checks (every finite bf16 value in
+    blocks both ways, special blocks, random magnitudes, batched)."""
+    if data == "every_bf16":
+        blocks = np.concatenate([_special_blocks(), _every_finite_bf16_in_blocks()])
+        n = blocks.size // (256 * 32) * (256 * 32)
+        bits = blocks.reshape(-1)[:n].reshape(1, -1, 256)
+    else:
+        g = W.rng(24, "x")
+        mags = np.exp2(g.integers(-30, 30, size=(3, 64, 1))).astype(np.float32)
+        bits = W.bf16_bits(g.standard_normal((3, 64, 96)).astype(np.float32) * mags)
+    src = bf16_dev(bits)
+    qc, qr = lp.lp_mx_quant_dual(src, fmt)
+    torch.cuda.synchronize()
+    rc, rs = F.mx_quant(bits, -1, ELEM[fmt])
+    assert_bits_equal(qc.codes.cpu().numpy(), rc, f"{fmt} dual, codes along -1")
+    assert_bits_equal(qc.scales.cpu().numpy(), rs, f"{fmt} dual, scales along -1")
+    rc, rs = F.mx_quant(bits, -2, ELEM[fmt])
+    assert_bits_equal(qr.codes.cpu().numpy(), rc, f"{fmt} dual, codes along -2")
+    assert_bits_equal(qr.scales.cpu().numpy(), rs, f"{fmt} dual, scales along -2")
