@@ -8,6 +8,7 @@ synthetic input already resident in HBM:
   nvfp4_linear    lp_linear_bwd: dX and dW, NVFP4 X and W
   mxfp4_grouped   lp_grouped_bwd: dX and dW over 8 experts, MXFP4 X and W
   mxfp8_deferred  lp_mx_quant(grad, -1) + lp_mx_quant(W, -2) + lp_grouped_bwd dX
+  mxfp8_dense     lp_mx_quant_dual(grad) + lp_mx_quant(W, -2) + lp_mx_quant(X, -2) + lp_linear_bwd dX, dW
   mxfp4_tiny      lp_linear_bwd: dX and dW, 64 x 128 x 128
 Input sets are rotated through about 1 GB so that the 256 MiB Infinity Cache
 cannot serve a repeated step.  Prints one JSON line (rank 0).
@@ -175,6 +176,41 @@ def build(lp, name: str):
             lp.lp_grouped_bwd(gq, None, wq, offsets, need_dw=False, grad_x=dx, stream=stream)
             return [t0, t1, ev.stop(stream)]
         standalone = []
+    elif name == "mxfp8_dense":
+        g = W.torch_normal_bf16((M, N), 1.0, 7700, "cuda")
+        wt = W.torch_normal_bf16((N, K), w.w_sigma, 7701, "cuda")
+        xt = W.torch_normal_bf16((M, K), w.x_sigma, 7702, "cuda")
+        gc, gr = lp.lp_mx_quant_dual(g, "mxfp8")
+        wq = lp.lp_mx_quant(wt, -2, "mxfp8")
+        xq = lp.lp_mx_quant(xt, -2, "mxfp8")
+        dx = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+        dw = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
+        phases.append(Phase("mx_quant_dual grad", "mx_quant_dual", nbytes=M * N * (2 + 2 * (1 + 1 / 32))))
+        phases.append(Phase("mx_quant W", "mx_quant_rows", nbytes=N * K * (2 + 1 + 1 / 32)))
+        phases.append(Phase("mx_quant X", "mx_quant_rows", nbytes=M * K * (2 + 1 + 1 / 32)))
+        phases.append(Phase("linear_bwd dX", "mx_dx_kernel", flops=2.0 * M * N * K, peak=PEAK_FP8_TFLOPS))
+        phases.append(Phase("linear_bwd dW", "mx_dx_kernel", flops=2.0 * M * N * K, peak=PEAK_FP8_TFLOPS))
+
+        def step(i, stream):
+            ts = []
+            ev = _events(stream)
+            lp.lib.lp_mx_quant_dual(g.data_ptr(), 1, M, N, lp.FMT["mxfp8"], gc.codes.data_ptr(), gc.scales.data_ptr(),
+                                    gr.codes.data_ptr(), gr.scales.data_ptr(), stream.cuda_stream)
+            ts.append(ev.stop(stream))
+            ev = _events(stream)
+            lp.lp_mx_quant(wt, -2, "mxfp8", codes=wq.codes, scales=wq.scales, stream=stream)
+            ts.append(ev.stop(stream))
+            ev = _events(stream)
+            lp.lp_mx_quant(xt, -2, "mxfp8", codes=xq.codes, scales=xq.scales, stream=stream)
+            ts.append(ev.stop(stream))
+            ev = _events(stream)
+            lp.lp_linear_bwd(gc, None, wq, need_dw=False, grad_x=dx, stream=stream)
+            ts.append(ev.stop(stream))
+            ev = _events(stream)
+            lp.lp_linear_bwd(gr, xq, None, need_dx=False, grad_w=dw, stream=stream)
+            ts.append(ev.stop(stream))
+            return ts
+        standalone = []
     else:
         raise SystemExit(f"unknown workload {name}")
     return w, phases, step, standalone
@@ -251,7 +287,29 @@ def cpu_baseline(name: str, budget_s: float = 12.0):
         cores = os.cpu_count()
     w = W.WORKLOADS[name]
     M, N, K = w.M, w.N, w.K
-    if name == "mxfp8_deferred":
+    if name == "mxfp8_dense":
+        # a slab of token rows: quantize grad both ways and X, W along -2,
+        # decode, contract dX and dW over the slab; extrapolate to all rows.
+        rows = 256
+        gb = W.bf16_bits(W.normal_f32(w.number, "grad", (rows, N), 1.0))
+        xb = W.bf16_bits(W.normal_f32(w.number, "x", (rows, K), w.x_sigma))
+        wb = W.bf16_bits(W.normal_f32(w.number, "w", (N, K), w.w_sigma))
+        t0 = time.perf_counter()
+        wc, ws = F.mx_quant(wb[None], -2, "e4m3")
+        wd = F.dequant("mxfp8", wc, ws, axis=-2)[0]
+        t_w = time.perf_counter() - t0
+        t1 = time.perf_counter()
+        gc1, gs1 = F.mx_quant(gb[None], -1, "e4m3")
+        gc2, gs2 = F.mx_quant(gb[None], -2, "e4m3")
+        xc, xs = F.mx_quant(xb[None], -2, "e4m3")
+        O.linear_dx(F.dequant("mxfp8", gc1, gs1, axis=-1)[0], wd)
+        O.linear_dw(F.dequant("mxfp8", gc2, gs2, axis=-2)[0], F.dequant("mxfp8", xc, xs, axis=-2)[0])
+        t_rows = time.perf_counter() - t1
+        total = t_w + t_rows * (M / rows)
+        flops = 4.0 * M * N * K
+        sample = (f"weight quantized+decoded once; {rows} token rows quantized both ways, decoded and contracted "
+                  f"(dX and dW); extrapolated to {M} rows")
+    elif name == "mxfp8_deferred":
         # one expert: quantize its weight along -2 and a slab of gradient rows
         # along -1, decode both, contract.
         rows = 256

@@ -431,3 +431,42 @@ def test_mxfp8_deferred_full_size(lp):
         wc, ws = F.mx_quant(wbits[None], -2, "e4m3")
         w_deq = F.dequant("mxfp8", wc, ws, axis=-2)[0]
         assert_close(dx[torch.from_numpy(rows).cuda()], O.linear_dx(g_deq, w_deq), f"expert {gi} dX")
+
+
+def test_mxfp8_dense_full_size(lp):
+    """The dense deferred MXFP8 backward at 8192 tokens x 4096 x 4096: the GPU
+    quantizes grad along both axes and W, X along their rows, then runs dX and
+    dW on the block-scaled MFMA.  Sampled outputs (rows x columns) are checked
+    against the oracle's own quantization of the same bf16 inputs; every
+    quantization involved is local to the sampled rows or columns."""
+    w = W.WORKLOADS["mxfp8_dense"]
+    M, N, K = w.M, w.N, w.K
+    Gt = W.torch_normal_bf16((M, N), 1.0, seed=6006, device="cuda")
+    Wt = W.torch_normal_bf16((N, K), w.w_sigma, seed=6007, device="cuda")
+    Xt = W.torch_normal_bf16((M, K), 1.0, seed=6008, device="cuda")
+    gc, gr = lp.lp_mx_quant_dual(Gt, "mxfp8")
+    wq = lp.lp_mx_quant(Wt, -2, "mxfp8")
+    xq = lp.lp_mx_quant(Xt, -2, "mxfp8")
+    dx, _ = lp.lp_linear_bwd(gc, None, wq, need_dw=False)
+    _, dw = lp.lp_linear_bwd(gr, xq, None, need_dx=False)
+    torch.cuda.synchronize()
+
+    def host(t):
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    rows, cols = _sample_rows(M, 16, 50), _sample_rows(K, 32, 51)
+    ic = torch.from_numpy(cols).cuda()
+    g = host(Gt[torch.from_numpy(rows).cuda()])
+    gq, gs = F.mx_quant(g[None], -1, "e4m3")
+    wcol = host(Wt[:, ic])
+    wc, ws = F.mx_quant(wcol[None], -2, "e4m3")
+    ref = O.linear_dx(F.dequant("mxfp8", gq, gs, axis=-1)[0], F.dequant("mxfp8", wc, ws, axis=-2)[0])
+    assert_close(dx[torch.from_numpy(rows).cuda()][:, ic], ref, "mxfp8 dense dX")
+
+    nrows = _sample_rows(N, 16, 52)
+    gcol = host(Gt[:, torch.from_numpy(nrows).cuda()])
+    gq, gs = F.mx_quant(gcol[None], -2, "e4m3")
+    xcol = host(Xt[:, ic])
+    xc, xs = F.mx_quant(xcol[None], -2, "e4m3")
+    ref = O.linear_dw(F.dequant("mxfp8", gq, gs, axis=-2)[0], F.dequant("mxfp8", xc, xs, axis=-2)[0])
+    assert_close(dw[torch.from_numpy(nrows).cuda()][:, ic], ref, "mxfp8 dense dW")

@@ -20,6 +20,10 @@ grouped backward of "perf: defer mxfp8 backward quantization"):
                  group sizes ~ Multinomial(16384, Dirichlet(1)); dX and dW
   mxfp8_deferred 64 experts, W bf16 64x2048x7168 N(0,0.02), grad_out bf16
                  32768x2048 N(0,1); group sizes ~ Multinomial(32768, Zipf 1.1)
+  mxfp8_dense    the dense form of the deferred MXFP8 backward (the page's
+                 MXFP8MatMul.backward): X 8192x4096 N(0,1), W 4096x4096
+                 N(0,0.02), grad_out 8192x4096 N(0,1), all bf16, quantized in
+                 the backward; dX and dW
 
 Every tensor has its own PCG64 stream: SeedSequence(entropy=1000 + config
 number, spawn_key=(tensor id,)), so a tensor's values do not depend on which
@@ -67,6 +71,7 @@ WORKLOADS = {
                               groups=8, routing="dirichlet"),
     "mxfp8_deferred": Workload("mxfp8_deferred", 5, "mxfp8", M=32768, N=2048, K=7168,
                                groups=64, w_sigma=0.02, need_dw=False, routing="zipf"),
+    "mxfp8_dense": Workload("mxfp8_dense", 6, "mxfp8", M=8192, N=4096, K=4096, w_sigma=0.02),
 }
 
 
