@@ -195,69 +195,69 @@ __global__ __launch_bounds__(kThreads) void mx_quant_rows(const uint16_t* __rest
   }
 }
 
-// Both axes at once ("perf: defer mxfp8 backward quantization",
-// MXFP8MatMul.backward, npu_dynamic_mx_quant_with_dual_axis): one read of
-// the bf16 tensor, two quantized copies.  Thread i owns a strip of 32 rows x
-// 8 columns as in mx_quant_rows, which gives the blocks along the rows
-// lane-locally; the four lanes of a quad hold 32 consecutive columns of the
-// same rows (cols % 32 == 0, so quads never straddle a row), and each row's
-// block along the columns takes its amax with two DPP exchanges.
-template <bool kFp4>
-__global__ __launch_bounds__(kThreads) void mx_quant_dual(const uint16_t* __restrict__ src,
+// Tiled form for cols % 32 == 0, used for axis -2 and for both axes at once
+// ("perf: defer mxfp8 backward quantization", MXFP8MatMul.backward,
+// npu_dynamic_mx_quant_with_dual_axis: one read of the bf16 tensor, two
+// quantized copies).  Sixteen lanes own a 32 x 32 tile, lane l = c + 4 r
+// holding rows 8 r .. 8 r + 7 and columns 8 c .. 8 c + 7 (16 bytes a row),
+// and the four 16-lane groups of a wave own consecutive tiles of a row of
+// tiles, so that each load covers 256 contiguous bytes of four rows.  A
+// column's amax over the tile's 32 rows combines the four lanes with its
+// column strip (DPP row rotations by 4 and 8); a row's amax over 32 columns
+// combines the lanes of a quad (quad permutations).  Four times as many
+// threads as a 32 x 8 strip per thread, and a quarter of the registers.
+__device__ __forceinline__ uint32_t pk_umax16(uint32_t a, uint32_t b) {
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a), __builtin_bit_cast(u16x2, b)));
+}
+
+template <bool kFp4, bool kDual>
+__global__ __launch_bounds__(kThreads) void mx_quant_tile(const uint16_t* __restrict__ src,
                                                           uint8_t* __restrict__ codes_c, uint8_t* __restrict__ scales_c,
                                                           uint8_t* __restrict__ codes_r, uint8_t* __restrict__ scales_r,
-                                                          uint32_t nstrips, FastDiv strips_per_row, uint32_t cols) {
-  uint32_t i = blockIdx.x * kThreads + threadIdx.x;
-  if (i >= nstrips) return;                              // whole quads (nstrips % 4 == 0)
-  uint32_t rb = fdiv(i, strips_per_row);                 // block of 32 rows over batch*rows
-  uint32_t c0 = (i - rb * strips_per_row.d) * 8u;
-  const uint16_t* base = src + (size_t)rb * 32u * cols + c0;
-  u32x4 v[32];
+                                                          uint32_t ntiles, FastDiv tiles_per_row, uint32_t cols) {
+  const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
+  const uint32_t tile = i >> 4;
+  if (tile >= ntiles) return;                            // whole 16-lane groups
+  const uint32_t l16 = threadIdx.x & 15, ci = l16 & 3, ri = l16 >> 2;
+  const uint32_t rb = fdiv(tile, tiles_per_row);         // block of 32 rows over batch*rows
+  const uint32_t tc = tile - rb * tiles_per_row.d;       // block of 32 columns
+  const uint32_t c0 = 32u * tc + 8u * ci;
+  const size_t row0 = (size_t)rb * 32u + 8u * ri;
+  const uint16_t* base = src + row0 * cols + c0;
+  u32x4 v[8];
 #pragma unroll
-  for (int r = 0; r < 32; ++r) v[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (size_t)r * cols));
+  for (int r = 0; r < 8; ++r) v[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (size_t)r * cols));
 
-  // Blocks along the rows (axis -2): one per column of the strip.
-  uint32_t amax[4] = {0, 0, 0, 0};   // packed pairs of column maxima
+  // Blocks along the rows (axis -2): column maxima over this lane's 8 rows,
+  // then over the 4 lanes of the column strip.
+  uint32_t cm[4] = {0, 0, 0, 0};
 #pragma unroll
-  for (int r = 0; r < 32; ++r)
+  for (int r = 0; r < 8; ++r)
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      uint32_t w = v[r][k] & 0x7FFF7FFFu;
-      amax[k] = umax(amax[k] & 0xFFFFu, w & 0xFFFFu) | (umax(amax[k] >> 16, w >> 16) << 16);
-    }
+    for (int k = 0; k < 4; ++k) cm[k] = pk_umax16(cm[k], v[r][k] & 0x7FFF7FFFu);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    cm[k] = pk_umax16(cm[k], (uint32_t)__builtin_amdgcn_update_dpp(0, (int)cm[k], 0x124, 0xF, 0xF, false));  // row_ror:4
+    cm[k] = pk_umax16(cm[k], (uint32_t)__builtin_amdgcn_update_dpp(0, (int)cm[k], 0x128, 0xF, 0xF, false));  // row_ror:8
+  }
   BlockScale s[8];
   uint32_t sbytes[2] = {0, 0};
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
-    s[c] = block_scale<kFp4>((amax[c >> 1] >> (16 * (c & 1))) & 0xFFFFu);
+    s[c] = block_scale<kFp4>((cm[c >> 1] >> (16 * (c & 1))) & 0xFFFFu);
     sbytes[c >> 2] |= s[c].byte << (8 * (c & 3));
   }
-  *reinterpret_cast<u32x2*>(scales_r + (size_t)rb * cols + c0) = u32x2{sbytes[0], sbytes[1]};
+  if (ri == 0) *reinterpret_cast<u32x2*>(scales_r + (size_t)rb * cols + c0) = u32x2{sbytes[0], sbytes[1]};
   const size_t row_bytes = kFp4 ? cols / 2 : cols;
-  uint8_t* out_r = codes_r + (size_t)rb * 32u * row_bytes + (kFp4 ? c0 / 2 : c0);
-  uint8_t* out_c = codes_c + (size_t)rb * 32u * row_bytes + (kFp4 ? c0 / 2 : c0);
-  const uint32_t sc_row = cols / 32;                     // column-block scales per row
-  uint8_t* sc_c = scales_c + (size_t)rb * 32u * sc_row + c0 / 32;
-  const bool leader = (threadIdx.x & 3) == 0;
+  uint8_t* out_r = codes_r + row0 * row_bytes + (kFp4 ? c0 / 2 : c0);
 #pragma unroll
-  for (int r = 0; r < 32; ++r) {
-    // Block along the columns (axis -1) of row r: 32 columns over the quad.
-    uint32_t m = 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t w = v[r][k] & 0x7FFF7FFFu;
-      m = umax(m, umax(w & 0xFFFFu, w >> 16));
-    }
-    const BlockScale sr = block_scale<kFp4>(quad_max(m));
-    if (leader) sc_c[(size_t)r * sc_row] = (uint8_t)sr.byte;
+  for (int r = 0; r < 8; ++r) {
     if constexpr (!kFp4) {
-      uint32_t oc[2], orr[2];
+      uint32_t o[2];
 #pragma unroll
       for (int k = 0; k < 4; k += 2) {
         const uint32_t w0 = v[r][k], w1 = v[r][k + 1];
-        const uint32_t lo = sr.bad ? nan_e4m3x2(w0) : to_e4m3x2(bf16_lo(w0) * sr.inv, bf16_hi(w0) * sr.inv);
-        const uint32_t hi = sr.bad ? nan_e4m3x2(w1) : to_e4m3x2(bf16_lo(w1) * sr.inv, bf16_hi(w1) * sr.inv);
-        oc[k / 2] = lo | (hi << 16);
         const int c = 2 * k;
         const uint32_t p0 = to_e4m3x2(bf16_lo(w0) * s[c].inv, bf16_hi(w0) * s[c + 1].inv);
         const uint32_t p1 = to_e4m3x2(bf16_lo(w1) * s[c + 2].inv, bf16_hi(w1) * s[c + 3].inv);
@@ -265,24 +265,51 @@ __global__ __launch_bounds__(kThreads) void mx_quant_dual(const uint16_t* __rest
         const uint32_t b1 = s[c + 1].bad ? (0x7Fu | ((w0 >> 24) & 0x80u)) : (p0 >> 8);
         const uint32_t b2 = s[c + 2].bad ? (0x7Fu | ((w1 >> 8) & 0x80u)) : (p1 & 0xFFu);
         const uint32_t b3 = s[c + 3].bad ? (0x7Fu | ((w1 >> 24) & 0x80u)) : (p1 >> 8);
-        orr[k / 2] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+        o[k / 2] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
       }
-      *reinterpret_cast<u32x2*>(out_c + (size_t)r * cols) = u32x2{oc[0], oc[1]};
-      *reinterpret_cast<u32x2*>(out_r + (size_t)r * cols) = u32x2{orr[0], orr[1]};
+      __builtin_nontemporal_store(u32x2{o[0], o[1]}, reinterpret_cast<u32x2*>(out_r + (size_t)r * row_bytes));
     } else {
-      uint32_t oc = 0, orr = 0;
+      uint32_t o = 0;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const uint32_t w = v[r][k];
-        oc |= to_e2m1x2(bf16_lo(w) * sr.inv, bf16_hi(w) * sr.inv) << (8 * k);
         const int c = 2 * k;
         const uint32_t b = to_e2m1x2(bf16_lo(w) * s[c].inv, bf16_hi(w) * s[c + 1].inv);
         const uint32_t lo = s[c].bad ? 0u : (b & 0xFu);
         const uint32_t hi = s[c + 1].bad ? 0u : (b >> 4);
-        orr |= (lo | (hi << 4)) << (8 * k);
+        o |= (lo | (hi << 4)) << (8 * k);
       }
-      *reinterpret_cast<uint32_t*>(out_c + (size_t)r * (cols / 2)) = sr.bad ? 0u : oc;
-      *reinterpret_cast<uint32_t*>(out_r + (size_t)r * (cols / 2)) = orr;
+      __builtin_nontemporal_store(o, reinterpret_cast<uint32_t*>(out_r + (size_t)r * row_bytes));
+    }
+  }
+  if constexpr (kDual) {
+    // Blocks along the columns (axis -1): each of the 8 rows over the quad.
+    uint8_t* out_c = codes_c + row0 * row_bytes + (kFp4 ? c0 / 2 : c0);
+    uint8_t* sc_c = scales_c + row0 * (cols / 32) + tc;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      uint32_t m = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) m = pk_umax16(m, v[r][k] & 0x7FFF7FFFu);
+      m = umax(m & 0xFFFFu, m >> 16);
+      const BlockScale sr = block_scale<kFp4>(quad_max(m));
+      if (ci == (uint32_t)(r >> 1)) sc_c[(size_t)r * (cols / 32)] = (uint8_t)sr.byte;   // two rows per lane
+      if constexpr (!kFp4) {
+        uint32_t o[2];
+#pragma unroll
+        for (int k = 0; k < 4; k += 2) {
+          const uint32_t w0 = v[r][k], w1 = v[r][k + 1];
+          const uint32_t lo = sr.bad ? nan_e4m3x2(w0) : to_e4m3x2(bf16_lo(w0) * sr.inv, bf16_hi(w0) * sr.inv);
+          const uint32_t hi = sr.bad ? nan_e4m3x2(w1) : to_e4m3x2(bf16_lo(w1) * sr.inv, bf16_hi(w1) * sr.inv);
+          o[k / 2] = lo | (hi << 16);
+        }
+        __builtin_nontemporal_store(u32x2{o[0], o[1]}, reinterpret_cast<u32x2*>(out_c + (size_t)r * row_bytes));
+      } else {
+        uint32_t o = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) o |= to_e2m1x2(bf16_lo(v[r][k]) * sr.inv, bf16_hi(v[r][k]) * sr.inv) << (8 * k);
+        __builtin_nontemporal_store(sr.bad ? 0u : o, reinterpret_cast<uint32_t*>(out_c + (size_t)r * row_bytes));
+      }
     }
   }
 }
@@ -303,6 +330,19 @@ hipError_t launch_mx_quant(const void* src, int64_t batch, int64_t rows, int64_t
       mx_quant_cols<true><<<grid, block, 0, stream>>>(s, static_cast<uint32_t*>(codes), sc, nunits);
     else
       mx_quant_cols<false><<<grid, block, 0, stream>>>(s, static_cast<u32x2*>(codes), sc, nunits);
+  } else if (cols % 32 == 0) {
+    const uint32_t tpr = (uint32_t)(cols / 32);
+    const uint32_t ntiles = (uint32_t)(batch * (rows / 32) * tpr);
+    const dim3 grid((ntiles * 16 + kThreads - 1) / kThreads), block(kThreads);
+    auto s = static_cast<const uint16_t*>(src);
+    auto c = static_cast<uint8_t*>(codes);
+    auto sc = static_cast<uint8_t*>(scales);
+    if (fp4)
+      mx_quant_tile<true, false><<<grid, block, 0, stream>>>(s, nullptr, nullptr, c, sc, ntiles, make_fastdiv(tpr),
+                                                              (uint32_t)cols);
+    else
+      mx_quant_tile<false, false><<<grid, block, 0, stream>>>(s, nullptr, nullptr, c, sc, ntiles, make_fastdiv(tpr),
+                                                               (uint32_t)cols);
   } else {
     const uint32_t spr = (uint32_t)(cols / 8);
     const uint32_t nstrips = (uint32_t)(batch * (rows / 32) * spr);
@@ -322,18 +362,18 @@ hipError_t launch_mx_quant_dual(const void* src, int64_t batch, int64_t rows, in
                                 void* codes_c, void* scales_c, void* codes_r, void* scales_r, hipStream_t stream) {
   const int64_t n = batch * rows * cols;
   if (n == 0) return hipSuccess;
-  const uint32_t spr = (uint32_t)(cols / 8);
-  const uint32_t nstrips = (uint32_t)(batch * (rows / 32) * spr);
-  const dim3 grid((nstrips + kThreads - 1) / kThreads), block(kThreads);
+  const uint32_t tpr = (uint32_t)(cols / 32);
+  const uint32_t ntiles = (uint32_t)(batch * (rows / 32) * tpr);
+  const dim3 grid((ntiles * 16 + kThreads - 1) / kThreads), block(kThreads);
   auto s = static_cast<const uint16_t*>(src);
   auto cc = static_cast<uint8_t*>(codes_c);
   auto scc = static_cast<uint8_t*>(scales_c);
   auto cr = static_cast<uint8_t*>(codes_r);
   auto scr = static_cast<uint8_t*>(scales_r);
   if (dst_fmt == LP_MXFP4)
-    mx_quant_dual<true><<<grid, block, 0, stream>>>(s, cc, scc, cr, scr, nstrips, make_fastdiv(spr), (uint32_t)cols);
+    mx_quant_tile<true, true><<<grid, block, 0, stream>>>(s, cc, scc, cr, scr, ntiles, make_fastdiv(tpr), (uint32_t)cols);
   else
-    mx_quant_dual<false><<<grid, block, 0, stream>>>(s, cc, scc, cr, scr, nstrips, make_fastdiv(spr), (uint32_t)cols);
+    mx_quant_tile<false, true><<<grid, block, 0, stream>>>(s, cc, scc, cr, scr, ntiles, make_fastdiv(tpr), (uint32_t)cols);
   return hipGetLastError();
 }
 
