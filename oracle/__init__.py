@@ -18,8 +18,12 @@ Pins (tests/test_oracle_*.py, all CPU):
 * MX quant: scale-exponent invariant, idempotence, special blocks.
 * GEMMs: pure-Python triple loops on tiny shapes, the ones-gradient closed
   forms of the FP8-adapter page's tests, grouped == per-group dense.
+* per-tensor FP8 (pertensor.py): the E5M2 table against torch's
+  float8_e5m2, quantization against torch's casts below saturation and a
+  brute-force nearest search, the scale formula and ring update of the
+  AstrAI page, triple-loop GEMMs with the scales applied to the sums.
 
 Parity unpinned by the pages: the E2M1 nibble order and the NVFP4
 tensor-scale reading (see formats.py).
 """
-from . import formats, gemm  # noqa: F401
+from . import formats, gemm, pertensor  # noqa: F401

@@ -17,6 +17,7 @@ import torch
 import workloads as W
 from oracle import formats as F
 from oracle import gemm as O
+from oracle import pertensor as PT
 
 GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_constants.json")))
 
@@ -405,6 +406,111 @@ def pin_grouped_equals_dense():
     assert np.all(dw[1] == 0)
     one_dx, _ = O.grouped_dx(g, w[:1], np.array([M], np.int32))
     assert np.allclose(one_dx, O.linear_dx(g, w[0]), rtol=1e-13)
+
+
+# ------------------------------------------------------------------ per-tensor FP8 ("AstrAI fp8.py")
+
+def pin_fp8_max_table_matches_page():
+    assert PT.FP8_MAX["e4m3"] == GOLDEN["e4m3_max"]["value"]
+    assert PT.FP8_MAX["e5m2"] == GOLDEN["e5m2_max"]["value"]
+    for elem in ("e4m3", "e5m2"):
+        t = PT.TABLES[elem]
+        assert np.nanmax(np.where(np.isinf(t), np.nan, t)) == PT.FP8_MAX[elem]
+
+
+def pin_e5m2_table_against_torch():
+    """All 256 E5M2 codes against torch's float8_e5m2 decode."""
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e5m2).double().numpy()
+    assert _same_bits_or_both_nan(PT.E5M2_TABLE, ref)
+    assert np.isinf(PT.E5M2_TABLE[0x7C]) and np.isnan(PT.E5M2_TABLE[0x7D])
+
+
+def pin_tensor_quantize_against_torch():
+    """Every finite bf16 value x, several scales: codes equal torch's
+    (x.float() / scale).to(float8) wherever the quotient is below the
+    format's maximum (torch does not saturate, so larger ones are left to
+    the saturation pin)."""
+    b = np.arange(1 << 16, dtype=np.uint32)
+    bits = b[((b >> 7) & 0xFF) != 0xFF].astype(np.uint16)
+    xf = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).float()
+    for elem, dt in (("e4m3", torch.float8_e4m3fn), ("e5m2", torch.float8_e5m2)):
+        for scale in (1.0, 0.0173, 3.0e-3, 97.0, 2.0 ** -20):
+            q = (xf / torch.tensor(scale, dtype=torch.float32))
+            ok = (q.abs() <= PT.FP8_MAX[elem]).numpy()
+            ref = q.to(dt).view(torch.uint8).numpy()
+            got = PT.quantize(bits, elem, np.float32(scale))
+            assert np.array_equal(got[ok], ref[ok]), (elem, scale)
+
+
+def pin_tensor_quantize_saturates():
+    """Brute force: beyond the maximum (infinities included) the code is the
+    signed maximum; NaN keeps its sign on the 0x7F pattern; otherwise the
+    code is the nearest value by exhaustive search, ties to the even code."""
+    for elem in ("e4m3", "e5m2"):
+        mx = PT.FP8_MAX[elem]
+        t = np.array([mx * 1.01, -mx * 4, np.inf, -np.inf, np.nan, -np.nan, mx, -0.0, 0.0])
+        c = PT.round_to_fp8(t, elem)
+        vals = PT.TABLES[elem]
+        assert vals[c[0]] == mx and vals[c[1]] == -mx and vals[c[2]] == mx and vals[c[3]] == -mx
+        assert c[4] == 0x7F and c[5] == 0xFF and vals[c[6]] == mx and c[7] == 0x80 and c[8] == 0x00
+        g = W.rng(60, "x")
+        r = g.standard_normal(4000) * g.choice([1e-6, 1e-3, 1.0, 10.0, 100.0, 1e4], 4000)
+        r = r[np.abs(r) < mx]
+        codes = PT.round_to_fp8(r, elem)
+        fin = np.arange(256)[np.isfinite(vals)]
+        d = np.abs(r[:, None] - vals[fin][None, :])
+        best = d.min(axis=1)
+        got = np.abs(r - vals[codes])
+        assert np.array_equal(got, best)
+
+
+def pin_scale_from_history_formula():
+    """scale = (max(history) / FP8_MAX) / 2^margin, at least 1e-12
+    (fp32), as the page's DelayedScaling / DynamicScaling define it."""
+    assert PT.scale_from_history([1.0, 57344.0, 2.0], "e5m2") == np.float32(1.0)
+    assert PT.scale_from_history([57344.0], "e5m2", margin=2) == np.float32(0.25)
+    assert PT.scale_from_history([448.0, 3.0], "e4m3") == np.float32(1.0)
+    assert PT.scale_from_history([0.0, 0.0], "e4m3") == np.float32(1e-12)
+    s = PT.scale_from_history([7.25], "e4m3", margin=1)
+    assert s == np.float32(np.float32(7.25 / 448.0) / 2)
+    hist = np.ones(4, np.float32)
+    i = 0
+    for v in (5.0, 9.0, 2.0, 3.0, 4.0):
+        i = PT.record(hist, i, v)
+    assert i == 1 and list(hist) == [4.0, 9.0, 2.0, 3.0]
+    assert PT.scale_from_history(hist, "e5m2") == np.float32(np.float32(9.0) / np.float32(57344.0))
+
+
+def pin_tensor_amax_and_dequant():
+    bits = W.bf16_bits(np.array([1.5, -7.0, 0.25, -0.0], dtype=np.float32))
+    assert PT.amax(bits) == np.float32(7.0)
+    assert np.isnan(PT.amax(np.array([0x3F80, 0x7FC0], dtype=np.uint16)))
+    # E5M2 0x3C = 1.0, 0x42 = 3.0, 0xBF = -1.75; times 3.0 -> 3.0, 9.0, -5.25
+    d = PT.dequant(np.array([0x3C, 0x42, 0xBF, 0x7F, 0xFF, 0x7C], dtype=np.uint8), "e5m2", 3.0)
+    assert list(d) == [0x4040, 0x4110, 0xC0A8, 0x7FC0, 0xFFC0, 0x7F80]
+
+
+def pin_tensor_gemms_brute_force():
+    """Pure-Python triple loops with the scales applied to the sums."""
+    g = W.rng(61, "grad")
+    gc = g.integers(0, 256, size=(3, 5), dtype=np.uint8) & 0x7B          # finite E5M2 codes
+    wc = g.integers(0, 256, size=(5, 4), dtype=np.uint8) & 0x77          # finite E4M3 codes
+    xc = g.integers(0, 256, size=(3, 4), dtype=np.uint8) & 0x7B
+    sg, sw, sx = 0.375, 1.5, 0.0625
+    dx = PT.linear_dx(gc, "e5m2", sg, wc, "e4m3", sw)
+    dw = PT.linear_dw(gc, "e5m2", sg, xc, "e5m2", sx)
+    for m in range(3):
+        for k in range(4):
+            acc = 0.0
+            for n in range(5):
+                acc += PT.e5m2_value(int(gc[m, n])) * sg * F.e4m3_value(int(wc[n, k])) * sw
+            assert abs(dx[m, k] - acc) <= 1e-12 * max(1.0, abs(acc))
+    for n in range(5):
+        for k in range(4):
+            acc = 0.0
+            for m in range(3):
+                acc += PT.e5m2_value(int(gc[m, n])) * sg * PT.e5m2_value(int(xc[m, k])) * sx
+            assert abs(dw[n, k] - acc) <= 1e-12 * max(1.0, abs(acc))
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

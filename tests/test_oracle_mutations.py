@@ -16,6 +16,7 @@ sys.path.insert(0, os.path.dirname(__file__))
 import oracle_pins  # noqa: E402
 from oracle import formats as F  # noqa: E402
 from oracle import gemm as O  # noqa: E402
+from oracle import pertensor as PT  # noqa: E402
 
 
 def _swap_nibbles(packed):
@@ -79,7 +80,47 @@ def _no_f32_step(x):
     return np.asarray(x, dtype=np.float64)
 
 
+_orig_pt_quant = PT.quantize
+
+
+def _pt_quant_multiplies(bits, elem, scale):
+    return _orig_pt_quant(bits, elem, np.float32(1.0) / np.float32(scale))
+
+
+_orig_pt_round = PT.round_to_fp8
+
+
+def _pt_no_saturation(t, elem):
+    t = np.asarray(t, dtype=np.float64)
+    return np.where(np.abs(t) > PT.FP8_MAX[elem], np.uint8(0x7F) | (np.signbit(t) * 0x80).astype(np.uint8),
+                    _orig_pt_round(t, elem)).astype(np.uint8)
+
+
+_orig_pt_scale = PT.scale_from_history
+
+
+def _pt_scale_no_margin(hist, elem, margin=0):
+    return _orig_pt_scale(hist, elem, 0)
+
+
+def _pt_scale_latest(hist, elem, margin=0):
+    return _orig_pt_scale(np.asarray(hist)[-1:], elem, margin)
+
+
+_orig_pt_dx = PT.linear_dx
+
+
+def _pt_dx_one_scale(g_codes, g_elem, g_scale, w_codes, w_elem, w_scale):
+    return _orig_pt_dx(g_codes, g_elem, g_scale, w_codes, w_elem, 1.0)
+
+
 MUTATIONS = {
+    "per-tensor quantization multiplies by the scale": (PT, "quantize", _pt_quant_multiplies),
+    "per-tensor quantization without saturation": (PT, "round_to_fp8", _pt_no_saturation),
+    "scale ignores the margin": (PT, "scale_from_history", _pt_scale_no_margin),
+    "delayed scale from the latest amax only": (PT, "scale_from_history", _pt_scale_latest),
+    "E5M2 bias 16": (PT, "TABLES", {"e4m3": F.E4M3_TABLE, "e5m2": PT.E5M2_TABLE / 2}),
+    "per-tensor dX drops the weight scale": (PT, "linear_dx", _pt_dx_one_scale),
     "nibble order swapped": (F, "unpack_e2m1", _swap_nibbles),
     "bf16 truncation instead of RNE": (F, "f32_to_bf16_bits", _truncating_bf16),
     "ties away from zero": (F, "round_to_grid", _ties_up),
