@@ -7,7 +7,8 @@ Every step of the computation runs in the library's HIP kernels; there is no
 fallback, and importing this package fails if the library is not built
 (`python fp8_gemm_backward_amd/build.py`).
 
-Formats (see include/lp.h): "bf16", "mxfp4", "nvfp4", "fp8_b128", "mxfp8".
+Formats (see include/lp.h): "bf16", "mxfp4", "nvfp4", "fp8_b128", "mxfp8",
+and the per-tensor scaled "fp8t_e4m3", "fp8t_e5m2".
 """
 from __future__ import annotations
 
@@ -23,7 +24,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "liblp.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "lp.h")
 
-FMT = {"bf16": 0, "mxfp4": 1, "nvfp4": 2, "fp8_b128": 3, "mxfp8": 4}
+FMT = {"bf16": 0, "mxfp4": 1, "nvfp4": 2, "fp8_b128": 3, "mxfp8": 4, "fp8t_e4m3": 5, "fp8t_e5m2": 6}
 STATUS = {0: "LP_OK", 1: "LP_ERR_NULL", 2: "LP_ERR_SHAPE", 3: "LP_ERR_FORMAT", 4: "LP_ERR_ALIGN",
           5: "LP_ERR_HIP"}
 
@@ -54,10 +55,14 @@ def _load() -> ctypes.CDLL:
     lib.lp_grouped_bwd.argtypes = [P, P, P, v, i64, v, v, v]
     lib.lp_linear_bwd_workspace.argtypes = [P, P, P, v, v, ctypes.POINTER(ctypes.c_size_t)]
     lib.lp_linear_bwd_ws.argtypes = [P, P, P, v, v, v, ctypes.c_size_t, v]
+    lib.lp_tensor_amax.argtypes = [v, i64, v, v]
+    lib.lp_tensor_quant.argtypes = [v, i64, i32, v, v, v, v]
+    lib.lp_scale_from_history.argtypes = [v, i32, i32, i32, v, v]
     lib.lp_status_string.argtypes = [i32]
     lib.lp_status_string.restype = ctypes.c_char_p
     for f in ("lp_dequant", "lp_mx_quant", "lp_mx_quant_dual", "lp_linear_bwd", "lp_grouped_bwd",
-              "lp_linear_bwd_workspace", "lp_linear_bwd_ws"):
+              "lp_linear_bwd_workspace", "lp_linear_bwd_ws", "lp_tensor_amax", "lp_tensor_quant",
+              "lp_scale_from_history"):
         getattr(lib, f).restype = ctypes.c_int32
     return lib
 
@@ -77,7 +82,8 @@ class QTensor:
 
     codes: bf16 values (fmt "bf16"), uint8 E4M3 codes, or uint8 packed E2M1
     pairs; scales: uint8 E8M0 / E4M3 bytes or float32 block scales; for
-    NVFP4 `tensor_scale` is a one-element float32 device tensor.
+    NVFP4 and the per-tensor FP8 formats `tensor_scale` is a one-element
+    float32 device tensor.
     """
     fmt: str
     codes: torch.Tensor
@@ -160,6 +166,38 @@ def lp_mx_quant_dual(src: torch.Tensor, fmt: str = "mxfp8", stream=None) -> tupl
     _check(lib.lp_mx_quant_dual(src.data_ptr(), b, r, c, FMT[fmt], codes_c.data_ptr(), scales_c.data_ptr(),
                                 codes_r.data_ptr(), scales_r.data_ptr(), _stream(stream)), "lp_mx_quant_dual")
     return QTensor(fmt, codes_c, scales_c, None, shape, -1), QTensor(fmt, codes_r, scales_r, None, shape, -2)
+
+
+def lp_tensor_amax(src: torch.Tensor, amax: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """max |x| of a bf16 tensor into a float32 device scalar (`amax` may be a
+    one-element view into an amax history)."""
+    if amax is None:
+        amax = torch.empty(1, dtype=torch.float32, device=src.device)
+    _check(lib.lp_tensor_amax(src.data_ptr(), src.numel(), amax.data_ptr(), _stream(stream)), "lp_tensor_amax")
+    return amax
+
+
+def lp_tensor_quant(src: torch.Tensor, fmt: str, scale: torch.Tensor, amax: Optional[torch.Tensor] = None,
+                    codes: Optional[torch.Tensor] = None, stream=None) -> QTensor:
+    """Per-tensor FP8 quantization ("fp8t_e4m3" / "fp8t_e5m2") of a bf16
+    tensor [batch, rows, cols] (or [rows, cols]) with the float32 device
+    scalar `scale`; the input's amax goes to `amax` when given."""
+    shape = tuple(src.shape) if src.dim() == 3 else (1,) + tuple(src.shape)
+    if codes is None:
+        codes = torch.empty(shape, dtype=torch.uint8, device=src.device)
+    _check(lib.lp_tensor_quant(src.data_ptr(), src.numel(), FMT[fmt], scale.data_ptr(), codes.data_ptr(),
+                               None if amax is None else amax.data_ptr(), _stream(stream)), "lp_tensor_quant")
+    return QTensor(fmt, codes, None, scale, shape, -1)
+
+
+def lp_scale_from_history(history: torch.Tensor, fmt: str, margin: int = 0, scale: Optional[torch.Tensor] = None,
+                          stream=None) -> torch.Tensor:
+    """Per-tensor scale (float32 device scalar) from a float32 amax history."""
+    if scale is None:
+        scale = torch.empty(1, dtype=torch.float32, device=history.device)
+    _check(lib.lp_scale_from_history(history.data_ptr(), history.numel(), FMT[fmt], margin, scale.data_ptr(),
+                                     _stream(stream)), "lp_scale_from_history")
+    return scale
 
 
 def lp_linear_bwd(grad_out: QTensor, x: Optional[QTensor], w: Optional[QTensor], need_dx: bool = True,

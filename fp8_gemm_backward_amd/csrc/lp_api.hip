@@ -12,14 +12,17 @@ constexpr int64_t kMaxDim = ((int64_t)1 << 31) - 1;
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 bool is_fp4(int f) { return f == LP_MXFP4 || f == LP_NVFP4; }
+bool is_fp8t(int f) { return f == LP_FP8T_E4M3 || f == LP_FP8T_E5M2; }
+bool has_tensor_scale(int f) { return f == LP_NVFP4 || is_fp8t(f); }
+bool has_block_scales(int f) { return f != LP_BF16 && !is_fp8t(f); }
 
 // Shape, pointer and alignment checks of one operand tensor.
 lp_status check_tensor(const lp_qtensor* t) {
   if (t == nullptr) return LP_ERR_NULL;
-  if (t->fmt < LP_BF16 || t->fmt > LP_MXFP8) return LP_ERR_FORMAT;
+  if (t->fmt < LP_BF16 || t->fmt > LP_FP8T_E5M2) return LP_ERR_FORMAT;
   if (t->batch < 0 || t->rows < 0 || t->cols < 0) return LP_ERR_SHAPE;
   if (t->rows > kMaxDim || t->cols > kMaxDim || t->batch > kMaxDim) return LP_ERR_SHAPE;
-  const int axis = t->fmt == LP_BF16 ? -1 : t->scale_axis;
+  const int axis = has_block_scales(t->fmt) ? t->scale_axis : -1;
   if (axis != -1 && axis != -2) return LP_ERR_FORMAT;
   if (axis == -2 && t->fmt != LP_MXFP8) return LP_ERR_FORMAT;
   if (t->cols % 16) return LP_ERR_SHAPE;
@@ -29,11 +32,11 @@ lp_status check_tensor(const lp_qtensor* t) {
   if (n / 8 >= kMaxUnits) return LP_ERR_SHAPE;
   if (n == 0) return LP_OK;
   if (t->codes == nullptr) return LP_ERR_NULL;
-  if (t->fmt != LP_BF16 && t->scales == nullptr) return LP_ERR_NULL;
-  if (t->fmt == LP_NVFP4 && t->tensor_scale == nullptr) return LP_ERR_NULL;
+  if (has_block_scales(t->fmt) && t->scales == nullptr) return LP_ERR_NULL;
+  if (has_tensor_scale(t->fmt) && t->tensor_scale == nullptr) return LP_ERR_NULL;
   if (!aligned(t->codes, 16)) return LP_ERR_ALIGN;
-  if (t->fmt != LP_BF16 && !aligned(t->scales, 16)) return LP_ERR_ALIGN;
-  if (t->fmt == LP_NVFP4 && !aligned(t->tensor_scale, 4)) return LP_ERR_ALIGN;
+  if (has_block_scales(t->fmt) && !aligned(t->scales, 16)) return LP_ERR_ALIGN;
+  if (has_tensor_scale(t->fmt) && !aligned(t->tensor_scale, 4)) return LP_ERR_ALIGN;
   return LP_OK;
 }
 
@@ -48,21 +51,25 @@ lp_status check_bwd(const lp_qtensor* grad, const lp_qtensor* x, const lp_qtenso
   if (grad->batch != 1) return LP_ERR_SHAPE;
   // grad_out: bf16 for every product; MXFP8 along its columns (the dX
   // contraction) for dX only; MXFP8 along its rows (the dW contraction) for a
-  // dense dW of an MXFP8 input scaled along its rows, only.
+  // dense dW of an MXFP8 input scaled along its rows, only; per-tensor FP8
+  // for both products, with per-tensor FP8 operands only.
   const bool g_mx_cols = grad->fmt == LP_MXFP8 && grad->scale_axis == -1;
   const bool g_mx_rows = grad->fmt == LP_MXFP8 && grad->scale_axis == -2;
-  if (grad->fmt != LP_BF16 && !g_mx_cols && !g_mx_rows) return LP_ERR_FORMAT;
+  const bool g_t = is_fp8t(grad->fmt);
+  if (grad->fmt != LP_BF16 && !g_mx_cols && !g_mx_rows && !g_t) return LP_ERR_FORMAT;
   if (g_mx_rows && (grad_x != nullptr || groups != 0)) return LP_ERR_FORMAT;
   const int64_t M = grad->rows, N = grad->cols;
   int64_t K = -1;
   if (grad_x != nullptr) {
     if ((st = check_tensor(w)) != LP_OK) return st;
+    if (is_fp8t(w->fmt) != g_t) return LP_ERR_FORMAT;
     if (w->batch != (groups ? groups : 1) || w->rows != N) return LP_ERR_SHAPE;
     K = w->cols;
   }
   if (grad_w != nullptr) {
     if (g_mx_cols) return LP_ERR_FORMAT;              // its scales do not run along the dW contraction
     if ((st = check_tensor(x)) != LP_OK) return st;
+    if (is_fp8t(x->fmt) != g_t) return LP_ERR_FORMAT;
     if (g_mx_rows && !(x->fmt == LP_MXFP8 && x->scale_axis == -2)) return LP_ERR_FORMAT;
     if (x->batch != 1 || x->rows != M) return LP_ERR_SHAPE;
     if (K >= 0 && x->cols != K) return LP_ERR_SHAPE;
@@ -122,6 +129,32 @@ lp_status lp_mx_quant_dual(const void* src, int64_t batch, int64_t rows, int64_t
     return LP_ERR_ALIGN;
   return hip_status(lp::launch_mx_quant_dual(src, batch, rows, cols, dst_fmt, codes_cols, scales_cols, codes_rows,
                                              scales_rows, static_cast<hipStream_t>(stream)));
+}
+
+lp_status lp_tensor_amax(const void* src, int64_t n, float* amax, void* stream) {
+  if (n < 0 || n % 8 || n / 8 >= kMaxUnits) return LP_ERR_SHAPE;
+  if (amax == nullptr || (n > 0 && src == nullptr)) return LP_ERR_NULL;
+  if (!aligned(amax, 4) || !aligned(src, 16)) return LP_ERR_ALIGN;
+  return hip_status(lp::launch_tensor_amax(src, n, amax, static_cast<hipStream_t>(stream)));
+}
+
+lp_status lp_tensor_quant(const void* src, int64_t n, int32_t dst_fmt, const float* scale, void* codes, float* amax,
+                          void* stream) {
+  if (!is_fp8t(dst_fmt)) return LP_ERR_FORMAT;
+  if (n < 0 || n % 8 || n / 8 >= kMaxUnits) return LP_ERR_SHAPE;
+  if (n > 0 && (src == nullptr || codes == nullptr || scale == nullptr)) return LP_ERR_NULL;
+  if (amax != nullptr && amax == scale) return LP_ERR_SHAPE;     // the amax would clear the scale first
+  if (!aligned(src, 16) || !aligned(codes, 16) || !aligned(scale, 4) || !aligned(amax, 4)) return LP_ERR_ALIGN;
+  return hip_status(lp::launch_tensor_quant(src, n, dst_fmt, scale, codes, amax, static_cast<hipStream_t>(stream)));
+}
+
+lp_status lp_scale_from_history(const float* history, int32_t len, int32_t fmt, int32_t margin, float* scale,
+                                void* stream) {
+  if (!is_fp8t(fmt)) return LP_ERR_FORMAT;
+  if (len < 1 || len > 65536 || margin < -64 || margin > 64) return LP_ERR_SHAPE;
+  if (history == nullptr || scale == nullptr) return LP_ERR_NULL;
+  if (!aligned(history, 4) || !aligned(scale, 4)) return LP_ERR_ALIGN;
+  return hip_status(lp::launch_scale_from_history(history, len, fmt, margin, scale, static_cast<hipStream_t>(stream)));
 }
 
 static lp_status run_bwd(const lp_qtensor* grad, const lp_qtensor* x, const lp_qtensor* w, const int32_t* offsets,

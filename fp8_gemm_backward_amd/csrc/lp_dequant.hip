@@ -215,6 +215,9 @@ hipError_t launch_dequant(const lp_qtensor& t, void* dst, hipStream_t stream) {
           c64, static_cast<const float*>(t.scales), out, nunits, make_fastdiv((uint32_t)(t.cols / 8)),
           make_fastdiv((uint32_t)t.rows), (uint32_t)((t.rows + 127) / 128), (uint32_t)((t.cols + 127) / 128));
       break;
+    case LP_FP8T_E4M3:
+    case LP_FP8T_E5M2:
+      return launch_tensor_dequant(t, dst, stream);
     default:
       return hipErrorInvalidValue;
   }

@@ -32,6 +32,10 @@ Op make_op(const lp_qtensor& t) {
       o.scale_ld = (int32_t)(((Cc + 127) / 128) * 4);
       o.scale_bytes = ((R + 127) / 128) * ((Cc + 127) / 128) * 4;
       break;
+    case LP_FP8T_E4M3:
+    case LP_FP8T_E5M2:
+      o.code_ld = (int32_t)Cc;
+      break;
     case LP_MXFP8:
       o.code_ld = (int32_t)Cc;
       if (t.scale_axis == -1) {
@@ -102,9 +106,14 @@ bool native_mx(const GemmCall& call) {
   return !call.dw || (call.grad->scale_axis == -2 && call.offsets == nullptr);
 }
 
+bool is_fp8t(int f) { return f == LP_FP8T_E4M3 || f == LP_FP8T_E5M2; }
+
+// Per-tensor scaled FP8 on both sides of the product.
+bool native_pt(const GemmCall& call) { return is_fp8t(call.grad->fmt) && is_fp8t(call.other->fmt); }
+
 SplitPlan split_plan(const GemmCall& call) {
   SplitPlan sp{1, 0, big_tiles(call), 0};
-  if (call.offsets != nullptr || native_mx(call) || narrow_tiles(call) >= kCUs / 2 || sp.tiles == 0) return sp;
+  if (call.offsets != nullptr || native_mx(call) || native_pt(call) || narrow_tiles(call) >= kCUs / 2 || sp.tiles == 0) return sp;
   const int64_t ktot = call.dw ? call.M : call.N;
   const int64_t nk = (ktot + BK - 1) / BK;
   int64_t s = kCUs / sp.tiles;
@@ -146,15 +155,17 @@ hipError_t launch_gemm(const GemmCall& call, hipStream_t stream) {
     prm.Ktot = (int32_t)call.M;
     prm.c_batch = call.N * call.K;
   }
-  if (native_mx(call)) {
+  if (native_mx(call) || native_pt(call)) {
+    const bool pt = native_pt(call);
+    const int fp = call.grad->fmt, fq = call.other->fmt;
     prm.nq = (int32_t)((prm.Qtot + Big::BQ - 1) / Big::BQ);
     if (call.dw) {
-      prm.ntiles = (int32_t)(((call.N + Big::BP - 1) / Big::BP) * prm.nq);
-      return dw_mx(prm, stream);
+      prm.ntiles = (int32_t)(((call.N + Big::BP - 1) / Big::BP) * prm.nq * call.groups);
+      return pt ? dw_pt(prm, fp, fq, stream) : dw_mx(prm, stream);
     }
     const int64_t ptiles = call.offsets ? (call.M / Big::BP + call.groups) : (call.M + Big::BP - 1) / Big::BP;
     prm.ntiles = (int32_t)(ptiles * prm.nq);
-    return dx_mx(prm, stream);
+    return pt ? dx_pt(prm, fp, fq, stream) : dx_mx(prm, stream);
   }
   if (big_tiles(call) >= kCUs) return launch_cfg<Big>(call, prm, stream);
   // Fewer than one full wave of 256 x 256 tiles across the CUs: split the

@@ -609,9 +609,10 @@ __device__ __forceinline__ Tile select_tile(const Params& p, int32_t* s_ends) {
 // 8-byte slot s of row r is staged at s ^ (r & 15), which keeps both the
 // staging writes (rows 0..15 of one column) and the row-wise reads free of
 // bank conflicts.
-template <class C, bool kDW>
+// alpha multiplies every result before rounding when kAlpha is set.
+template <class C, bool kDW, bool kAlpha = false>
 __device__ __forceinline__ void store_acc(const Params& p, const Tile& t, f32x16 (&acc)[C::FP][C::FQ], int wp,
-                                          int wq, int lane, uint8_t* stage) {
+                                          int wq, int lane, uint8_t* stage, float alpha = 1.0f) {
   constexpr int ROWB = C::WQ * 2;                                  // staged row bytes
   constexpr int SLOTS = ROWB / 8;                                  // 8-byte slots per row
   static_assert(SLOTS >= 16, "swizzle needs 16 slots per row");
@@ -623,8 +624,10 @@ __device__ __forceinline__ void store_acc(const Params& p, const Tile& t, f32x16
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int slot = (j * 32 + 8 * r4 + 4 * (lane >> 5)) / 4;
-        const u32x2 v = {pack_bf16x2(acc[i][j][4 * r4], acc[i][j][4 * r4 + 1]),
-                         pack_bf16x2(acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3])};
+        float e[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) e[d] = kAlpha ? acc[i][j][4 * r4 + d] * alpha : acc[i][j][4 * r4 + d];
+        const u32x2 v = {pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3])};
         *reinterpret_cast<u32x2*>(stage + r * ROWB + 8 * (slot ^ (r & 15))) = v;
       }
     }
@@ -955,6 +958,11 @@ hipError_t dx_mx(const Params& prm, hipStream_t s);
 // Dense grad_W of an MXFP8 gradient and an MXFP8 input, both scaled along
 // their rows (the contraction), on the block-scaled MFMA.
 hipError_t dw_mx(const Params& prm, hipStream_t s);
+// grad_X / grad_W of a per-tensor scaled FP8 gradient and a per-tensor
+// scaled FP8 operand (formats LP_FP8T_*), on the same MFMA with unit block
+// scales; grouped calls included.
+hipError_t dx_pt(const Params& prm, int fmt_p, int fmt_q, hipStream_t s);
+hipError_t dw_pt(const Params& prm, int fmt_p, int fmt_q, hipStream_t s);
 
 }  // namespace gk
 }  // namespace lp

@@ -38,6 +38,14 @@ hipError_t launch_mx_quant(const void* src, int64_t batch, int64_t rows, int64_t
                            int dst_fmt, void* codes, void* scales, hipStream_t stream);
 hipError_t launch_mx_quant_dual(const void* src, int64_t batch, int64_t rows, int64_t cols, int dst_fmt,
                                 void* codes_c, void* scales_c, void* codes_r, void* scales_r, hipStream_t stream);
+// Per-tensor scaled FP8 (lp_tensor.hip).  n is a multiple of 8; amax may be
+// null in launch_tensor_quant.
+hipError_t launch_tensor_amax(const void* src, int64_t n, float* amax, hipStream_t stream);
+hipError_t launch_tensor_quant(const void* src, int64_t n, int fmt, const float* scale, void* codes, float* amax,
+                               hipStream_t stream);
+hipError_t launch_scale_from_history(const float* hist, int32_t len, int fmt, int32_t margin, float* scale,
+                                     hipStream_t stream);
+hipError_t launch_tensor_dequant(const lp_qtensor& t, void* dst, hipStream_t stream);
 
 // One backward contraction (grad_X or grad_W) over `groups` groups.
 //   dx: C[m][k] = sum_n grad[m][n] * W[g][n][k]  (groups partition the rows m)

@@ -1,0 +1,238 @@
+// Per-tensor scaled FP8: quantization with amax recording, amax, scale from
+// an amax history, and decoding (HBM-bound; quantization and decoding are
+// bit-exact).
+//
+// "AstrAI fp8.py": every operand's scale is a quantization step
+// scale = (amax / FP8_MAX) / 2^margin (at least 1e-12), FP8_MAX = 448 (E4M3)
+// or 57344 (E5M2), taken over an amax history ring (delayed scaling) or the
+// current amax (dynamic scaling); the backward quantizes its operands with
+// those scales and records the gradient's amax for the ring.
+//
+// Quantization: t = x / scale (IEEE fp32 division), saturated to
+// +-FP8_MAX (infinities included), then rounded to nearest even by the
+// hardware conversion; NaN becomes 0x7F with the element's sign.  amax is
+// max |x| as the fp32 bit pattern of the largest bf16 magnitude: the bit
+// patterns of non-negative floats order like the floats, NaN patterns above
+// infinity, so an integer atomic max over them is max |x| with NaN winning.
+#include "lp_device.hpp"
+#include "lp_internal.hpp"
+
+namespace lp {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnits = 4;                       // 8-element units per thread
+constexpr int kSpan = kThreads * kUnits;
+
+__device__ __forceinline__ float fp8_max(bool e5m2) { return e5m2 ? 57344.0f : 448.0f; }
+
+// Largest bf16 magnitude (as fp32 bits) of a unit's eight elements.
+__device__ __forceinline__ uint32_t unit_amax_bits(const u32x4& v) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t w = v[k] & 0x7FFF7FFFu;
+    const uint32_t a = w & 0xFFFFu, b = w >> 16;
+    m = m > a ? m : a;
+    m = m > b ? m : b;
+  }
+  return m << 16;
+}
+
+// Wave maximum, then one atomic per wave.
+__device__ __forceinline__ void record_amax(uint32_t m, uint32_t* out) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint32_t o = (uint32_t)__shfl_xor((int)m, off);
+    m = m > o ? m : o;
+  }
+  if ((threadIdx.x & 63) == 0 && m != 0) __hip_atomic_fetch_max(out, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__global__ void zero_u32(uint32_t* p) { *p = 0u; }
+
+__global__ __launch_bounds__(kThreads) void tensor_amax(const u32x4* __restrict__ src, uint32_t nunits,
+                                                        uint32_t* __restrict__ amax) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int j = 0; j < kUnits; ++j) {
+    const uint32_t u = blockIdx.x * kSpan + j * kThreads + threadIdx.x;
+    if (u < nunits) {
+      const uint32_t a = unit_amax_bits(__builtin_nontemporal_load(src + u));
+      m = m > a ? m : a;
+    }
+  }
+  record_amax(m, amax);
+}
+
+// Two elements -> two FP8 codes (low byte first).
+template <bool kE5M2>
+__device__ __forceinline__ uint32_t quant_pair(float a, float b, float s) {
+  const float mx = fp8_max(kE5M2);
+  const float ta = a / s, tb = b / s;
+  const float ca = __builtin_amdgcn_fmed3f(ta, -mx, mx), cb = __builtin_amdgcn_fmed3f(tb, -mx, mx);
+  i16x2 old = {0, 0};
+  uint32_t r;
+  if constexpr (kE5M2)
+    r = (uint32_t)(uint16_t)__builtin_amdgcn_cvt_scalef32_pk_bf8_f32(old, ca, cb, 1.0f, false)[0];
+  else
+    r = (uint32_t)(uint16_t)__builtin_amdgcn_cvt_scalef32_pk_fp8_f32(old, ca, cb, 1.0f, false)[0];
+  // NaN in, NaN code out (0x7F with the sign); the clamp does not keep NaN.
+  const uint32_t na = __builtin_isnan(ta) ? (0x7Fu | (__builtin_bit_cast(uint32_t, a) >> 24 & 0x80u)) : (r & 0xFFu);
+  const uint32_t nb = __builtin_isnan(tb) ? (0x7Fu | (__builtin_bit_cast(uint32_t, b) >> 24 & 0x80u)) : (r >> 8);
+  return na | (nb << 8);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
+
+// Unit u: 8 bf16 in (16 bytes), 8 codes out (8 bytes); the amax of the
+// input goes to `amax` when it is not null.
+template <bool kE5M2>
+__global__ __launch_bounds__(kThreads) void tensor_quant(const u32x4* __restrict__ src, uint32_t nunits,
+                                                         const float* __restrict__ scale, u32x2* __restrict__ codes,
+                                                         uint32_t* __restrict__ amax) {
+  u32x4 v[kUnits];
+#pragma unroll
+  for (int j = 0; j < kUnits; ++j) {
+    const uint32_t u = blockIdx.x * kSpan + j * kThreads + threadIdx.x;
+    v[j] = u < nunits ? __builtin_nontemporal_load(src + u) : u32x4{0u, 0u, 0u, 0u};
+  }
+  const float s = *scale;
+  uint32_t m = 0;
+#pragma unroll
+  for (int j = 0; j < kUnits; ++j) {
+    const uint32_t u = blockIdx.x * kSpan + j * kThreads + threadIdx.x;
+    if (u >= nunits) continue;
+    const uint32_t a = unit_amax_bits(v[j]);
+    m = m > a ? m : a;
+    uint32_t o[2];
+#pragma unroll
+    for (int k = 0; k < 4; k += 2) {
+      const uint32_t lo = quant_pair<kE5M2>(bf16_lo(v[j][k]), bf16_hi(v[j][k]), s);
+      const uint32_t hi = quant_pair<kE5M2>(bf16_lo(v[j][k + 1]), bf16_hi(v[j][k + 1]), s);
+      o[k / 2] = lo | (hi << 16);
+    }
+    __builtin_nontemporal_store(u32x2{o[0], o[1]}, codes + u);
+  }
+  if (amax != nullptr) record_amax(m, amax);
+}
+
+// scale = (max(history) / FP8_MAX) / 2^margin, at least 1e-12, NaN kept.
+// One workgroup: a strided maximum per lane, then across the workgroup.  The
+// running maximum starts at 0: a history whose maximum is at most 0 gives
+// the floor either way.
+__global__ __launch_bounds__(kThreads) void scale_from_history(const float* __restrict__ hist, int32_t len, bool e5m2,
+                                                               int32_t margin, float* __restrict__ scale) {
+  __shared__ float s_peak[kThreads / 64];
+  __shared__ int s_nan[kThreads / 64];
+  float peak = 0.0f;
+  int nan = 0;
+  for (int i = threadIdx.x; i < len; i += kThreads) {
+    const float h = hist[i];
+    nan |= __builtin_isnan(h) ? 1 : 0;
+    peak = h > peak ? h : peak;                                  // false for NaN
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const float o = __shfl_xor(peak, off);
+    peak = o > peak ? o : peak;
+    nan |= __shfl_xor(nan, off);
+  }
+  if (threadIdx.x % 64 == 0) {
+    s_peak[threadIdx.x / 64] = peak;
+    s_nan[threadIdx.x / 64] = nan;
+  }
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  for (int w = 1; w < kThreads / 64; ++w) {
+    peak = s_peak[w] > peak ? s_peak[w] : peak;
+    nan |= s_nan[w];
+  }
+  float s = peak / fp8_max(e5m2);
+  s = s / __builtin_ldexpf(1.0f, margin);
+  *scale = nan ? __builtin_nanf("") : (s < 1e-12f ? 1e-12f : s);
+}
+
+// Decode: unit u = 8 codes -> 8 bf16, bf16_rne(fp32_rne(code * scale)), a
+// NaN result 0x7FC0 with the code's sign.
+template <bool kE5M2>
+__global__ __launch_bounds__(kThreads) void tensor_dequant(const u32x2* __restrict__ codes, uint32_t nunits,
+                                                           const float* __restrict__ scale, u32x4* __restrict__ out) {
+  u32x2 c[kUnits];
+#pragma unroll
+  for (int j = 0; j < kUnits; ++j) {
+    const uint32_t u = blockIdx.x * kSpan + j * kThreads + threadIdx.x;
+    c[j] = u < nunits ? __builtin_nontemporal_load(codes + u) : u32x2{0u, 0u};
+  }
+  const float S = *scale;
+#pragma unroll
+  for (int j = 0; j < kUnits; ++j) {
+    const uint32_t u = blockIdx.x * kSpan + j * kThreads + threadIdx.x;
+    if (u >= nunits) break;
+    uint32_t o[4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t w = c[j][h];
+      f32x2 lo, hi;
+      if constexpr (kE5M2) {
+        lo = __builtin_amdgcn_cvt_scalef32_pk_f32_bf8(w, 1.0f, false);
+        hi = __builtin_amdgcn_cvt_scalef32_pk_f32_bf8(w, 1.0f, true);
+      } else {
+        lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, false);
+        hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, true);
+      }
+      o[2 * h] = fix_nan_pair(pack_bf16x2(lo[0] * S, lo[1] * S), (w >> 7) & 1u, (w >> 15) & 1u);
+      o[2 * h + 1] = fix_nan_pair(pack_bf16x2(hi[0] * S, hi[1] * S), (w >> 23) & 1u, w >> 31);
+    }
+    __builtin_nontemporal_store(u32x4{o[0], o[1], o[2], o[3]}, out + u);
+  }
+}
+
+dim3 grid_of(uint32_t nunits) { return dim3((nunits + kSpan - 1) / kSpan); }
+
+}  // namespace
+
+hipError_t launch_tensor_amax(const void* src, int64_t n, float* amax, hipStream_t stream) {
+  uint32_t* a = reinterpret_cast<uint32_t*>(amax);
+  zero_u32<<<1, 1, 0, stream>>>(a);
+  const uint32_t nunits = (uint32_t)(n / 8);
+  if (nunits > 0) tensor_amax<<<grid_of(nunits), kThreads, 0, stream>>>(static_cast<const u32x4*>(src), nunits, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_tensor_quant(const void* src, int64_t n, int fmt, const float* scale, void* codes, float* amax,
+                               hipStream_t stream) {
+  uint32_t* a = reinterpret_cast<uint32_t*>(amax);
+  if (a != nullptr) zero_u32<<<1, 1, 0, stream>>>(a);
+  const uint32_t nunits = (uint32_t)(n / 8);
+  if (nunits == 0) return hipGetLastError();
+  auto s = static_cast<const u32x4*>(src);
+  auto c = static_cast<u32x2*>(codes);
+  if (fmt == LP_FP8T_E5M2)
+    tensor_quant<true><<<grid_of(nunits), kThreads, 0, stream>>>(s, nunits, scale, c, a);
+  else
+    tensor_quant<false><<<grid_of(nunits), kThreads, 0, stream>>>(s, nunits, scale, c, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_scale_from_history(const float* hist, int32_t len, int fmt, int32_t margin, float* scale,
+                                     hipStream_t stream) {
+  scale_from_history<<<1, kThreads, 0, stream>>>(hist, len, fmt == LP_FP8T_E5M2, margin, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_tensor_dequant(const lp_qtensor& t, void* dst, hipStream_t stream) {
+  const uint32_t nunits = (uint32_t)(t.batch * t.rows * t.cols / 8);
+  if (nunits == 0) return hipSuccess;
+  auto c = static_cast<const u32x2*>(t.codes);
+  auto o = static_cast<u32x4*>(dst);
+  if (t.fmt == LP_FP8T_E5M2)
+    tensor_dequant<true><<<grid_of(nunits), kThreads, 0, stream>>>(c, nunits, t.tensor_scale, o);
+  else
+    tensor_dequant<false><<<grid_of(nunits), kThreads, 0, stream>>>(c, nunits, t.tensor_scale, o);
+  return hipGetLastError();
+}
+
+}  // namespace lp

@@ -26,7 +26,7 @@
  *   is written.
  * - Tensors are dense and row-major.  Element (b, r, c) of a [batch][rows][cols]
  *   tensor is at offset (b*rows + r)*cols + c, in units of elements.
- * - Codes, scales and outputs must be 16-byte aligned; an NVFP4 tensor scale
+ * - Codes, scales and outputs must be 16-byte aligned; a tensor scale
  *   4-byte aligned.  A pointer may be NULL only when its tensor is empty.
  * - A tensor holds fewer than 2^34 elements and each of batch, rows, cols is
  *   below 2^31 (LP_ERR_SHAPE otherwise).
@@ -51,12 +51,22 @@
  *                backward quantization", npu_dynamic_mx_quant axis argument
  *                and group_sizes [1, 1, 32]).
  *
+ * *   LP_FP8T_E4M3 E4M3 codes, one byte each, with ONE fp32 scale for the
+ *                whole tensor (tensor_scale: the decode multiplier, which is
+ *                the quantization step); no block scales (`scales` and
+ *                `scale_axis` are ignored).
+ *   LP_FP8T_E5M2 E5M2 codes, one byte each, one fp32 tensor scale likewise.
+ *                ("AstrAI fp8.py": per-tensor scaled FP8, E4M3 for the
+ *                forward operands and E5M2 for gradients.)
+ *
  * Element values: E2M1 (1 sign, 2 exponent bits with bias 1, 1 mantissa bit:
  * 0, 0.5, 1, 1.5, 2, 3, 4, 6), E4M3 (bias 7, max 448, no infinities,
- * S.1111.111 = NaN), E8M0 (2^(byte-127), 0xFF = NaN).
+ * S.1111.111 = NaN), E5M2 (bias 15, max 57344, S.11111.00 = infinity,
+ * S.11111.01..11 = NaN), E8M0 (2^(byte-127), 0xFF = NaN).
  *
  * Decoded value: bf16_rne(fp32_rne(code_value * S)) where S is the fp32
- * block multiplier (NVFP4: S = fp32_rne(E4M3(block byte) * tensor_scale)).
+ * block multiplier (NVFP4: S = fp32_rne(E4M3(block byte) * tensor_scale);
+ * LP_FP8T_*: S = tensor_scale).
  * A NaN result is 0x7FC0 carrying the code's sign bit.
  */
 #ifndef LP_H
@@ -85,7 +95,9 @@ typedef enum {
   LP_MXFP4 = 1,
   LP_NVFP4 = 2,
   LP_FP8_B128 = 3,
-  LP_MXFP8 = 4
+  LP_MXFP8 = 4,
+  LP_FP8T_E4M3 = 5,
+  LP_FP8T_E5M2 = 6
 } lp_fmt;
 
 /* A (possibly block-scaled) tensor of logical shape [batch][rows][cols]. */
@@ -98,7 +110,8 @@ typedef struct {
   int64_t cols;              /* logical elements (not packed bytes)             */
   const void* codes;         /* device pointer, layout per format above          */
   const void* scales;        /* device pointer, NULL for LP_BF16                 */
-  const float* tensor_scale; /* device pointer to one fp32, LP_NVFP4 only       */
+  const float* tensor_scale; /* device pointer to one fp32, LP_NVFP4 and
+                                LP_FP8T_* only                                  */
 } lp_qtensor;
 
 /*
@@ -112,8 +125,8 @@ typedef struct {
  * src       any format except LP_BF16.  Divisibility: cols % 32 == 0 for
  *           LP_MXFP4 and for LP_MXFP8 with scale_axis -1; rows % 32 == 0 and
  *           cols % 16 == 0 for LP_MXFP8 with scale_axis -2; cols % 16 == 0 for
- *           LP_NVFP4 and LP_FP8_B128 (rows arbitrary; partial 128-blocks are
- *           cut at the edge).
+ *           LP_NVFP4, LP_FP8_B128 and LP_FP8T_* (rows arbitrary; partial
+ *           128-blocks are cut at the edge).
  * dst_bf16  device bf16 output [batch][rows][cols].
  * Result is bit-exact: the rule in the header comment above.
  */
@@ -165,6 +178,60 @@ lp_status lp_mx_quant_dual(const void* src_bf16, int64_t batch, int64_t rows, in
                            void* stream);
 
 /*
+ * lp_tensor_amax - amax of a bf16 tensor.
+ *
+ * Cites: "AstrAI fp8.py" (each quantization records the amax of its tensor,
+ * max |x| over every element, into an amax history).
+ *
+ * src_bf16  device bf16, n elements; n % 8 == 0 and n < 2^34.
+ * amax      device fp32: max |x| (exact), 0 when n == 0, NaN when any
+ *           element is NaN.  It may point into an amax history ring.
+ */
+lp_status lp_tensor_amax(const void* src_bf16, int64_t n, float* amax, void* stream);
+
+/*
+ * lp_tensor_quant - per-tensor FP8 quantization of a bf16 tensor, recording
+ * its amax in the same pass.
+ *
+ * Cites: "AstrAI fp8.py" (codes are the FP8 cast of x / scale with one scale
+ * per tensor; FP8_MAX is 448 for E4M3 and 57344 for E5M2; the backward
+ * quantizes the gradient once and returns its amax for the history).
+ *
+ * src_bf16   device bf16, n elements; n % 8 == 0 and n < 2^34.
+ * dst_fmt    LP_FP8T_E4M3 or LP_FP8T_E5M2.
+ * scale      device fp32: the quantization step (the decode multiplier of
+ *            the result), e.g. written by lp_scale_from_history.
+ * dst_codes  device bytes [n], 16-byte aligned.
+ * amax       device fp32, or NULL: receives the input's amax as
+ *            lp_tensor_amax computes it.  Must not be `scale`
+ *            (LP_ERR_SHAPE).
+ * Each code: t = x / scale in fp32 (IEEE division, nearest even); |t| above
+ * FP8_MAX, infinity included, saturates to FP8_MAX with t's sign; otherwise
+ * the nearest FP8 value, ties to the even code; NaN becomes 0x7F with x's
+ * sign bit.  Bit-exact.
+ */
+lp_status lp_tensor_quant(const void* src_bf16, int64_t n, int32_t dst_fmt, const float* scale,
+                          void* dst_codes, float* amax, void* stream);
+
+/*
+ * lp_scale_from_history - per-tensor scale from an amax history.
+ *
+ * Cites: "AstrAI fp8.py" (scale = (amax / FP8_MAX) / 2^margin, at least
+ * 1e-12; delayed scaling takes the largest amax of the history ring,
+ * dynamic scaling the current amax).
+ *
+ * history  device fp32 [len], 1 <= len <= 65536.  A history of one entry,
+ *          the current amax, is dynamic scaling.
+ * fmt      LP_FP8T_E4M3 (FP8_MAX 448) or LP_FP8T_E5M2 (FP8_MAX 57344).
+ * margin   -64 <= margin <= 64.
+ * scale    device fp32: s = fp32(max(history) / FP8_MAX), then
+ *          fp32(s / 2^margin), raised to fp32(1e-12) when below it; NaN when
+ *          any entry is NaN.
+ */
+lp_status lp_scale_from_history(const float* history, int32_t len, int32_t fmt, int32_t margin, float* scale,
+                                void* stream);
+
+/*
  * lp_linear_bwd - backward of a linear layer y = x @ W^T with saved
  * block-scaled operands.
  *
@@ -180,10 +247,14 @@ lp_status lp_mx_quant_dual(const void* src_bf16, int64_t batch, int64_t rows, in
  *           LP_MXFP8 with scale_axis -2), as produced by lp_mx_quant_dual.
  *           ("perf: defer mxfp8 backward quantization", MXFP8MatMul.backward:
  *           the gradient is quantized along both axes, one copy per product.)
+ *           Or LP_FP8T_E4M3 / LP_FP8T_E5M2, one copy for both products, with
+ *           x and w LP_FP8T_* too ("AstrAI fp8.py", _LinearFp8.backward):
+ *           per-tensor scaled operands pair only with each other.
  * x         [M][K] saved input, or NULL when grad_w == NULL.
  * w         [N][K] saved weight, or NULL when grad_x == NULL.
  *           x and w: LP_BF16, LP_MXFP4, LP_NVFP4 (scale_axis -1), LP_FP8_B128,
- *           or LP_MXFP8 (scale_axis -1 or -2).
+ *           or LP_MXFP8 (scale_axis -1 or -2) with a bf16 or MXFP8 grad_out;
+ *           LP_FP8T_* with an LP_FP8T_* grad_out.
  * grad_x    device bf16 [M][K], or NULL to skip grad_X.
  * grad_w    device bf16 [N][K], or NULL to skip grad_W.
  * Sizes: M >= 0 arbitrary; N % 16 == 0, K % 16 == 0, plus each operand's
@@ -194,7 +265,9 @@ lp_status lp_mx_quant_dual(const void* src_bf16, int64_t batch, int64_t rows, in
  * contraction (dX: grad_out -1, w -2; dW: grad_out -2, x -2), the product
  * runs on the block-scaled FP8 MFMA: each code product times its two E8M0
  * scales is exact, so the result equals the decode-then-bf16 route up to
- * fp32 summation order.
+ * fp32 summation order.  Per-tensor scaled operands run on the same MFMA
+ * with unit block scales: the fp32 sum of exact code products is multiplied
+ * by fp32(scale_grad * scale_other), then rounded to bf16.
  */
 lp_status lp_linear_bwd(const lp_qtensor* grad_out, const lp_qtensor* x, const lp_qtensor* w,
                         void* grad_x, void* grad_w, void* stream);

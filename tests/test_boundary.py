@@ -15,7 +15,8 @@ FAKE = 0x10000          # 16-byte aligned stand-in pointer; never dereferenced h
 def test_library_exports_every_header_function():
     names = lp.header_functions()
     assert set(names) == {"lp_dequant", "lp_mx_quant", "lp_linear_bwd", "lp_grouped_bwd", "lp_status_string",
-                          "lp_linear_bwd_workspace", "lp_linear_bwd_ws", "lp_mx_quant_dual"}
+                          "lp_linear_bwd_workspace", "lp_linear_bwd_ws", "lp_mx_quant_dual", "lp_tensor_amax",
+                          "lp_tensor_quant", "lp_scale_from_history"}
     for n in names:
         assert hasattr(lp.lib, n), n
 
@@ -52,6 +53,10 @@ def dq(t, dst=FAKE):
     (q("mxfp4", 4, 64, scales=FAKE + 4), FAKE, ALIGN),
     (q("mxfp4", 4, 64), FAKE + 2, ALIGN),
     (q("mxfp4", 0, 64, codes=None, scales=None), None, OK),   # empty: nothing to do
+    (q("fp8t_e5m2", 4, 64, ts=None), FAKE, NULL),          # per-tensor: the tensor scale is required
+    (q("fp8t_e4m3", 4, 40), FAKE, SHAPE),
+    (q("fp8t_e4m3", 4, 64, ts=FAKE + 2), FAKE, ALIGN),
+    (_QTensorC(7, -1, 1, 4, 64, FAKE, FAKE, FAKE), FAKE, FORMAT),
 ])
 def test_dequant_rejects(t, dst, expect):
     assert dq(t, dst) == expect
@@ -84,6 +89,39 @@ def test_mx_quant_dual_rejects(args, expect):
     assert lp.lib.lp_mx_quant_dual(*args, None) == expect
 
 
+E4M3T, E5M2T = lp.FMT["fp8t_e4m3"], lp.FMT["fp8t_e5m2"]
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((FAKE, 64, lp.FMT["mxfp8"], FAKE, FAKE, FAKE), FORMAT),
+    ((FAKE, 12, E4M3T, FAKE, FAKE, FAKE), SHAPE),          # n % 8
+    ((FAKE, -8, E4M3T, FAKE, FAKE, FAKE), SHAPE),
+    ((None, 64, E5M2T, FAKE, FAKE, FAKE), NULL),
+    ((FAKE, 64, E5M2T, None, FAKE, None), NULL),           # the scale is required
+    ((FAKE, 64, E5M2T, FAKE, FAKE, FAKE), SHAPE),          # amax would overwrite the scale
+    ((FAKE, 64, E5M2T, FAKE, FAKE + 8, FAKE + 4), ALIGN),
+    ((FAKE, 64, E5M2T, FAKE + 2, FAKE, FAKE + 4), ALIGN),
+    ((FAKE + 8, 64, E4M3T, FAKE, FAKE, None), ALIGN),
+])
+def test_tensor_quant_rejects(args, expect):
+    assert lp.lib.lp_tensor_quant(*args, None) == expect
+
+
+def test_tensor_amax_and_scale_reject():
+    assert lp.lib.lp_tensor_amax(FAKE, 20, FAKE, None) == SHAPE
+    assert lp.lib.lp_tensor_amax(FAKE, 64, None, None) == NULL
+    assert lp.lib.lp_tensor_amax(None, 64, FAKE, None) == NULL
+    assert lp.lib.lp_tensor_amax(FAKE + 8, 64, FAKE, None) == ALIGN
+    sfh = lp.lib.lp_scale_from_history
+    assert sfh(FAKE, 16, lp.FMT["mxfp8"], 0, FAKE, None) == FORMAT
+    assert sfh(FAKE, 0, E4M3T, 0, FAKE, None) == SHAPE
+    assert sfh(FAKE, 65537, E4M3T, 0, FAKE, None) == SHAPE
+    assert sfh(FAKE, 16, E4M3T, 65, FAKE, None) == SHAPE
+    assert sfh(FAKE, 16, E5M2T, -65, FAKE, None) == SHAPE
+    assert sfh(None, 16, E5M2T, 0, FAKE, None) == NULL
+    assert sfh(FAKE, 16, E5M2T, 0, FAKE + 1, None) == ALIGN
+
+
 def test_grouped_rejects_row_scaled_grad():
     g, x = q("mxfp8", 64, 128, axis=-2), q("mxfp8", 64, 128, axis=-2)
     assert lp.lib.lp_grouped_bwd(ctypes.byref(g), ctypes.byref(x), None, FAKE, 2, None, FAKE, None) == FORMAT
@@ -111,6 +149,14 @@ def lin(g, x, w, dx=FAKE, dw=FAKE):
     (q("bf16", 64, 128), q("mxfp4", 64, 128), q("nvfp4", 128, 48), FAKE, None, SHAPE),   # FP4 K % 32
     (q("bf16", 64, 128), q("mxfp4", 64, 128), q("mxfp4", 128, 128, batch=2), FAKE, None, SHAPE),
     (q("bf16", 64, 128), q("mxfp4", 64, 128), q("mxfp4", 128, 128), FAKE + 8, None, ALIGN),
+    # per-tensor FP8 operands pair only with each other
+    (q("fp8t_e5m2", 64, 128), None, q("bf16", 128, 128), FAKE, None, FORMAT),
+    (q("bf16", 64, 128), None, q("fp8t_e4m3", 128, 128), FAKE, None, FORMAT),
+    (q("fp8t_e5m2", 64, 128), q("mxfp8", 64, 128, axis=-2), None, None, FAKE, FORMAT),
+    (q("mxfp8", 64, 128, axis=-2), q("fp8t_e4m3", 64, 128), None, None, FAKE, FORMAT),
+    (q("fp8t_e5m2", 64, 128), None, q("fp8t_e4m3", 128, 128, ts=None), FAKE, None, NULL),
+    (q("fp8t_e5m2", 64, 128, ts=FAKE + 1), None, q("fp8t_e4m3", 128, 128), FAKE, None, ALIGN),
+    (q("fp8t_e5m2", 64, 120), None, q("fp8t_e4m3", 120, 128), FAKE, None, SHAPE),
 ])
 def test_linear_bwd_rejects(g, x, w, dx, dw, expect):
     assert lin(g, x, w, dx, dw) == expect
@@ -153,6 +199,9 @@ def test_workspace_size_rules():
     # dW over a long token axis: 1 x 2 tiles, 4096 / 64 = 64 slabs -> 4 splits of 16 slabs
     st, n = ws_bytes(q("bf16", 4096, 256), q("bf16", 4096, 512), None, dx=False)
     assert st == OK and n == 256 + 2 * 4 * 256 * 256 * 4
+    # per-tensor FP8 products never split
+    st, n = ws_bytes(q("fp8t_e5m2", 300, 4096), None, q("fp8t_e4m3", 4096, 544), dw=False)
+    assert st == OK and n == 0
     # argument errors as for lp_linear_bwd
     st, n = ws_bytes(q("bf16", 64, 128), q("mxfp4", 63, 128), None, dx=False)
     assert st == SHAPE and n == 0

@@ -37,7 +37,7 @@ import numpy as np
 
 # Tensor ids for the per-tensor random streams.
 _STREAM = {"x": 0, "w": 1, "grad": 2, "route": 3, "x_outlier": 4, "w_outlier": 5,
-           "perm": 6}
+           "perm": 6, "grad_outlier": 7}
 
 
 @dataclasses.dataclass(frozen=True)
