@@ -9,6 +9,8 @@ synthetic input already resident in HBM:
   mxfp4_grouped   lp_grouped_bwd: dX and dW over 8 experts, MXFP4 X and W
   mxfp8_deferred  lp_mx_quant(grad, -1) + lp_mx_quant(W, -2) + lp_grouped_bwd dX
   mxfp8_dense     lp_mx_quant_dual(grad) + lp_mx_quant(W, -2) + lp_mx_quant(X, -2) + lp_linear_bwd dX, dW
+  fp8_hybrid      lp_scale_from_history(grad ring) + lp_tensor_quant(grad -> E5M2, amax into the ring)
+                  + lp_linear_bwd dX, dW against E4M3 X and W (per-tensor scales)
   mxfp4_tiny      lp_linear_bwd: dX and dW, 64 x 128 x 128
 Input sets are rotated through about 1 GB so that the 256 MiB Infinity Cache
 cannot serve a repeated step.  Prints one JSON line (rank 0).
@@ -211,6 +213,48 @@ def build(lp, name: str):
             ts.append(ev.stop(stream))
             return ts
         standalone = []
+    elif name == "fp8_hybrid":
+        # Saved forward operands: E4M3 codes with their dynamic scales (set-up).
+        # Per step: the gradient's delayed scale from its amax ring, E5M2
+        # quantization recording the gradient's amax into the ring's next slot,
+        # then dX and dW.
+        per_set = M * N * 3 + (M * K + N * K) * 3
+        nsets = max(1, min(16, math.ceil(ROTATE_BYTES / per_set)))
+        for i in range(nsets):
+            g = W.torch_normal_bf16((M, N), 1.0, 7800 + i, "cuda")
+            saved = []
+            for shape, sigma, seed in (((M, K), w.x_sigma, 7900 + i), ((N, K), w.w_sigma, 8000 + i)):
+                t = W.torch_normal_bf16(shape, sigma, seed, "cuda")
+                sc = lp.lp_scale_from_history(lp.lp_tensor_amax(t), "fp8t_e4m3")
+                saved.append(lp.lp_tensor_quant(t, "fp8t_e4m3", sc))
+            ring = torch.empty(W.AMAX_RING, dtype=torch.float32, device="cuda")
+            ring.copy_(lp.lp_tensor_amax(g).expand(W.AMAX_RING))    # a first use fills the ring
+            gq = lp.QTensor("fp8t_e5m2", torch.empty((1, M, N), dtype=torch.uint8, device="cuda"), None,
+                            torch.empty(1, dtype=torch.float32, device="cuda"), shape=(1, M, N))
+            dx = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+            dw = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
+            sets.append((g, ring, gq, saved[0], saved[1], dx, dw))
+        phases.append(Phase("scale_from_history grad", "scale_from_history"))
+        phases.append(Phase("tensor_quant grad E5M2", "tensor_quant", nbytes=M * N * 3))
+        # dX and dW of the one E5M2 gradient in one call: one launch of both
+        phases.append(Phase("linear_bwd dX+dW", "pt_pair_kernel", flops=4.0 * M * N * K, peak=PEAK_FP8_TFLOPS))
+
+        def step(i, stream):
+            g, ring, gq, xq, wq, dx, dw = sets[i % len(sets)]
+            slot = (i // len(sets)) % W.AMAX_RING
+            ts = []
+            ev = _events(stream)
+            lp.lp_scale_from_history(ring, "fp8t_e5m2", scale=gq.tensor_scale, stream=stream)
+            ts.append(ev.stop(stream))
+            ev = _events(stream)
+            lp.lp_tensor_quant(g, "fp8t_e5m2", gq.tensor_scale, amax=ring[slot:slot + 1], codes=gq.codes,
+                               stream=stream)
+            ts.append(ev.stop(stream))
+            ev = _events(stream)
+            lp.lp_linear_bwd(gq, xq, wq, grad_x=dx, grad_w=dw, stream=stream)
+            ts.append(ev.stop(stream))
+            return ts
+        standalone = []
     else:
         raise SystemExit(f"unknown workload {name}")
     return w, phases, step, standalone
@@ -287,7 +331,34 @@ def cpu_baseline(name: str, budget_s: float = 12.0):
         cores = os.cpu_count()
     w = W.WORKLOADS[name]
     M, N, K = w.M, w.N, w.K
-    if name == "mxfp8_dense":
+    if name == "fp8_hybrid":
+        # a slab of token rows: the gradient's amax and E5M2 quantization, the
+        # saved operands' E4M3 quantization, and the fp64 dX / dW over the slab;
+        # extrapolated to all rows (W's quantization counted once).
+        from oracle import pertensor as PT
+        rows = 256
+        gb = W.bf16_bits(W.normal_f32(w.number, "grad", (rows, N), 1.0))
+        xb = W.bf16_bits(W.normal_f32(w.number, "x", (rows, K), w.x_sigma))
+        wb = W.bf16_bits(W.normal_f32(w.number, "w", (N, K), w.w_sigma))
+        t0 = time.perf_counter()
+        ws_ = PT.scale_from_history([PT.amax(wb)], "e4m3")
+        wc = PT.quantize(wb, "e4m3", ws_)
+        t_w = time.perf_counter() - t0
+        t1 = time.perf_counter()
+        hist = np.full(W.AMAX_RING, PT.amax(gb), np.float32)
+        gs = PT.scale_from_history(hist, "e5m2")
+        gc = PT.quantize(gb, "e5m2", gs)
+        PT.record(hist, 0, PT.amax(gb))
+        xs = PT.scale_from_history([PT.amax(xb)], "e4m3")
+        xc = PT.quantize(xb, "e4m3", xs)
+        PT.linear_dx(gc, "e5m2", gs, wc, "e4m3", ws_)
+        PT.linear_dw(gc, "e5m2", gs, xc, "e4m3", xs)
+        t_rows = time.perf_counter() - t1
+        total = t_w + t_rows * (M / rows)
+        flops = 4.0 * M * N * K
+        sample = (f"W quantized once; {rows} token rows: gradient amax, E5M2 quantization, X quantization, fp64 "
+                  f"dX and dW over the rows; extrapolated to {M} rows")
+    elif name == "mxfp8_dense":
         # a slab of token rows: quantize grad both ways and X, W along -2,
         # decode, contract dX and dW over the slab; extrapolate to all rows.
         rows = 256
@@ -428,7 +499,7 @@ def main():
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "vs_baseline": None, "dtype": "fp8" if w.fmt in ("mxfp8", "fp8t") else "bf16", "data": "synthetic",
         "config": {"workload": w.name, "format": w.fmt, "M": w.M, "N": w.N, "K": w.K, "groups": w.groups,
                    "grad_x": w.need_dx, "grad_w": w.need_dw, "global_batch": w.M, "parallelism": "none (1 GPU)"},
         "roofline": roof, "phases": phase_rec, "standalone_hbm": hbm,

@@ -162,6 +162,12 @@ static lp_status run_bwd(const lp_qtensor* grad, const lp_qtensor* x, const lp_q
   const int64_t M = grad->rows, N = grad->cols;
   const int64_t K = grad_x ? w->cols : x->cols;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const int32_t G = (int32_t)(groups ? groups : 1);
+  if (grad_x != nullptr && M * K > 0 && grad_w != nullptr && N * K > 0 && ws == nullptr) {
+    lp::GemmCall cx{false, grad, w, offsets, G, M, N, K, grad_x, nullptr, 0};
+    lp::GemmCall cw{true, grad, x, offsets, G, M, N, K, grad_w, nullptr, 0};
+    return lp::launch_gemm_pair(cx, cw, s) == hipSuccess ? LP_OK : LP_ERR_HIP;
+  }
   // dX and dW run one after the other on the stream, so they can share the workspace.
   if (grad_x != nullptr && M * K > 0) {
     lp::GemmCall c{false, grad, w, offsets, (int32_t)(groups ? groups : 1), M, N, K, grad_x, ws, ws_bytes};

@@ -136,7 +136,9 @@ using namespace gk;
 
 size_t gemm_workspace_bytes(const GemmCall& call) { return split_plan(call).bytes; }
 
-hipError_t launch_gemm(const GemmCall& call, hipStream_t stream) {
+namespace {
+
+Params base_params(const GemmCall& call) {
   Params prm{};
   prm.P = make_op(*call.grad);
   prm.Q = make_op(*call.other);
@@ -155,18 +157,32 @@ hipError_t launch_gemm(const GemmCall& call, hipStream_t stream) {
     prm.Ktot = (int32_t)call.M;
     prm.c_batch = call.N * call.K;
   }
-  if (native_mx(call) || native_pt(call)) {
-    const bool pt = native_pt(call);
-    const int fp = call.grad->fmt, fq = call.other->fmt;
-    prm.nq = (int32_t)((prm.Qtot + Big::BQ - 1) / Big::BQ);
-    if (call.dw) {
-      prm.ntiles = (int32_t)(((call.N + Big::BP - 1) / Big::BP) * prm.nq * call.groups);
-      return pt ? dw_pt(prm, fp, fq, stream) : dw_mx(prm, stream);
-    }
+  return prm;
+}
+
+// Tile counts of a contraction on the FP8 MFMA kernel (256 x 256 tiles).
+Params native_params(const GemmCall& call) {
+  Params prm = base_params(call);
+  prm.nq = (int32_t)((prm.Qtot + Big::BQ - 1) / Big::BQ);
+  if (call.dw) {
+    prm.ntiles = (int32_t)(((call.N + Big::BP - 1) / Big::BP) * prm.nq * call.groups);
+  } else {
     const int64_t ptiles = call.offsets ? (call.M / Big::BP + call.groups) : (call.M + Big::BP - 1) / Big::BP;
     prm.ntiles = (int32_t)(ptiles * prm.nq);
-    return pt ? dx_pt(prm, fp, fq, stream) : dx_mx(prm, stream);
   }
+  return prm;
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const GemmCall& call, hipStream_t stream) {
+  if (native_mx(call) || native_pt(call)) {
+    const Params prm = native_params(call);
+    const int fp = call.grad->fmt, fq = call.other->fmt;
+    if (native_pt(call)) return call.dw ? dw_pt(prm, fp, fq, stream) : dx_pt(prm, fp, fq, stream);
+    return call.dw ? dw_mx(prm, stream) : dx_mx(prm, stream);
+  }
+  Params prm = base_params(call);
   if (big_tiles(call) >= kCUs) return launch_cfg<Big>(call, prm, stream);
   // Fewer than one full wave of 256 x 256 tiles across the CUs: split the
   // contraction when a large enough workspace is given, else halve the tile
@@ -181,6 +197,13 @@ hipError_t launch_gemm(const GemmCall& call, hipStream_t stream) {
     return launch_cfg<Big>(call, prm, stream);
   }
   return launch_cfg<Narrow>(call, prm, stream);
+}
+
+hipError_t launch_gemm_pair(const GemmCall& dx, const GemmCall& dw, hipStream_t stream) {
+  if (native_pt(dx) && native_pt(dw) && dx.other->fmt == dw.other->fmt)
+    return pt_pair(native_params(dx), native_params(dw), dx.grad->fmt, dx.other->fmt, stream);
+  const hipError_t e = launch_gemm(dx, stream);
+  return e != hipSuccess ? e : launch_gemm(dw, stream);
 }
 
 }  // namespace lp

@@ -499,11 +499,13 @@ struct Tile {
   bool valid;
 };
 
-// Map the workgroup to its tile.  s_ends: LDS for the group offsets.
+// Map the workgroup to its tile.  s_ends: LDS for the group offsets.  hw:
+// the workgroup's index among the p.ntiles of this contraction, in dispatch
+// order (blockIdx.x unless several contractions share a launch).
 template <class C, bool kDW>
-__device__ __forceinline__ Tile select_tile(const Params& p, int32_t* s_ends) {
+__device__ __forceinline__ Tile select_tile(const Params& p, int32_t* s_ends, int hw = blockIdx.x) {
   const int tid = threadIdx.x;
-  int tile = xcd_remap(blockIdx.x, p.ntiles);
+  int tile = xcd_remap(hw, p.ntiles);
   int split = 0;
   if (p.splits > 1) {                                          // the splits of a tile are neighbours
     split = tile % p.splits;
@@ -556,7 +558,7 @@ __device__ __forceinline__ Tile select_tile(const Params& p, int32_t* s_ends) {
     }
     __syncthreads();
     const int per = p.ntiles / p.groups;                       // tiles per group
-    const int pos = blockIdx.x;
+    const int pos = hw;
     const int rank = pos / per;
     for (int i = tid; i < p.groups; i += NT) {
       const int si = ends[i] - (i ? ends[i - 1] : 0);
@@ -963,6 +965,8 @@ hipError_t dw_mx(const Params& prm, hipStream_t s);
 // scales; grouped calls included.
 hipError_t dx_pt(const Params& prm, int fmt_p, int fmt_q, hipStream_t s);
 hipError_t dw_pt(const Params& prm, int fmt_p, int fmt_q, hipStream_t s);
+// Both of them in one launch (X and W in the same format fmt_q).
+hipError_t pt_pair(const Params& dx, const Params& dw, int fmt_p, int fmt_q, hipStream_t s);
 
 }  // namespace gk
 }  // namespace lp

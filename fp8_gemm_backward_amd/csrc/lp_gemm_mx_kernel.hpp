@@ -93,30 +93,42 @@ __device__ __forceinline__ int q_swz(int n) { return 2 * (n & 7); }
 //   memory request per byte, which costs a quarter of the dense throughput.
 enum : int { kGatherMode = 0, kChunkMode = 1, kTensorMode = 2 };
 
-// kFP, kFQ: MFMA format codes of the gradient and the other operand (0 E4M3,
-// 1 E5M2); the MX modes take E4M3 only.
+template <int kMode>
+constexpr int stage_bytes() { return kMode == kGatherMode ? kTileBytes + kGatherBytes : kTileBytes; }
+template <int kMode>
+constexpr int chunk_bytes() { return kMode == kChunkMode ? kChunkBytes : 16; }
+
+// The LDS of one workgroup: four slab stages and two scale-chunk buffers.
+#define LP_MX_LDS(kMode)                                                                   \
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[stage_bytes<kMode>()];             \
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[stage_bytes<kMode>()];             \
+  __shared__ __attribute__((aligned(1024))) uint8_t st2[stage_bytes<kMode>()];             \
+  __shared__ __attribute__((aligned(1024))) uint8_t st3[stage_bytes<kMode>()];             \
+  __shared__ __attribute__((aligned(1024))) uint8_t sc0[chunk_bytes<kMode>()];             \
+  __shared__ __attribute__((aligned(1024))) uint8_t sc1[chunk_bytes<kMode>()]
+
+// One output tile.  hw: the workgroup's index among p.ntiles (see
+// select_tile); indices at or past p.ntiles have no tile.  kFP, kFQ: MFMA
+// format codes of the gradient and the other operand (0 E4M3, 1 E5M2); the
+// MX modes take E4M3 only.
 template <bool kDW, int kMode, int kFP = 0, int kFQ = 0>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void mx_dx_kernel(Params p) {
+__device__ __forceinline__ void mx_tile(const Params& p, int hw, uint8_t* st0, uint8_t* st1, uint8_t* st2,
+                                        uint8_t* st3, uint8_t* sc0, uint8_t* sc1) {
   constexpr bool kChunk = kMode == kChunkMode, kGather = kMode == kGatherMode;
   static_assert(!kDW || !kGather, "dW scale rows (N or K bytes, multiples of 16) always load in chunks");
   static_assert(kMode == kTensorMode || (kFP == 0 && kFQ == 0), "MX operands are E4M3");
-  constexpr int kStage = kGather ? kTileBytes + kGatherBytes : kTileBytes;
+  constexpr int kStage = stage_bytes<kMode>();
   constexpr int T = kGather ? 12 : 8;                            // direct loads per wave and slab
   constexpr int S = 2;                                           // chunk loads per wave
   constexpr int UNROLL = kChunk ? 2 * kChunkSlabs : 4;           // stage, register set and chunk buffer fixed
-  __shared__ __attribute__((aligned(1024))) uint8_t st0[kStage];
-  __shared__ __attribute__((aligned(1024))) uint8_t st1[kStage];
-  __shared__ __attribute__((aligned(1024))) uint8_t st2[kStage];
-  __shared__ __attribute__((aligned(1024))) uint8_t st3[kStage];
-  __shared__ __attribute__((aligned(1024))) uint8_t sc0[kChunk ? kChunkBytes : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t sc1[kChunk ? kChunkBytes : 16];
   static_assert(kMaxGroups * 4 <= kStage, "group ends alias stage 0");
   static_assert(XWP * XWQ * 2 <= kStage, "epilogue staging fits a stage");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wp = wave >> 1, wq = wave & 1;
-  const Tile t = select_tile<XCfg, kDW>(p, reinterpret_cast<int32_t*>(st0));
+  if (hw >= p.ntiles) return;
+  const Tile t = select_tile<XCfg, kDW>(p, reinterpret_cast<int32_t*>(st0), hw);
   if (!t.valid) return;
   __syncthreads();                                               // group ends read; stage 0 reusable
 
@@ -380,6 +392,30 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     store_acc<XCfg, kDW, true>(p, t, acc, wp, wq, lane, stg, *p.P.tensor_scale * *p.Q.tensor_scale);
   else
     store_acc<XCfg, kDW>(p, t, acc, wp, wq, lane, stg);
+}
+
+template <bool kDW, int kMode, int kFP = 0, int kFQ = 0>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void mx_dx_kernel(Params p) {
+  LP_MX_LDS(kMode);
+  mx_tile<kDW, kMode, kFP, kFQ>(p, blockIdx.x, st0, st1, st2, st3, sc0, sc1);
+}
+
+// grad_X and grad_W of one per-tensor scaled gradient in one launch: the
+// first dx_blocks workgroups (dx.ntiles rounded up to a multiple of the 8
+// XCDs, so that both parts keep the dispatch-order dealing that
+// select_tile assumes) take grad_X's tiles, the rest grad_W's.  When
+// neither contraction has tiles enough for every compute unit, the two
+// together fill more of the GPU than either one after the other; the
+// longer grad_X tiles are dispatched first.  kFQ: format of X and W.
+template <int kFP, int kFQ>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void pt_pair_kernel(Params dx, Params dw,
+                                                                                                  int dx_blocks) {
+  LP_MX_LDS(kTensorMode);
+  const int b = blockIdx.x;
+  if (b < dx_blocks)
+    mx_tile<false, kTensorMode, kFP, kFQ>(dx, b, st0, st1, st2, st3, sc0, sc1);
+  else
+    mx_tile<true, kTensorMode, kFP, kFQ>(dw, b - dx_blocks, st0, st1, st2, st3, sc0, sc1);
 }
 
 }  // namespace gk

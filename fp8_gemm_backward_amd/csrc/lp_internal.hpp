@@ -64,6 +64,10 @@ struct GemmCall {
 };
 hipError_t launch_gemm(const GemmCall& call, hipStream_t stream);
 
+// grad_X then grad_W of one call (same gradient); per-tensor FP8 operands
+// run both in one launch.
+hipError_t launch_gemm_pair(const GemmCall& dx, const GemmCall& dw, hipStream_t stream);
+
 // Workspace bytes the contraction would use to split its contraction
 // (0: it does not split).
 size_t gemm_workspace_bytes(const GemmCall& call);

@@ -10,10 +10,26 @@
 //
 // Quantization: t = x / scale (IEEE fp32 division), saturated to
 // +-FP8_MAX (infinities included), then rounded to nearest even by the
-// hardware conversion; NaN becomes 0x7F with the element's sign.  amax is
+// hardware conversion; NaN becomes 0x7F with the element's sign.  The scale
+// is one value for the whole tensor, so the quotient is formed from its
+// correctly rounded reciprocal y (one IEEE division per thread) with
+// Markstein's correction: q ~ x y, r = x - s q (exact, one fma), t = q + r y
+// rounded once, which is the correctly rounded x / s when q is within an ulp
+// of it and nothing underflows or overflows (P. Markstein, "Computation of
+// elementary functions on the IBM RISC System/6000 processor", IBM J. Res.
+// Dev. 34(1), 1990).  For 2^-80 <= s <= 2^100 every intermediate of a
+// quotient that can round to a nonzero FP8 value is a normal number, and
+// quotients beyond 2^20 (saturated in any case) are clamped before the
+// correction, and the result takes x's sign (a zero quotient would lose it);
+// other scales take the IEEE division.  amax is
 // max |x| as the fp32 bit pattern of the largest bf16 magnitude: the bit
 // patterns of non-negative floats order like the floats, NaN patterns above
 // infinity, so an integer atomic max over them is max |x| with NaN winning.
+//
+// Atomic maxima on one address are serialised by the memory system (about
+// 10 ns each, measured), so a kernel that records an amax runs at most one
+// workgroup per compute unit, loops over the tensor, reduces across the
+// workgroup in LDS and issues a single atomic.
 #include "lp_device.hpp"
 #include "lp_internal.hpp"
 
@@ -24,99 +40,178 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kUnits = 4;                       // 8-element units per thread
 constexpr int kSpan = kThreads * kUnits;
+constexpr int kRedThreads = 1024;               // workgroup of the amax-recording kernels
+constexpr int kRedBlocks = 256;                 // at most one per compute unit
+
+template <bool B>
+struct Flag {
+  static constexpr bool value = B;
+};
 
 __device__ __forceinline__ float fp8_max(bool e5m2) { return e5m2 ? 57344.0f : 448.0f; }
 
-// Largest bf16 magnitude (as fp32 bits) of a unit's eight elements.
-__device__ __forceinline__ uint32_t unit_amax_bits(const u32x4& v) {
-  uint32_t m = 0;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const uint32_t w = v[k] & 0x7FFF7FFFu;
-    const uint32_t a = w & 0xFFFFu, b = w >> 16;
-    m = m > a ? m : a;
-    m = m > b ? m : b;
-  }
-  return m << 16;
+__device__ __forceinline__ uint32_t pk_umax16(uint32_t a, uint32_t b) {
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t,
+                            __builtin_elementwise_max(__builtin_bit_cast(u16x2, a), __builtin_bit_cast(u16x2, b)));
 }
 
-// Wave maximum, then one atomic per wave.
+// Largest bf16 magnitude (as fp32 bits) of a unit's eight elements: a
+// packed 16-bit maximum over the sign-cleared pairs, then the two halves.
+__device__ __forceinline__ uint32_t unit_amax_bits(const u32x4& v) {
+  const uint32_t m = pk_umax16(pk_umax16(v[0] & 0x7FFF7FFFu, v[1] & 0x7FFF7FFFu),
+                               pk_umax16(v[2] & 0x7FFF7FFFu, v[3] & 0x7FFF7FFFu));
+  const uint32_t lo = m & 0xFFFFu, hi = m >> 16;
+  return (lo > hi ? lo : hi) << 16;
+}
+
+// Workgroup maximum (every thread calls), then one atomic per workgroup.
 __device__ __forceinline__ void record_amax(uint32_t m, uint32_t* out) {
+  __shared__ uint32_t s_max[kRedThreads / 64];
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
     const uint32_t o = (uint32_t)__shfl_xor((int)m, off);
     m = m > o ? m : o;
   }
-  if ((threadIdx.x & 63) == 0 && m != 0) __hip_atomic_fetch_max(out, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if ((threadIdx.x & 63) == 0) s_max[threadIdx.x / 64] = m;
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  for (int w = 1; w < (int)(blockDim.x / 64); ++w) m = m > s_max[w] ? m : s_max[w];
+  if (m != 0) __hip_atomic_fetch_max(out, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __global__ void zero_u32(uint32_t* p) { *p = 0u; }
 
-__global__ __launch_bounds__(kThreads) void tensor_amax(const u32x4* __restrict__ src, uint32_t nunits,
-                                                        uint32_t* __restrict__ amax) {
-  uint32_t m = 0;
+// Units base + j NT + tid (j < kUnits) of src into v; zeros past the end.
+template <int NT>
+__device__ __forceinline__ void load_units(const u32x4* __restrict__ src, uint32_t nunits, uint32_t base,
+                                           u32x4 (&v)[kUnits]) {
 #pragma unroll
   for (int j = 0; j < kUnits; ++j) {
-    const uint32_t u = blockIdx.x * kSpan + j * kThreads + threadIdx.x;
-    if (u < nunits) {
-      const uint32_t a = unit_amax_bits(__builtin_nontemporal_load(src + u));
+    const uint32_t u = base + j * NT + threadIdx.x;
+    v[j] = u < nunits ? __builtin_nontemporal_load(src + u) : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+// A workgroup's share of a grid-stride loop over spans of NT * kUnits
+// units: body(v, base) for each span, with the next span's loads issued
+// before the current span is processed.
+template <int NT, class Body>
+__device__ __forceinline__ void stride_loop(const u32x4* __restrict__ src, uint32_t nunits, Body body) {
+  const uint32_t span = NT * kUnits, stride = gridDim.x * span;
+  uint32_t base = blockIdx.x * span;
+  if (base >= nunits) return;
+  u32x4 cur[kUnits];
+  load_units<NT>(src, nunits, base, cur);
+  while (true) {
+    const uint32_t next = base + stride;
+    u32x4 nxt[kUnits];
+    if (next < nunits) load_units<NT>(src, nunits, next, nxt);
+    body(cur, base);
+    if (next >= nunits) break;
+#pragma unroll
+    for (int j = 0; j < kUnits; ++j) cur[j] = nxt[j];
+    base = next;
+  }
+}
+
+__global__ __launch_bounds__(kRedThreads) void tensor_amax(const u32x4* __restrict__ src, uint32_t nunits,
+                                                           uint32_t* __restrict__ amax) {
+  uint32_t m = 0;
+  stride_loop<kRedThreads>(src, nunits, [&](const u32x4 (&v)[kUnits], uint32_t) {
+#pragma unroll
+    for (int j = 0; j < kUnits; ++j) {
+      const uint32_t a = unit_amax_bits(v[j]);
       m = m > a ? m : a;
     }
-  }
+  });
   record_amax(m, amax);
 }
 
-// Two elements -> two FP8 codes (low byte first).
-template <bool kE5M2>
-__device__ __forceinline__ uint32_t quant_pair(float a, float b, float s) {
+// x / s: with kFast, from y = RN(1 / s) as described above.
+template <bool kFast>
+__device__ __forceinline__ float quotient(float x, float s, float y) {
+  if constexpr (kFast) {
+    const float q = __builtin_amdgcn_fmed3f(x * y, -0x1p20f, 0x1p20f);
+    const float r = __builtin_fmaf(-s, q, x);
+    return __builtin_copysignf(__builtin_fmaf(r, y, q), x);       // q = -0 would give +0
+  } else {
+    return x / s;
+  }
+}
+
+// Two elements -> two FP8 codes (low byte first).  NaN inputs are fixed by
+// the caller.
+template <bool kE5M2, bool kFast>
+__device__ __forceinline__ uint32_t quant_pair(float a, float b, float s, float y) {
   const float mx = fp8_max(kE5M2);
-  const float ta = a / s, tb = b / s;
-  const float ca = __builtin_amdgcn_fmed3f(ta, -mx, mx), cb = __builtin_amdgcn_fmed3f(tb, -mx, mx);
+  const float ca = __builtin_amdgcn_fmed3f(quotient<kFast>(a, s, y), -mx, mx);
+  const float cb = __builtin_amdgcn_fmed3f(quotient<kFast>(b, s, y), -mx, mx);
   i16x2 old = {0, 0};
-  uint32_t r;
   if constexpr (kE5M2)
-    r = (uint32_t)(uint16_t)__builtin_amdgcn_cvt_scalef32_pk_bf8_f32(old, ca, cb, 1.0f, false)[0];
+    return (uint32_t)(uint16_t)__builtin_amdgcn_cvt_scalef32_pk_bf8_f32(old, ca, cb, 1.0f, false)[0];
   else
-    r = (uint32_t)(uint16_t)__builtin_amdgcn_cvt_scalef32_pk_fp8_f32(old, ca, cb, 1.0f, false)[0];
-  // NaN in, NaN code out (0x7F with the sign); the clamp does not keep NaN.
-  const uint32_t na = __builtin_isnan(ta) ? (0x7Fu | (__builtin_bit_cast(uint32_t, a) >> 24 & 0x80u)) : (r & 0xFFu);
-  const uint32_t nb = __builtin_isnan(tb) ? (0x7Fu | (__builtin_bit_cast(uint32_t, b) >> 24 & 0x80u)) : (r >> 8);
-  return na | (nb << 8);
+    return (uint32_t)(uint16_t)__builtin_amdgcn_cvt_scalef32_pk_fp8_f32(old, ca, cb, 1.0f, false)[0];
+}
+
+// The NaN elements of a unit (8 bf16 in v) get code 0x7F with their sign.
+__device__ __forceinline__ void fix_nan_codes(const u32x4& v, uint32_t o[2]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t h = (v[e / 2] >> (16 * (e & 1))) & 0xFFFFu;
+    if ((h & 0x7FFFu) > 0x7F80u) {
+      const uint32_t sh = 8 * (e & 3);
+      o[e / 4] = (o[e / 4] & ~(0xFFu << sh)) | ((0x7Fu | ((h >> 8) & 0x80u)) << sh);
+    }
+  }
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
 
-// Unit u: 8 bf16 in (16 bytes), 8 codes out (8 bytes); the amax of the
-// input goes to `amax` when it is not null.
-template <bool kE5M2>
-__global__ __launch_bounds__(kThreads) void tensor_quant(const u32x4* __restrict__ src, uint32_t nunits,
-                                                         const float* __restrict__ scale, u32x2* __restrict__ codes,
-                                                         uint32_t* __restrict__ amax) {
-  u32x4 v[kUnits];
-#pragma unroll
-  for (int j = 0; j < kUnits; ++j) {
-    const uint32_t u = blockIdx.x * kSpan + j * kThreads + threadIdx.x;
-    v[j] = u < nunits ? __builtin_nontemporal_load(src + u) : u32x4{0u, 0u, 0u, 0u};
-  }
+// Unit u: 8 bf16 in (16 bytes), 8 codes out (8 bytes).  kAmax: the amax of
+// the input goes to `amax` (one workgroup per compute unit at most, looping;
+// else one pass of kSpan units per workgroup).
+template <bool kE5M2, bool kAmax>
+__global__ __launch_bounds__(kAmax ? kRedThreads : kThreads) void tensor_quant(
+    const u32x4* __restrict__ src, uint32_t nunits, const float* __restrict__ scale, u32x2* __restrict__ codes,
+    uint32_t* __restrict__ amax) {
+  constexpr uint32_t NT_ = kAmax ? kRedThreads : kThreads;
+  constexpr uint32_t span = NT_ * kUnits;
   const float s = *scale;
+  const float y = 1.0f / s;
   uint32_t m = 0;
+  auto pass = [&](auto fast) {
+    constexpr bool kFast = decltype(fast)::value;
+    auto body = [&](const u32x4 (&v)[kUnits], uint32_t base) {
 #pragma unroll
-  for (int j = 0; j < kUnits; ++j) {
-    const uint32_t u = blockIdx.x * kSpan + j * kThreads + threadIdx.x;
-    if (u >= nunits) continue;
-    const uint32_t a = unit_amax_bits(v[j]);
-    m = m > a ? m : a;
-    uint32_t o[2];
+      for (int j = 0; j < kUnits; ++j) {
+        const uint32_t u = base + j * NT_ + threadIdx.x;
+        if (u >= nunits) continue;
+        const uint32_t a = unit_amax_bits(v[j]);
+        if constexpr (kAmax) m = m > a ? m : a;
+        uint32_t o[2];
 #pragma unroll
-    for (int k = 0; k < 4; k += 2) {
-      const uint32_t lo = quant_pair<kE5M2>(bf16_lo(v[j][k]), bf16_hi(v[j][k]), s);
-      const uint32_t hi = quant_pair<kE5M2>(bf16_lo(v[j][k + 1]), bf16_hi(v[j][k + 1]), s);
-      o[k / 2] = lo | (hi << 16);
+        for (int k = 0; k < 4; k += 2) {
+          const uint32_t lo = quant_pair<kE5M2, kFast>(bf16_lo(v[j][k]), bf16_hi(v[j][k]), s, y);
+          const uint32_t hi = quant_pair<kE5M2, kFast>(bf16_lo(v[j][k + 1]), bf16_hi(v[j][k + 1]), s, y);
+          o[k / 2] = lo | (hi << 16);
+        }
+        if (a > 0x7F800000u) fix_nan_codes(v[j], o);              // a NaN in the unit
+        __builtin_nontemporal_store(u32x2{o[0], o[1]}, codes + u);
+      }
+    };
+    if constexpr (kAmax) {
+      stride_loop<NT_>(src, nunits, body);
+    } else {                                                     // the grid covers every unit once
+      u32x4 v[kUnits];
+      load_units<NT_>(src, nunits, blockIdx.x * span, v);
+      body(v, blockIdx.x * span);
     }
-    __builtin_nontemporal_store(u32x2{o[0], o[1]}, codes + u);
-  }
-  if (amax != nullptr) record_amax(m, amax);
+  };
+  if (s >= 0x1p-80f && s <= 0x1p100f) pass(Flag<true>{});
+  else pass(Flag<false>{});
+  if constexpr (kAmax) record_amax(m, amax);
 }
 
 // scale = (max(history) / FP8_MAX) / 2^margin, at least 1e-12, NaN kept.
@@ -192,13 +287,19 @@ __global__ __launch_bounds__(kThreads) void tensor_dequant(const u32x2* __restri
 
 dim3 grid_of(uint32_t nunits) { return dim3((nunits + kSpan - 1) / kSpan); }
 
+// Grid of a kernel that records an amax.
+dim3 red_grid_of(uint32_t nunits) {
+  const uint32_t b = (nunits + kRedThreads * kUnits - 1) / (kRedThreads * kUnits);
+  return dim3(b < (uint32_t)kRedBlocks ? b : (uint32_t)kRedBlocks);
+}
+
 }  // namespace
 
 hipError_t launch_tensor_amax(const void* src, int64_t n, float* amax, hipStream_t stream) {
   uint32_t* a = reinterpret_cast<uint32_t*>(amax);
   zero_u32<<<1, 1, 0, stream>>>(a);
   const uint32_t nunits = (uint32_t)(n / 8);
-  if (nunits > 0) tensor_amax<<<grid_of(nunits), kThreads, 0, stream>>>(static_cast<const u32x4*>(src), nunits, a);
+  if (nunits > 0) tensor_amax<<<red_grid_of(nunits), kRedThreads, 0, stream>>>(static_cast<const u32x4*>(src), nunits, a);
   return hipGetLastError();
 }
 
@@ -210,10 +311,14 @@ hipError_t launch_tensor_quant(const void* src, int64_t n, int fmt, const float*
   if (nunits == 0) return hipGetLastError();
   auto s = static_cast<const u32x4*>(src);
   auto c = static_cast<u32x2*>(codes);
-  if (fmt == LP_FP8T_E5M2)
-    tensor_quant<true><<<grid_of(nunits), kThreads, 0, stream>>>(s, nunits, scale, c, a);
-  else
-    tensor_quant<false><<<grid_of(nunits), kThreads, 0, stream>>>(s, nunits, scale, c, a);
+  const bool e5 = fmt == LP_FP8T_E5M2;
+  if (a != nullptr) {
+    if (e5) tensor_quant<true, true><<<red_grid_of(nunits), kRedThreads, 0, stream>>>(s, nunits, scale, c, a);
+    else tensor_quant<false, true><<<red_grid_of(nunits), kRedThreads, 0, stream>>>(s, nunits, scale, c, a);
+  } else {
+    if (e5) tensor_quant<true, false><<<grid_of(nunits), kThreads, 0, stream>>>(s, nunits, scale, c, a);
+    else tensor_quant<false, false><<<grid_of(nunits), kThreads, 0, stream>>>(s, nunits, scale, c, a);
+  }
   return hipGetLastError();
 }
 

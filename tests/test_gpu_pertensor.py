@@ -51,6 +51,32 @@ def test_quant_every_bf16(lp, fmt, scale):
     assert np.isnan(amax.item()), "a NaN input makes the amax NaN"
 
 
+def _scales_across_ranges() -> np.ndarray:
+    """Random fp32 scales, log-uniform over 2^-80 .. 2^100 with random
+    mantissas, plus the ends of that range and their neighbours outside it,
+    and a few far outside (the quantizer forms its quotients differently
+    inside and outside the range)."""
+    g = W.rng(39, "w")
+    e = g.uniform(-80.0, 100.0, 48)
+    r = (2.0 ** e).astype(np.float32)
+    r = (r.view(np.uint32) ^ (g.integers(0, 1 << 23, 48, dtype=np.uint32))).view(np.float32)
+    edges = np.array([2.0 ** -80, 2.0 ** 100, 1e-12, 1e30, 2.0 ** -100, 2.0 ** 120], np.float32)
+    near = np.concatenate([np.nextafter(edges[:2], np.float32(0)), np.nextafter(edges[:2], np.float32(np.inf))])
+    return np.concatenate([r, edges, near.astype(np.float32)])
+
+
+@pytest.mark.parametrize("fmt", ["fp8t_e4m3", "fp8t_e5m2"])
+def test_quant_every_bf16_many_scales(lp, fmt):
+    """Every bf16 value at 58 scales, against fp32 IEEE division on the host."""
+    bits = _every_bf16()
+    src = bf16_dev(bits)
+    for scale in _scales_across_ranges():
+        q = lp.lp_tensor_quant(src, fmt, _f32_dev([scale]))
+        torch.cuda.synchronize()
+        assert_bits_equal(q.codes.cpu().numpy().reshape(-1), PT.quantize(bits, ELEM[fmt], scale),
+                          f"{fmt} codes at scale {scale!r}")
+
+
 @pytest.mark.parametrize("fmt", ["fp8t_e4m3", "fp8t_e5m2"])
 @pytest.mark.parametrize("scale", [1.0, 0.37, 1e-12, 2.0 ** -140, 3.0e38, 0.0, float("nan")])
 def test_dequant_every_code(lp, fmt, scale):
@@ -228,3 +254,37 @@ def test_hybrid_step_dynamic_scaling(lp):
     assert_bits_equal(g.codes.cpu().numpy().reshape(M, N), codes, "gradient codes")
     assert_close(dx, PT.linear_dx(codes, "e5m2", s, wc, "e4m3", ws), "dX")
     assert_close(dw, PT.linear_dw(codes, "e5m2", s, xc, "e4m3", xs), "dW")
+
+
+def test_fp8_hybrid_full_size(lp):
+    """The benchmark's workload at full size, through the same calls: every
+    code of the three quantizations against the oracle, then sampled rows of
+    dX and dW (all tiles' row and column ranges, the last rows included)."""
+    w = W.WORKLOADS["fp8_hybrid"]
+    M, N, K = w.M, w.N, w.K
+    gb = W.bf16_bits(W.normal_f32(w.number, "grad", (M, N), 1.0))
+    xb = W.bf16_bits(W.normal_f32(w.number, "x", (M, K), w.x_sigma))
+    wb = W.bf16_bits(W.normal_f32(w.number, "w", (N, K), w.w_sigma))
+    ops = {}
+    for name, bits, fmt in (("grad", gb, "fp8t_e5m2"), ("x", xb, "fp8t_e4m3"), ("w", wb, "fp8t_e4m3")):
+        t = bf16_dev(bits)
+        hist = torch.empty(W.AMAX_RING, device="cuda")
+        hist.copy_(lp.lp_tensor_amax(t).expand(W.AMAX_RING))
+        scale = lp.lp_scale_from_history(hist, fmt)
+        q = lp.lp_tensor_quant(t, fmt, scale, amax=hist[3:4])
+        torch.cuda.synchronize()
+        a = PT.amax(bits)
+        s = PT.scale_from_history(np.full(W.AMAX_RING, a, np.float32), ELEM[fmt])
+        codes = PT.quantize(bits, ELEM[fmt], s)
+        _same_f32(scale, s, f"{name} scale")
+        _same_f32(hist[3:4], a, f"{name} recorded amax")
+        assert_bits_equal(q.codes.cpu().numpy().reshape(bits.shape), codes, f"{name} codes")
+        ops[name] = (q, codes, s)
+    (gq, gc, gs), (xq, xc, xs), (wq, wc, ws) = ops["grad"], ops["x"], ops["w"]
+    dx, _ = lp.lp_linear_bwd(gq, None, wq, need_dw=False)
+    _, dw = lp.lp_linear_bwd(gq, xq, None, need_dx=False)
+    torch.cuda.synchronize()
+    rs = np.unique(np.concatenate([np.arange(0, M, 61), [M - 1]]))
+    ns = np.unique(np.concatenate([np.arange(0, N, 97), [N - 1]]))
+    assert_close(dx[torch.from_numpy(rs).cuda()], PT.linear_dx(gc[rs], "e5m2", gs, wc, "e4m3", ws), "dX rows")
+    assert_close(dw[torch.from_numpy(ns).cuda()], PT.linear_dw(gc[:, ns], "e5m2", gs, xc, "e4m3", xs), "dW rows")

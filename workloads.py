@@ -24,6 +24,15 @@ grouped backward of "perf: defer mxfp8 backward quantization"):
                  MXFP8MatMul.backward): X 8192x4096 N(0,1), W 4096x4096
                  N(0,0.02), grad_out 8192x4096 N(0,1), all bf16, quantized in
                  the backward; dX and dW
+  fp8_hybrid     the per-tensor FP8 hybrid backward of "AstrAI fp8.py"
+                 (_LinearFp8.backward): X 4096x1536 N(0,1) and W 6144x1536
+                 N(0,0.02) saved as E4M3 with their dynamic scales; grad_out
+                 4096x6144 N(0,1) bf16, quantized to E5M2 in the backward with
+                 the delayed scale of a 16-entry amax ring; dX and dW.  The page
+                 times a 0.67B model at batch 4x1024 without giving its layer
+                 sizes: 4096 tokens and the FFN up-projection (1536 -> 6144) of
+                 a GPT-style block with d = 1536 (12 * 24 * 1536^2 = 0.68B over
+                 24 blocks) stand in for it.
 
 Every tensor has its own PCG64 stream: SeedSequence(entropy=1000 + config
 number, spawn_key=(tensor id,)), so a tensor's values do not depend on which
@@ -72,7 +81,10 @@ WORKLOADS = {
     "mxfp8_deferred": Workload("mxfp8_deferred", 5, "mxfp8", M=32768, N=2048, K=7168,
                                groups=64, w_sigma=0.02, need_dw=False, routing="zipf"),
     "mxfp8_dense": Workload("mxfp8_dense", 6, "mxfp8", M=8192, N=4096, K=4096, w_sigma=0.02),
+    "fp8_hybrid": Workload("fp8_hybrid", 7, "fp8t", M=4096, N=6144, K=1536, w_sigma=0.02),
 }
+
+AMAX_RING = 16               # amax history length of the delayed-scaling recipe
 
 
 def rng(number: int, tensor: str) -> np.random.Generator:
