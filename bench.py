@@ -11,6 +11,8 @@ synthetic input already resident in HBM:
   mxfp8_dense     lp_mx_quant_dual(grad) + lp_mx_quant(W, -2) + lp_mx_quant(X, -2) + lp_linear_bwd dX, dW
   fp8_hybrid      lp_scale_from_history(grad ring) + lp_tensor_quant(grad -> E5M2, amax into the ring)
                   + lp_linear_bwd dX, dW against E4M3 X and W (per-tensor scales)
+  mxfp4_forward   lp_linear_fwd: y = X @ W^T, MXFP4 X 8192x4096 and W 4096x4096 (the forward
+                  the FP4 backward pairs with, on the block-scaled FP4 MFMA)
   mxfp4_tiny      lp_linear_bwd: dX and dW, 64 x 128 x 128
 Input sets are rotated through about 1 GB so that the 256 MiB Infinity Cache
 cannot serve a repeated step.  Prints one JSON line (rank 0).
@@ -41,6 +43,7 @@ import workloads as W  # noqa: E402
 METRIC = "backward TFLOP/s (dX+dW) and % BF16 MFMA peak; dequant/quant GB/s vs HBM"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA (the block-scaled MXFP8 contraction)
+PEAK_FP4_TFLOPS = 10100.0      # MI355X dense fp4 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 ROTATE_BYTES = 1 << 30
 
@@ -255,6 +258,21 @@ def build(lp, name: str):
             ts.append(ev.stop(stream))
             return ts
         standalone = []
+    elif name == "mxfp4_forward":
+        per_set = (M * K + N * K) * (0.5 + 1 / 16) + M * N * 2
+        nsets = max(1, min(16, math.ceil(ROTATE_BYTES / per_set)))
+        for i in range(nsets):
+            xq = lp.lp_mx_quant(W.torch_normal_bf16((M, K), w.x_sigma, 8100 + i, "cuda"), -1, "mxfp4")
+            wq = lp.lp_mx_quant(W.torch_normal_bf16((N, K), w.w_sigma, 8200 + i, "cuda"), -1, "mxfp4")
+            sets.append((xq, wq, torch.empty((M, N), dtype=torch.bfloat16, device="cuda")))
+        phases.append(Phase("linear_fwd", "mx_fwd_kernel", flops=2.0 * M * N * K, peak=PEAK_FP4_TFLOPS))
+
+        def step(i, stream):
+            xq, wq, y = sets[i % len(sets)]
+            ev = _events(stream)
+            lp.lp_linear_fwd(xq, wq, y=y, stream=stream)
+            return [ev.stop(stream)]
+        standalone = []
     else:
         raise SystemExit(f"unknown workload {name}")
     return w, phases, step, standalone
@@ -331,7 +349,23 @@ def cpu_baseline(name: str, budget_s: float = 12.0):
         cores = os.cpu_count()
     w = W.WORKLOADS[name]
     M, N, K = w.M, w.N, w.K
-    if name == "fp8_hybrid":
+    if name == "mxfp4_forward":
+        # W quantized and decoded once; a slab of token rows quantized,
+        # decoded and multiplied; extrapolated to all rows.
+        rows = 256
+        x = W.normal_f32(w.number, "x", (rows, K), w.x_sigma)
+        wt = W.normal_f32(w.number, "w", (N, K), w.w_sigma)
+        t0 = time.perf_counter()
+        wd = F.dequant("mxfp4", *F.quant_mxfp4_f32(wt[None]))[0]
+        t_w = time.perf_counter() - t0
+        t1 = time.perf_counter()
+        xd = F.dequant("mxfp4", *F.quant_mxfp4_f32(x[None]))[0]
+        O.linear_fwd(xd, wd)
+        t_rows = time.perf_counter() - t1
+        total = t_w + t_rows * (M / rows)
+        flops = 2.0 * M * N * K
+        sample = f"W quantized+decoded once; {rows} token rows quantized, decoded and multiplied (fp64); extrapolated to {M}"
+    elif name == "fp8_hybrid":
         # a slab of token rows: the gradient's amax and E5M2 quantization, the
         # saved operands' E4M3 quantization, and the fp64 dX / dW over the slab;
         # extrapolated to all rows (W's quantization counted once).
@@ -499,7 +533,8 @@ def main():
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "fp8" if w.fmt in ("mxfp8", "fp8t") else "bf16", "data": "synthetic",
+        "vs_baseline": None, "data": "synthetic",
+        "dtype": "fp4" if w.name == "mxfp4_forward" else ("fp8" if w.fmt in ("mxfp8", "fp8t") else "bf16"),
         "config": {"workload": w.name, "format": w.fmt, "M": w.M, "N": w.N, "K": w.K, "groups": w.groups,
                    "grad_x": w.need_dx, "grad_w": w.need_dw, "global_batch": w.M, "parallelism": "none (1 GPU)"},
         "roofline": roof, "phases": phase_rec, "standalone_hbm": hbm,

@@ -58,11 +58,13 @@ def _load() -> ctypes.CDLL:
     lib.lp_tensor_amax.argtypes = [v, i64, v, v]
     lib.lp_tensor_quant.argtypes = [v, i64, i32, v, v, v, v]
     lib.lp_scale_from_history.argtypes = [v, i32, i32, i32, v, v]
+    lib.lp_linear_fwd.argtypes = [P, P, v, v]
+    lib.lp_grouped_fwd.argtypes = [P, P, v, i64, v, v]
     lib.lp_status_string.argtypes = [i32]
     lib.lp_status_string.restype = ctypes.c_char_p
     for f in ("lp_dequant", "lp_mx_quant", "lp_mx_quant_dual", "lp_linear_bwd", "lp_grouped_bwd",
               "lp_linear_bwd_workspace", "lp_linear_bwd_ws", "lp_tensor_amax", "lp_tensor_quant",
-              "lp_scale_from_history"):
+              "lp_scale_from_history", "lp_linear_fwd", "lp_grouped_fwd"):
         getattr(lib, f).restype = ctypes.c_int32
     return lib
 
@@ -264,6 +266,28 @@ def lp_grouped_bwd(grad_out: QTensor, x: Optional[QTensor], w: Optional[QTensor]
                             grad_w.data_ptr() if need_dw else None, _stream(stream))
     _check(st, "lp_grouped_bwd")
     return (grad_x if need_dx else None), (grad_w if need_dw else None)
+
+
+def lp_linear_fwd(x: QTensor, w: QTensor, y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """y [M, N] = x @ w^T for MX operands scaled along k (both "mxfp4" or
+    both "mxfp8")."""
+    if y is None:
+        y = torch.empty((x.rows, w.rows), dtype=torch.bfloat16, device=x.codes.device)
+    xc, wc = x.c(), w.c()
+    _check(lib.lp_linear_fwd(ctypes.byref(xc), ctypes.byref(wc), y.data_ptr(), _stream(stream)), "lp_linear_fwd")
+    return y
+
+
+def lp_grouped_fwd(x: QTensor, w: QTensor, offsets: torch.Tensor, y: Optional[torch.Tensor] = None,
+                   stream=None) -> torch.Tensor:
+    """y [M, N]: rows of group g are x[rows] @ w[g]^T; rows at or past
+    offsets[-1] are left as they were in `y`."""
+    if y is None:
+        y = torch.empty((x.rows, w.rows), dtype=torch.bfloat16, device=x.codes.device)
+    xc, wc = x.c(), w.c()
+    _check(lib.lp_grouped_fwd(ctypes.byref(xc), ctypes.byref(wc), offsets.data_ptr(), offsets.numel(), y.data_ptr(),
+                              _stream(stream)), "lp_grouped_fwd")
+    return y
 
 
 def lp_status_string(status: int) -> str:

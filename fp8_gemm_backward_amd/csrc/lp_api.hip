@@ -226,6 +226,39 @@ lp_status lp_linear_bwd_ws(const lp_qtensor* grad_out, const lp_qtensor* x, cons
   return run_bwd(grad_out, x, w, nullptr, 0, grad_x, grad_w, workspace, workspace_bytes, stream);
 }
 
+// Checks of the forward: x [M][K] and w [G][N][K], both MXFP4 or both
+// MXFP8 scaled along k; K % 128 (MXFP4) or K % 64 (MXFP8); N % 16.
+static lp_status check_fwd(const lp_qtensor* x, const lp_qtensor* w, void* y, int64_t groups) {
+  lp_status st = check_tensor(x);
+  if (st != LP_OK) return st;
+  if ((st = check_tensor(w)) != LP_OK) return st;
+  if ((x->fmt != LP_MXFP4 && x->fmt != LP_MXFP8) || w->fmt != x->fmt) return LP_ERR_FORMAT;
+  if (x->scale_axis != -1 || w->scale_axis != -1) return LP_ERR_FORMAT;
+  if (x->batch != 1 || w->batch != (groups ? groups : 1) || w->cols != x->cols) return LP_ERR_SHAPE;
+  if (x->cols % (x->fmt == LP_MXFP4 ? 128 : 64) || w->rows % 16) return LP_ERR_SHAPE;
+  if (x->rows * w->rows > 0 && y == nullptr) return LP_ERR_NULL;
+  if (!aligned(y, 16)) return LP_ERR_ALIGN;
+  return LP_OK;
+}
+
+lp_status lp_linear_fwd(const lp_qtensor* x, const lp_qtensor* w, void* y, void* stream) {
+  lp_status st = check_fwd(x, w, y, 0);
+  if (st != LP_OK) return st;
+  if (x->rows * w->rows == 0) return LP_OK;
+  return hip_status(lp::launch_fwd(*x, *w, nullptr, 1, y, static_cast<hipStream_t>(stream)));
+}
+
+lp_status lp_grouped_fwd(const lp_qtensor* x, const lp_qtensor* w, const int32_t* offsets, int64_t groups, void* y,
+                         void* stream) {
+  if (groups < 1 || groups > 1024) return LP_ERR_SHAPE;
+  lp_status st = check_fwd(x, w, y, groups);
+  if (st != LP_OK) return st;
+  if (offsets == nullptr) return LP_ERR_NULL;
+  if (!aligned(offsets, 4)) return LP_ERR_ALIGN;
+  if (x->rows * w->rows == 0) return LP_OK;
+  return hip_status(lp::launch_fwd(*x, *w, offsets, (int32_t)groups, y, static_cast<hipStream_t>(stream)));
+}
+
 lp_status lp_grouped_bwd(const lp_qtensor* grad_out, const lp_qtensor* x, const lp_qtensor* w,
                          const int32_t* offsets, int64_t groups, void* grad_x, void* grad_w, void* stream) {
   if (grad_x == nullptr && grad_w == nullptr) return LP_OK;

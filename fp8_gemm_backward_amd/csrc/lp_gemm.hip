@@ -199,6 +199,25 @@ hipError_t launch_gemm(const GemmCall& call, hipStream_t stream) {
   return launch_cfg<Narrow>(call, prm, stream);
 }
 
+hipError_t launch_fwd(const lp_qtensor& x, const lp_qtensor& w, const int32_t* offsets, int32_t groups, void* y,
+                      hipStream_t stream) {
+  Params prm{};
+  prm.P = make_op(x);
+  prm.Q = make_op(w);
+  prm.C = static_cast<uint16_t*>(y);
+  prm.Ptot = (int32_t)x.rows;
+  prm.Qtot = (int32_t)w.rows;
+  prm.Ktot = (int32_t)x.cols;
+  prm.ldc = prm.Qtot;
+  prm.offsets = offsets;
+  prm.groups = groups;
+  prm.splits = 1;
+  prm.nq = (int32_t)((prm.Qtot + Big::BQ - 1) / Big::BQ);
+  const int64_t ptiles = offsets ? (x.rows / Big::BP + groups) : (x.rows + Big::BP - 1) / Big::BP;
+  prm.ntiles = (int32_t)(ptiles * prm.nq);
+  return fwd_mx(prm, x.fmt == LP_MXFP4, stream);
+}
+
 hipError_t launch_gemm_pair(const GemmCall& dx, const GemmCall& dw, hipStream_t stream) {
   if (native_pt(dx) && native_pt(dw) && dx.other->fmt == dw.other->fmt)
     return pt_pair(native_params(dx), native_params(dw), dx.grad->fmt, dx.other->fmt, stream);

@@ -965,6 +965,9 @@ hipError_t dw_mx(const Params& prm, hipStream_t s);
 // scales; grouped calls included.
 hipError_t dx_pt(const Params& prm, int fmt_p, int fmt_q, hipStream_t s);
 hipError_t dw_pt(const Params& prm, int fmt_p, int fmt_q, hipStream_t s);
+// Forward y = x @ w^T of MX operands scaled along k, both MXFP4 (fp4) or
+// both MXFP8.
+hipError_t fwd_mx(const Params& prm, bool fp4, hipStream_t s);
 // Both of them in one launch (X and W in the same format fmt_q).
 hipError_t pt_pair(const Params& dx, const Params& dw, int fmt_p, int fmt_q, hipStream_t s);
 

@@ -64,6 +64,12 @@ struct GemmCall {
 };
 hipError_t launch_gemm(const GemmCall& call, hipStream_t stream);
 
+// Forward y[m][n] = sum_k x[m][k] w[g][n][k] (groups partition the rows m;
+// offsets == nullptr: one group).  x and w are both MXFP4 or both MXFP8,
+// scaled along k.
+hipError_t launch_fwd(const lp_qtensor& x, const lp_qtensor& w, const int32_t* offsets, int32_t groups, void* y,
+                      hipStream_t stream);
+
 // grad_X then grad_W of one call (same gradient); per-tensor FP8 operands
 // run both in one launch.
 hipError_t launch_gemm_pair(const GemmCall& dx, const GemmCall& dw, hipStream_t stream);

@@ -343,6 +343,43 @@ lp_status lp_grouped_bwd(const lp_qtensor* grad_out, const lp_qtensor* x, const 
                          const int32_t* offsets, int64_t groups, void* grad_x, void* grad_w,
                          void* stream);
 
+/*
+ * lp_linear_fwd - forward of a linear layer y = x @ W^T whose operands are
+ * both MX-quantized along the contraction.
+ *
+ * Cites: "Add Autograd Backward Support for FP4 GEMM Custom Ops" (the forward
+ * ops that the backward pairs with multiply FP4 inputs by FP4 weights into
+ * BF16); "perf: defer mxfp8 backward quantization", MXFP8MatMul.forward (x
+ * quantized along its last axis, the weight along its reduction axis, one
+ * E8M0 scale per 32).
+ *
+ * x  [M][K], w [N][K]: both LP_MXFP4 or both LP_MXFP8, scale_axis -1 (blocks
+ *    of 32 along K).  K % 128 == 0 (LP_MXFP4) or K % 64 == 0 (LP_MXFP8);
+ *    N % 16 == 0; M >= 0 arbitrary.
+ * y  device bf16 [M][N].
+ * y[m][n] = sum_k dec(x)[m][k] * dec(w)[n][k] on the block-scaled MFMA: each
+ * product code_x * code_w * 2^(sx + sw) is exact, the sum is fp32, the
+ * result is rounded to bf16 (nearest even).  LP_ERR_FORMAT for other
+ * formats.
+ */
+lp_status lp_linear_fwd(const lp_qtensor* x, const lp_qtensor* w, void* y, void* stream);
+
+/*
+ * lp_grouped_fwd - forward of a grouped (per-expert) matmul with MX operands.
+ *
+ * Cites: "Add Autograd Backward Support for FP4 GEMM Custom Ops" (grouped FP4
+ * forward); "Train adapters on top of FP8 weights", FP8GroupedLinear.forward
+ * (int32 cumulative end offsets; rows past the last offset are not written).
+ *
+ * x        [M][K] rows grouped by offsets; w [groups][N][K]; formats and sizes
+ *          as lp_linear_fwd.  offsets as lp_grouped_bwd (read on the device,
+ *          clamped the same way); 1 <= groups <= 1024.
+ * y        device bf16 [M][N]: rows of group g are x[rows] @ w[g]^T; rows at or
+ *          past offsets[G-1] are NOT written.
+ */
+lp_status lp_grouped_fwd(const lp_qtensor* x, const lp_qtensor* w, const int32_t* offsets, int64_t groups,
+                         void* y, void* stream);
+
 /* A static, human-readable name for a status code. */
 const char* lp_status_string(int32_t status);
 

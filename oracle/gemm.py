@@ -13,6 +13,11 @@ benchmark's CPU-baseline leg may import this module; the library never does.
   EP-sentinel comment in `fp8_grouped_mm_experts_forward`: rows past the last
   offset are not written.
 
+The forward that the backward pairs with ("Add Autograd Backward Support for
+FP4 GEMM Custom Ops": FP4 inputs times FP4 weights into BF16, dense and
+grouped; "perf: defer mxfp8 backward quantization", MXFP8MatMul.forward) is
+y = x @ W^T with the same decoded operands.
+
 The inputs are bf16 values (bit patterns) that the format oracle produced;
 every bf16 x bf16 product is exact in fp64 and the sums are fp64 (numpy's
 float64 matmul).  Grouped weight gradients of an empty group are the empty
@@ -71,6 +76,23 @@ def grouped_dw(grad_bits: np.ndarray, x_bits: np.ndarray, offsets) -> np.ndarray
     for g, (s, e) in enumerate(bounds):
         if e > s:
             out[g] = G[s:e].T @ X[s:e]
+    return out
+
+
+def linear_fwd(x_bits: np.ndarray, w_bits: np.ndarray) -> np.ndarray:
+    """y[m,n] = sum_k x[m,k] * W[n,k]; x [M,K], W [N,K]."""
+    return _f64(x_bits) @ _f64(w_bits).T
+
+
+def grouped_fwd(x_bits: np.ndarray, w_bits: np.ndarray, offsets) -> np.ndarray:
+    """Per group g: y[rows of g] = x[rows of g] @ W[g]^T; rows at or past the
+    last offset are NaN here ("not written")."""
+    X = _f64(x_bits)
+    W = _f64(w_bits)
+    out = np.full((X.shape[0], W.shape[1]), np.nan)
+    for g, (s, e) in enumerate(group_bounds(offsets)):
+        if e > s:
+            out[s:e] = X[s:e] @ W[g].T
     return out
 
 

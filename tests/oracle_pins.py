@@ -513,4 +513,42 @@ def pin_tensor_gemms_brute_force():
             assert abs(dw[n, k] - acc) <= 1e-12 * max(1.0, abs(acc))
 
 
+# ------------------------------------------------------------------ forward (FP4 page; Deferred-MXFP8 page)
+
+def pin_forward_triple_loop_and_adjoint():
+    """y = x @ W^T against a pure-Python triple loop, and the adjoint identity
+    that ties the forward to the backward: sum(y * g) = sum(x * grad_X) for
+    grad_X = g @ W, and = sum(W * grad_W) for grad_W = g^T @ x.  A transposed
+    operand in either direction breaks one of them."""
+    M, N, K = 3, 5, 4
+    x = _tiny_bf16(102, "x", (M, K))
+    w = _tiny_bf16(102, "w", (N, K))
+    g = _tiny_bf16(102, "grad", (M, N))
+    y = O.linear_fwd(x, w)
+    xv, wv = F.bf16_bits_to_f64(x), F.bf16_bits_to_f64(w)
+    for m in range(M):
+        for n in range(N):
+            acc = 0.0
+            for k in range(K):
+                acc += float(xv[m, k]) * float(wv[n, k])
+            assert abs(y[m, n] - acc) <= 1e-12 * max(1.0, abs(acc))
+    gv = F.bf16_bits_to_f64(g)
+    lhs = float(np.sum(y * gv))
+    assert abs(lhs - float(np.sum(xv * O.linear_dx(g, w)))) <= 1e-12 * max(1.0, abs(lhs))
+    assert abs(lhs - float(np.sum(wv * O.linear_dw(g, x)))) <= 1e-12 * max(1.0, abs(lhs))
+
+
+def pin_grouped_forward_equals_dense():
+    """Grouped forward equals the per-group dense forward; rows past the last
+    offset stay unwritten; an empty group writes nothing."""
+    M, N, K, G = 30, 8, 16, 3
+    x = _tiny_bf16(103, "x", (M, K))
+    w = _tiny_bf16(103, "w", (G, N, K))
+    offsets = np.array([9, 9, 25], dtype=np.int32)
+    y = O.grouped_fwd(x, w, offsets)
+    assert np.all(np.isnan(y[25:]))
+    assert np.allclose(y[0:9], O.linear_fwd(x[0:9], w[0]), rtol=1e-13)
+    assert np.allclose(y[9:25], O.linear_fwd(x[9:25], w[2]), rtol=1e-13)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -16,7 +16,7 @@ def test_library_exports_every_header_function():
     names = lp.header_functions()
     assert set(names) == {"lp_dequant", "lp_mx_quant", "lp_linear_bwd", "lp_grouped_bwd", "lp_status_string",
                           "lp_linear_bwd_workspace", "lp_linear_bwd_ws", "lp_mx_quant_dual", "lp_tensor_amax",
-                          "lp_tensor_quant", "lp_scale_from_history"}
+                          "lp_tensor_quant", "lp_scale_from_history", "lp_linear_fwd", "lp_grouped_fwd"}
     for n in names:
         assert hasattr(lp.lib, n), n
 
@@ -120,6 +120,39 @@ def test_tensor_amax_and_scale_reject():
     assert sfh(FAKE, 16, E5M2T, -65, FAKE, None) == SHAPE
     assert sfh(None, 16, E5M2T, 0, FAKE, None) == NULL
     assert sfh(FAKE, 16, E5M2T, 0, FAKE + 1, None) == ALIGN
+
+
+def fwd(x, w, y=FAKE):
+    ref = lambda t: ctypes.byref(t) if t is not None else None  # noqa: E731
+    return lp.lib.lp_linear_fwd(ref(x), ref(w), y, None)
+
+
+@pytest.mark.parametrize("x,w,y,expect", [
+    (None, q("mxfp4", 64, 128), FAKE, NULL),
+    (q("mxfp4", 64, 128), q("mxfp4", 32, 128), None, NULL),
+    (q("mxfp4", 64, 128), q("mxfp8", 32, 128), FAKE, FORMAT),       # formats must agree
+    (q("bf16", 64, 128), q("bf16", 32, 128), FAKE, FORMAT),
+    (q("nvfp4", 64, 128), q("nvfp4", 32, 128), FAKE, FORMAT),
+    (q("mxfp8", 64, 128, axis=-2), q("mxfp8", 32, 128), FAKE, FORMAT),
+    (q("mxfp4", 64, 96), q("mxfp4", 32, 96), FAKE, SHAPE),          # MXFP4: K % 128
+    (q("mxfp8", 64, 96), q("mxfp8", 32, 96), FAKE, SHAPE),          # MXFP8: K % 64
+    (q("mxfp4", 64, 128), q("mxfp4", 40, 128), FAKE, SHAPE),        # N % 16
+    (q("mxfp4", 64, 128), q("mxfp4", 32, 256), FAKE, SHAPE),        # K disagrees
+    (q("mxfp4", 64, 128), q("mxfp4", 32, 128, batch=2), FAKE, SHAPE),
+    (q("mxfp4", 64, 128), q("mxfp4", 32, 128), FAKE + 8, ALIGN),
+    (q("mxfp4", 0, 128, codes=None, scales=None), q("mxfp4", 32, 128), None, OK),   # M = 0: nothing to do
+])
+def test_linear_fwd_rejects(x, w, y, expect):
+    assert fwd(x, w, y) == expect
+
+
+def test_grouped_fwd_rejects():
+    x, w = q("mxfp4", 64, 128), q("mxfp4", 32, 128, batch=4)
+    call = lambda off, G: lp.lib.lp_grouped_fwd(ctypes.byref(x), ctypes.byref(w), off, G, FAKE, None)  # noqa: E731
+    assert call(FAKE, 0) == SHAPE
+    assert call(FAKE, 3) == SHAPE            # w batch must equal groups
+    assert call(None, 4) == NULL
+    assert call(FAKE + 2, 4) == ALIGN
 
 
 def test_grouped_rejects_row_scaled_grad():

@@ -114,7 +114,12 @@ def _pt_dx_one_scale(g_codes, g_elem, g_scale, w_codes, w_elem, w_scale):
     return _orig_pt_dx(g_codes, g_elem, g_scale, w_codes, w_elem, 1.0)
 
 
+def _fwd_no_transpose(x_bits, w_bits):
+    return O._f64(x_bits) @ O._f64(w_bits).reshape(O._f64(w_bits).shape[::-1])
+
+
 MUTATIONS = {
+    "forward multiplies W untransposed": (O, "linear_fwd", _fwd_no_transpose),
     "per-tensor quantization multiplies by the scale": (PT, "quantize", _pt_quant_multiplies),
     "per-tensor quantization without saturation": (PT, "round_to_fp8", _pt_no_saturation),
     "scale ignores the margin": (PT, "scale_from_history", _pt_scale_no_margin),

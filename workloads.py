@@ -33,6 +33,9 @@ grouped backward of "perf: defer mxfp8 backward quantization"):
                  sizes: 4096 tokens and the FFN up-projection (1536 -> 6144) of
                  a GPT-style block with d = 1536 (12 * 24 * 1536^2 = 0.68B over
                  24 blocks) stand in for it.
+  mxfp4_forward  the forward the FP4 backward pairs with ("Add Autograd Backward
+                 Support for FP4 GEMM Custom Ops"): X 8192x4096 N(0,1) and W
+                 4096x4096 N(0,1), both MXFP4 along K; y = X @ W^T
 
 Every tensor has its own PCG64 stream: SeedSequence(entropy=1000 + config
 number, spawn_key=(tensor id,)), so a tensor's values do not depend on which
@@ -82,6 +85,7 @@ WORKLOADS = {
                                groups=64, w_sigma=0.02, need_dw=False, routing="zipf"),
     "mxfp8_dense": Workload("mxfp8_dense", 6, "mxfp8", M=8192, N=4096, K=4096, w_sigma=0.02),
     "fp8_hybrid": Workload("fp8_hybrid", 7, "fp8t", M=4096, N=6144, K=1536, w_sigma=0.02),
+    "mxfp4_forward": Workload("mxfp4_forward", 8, "mxfp4", M=8192, N=4096, K=4096, need_dx=False, need_dw=False),
 }
 
 AMAX_RING = 16               # amax history length of the delayed-scaling recipe
