@@ -105,20 +105,18 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     const int kb = k0 * kRowBytes / KS;                          // byte offset of the slab in a row
     if constexpr (u < 4) {
       const Rsrc r = make_rsrc(pc + kb, prows * ldp - kb);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(sb + 1024 * (4 * wave + u)), 16, p_off,
-                                               16 * u * ldp, 0, 0);
+      dma<16>(r, (lds_void*)(sb + 1024 * (4 * wave + u)), p_off, 16 * u * ldp);
     } else if constexpr (u < 8) {
       constexpr int v = u - 4;
       const Rsrc r = make_rsrc(qc + kb, qrows * ldq - kb);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(sb + kOpBytes + 1024 * (4 * wave + v)), 16, q_off,
-                                               16 * v * ldq, 0, 0);
+      dma<16>(r, (lds_void*)(sb + kOpBytes + 1024 * (4 * wave + v)), q_off, 16 * v * ldq);
     } else {
       const Rsrc r = u == 8 ? ps_r : qs_r;
       uint8_t* dst = sb + 2 * kOpBytes + (u == 8 ? 0 : kScaleBytes) + 256 * wave;
       if constexpr (kFp4)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, u == 8 ? ps_off : qs_off, k0 / 32, 0, 0);
+        dma<4>(r, (lds_void*)dst, u == 8 ? ps_off : qs_off, k0 / 32);
       else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 2, u == 8 ? ps_off : qs_off, k0 / 32, 0, 0);
+        dma<2>(r, (lds_void*)dst, u == 8 ? ps_off : qs_off, k0 / 32);
     }
   };
 

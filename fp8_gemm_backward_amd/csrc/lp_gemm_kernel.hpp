@@ -136,6 +136,30 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* base, int64_t bytes) {
   bytes = bytes < 0 ? 0 : (bytes > 0x7FFFFFFF ? 0x7FFFFFFF : bytes);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
+// Direct global -> LDS load of kSize bytes per lane (written at M0 = dst,
+// lane i at dst + kSize * i; 1- and 2-byte loads write a zero-extended dword
+// at dst + 4 i), issued as inline assembly.  The compiler's waitcnt pass
+// cannot tell apart the LDS stages that such loads fill across loop
+// iterations, and would make every LDS read wait for all of them; the
+// kernels that use this wait for their loads themselves (barrier_vm) before
+// reading what they wrote.
+template <int kSize>
+__device__ __forceinline__ void dma(Rsrc r, lds_void* dst, int32_t voff, int32_t soff) {
+  const uint32_t m0 = (uint32_t)(size_t)dst;
+  if constexpr (kSize == 16)
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(m0), "v"(voff), "s"(r), "s"(soff)
+                 : "memory", "m0");
+  else if constexpr (kSize == 4)
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds" ::"s"(m0), "v"(voff), "s"(r), "s"(soff)
+                 : "memory", "m0");
+  else if constexpr (kSize == 2)
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_ushort %1, %2, %3 offen lds" ::"s"(m0), "v"(voff), "s"(r), "s"(soff)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_ubyte %1, %2, %3 offen lds" ::"s"(m0), "v"(voff), "s"(r), "s"(soff)
+                 : "memory", "m0");
+}
+
 __device__ __forceinline__ u32x4 bload16(Rsrc r, int32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }

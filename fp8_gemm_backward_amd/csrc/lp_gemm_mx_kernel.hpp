@@ -198,24 +198,20 @@ __device__ __forceinline__ void mx_tile(const Params& p, int hw, uint8_t* st0, u
     constexpr int u = decltype(ui)::value;
     if constexpr (u < 4 && kDW) {
       const Rsrc r = make_rsrc(p.P.codes + (int64_t)k0 * ldp, (int64_t)(kend - k0) * ldp);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(sb + 1024 * (4 * wave + u)), 16,
-                                               (u & 1) ? pq_off_odd : pq_off_even, 4 * u * ldp, 0, 0);
+      dma<16>(r, (lds_void*)(sb + 1024 * (4 * wave + u)), (u & 1) ? pq_off_odd : pq_off_even, 4 * u * ldp);
     } else if constexpr (u < 4) {
       const Rsrc r = make_rsrc(pc + k0, prow_bytes - k0);
       const bool out = k0 + p_col >= kend;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(sb + 1024 * (4 * wave + u)), 16, out ? kOOB : p_off,
-                                               16 * u * ldp, 0, 0);
+      dma<16>(r, (lds_void*)(sb + 1024 * (4 * wave + u)), out ? kOOB : p_off, 16 * u * ldp);
     } else if constexpr (u < 8) {
       constexpr int v = u - 4;
       const Rsrc r = make_rsrc(qc + (int64_t)k0 * ldq, (int64_t)(kend - k0) * ldq);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(sb + kPBytes + 1024 * (4 * wave + v)), 16,
-                                               (v & 1) ? q_off_odd : q_off_even, 4 * v * ldq, 0, 0);
+      dma<16>(r, (lds_void*)(sb + kPBytes + 1024 * (4 * wave + v)), (v & 1) ? q_off_odd : q_off_even, 4 * v * ldq);
     } else {
       constexpr int v = u - 8;
       const bool out = k0 + 32 * (v / 2) >= kend;
       const int32_t so = 16 * (v & 1) * s_rstep + ((k0 >> 5) + v / 2) * s_bstep;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rsrc, (lds_void*)(sb + s_dst + 256 * v), 1,
-                                               out ? kOOB : s_lane, so, 0, 0);
+      dma<1>(s_rsrc, (lds_void*)(sb + s_dst + 256 * v), out ? kOOB : s_lane, so);
     }
   };
   // Chunk mode: scale blocks [kb, kb + 16) of the tile, kb = k0 / 32 of the
@@ -224,13 +220,11 @@ __device__ __forceinline__ void mx_tile(const Params& p, int hw, uint8_t* st0, u
   auto issue_chunk = [&](uint8_t* cb, int k0) {
     const int kb = k0 >> 5;
     if constexpr (kDW)   // gradient scales [M / 32][N]: block row 4 w + i / 16, columns p0 + 16 (i % 16)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ps_r, (lds_void*)(cb + 1024 * wave), 16,
-                                               (4 * wave + lane / 16) * sldp + t.p0 + 16 * (lane & 15), kb * sldp, 0, 0);
+      dma<16>(ps_r, (lds_void*)(cb + 1024 * wave), (4 * wave + lane / 16) * sldp + t.p0 + 16 * (lane & 15), kb * sldp);
     else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ps_r, (lds_void*)(cb + 1024 * wave), 16, (64 * wave + lane) * sldp,
-                                               kb, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(qs_r, (lds_void*)(cb + XBP * 16 + 1024 * wave), 16,
-                                             (4 * wave + lane / 16) * sldq + t.q0 + 16 * (lane & 15), kb * sldq, 0, 0);
+      dma<16>(ps_r, (lds_void*)(cb + 1024 * wave), (64 * wave + lane) * sldp, kb);
+    dma<16>(qs_r, (lds_void*)(cb + XBP * 16 + 1024 * wave), (4 * wave + lane / 16) * sldq + t.q0 + 16 * (lane & 15),
+            kb * sldq);
   };
 
   // Fragment addresses inside a stage.  Gradient fragment f of lane l: row
