@@ -129,11 +129,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   const int32_t psa = 2 * kOpBytes + (wp * FWP + r32) * 4, qsa = 2 * kOpBytes + kScaleBytes + (wq * FWQ + r32) * 4;
 
   i32x4 pf[2][FFP][2], qf[2][FFQ][2];
-  int32_t psc[2][FFP], qsc[2][FFQ];
+  uint32_t psc[2][FFP], qsc[2][FFQ];
   constexpr int NREAD = 2 * FFP + 2 * FFQ + FFP + FFQ;
   // Read r of the slab in stage sb into register set SET: x chunks, w
-  // chunks, then the scale dwords shifted so that this lane's block h is the
-  // low byte (E2M1: block 2 + h is then byte 2).
+  // chunks, then the scale dwords.  Nothing here computes on a loaded value:
+  // an operation on one would make the wave wait for every LDS read in
+  // flight in the middle of the MFMA stream.
   auto read = [&](auto ri, auto seti, const uint8_t* sb) {
     constexpr int r = decltype(ri)::value, SET = decltype(seti)::value;
     if constexpr (r < 2 * FFP) {
@@ -144,11 +145,21 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
       qf[SET][j][e] = *reinterpret_cast<const i32x4*>(sb + qa + (e ? a1 : a0) + j * 32 * kRowBytes);
     } else if constexpr (r < 2 * FFP + 2 * FFQ + FFP) {
       constexpr int f = r - 2 * FFP - 2 * FFQ;
-      psc[SET][f] = (int32_t)(*reinterpret_cast<const uint32_t*>(sb + psa + f * 32 * 4) >> (8 * hh));
+      psc[SET][f] = *reinterpret_cast<const uint32_t*>(sb + psa + f * 32 * 4);
     } else {
       constexpr int j = r - 2 * FFP - 2 * FFQ - FFP;
-      qsc[SET][j] = (int32_t)(*reinterpret_cast<const uint32_t*>(sb + qsa + j * 32 * 4) >> (8 * hh));
+      qsc[SET][j] = *reinterpret_cast<const uint32_t*>(sb + qsa + j * 32 * 4);
     }
+  };
+  // At the top of a slab (its reads complete): the scale dwords shifted so
+  // that this lane's block h is the low byte (E2M1: block 2 + h is byte 2).
+  int32_t ps[FFP], qs[FFQ];
+  auto scales = [&](auto seti) {
+    constexpr int SET = decltype(seti)::value;
+#pragma unroll
+    for (int i = 0; i < FFP; ++i) ps[i] = (int32_t)(psc[SET][i] >> (8 * hh));
+#pragma unroll
+    for (int j = 0; j < FFQ; ++j) qs[j] = (int32_t)(qsc[SET][j] >> (8 * hh));
   };
 
   f32x16 acc[FFP][FFQ];
@@ -166,13 +177,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     if constexpr (kFp4) {
       constexpr int e = m / (FFP * FFQ);                         // k 0..63 or 64..127 of the slab
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(low_half(qf[SET][j][e]), low_half(pf[SET][i][e]),
-                                                                   acc[i][j], FMT, FMT, 2 * e, qsc[SET][j], 2 * e,
-                                                                   psc[SET][i]);
+                                                                   acc[i][j], FMT, FMT, 2 * e, qs[j], 2 * e, ps[i]);
     } else {
       const i32x8 qv = __builtin_shufflevector(qf[SET][j][0], qf[SET][j][1], 0, 1, 2, 3, 4, 5, 6, 7);
       const i32x8 pv = __builtin_shufflevector(pf[SET][i][0], pf[SET][i][1], 0, 1, 2, 3, 4, 5, 6, 7);
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qv, pv, acc[i][j], FMT, FMT, 0, qsc[SET][j], 0,
-                                                                   psc[SET][i]);
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qv, pv, acc[i][j], FMT, FMT, 0, qs[j], 0, ps[i]);
     }
   };
 
@@ -188,7 +197,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   }
 
   // Slab k = kt + J (stage J % 4): publish slab k+1, issue slab k+3 into the
-  // stage of slab k-1, multiply slab k while reading slab k+1's fragments.
+  // stage of slab k-1 (all at once: measured faster than spreading them over
+  // the MFMAs), multiply slab k while reading slab k+1's fragments.
   auto slab = [&](auto ji, int k) {
     constexpr int J = decltype(ji)::value;
     constexpr int CUR = J & 1, NXT = CUR ^ 1;
@@ -196,12 +206,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     uint8_t* const nxt = stage(IC<J + 1>{});
     uint8_t* const dst = stage(IC<J + 3>{});
     const int k3 = kbeg + (k + 3) * KS;
+    scales(IC<CUR>{});
+    static_for<T>([&](auto ui) { issue(ui, dst, k3); });         // all of slab k+3's loads first
     static_for<NM>([&](auto mi) {
       constexpr int m = decltype(mi)::value;
       mfma(mi, IC<CUR>{});
-      static_for<T>([&](auto ui) {
-        if constexpr (decltype(ui)::value == m) issue(ui, dst, k3);
-      });
       static_for<NREAD>([&](auto ri) {
         if constexpr (decltype(ri)::value * NM / NREAD == m) read(ri, IC<NXT>{}, nxt);
       });

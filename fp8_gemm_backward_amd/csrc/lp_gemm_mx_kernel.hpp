@@ -264,6 +264,7 @@ __device__ __forceinline__ void mx_tile(const Params& p, int hw, uint8_t* st0, u
 
   i32x8 pf[2][XFP], qf[2][XFQ];
   int32_t psc[2][XFP], qsc[2][XFQ];
+  bool sval[2];                                                  // chunk mode: this lane's scale block exists
   // Read r of the fragments of the slab at contraction k0 (stage sb, slab
   // position S8 in its scale chunk cb) into register set SET: gradient
   // fragments (two 16-byte reads each), weight fragments (four transposing
@@ -301,16 +302,29 @@ __device__ __forceinline__ void mx_tile(const Params& p, int hw, uint8_t* st0, u
         else qsc[SET][f] = (int)v[f];
       }
     } else {
-      const bool valid = k0 + 32 * hh < kend;                    // this lane's scale block exists
+      // Raw bytes: masking them here would make the wave wait for every LDS
+      // read in flight in the middle of the MFMA stream; `scales` masks them
+      // at the top of the slab that uses them.
+      if constexpr (r == NFRAG) sval[SET] = k0 + 32 * hh < kend;
       if constexpr (r < NFRAG + XFP) {
         constexpr int f = r - NFRAG;
-        const int b = kDW ? cb[psa + 32 * f + 2 * S8 * XBP] : cb[psa + 16 * 32 * f + 2 * S8];
-        psc[SET][f] = valid ? b : 0;
+        psc[SET][f] = kDW ? cb[psa + 32 * f + 2 * S8 * XBP] : cb[psa + 16 * 32 * f + 2 * S8];
       } else {
         constexpr int j = r - NFRAG - XFP;
-        const int b = cb[qsa + 32 * j + 2 * S8 * XBQ];
-        qsc[SET][j] = valid ? b : 0;
+        qsc[SET][j] = cb[qsa + 32 * j + 2 * S8 * XBQ];
       }
+    }
+  };
+  // Chunk mode, at the top of a slab: scale blocks at or past the end of the
+  // contraction are zeroed (their codes are zero, and a NaN scale would turn
+  // the zero products into NaN).
+  auto scales = [&](auto seti) {
+    constexpr int SET = decltype(seti)::value;
+    if constexpr (kChunk) {
+#pragma unroll
+      for (int i = 0; i < XFP; ++i) psc[SET][i] = sval[SET] ? psc[SET][i] : 0;
+#pragma unroll
+      for (int j = 0; j < XFQ; ++j) qsc[SET][j] = sval[SET] ? qsc[SET][j] : 0;
     }
   };
 
@@ -361,6 +375,7 @@ __device__ __forceinline__ void mx_tile(const Params& p, int hw, uint8_t* st0, u
     const int k3 = kbeg + (k + 3) * XBK;
     const int k1 = kbeg + (k + 1) * XBK;
     if constexpr (kChunk && S8 == 4) issue_chunk(chunkbuf(IC<J / kChunkSlabs + 1>{}), kbeg + (k + 4) * XBK);
+    scales(IC<CUR>{});
     static_for<NM>([&](auto mi) {
       constexpr int m = decltype(mi)::value;
       mfma(mi, IC<CUR>{});
