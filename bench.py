@@ -9,7 +9,7 @@ synthetic input already resident in HBM:
   mxfp4_grouped   lp_grouped_bwd: dX and dW over 8 experts, MXFP4 X and W
   mxfp8_deferred  lp_mx_quant(grad, -1) + lp_mx_quant(W, -2) + lp_grouped_bwd dX
   mxfp8_dense     lp_mx_quant_dual(grad) + lp_mx_quant(W, -2) + lp_mx_quant(X, -2) + lp_linear_bwd dX, dW
-  fp8_hybrid      lp_scale_from_history(grad ring) + lp_tensor_quant(grad -> E5M2, amax into the ring)
+  fp8_hybrid      lp_tensor_quant_delayed(grad -> E5M2 with the ring's scale, amax into the ring)
                   + lp_linear_bwd dX, dW against E4M3 X and W (per-tensor scales)
   mxfp4_forward   lp_linear_fwd: y = X @ W^T, MXFP4 X 8192x4096 and W 4096x4096 (the forward
                   the FP4 backward pairs with, on the block-scaled FP4 MFMA)
@@ -237,8 +237,7 @@ def build(lp, name: str):
             dx = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
             dw = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
             sets.append((g, ring, gq, saved[0], saved[1], dx, dw))
-        phases.append(Phase("scale_from_history grad", "scale_from_history"))
-        phases.append(Phase("tensor_quant grad E5M2", "tensor_quant", nbytes=M * N * 3))
+        phases.append(Phase("tensor_quant_delayed grad E5M2", "tensor_quant", nbytes=M * N * 3))
         # dX and dW of the one E5M2 gradient in one call: one launch of both
         phases.append(Phase("linear_bwd dX+dW", "pt_pair_kernel", flops=4.0 * M * N * K, peak=PEAK_FP8_TFLOPS))
 
@@ -247,11 +246,8 @@ def build(lp, name: str):
             slot = (i // len(sets)) % W.AMAX_RING
             ts = []
             ev = _events(stream)
-            lp.lp_scale_from_history(ring, "fp8t_e5m2", scale=gq.tensor_scale, stream=stream)
-            ts.append(ev.stop(stream))
-            ev = _events(stream)
-            lp.lp_tensor_quant(g, "fp8t_e5m2", gq.tensor_scale, amax=ring[slot:slot + 1], codes=gq.codes,
-                               stream=stream)
+            lp.lp_tensor_quant_delayed(g, "fp8t_e5m2", ring, slot, codes=gq.codes, scale=gq.tensor_scale,
+                                       stream=stream)
             ts.append(ev.stop(stream))
             ev = _events(stream)
             lp.lp_linear_bwd(gq, xq, wq, grad_x=dx, grad_w=dw, stream=stream)

@@ -58,13 +58,14 @@ def _load() -> ctypes.CDLL:
     lib.lp_tensor_amax.argtypes = [v, i64, v, v]
     lib.lp_tensor_quant.argtypes = [v, i64, i32, v, v, v, v]
     lib.lp_scale_from_history.argtypes = [v, i32, i32, i32, v, v]
+    lib.lp_tensor_quant_delayed.argtypes = [v, i64, i32, v, i32, i32, i32, v, v, v]
     lib.lp_linear_fwd.argtypes = [P, P, v, v]
     lib.lp_grouped_fwd.argtypes = [P, P, v, i64, v, v]
     lib.lp_status_string.argtypes = [i32]
     lib.lp_status_string.restype = ctypes.c_char_p
     for f in ("lp_dequant", "lp_mx_quant", "lp_mx_quant_dual", "lp_linear_bwd", "lp_grouped_bwd",
               "lp_linear_bwd_workspace", "lp_linear_bwd_ws", "lp_tensor_amax", "lp_tensor_quant",
-              "lp_scale_from_history", "lp_linear_fwd", "lp_grouped_fwd"):
+              "lp_scale_from_history", "lp_linear_fwd", "lp_grouped_fwd", "lp_tensor_quant_delayed"):
         getattr(lib, f).restype = ctypes.c_int32
     return lib
 
@@ -189,6 +190,22 @@ def lp_tensor_quant(src: torch.Tensor, fmt: str, scale: torch.Tensor, amax: Opti
         codes = torch.empty(shape, dtype=torch.uint8, device=src.device)
     _check(lib.lp_tensor_quant(src.data_ptr(), src.numel(), FMT[fmt], scale.data_ptr(), codes.data_ptr(),
                                None if amax is None else amax.data_ptr(), _stream(stream)), "lp_tensor_quant")
+    return QTensor(fmt, codes, None, scale, shape, -1)
+
+
+def lp_tensor_quant_delayed(src: torch.Tensor, fmt: str, history: torch.Tensor, slot: int, margin: int = 0,
+                            codes: Optional[torch.Tensor] = None, scale: Optional[torch.Tensor] = None,
+                            stream=None) -> QTensor:
+    """Delayed scaling in one call: scale from `history` (float32 device
+    ring), quantization with it, the input's amax into history[slot]."""
+    shape = tuple(src.shape) if src.dim() == 3 else (1,) + tuple(src.shape)
+    if codes is None:
+        codes = torch.empty(shape, dtype=torch.uint8, device=src.device)
+    if scale is None:
+        scale = torch.empty(1, dtype=torch.float32, device=src.device)
+    _check(lib.lp_tensor_quant_delayed(src.data_ptr(), src.numel(), FMT[fmt], history.data_ptr(), history.numel(),
+                                       slot, margin, codes.data_ptr(), scale.data_ptr(), _stream(stream)),
+           "lp_tensor_quant_delayed")
     return QTensor(fmt, codes, None, scale, shape, -1)
 
 

@@ -157,6 +157,18 @@ lp_status lp_scale_from_history(const float* history, int32_t len, int32_t fmt, 
   return hip_status(lp::launch_scale_from_history(history, len, fmt, margin, scale, static_cast<hipStream_t>(stream)));
 }
 
+lp_status lp_tensor_quant_delayed(const void* src, int64_t n, int32_t dst_fmt, float* history, int32_t len,
+                                  int32_t slot, int32_t margin, void* codes, float* scale, void* stream) {
+  if (!is_fp8t(dst_fmt)) return LP_ERR_FORMAT;
+  if (n < 0 || n % 8 || n / 8 >= kMaxUnits) return LP_ERR_SHAPE;
+  if (len < 1 || len > 65536 || slot < 0 || slot >= len || margin < -64 || margin > 64) return LP_ERR_SHAPE;
+  if (history == nullptr || scale == nullptr || (n > 0 && (src == nullptr || codes == nullptr))) return LP_ERR_NULL;
+  if (scale >= history && scale < history + len) return LP_ERR_SHAPE;   // the scale must not live in the ring
+  if (!aligned(src, 16) || !aligned(codes, 16) || !aligned(history, 4) || !aligned(scale, 4)) return LP_ERR_ALIGN;
+  return hip_status(lp::launch_tensor_quant_delayed(src, n, dst_fmt, history, len, slot, margin, codes, scale,
+                                                    static_cast<hipStream_t>(stream)));
+}
+
 static lp_status run_bwd(const lp_qtensor* grad, const lp_qtensor* x, const lp_qtensor* w, const int32_t* offsets,
                          int64_t groups, void* grad_x, void* grad_w, void* ws, size_t ws_bytes, void* stream) {
   const int64_t M = grad->rows, N = grad->cols;

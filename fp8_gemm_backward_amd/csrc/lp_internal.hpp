@@ -46,6 +46,10 @@ hipError_t launch_tensor_quant(const void* src, int64_t n, int fmt, const float*
 hipError_t launch_scale_from_history(const float* hist, int32_t len, int fmt, int32_t margin, float* scale,
                                      hipStream_t stream);
 hipError_t launch_tensor_dequant(const lp_qtensor& t, void* dst, hipStream_t stream);
+// Scale from hist (then hist[slot] cleared), quantization with that scale,
+// the input's amax into hist[slot].
+hipError_t launch_tensor_quant_delayed(const void* src, int64_t n, int fmt, float* hist, int32_t len, int32_t slot,
+                                       int32_t margin, void* codes, float* scale, hipStream_t stream);
 
 // One backward contraction (grad_X or grad_W) over `groups` groups.
 //   dx: C[m][k] = sum_n grad[m][n] * W[g][n][k]  (groups partition the rows m)

@@ -217,9 +217,11 @@ __global__ __launch_bounds__(kAmax ? kRedThreads : kThreads) void tensor_quant(
 // scale = (max(history) / FP8_MAX) / 2^margin, at least 1e-12, NaN kept.
 // One workgroup: a strided maximum per lane, then across the workgroup.  The
 // running maximum starts at 0: a history whose maximum is at most 0 gives
-// the floor either way.
-__global__ __launch_bounds__(kThreads) void scale_from_history(const float* __restrict__ hist, int32_t len, bool e5m2,
-                                                               int32_t margin, float* __restrict__ scale) {
+// the floor either way.  `clear`, when not null, is a history slot that is
+// zeroed after every entry has been read (the slot the next amax goes to).
+__global__ __launch_bounds__(kThreads) void scale_from_history(const float* hist, int32_t len, bool e5m2,
+                                                               int32_t margin, float* __restrict__ scale,
+                                                               uint32_t* clear) {
   __shared__ float s_peak[kThreads / 64];
   __shared__ int s_nan[kThreads / 64];
   float peak = 0.0f;
@@ -248,6 +250,7 @@ __global__ __launch_bounds__(kThreads) void scale_from_history(const float* __re
   float s = peak / fp8_max(e5m2);
   s = s / __builtin_ldexpf(1.0f, margin);
   *scale = nan ? __builtin_nanf("") : (s < 1e-12f ? 1e-12f : s);
+  if (clear != nullptr) *clear = 0u;                             // every lane's reads are behind the barrier
 }
 
 // Decode: unit u = 8 codes -> 8 bf16, bf16_rne(fp32_rne(code * scale)), a
@@ -303,10 +306,10 @@ hipError_t launch_tensor_amax(const void* src, int64_t n, float* amax, hipStream
   return hipGetLastError();
 }
 
-hipError_t launch_tensor_quant(const void* src, int64_t n, int fmt, const float* scale, void* codes, float* amax,
-                               hipStream_t stream) {
+// The quantization proper; `amax`, when not null, must already be zero.
+static hipError_t quant_kernels(const void* src, int64_t n, int fmt, const float* scale, void* codes, float* amax,
+                                hipStream_t stream) {
   uint32_t* a = reinterpret_cast<uint32_t*>(amax);
-  if (a != nullptr) zero_u32<<<1, 1, 0, stream>>>(a);
   const uint32_t nunits = (uint32_t)(n / 8);
   if (nunits == 0) return hipGetLastError();
   auto s = static_cast<const u32x4*>(src);
@@ -322,10 +325,23 @@ hipError_t launch_tensor_quant(const void* src, int64_t n, int fmt, const float*
   return hipGetLastError();
 }
 
+hipError_t launch_tensor_quant(const void* src, int64_t n, int fmt, const float* scale, void* codes, float* amax,
+                               hipStream_t stream) {
+  if (amax != nullptr) zero_u32<<<1, 1, 0, stream>>>(reinterpret_cast<uint32_t*>(amax));
+  return quant_kernels(src, n, fmt, scale, codes, amax, stream);
+}
+
 hipError_t launch_scale_from_history(const float* hist, int32_t len, int fmt, int32_t margin, float* scale,
                                      hipStream_t stream) {
-  scale_from_history<<<1, kThreads, 0, stream>>>(hist, len, fmt == LP_FP8T_E5M2, margin, scale);
+  scale_from_history<<<1, kThreads, 0, stream>>>(hist, len, fmt == LP_FP8T_E5M2, margin, scale, nullptr);
   return hipGetLastError();
+}
+
+hipError_t launch_tensor_quant_delayed(const void* src, int64_t n, int fmt, float* hist, int32_t len, int32_t slot,
+                                       int32_t margin, void* codes, float* scale, hipStream_t stream) {
+  uint32_t* rec = reinterpret_cast<uint32_t*>(hist + slot);
+  scale_from_history<<<1, kThreads, 0, stream>>>(hist, len, fmt == LP_FP8T_E5M2, margin, scale, rec);
+  return quant_kernels(src, n, fmt, scale, codes, hist + slot, stream);
 }
 
 hipError_t launch_tensor_dequant(const lp_qtensor& t, void* dst, hipStream_t stream) {

@@ -232,6 +232,26 @@ lp_status lp_scale_from_history(const float* history, int32_t len, int32_t fmt, 
                                 void* stream);
 
 /*
+ * lp_tensor_quant_delayed - one delayed-scaling quantization step: the
+ * scale from an amax history, quantization with it, and the input's amax
+ * recorded into the history.
+ *
+ * Cites: "AstrAI fp8.py" (DelayedScaling: the scale of a step comes from the
+ * largest amax of the ring; the step's amax is then recorded at the ring's
+ * index; _LinearFp8.backward quantizes the gradient this way).
+ *
+ * src_bf16, n, dst_fmt, dst_codes: as lp_tensor_quant.
+ * history  device fp32 [len], 1 <= len <= 65536; slot: 0 <= slot < len (the
+ *          caller's ring index); margin: as lp_scale_from_history.
+ * scale    device fp32, outside history: receives the step's scale.
+ * Results are bit-identical to lp_scale_from_history(history, len, ...,
+ * scale) followed by lp_tensor_quant(src, ..., scale, codes, history + slot):
+ * the scale sees history[slot] before it is overwritten.  Two launches.
+ */
+lp_status lp_tensor_quant_delayed(const void* src_bf16, int64_t n, int32_t dst_fmt, float* history, int32_t len,
+                                  int32_t slot, int32_t margin, void* dst_codes, float* scale, void* stream);
+
+/*
  * lp_linear_bwd - backward of a linear layer y = x @ W^T with saved
  * block-scaled operands.
  *

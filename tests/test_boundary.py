@@ -16,7 +16,8 @@ def test_library_exports_every_header_function():
     names = lp.header_functions()
     assert set(names) == {"lp_dequant", "lp_mx_quant", "lp_linear_bwd", "lp_grouped_bwd", "lp_status_string",
                           "lp_linear_bwd_workspace", "lp_linear_bwd_ws", "lp_mx_quant_dual", "lp_tensor_amax",
-                          "lp_tensor_quant", "lp_scale_from_history", "lp_linear_fwd", "lp_grouped_fwd"}
+                          "lp_tensor_quant", "lp_scale_from_history", "lp_linear_fwd", "lp_grouped_fwd",
+                          "lp_tensor_quant_delayed"}
     for n in names:
         assert hasattr(lp.lib, n), n
 
@@ -105,6 +106,21 @@ E4M3T, E5M2T = lp.FMT["fp8t_e4m3"], lp.FMT["fp8t_e5m2"]
 ])
 def test_tensor_quant_rejects(args, expect):
     assert lp.lib.lp_tensor_quant(*args, None) == expect
+
+
+def test_tensor_quant_delayed_rejects():
+    f = lp.lib.lp_tensor_quant_delayed
+    ring = 0x20000
+    assert f(FAKE, 64, lp.FMT["mxfp8"], ring, 16, 0, 0, FAKE, FAKE, None) == FORMAT
+    assert f(FAKE, 12, E5M2T, ring, 16, 0, 0, FAKE, FAKE, None) == SHAPE      # n % 8
+    assert f(FAKE, 64, E5M2T, ring, 16, 16, 0, FAKE, FAKE, None) == SHAPE     # slot past the ring
+    assert f(FAKE, 64, E5M2T, ring, 16, -1, 0, FAKE, FAKE, None) == SHAPE
+    assert f(FAKE, 64, E5M2T, ring, 0, 0, 0, FAKE, FAKE, None) == SHAPE       # empty ring
+    assert f(FAKE, 64, E5M2T, ring, 16, 0, 65, FAKE, FAKE, None) == SHAPE     # margin
+    assert f(FAKE, 64, E5M2T, ring, 16, 0, 0, FAKE, ring + 8, None) == SHAPE  # scale inside the ring
+    assert f(FAKE, 64, E5M2T, None, 16, 0, 0, FAKE, FAKE, None) == NULL
+    assert f(FAKE, 64, E5M2T, ring, 16, 0, 0, FAKE, None, None) == NULL
+    assert f(FAKE, 64, E5M2T, ring, 16, 0, 0, FAKE + 8, FAKE, None) == ALIGN
 
 
 def test_tensor_amax_and_scale_reject():

@@ -151,6 +151,36 @@ def test_quant_records_amax_into_ring_slot(lp):
     assert_bits_equal(q.codes.cpu().numpy().reshape(-1), PT.quantize(bits, "e5m2", want_scale).reshape(-1), "codes")
 
 
+@pytest.mark.parametrize("fmt", ["fp8t_e5m2", "fp8t_e4m3"])
+def test_quant_delayed_equals_scale_then_quant(lp, fmt):
+    """20 delayed-scaling steps on a 16-entry ring: the one-call step and the
+    two-call sequence agree bit for bit (codes, scale, ring) every step, and
+    the first step equals the oracle's."""
+    L, shape = W.AMAX_RING, (96, 512)
+    ring_a = torch.zeros(L, device="cuda")
+    first = W.bf16_bits(W.normal_f32(47, "grad", shape, 1e-3))
+    ring_a.copy_(torch.tensor([PT.amax(first)] * L, device="cuda"))
+    ring_b = ring_a.clone()
+    hist = ring_a.cpu().numpy().copy()
+    for step in range(20):
+        bits = W.bf16_bits(W.normal_f32(47, "grad", shape, 10.0 ** ((step % 7) - 4)))
+        src = bf16_dev(bits)
+        slot = step % L
+        qa = lp.lp_tensor_quant_delayed(src, fmt, ring_a, slot)
+        sb = lp.lp_scale_from_history(ring_b, fmt)
+        qb = lp.lp_tensor_quant(src, fmt, sb, amax=ring_b[slot:slot + 1])
+        torch.cuda.synchronize()
+        assert torch.equal(qa.codes, qb.codes), f"codes differ at step {step}"
+        assert torch.equal(qa.tensor_scale.view(torch.int32), sb.view(torch.int32)), f"scale differs at step {step}"
+        assert torch.equal(ring_a.view(torch.int32), ring_b.view(torch.int32)), f"ring differs at step {step}"
+        if step == 0:
+            s = PT.scale_from_history(hist, ELEM[fmt])
+            _same_f32(qa.tensor_scale, s, "oracle scale")
+            assert_bits_equal(qa.codes.cpu().numpy().reshape(shape), PT.quantize(bits, ELEM[fmt], s), "oracle codes")
+            PT.record(hist, slot, PT.amax(bits))
+            _same_f32(ring_a, hist, "oracle ring")
+
+
 def _pt_operand(lp, number, tensor, shape, sigma, fmt, outliers=False):
     """bf16 values -> the oracle's per-tensor codes with the dynamic scale of
     their amax; returns (descriptor on the GPU, codes, scale)."""
