@@ -166,7 +166,7 @@ def build(lp, name: str):
         phases.append(Phase("mx_quant grad", "mx_quant_cols", nbytes=M * N * (2 + 1 + 1 / 32)))
         phases.append(Phase("mx_quant W", "mx_quant_rows", nbytes=w.groups * N * K * (2 + 1 + 1 / 32)))
         # MXFP8 x MXFP8 with both scales along the contraction: block-scaled FP8 MFMA
-        phases.append(Phase("grouped_bwd dX", "mx_dx_kernel", flops=2.0 * M * N * K, peak=PEAK_FP8_TFLOPS))
+        phases.append(Phase("grouped_bwd dX", "fp8_mfma_kernel", flops=2.0 * M * N * K, peak=PEAK_FP8_TFLOPS))
 
         def step(i, stream):
             g, wt, gq, wq, dx = sets[0]
@@ -193,8 +193,8 @@ def build(lp, name: str):
         phases.append(Phase("mx_quant_dual grad", "mx_quant_dual", nbytes=M * N * (2 + 2 * (1 + 1 / 32))))
         phases.append(Phase("mx_quant W", "mx_quant_rows", nbytes=N * K * (2 + 1 + 1 / 32)))
         phases.append(Phase("mx_quant X", "mx_quant_rows", nbytes=M * K * (2 + 1 + 1 / 32)))
-        phases.append(Phase("linear_bwd dX", "mx_dx_kernel", flops=2.0 * M * N * K, peak=PEAK_FP8_TFLOPS))
-        phases.append(Phase("linear_bwd dW", "mx_dx_kernel", flops=2.0 * M * N * K, peak=PEAK_FP8_TFLOPS))
+        phases.append(Phase("linear_bwd dX", "fp8_mfma_kernel", flops=2.0 * M * N * K, peak=PEAK_FP8_TFLOPS))
+        phases.append(Phase("linear_bwd dW", "fp8_mfma_kernel", flops=2.0 * M * N * K, peak=PEAK_FP8_TFLOPS))
 
         def step(i, stream):
             ts = []

@@ -404,7 +404,7 @@ __device__ __forceinline__ void mx_tile(const Params& p, int hw, uint8_t* st0, u
 }
 
 template <bool kDW, int kMode, int kFP = 0, int kFQ = 0>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void mx_dx_kernel(Params p) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void fp8_mfma_kernel(Params p) {
   LP_MX_LDS(kMode);
   mx_tile<kDW, kMode, kFP, kFQ>(p, blockIdx.x, st0, st1, st2, st3, sc0, sc1);
 }
