@@ -53,9 +53,30 @@ Op make_op(const lp_qtensor& t) {
 }
 
 
+constexpr int kCUsPerXcd = 32;
+
+// P-tile rows per group of the tile order (grouped_order): a group of g rows
+// and kCUsPerXcd / g columns of tiles runs on one XCD at a time and fetches
+// g * a + (kCUsPerXcd / g) * b bytes per slab into its L2 (a, b: bytes of one
+// P-tile row and one Q-tile column of a slab), least at g = sqrt(32 b / a);
+// the power of two nearest to it, ties to the smaller.
+int32_t tile_group(int64_t a, int64_t b, int64_t np) {
+  int32_t g = 1;
+  while (g < kCUsPerXcd && (int64_t)(2 * g) * (2 * g) * a < (int64_t)kCUsPerXcd * b * 2) g *= 2;
+  return (int32_t)(g < np ? g : (np > 0 ? np : 1));
+}
+
+// Bytes per element of an operand's codes, times 2.
+int64_t code_bytes2(int fmt) {
+  return fmt == LP_BF16 ? 4 : (fmt == LP_MXFP4 || fmt == LP_NVFP4) ? 1 : 2;
+}
+
 template <class C>
 hipError_t launch_cfg(const GemmCall& call, Params prm, hipStream_t stream) {
   prm.nq = (int32_t)((prm.Qtot + C::BQ - 1) / C::BQ);
+  if (call.offsets == nullptr && prm.splits == 1)
+    prm.gm = tile_group(C::BP * code_bytes2(call.grad->fmt), C::BQ * code_bytes2(call.other->fmt),
+                        (prm.Ptot + C::BP - 1) / C::BP);
   if (!call.dw) {
     const int64_t ptiles = call.offsets ? (call.M / C::BP + call.groups) : (call.M + C::BP - 1) / C::BP;
     prm.ntiles = (int32_t)(ptiles * prm.nq * prm.splits);
@@ -164,6 +185,9 @@ Params base_params(const GemmCall& call) {
 Params native_params(const GemmCall& call) {
   Params prm = base_params(call);
   prm.nq = (int32_t)((prm.Qtot + Big::BQ - 1) / Big::BQ);
+  if (call.offsets == nullptr)
+    prm.gm = tile_group(Big::BP * code_bytes2(call.grad->fmt), Big::BQ * code_bytes2(call.other->fmt),
+                        (prm.Ptot + Big::BP - 1) / Big::BP);
   if (call.dw) {
     prm.ntiles = (int32_t)(((call.N + Big::BP - 1) / Big::BP) * prm.nq * call.groups);
   } else {
@@ -213,6 +237,8 @@ hipError_t launch_fwd(const lp_qtensor& x, const lp_qtensor& w, const int32_t* o
   prm.groups = groups;
   prm.splits = 1;
   prm.nq = (int32_t)((prm.Qtot + Big::BQ - 1) / Big::BQ);
+  if (offsets == nullptr)
+    prm.gm = tile_group(Big::BP * code_bytes2(x.fmt), Big::BQ * code_bytes2(w.fmt), (prm.Ptot + Big::BP - 1) / Big::BP);
   const int64_t ptiles = offsets ? (x.rows / Big::BP + groups) : (x.rows + Big::BP - 1) / Big::BP;
   prm.ntiles = (int32_t)(ptiles * prm.nq);
   return fwd_mx(prm, x.fmt == LP_MXFP4, stream);

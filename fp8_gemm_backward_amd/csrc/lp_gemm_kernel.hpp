@@ -109,6 +109,7 @@ struct Params {
   int32_t groups;
   int32_t nq;            // Q-tiles
   int32_t ntiles;        // grid size (output tiles x splits)
+  int32_t gm;            // dense calls: P-tile rows per group of the tile order (1: row-major order)
   // Split contraction (dense calls only): `splits` workgroups share each
   // output tile, split s covering contraction [s * split_len, (s+1) * split_len).
   int32_t splits;        // 1: no split
@@ -520,6 +521,19 @@ __device__ __forceinline__ int xcd_remap(int hw, int n) {
   return x < rem ? x * (per + 1) + j : rem * (per + 1) + (x - rem) * per + j;
 }
 
+// Tile order of a dense contraction: groups of gm P-tile rows, each group's
+// tiles column by column, so that the tiles one XCD runs at a time (a
+// contiguous range of tile indices) form a gm x (32 / gm) block that shares
+// operand rows and columns in that XCD's L2.  Returns (P-tile, Q-tile);
+// a bijection of [0, np * nq).
+__device__ __forceinline__ int2 grouped_order(int tile, int np, int nq, int gm) {
+  const int per = gm * nq;
+  const int gid = tile / per, first = gid * gm;
+  const int gsz = np - first < gm ? np - first : gm;
+  const int r = tile - gid * per;
+  return make_int2(first + r % gsz, r / gsz);
+}
+
 // The output tile, group and contraction range of one workgroup.
 struct Tile {
   int g, p0, pend, q0, kbeg, kend;
@@ -546,9 +560,14 @@ __device__ __forceinline__ Tile select_tile(const Params& p, int32_t* s_ends, in
   }
   if (!kDW) {
     // Groups partition the output rows; tiles never straddle a group.
-    const int pidx = tile / p.nq;
+    int pidx = tile / p.nq;
     t.q0 = (tile % p.nq) * C::BQ;
     if (p.offsets == nullptr) {
+      if (p.gm > 1) {
+        const int2 pq = grouped_order(tile, (p.Ptot + C::BP - 1) / C::BP, p.nq, p.gm);
+        pidx = pq.x;
+        t.q0 = pq.y * C::BQ;
+      }
       t.p0 = pidx * C::BP;
       t.pend = p.Ptot;
     } else {
@@ -613,6 +632,11 @@ __device__ __forceinline__ Tile select_tile(const Params& p, int32_t* s_ends, in
     const int r = tile / p.groups;
     t.p0 = (r / p.nq) * C::BP;
     t.q0 = (r % p.nq) * C::BQ;
+    if (p.offsets == nullptr && p.gm > 1) {
+      const int2 pq = grouped_order(r, (p.Ptot + C::BP - 1) / C::BP, p.nq, p.gm);
+      t.p0 = pq.x * C::BP;
+      t.q0 = pq.y * C::BQ;
+    }
     t.pend = p.Ptot;
     if (p.offsets != nullptr) {
       int start = 0, e = 0;
