@@ -210,6 +210,19 @@ def test_linear_dx_dw(lp, gfmt, ofmt, M, N, K):
     assert_close(dw, PT.linear_dw(gc, ELEM[gfmt], gs, xc, ELEM[ofmt], xs), f"dW {gfmt}x{ofmt} {M}x{N}x{K}")
 
 
+def test_linear_x_and_w_in_different_formats(lp):
+    """X and W of different per-tensor formats: the two products are launched
+    one after the other instead of together; same results as the oracle."""
+    M, N, K = 300, 272, 400
+    g, gc, gs = _pt_operand(lp, 48, "grad", (M, N), 1e-3, "fp8t_e5m2")
+    w, wc, ws = _pt_operand(lp, 48, "w", (N, K), 0.02, "fp8t_e4m3")
+    x, xc, xs = _pt_operand(lp, 48, "x", (M, K), 1.0, "fp8t_e5m2")
+    dx, dw = lp.lp_linear_bwd(g, x, w)
+    torch.cuda.synchronize()
+    assert_close(dx, PT.linear_dx(gc, "e5m2", gs, wc, "e4m3", ws), "dX, W in E4M3")
+    assert_close(dw, PT.linear_dw(gc, "e5m2", gs, xc, "e5m2", xs), "dW, X in E5M2")
+
+
 def test_linear_each_output_alone(lp):
     M, N, K = 320, 256, 288
     g, gc, gs = _pt_operand(lp, 35, "grad", (M, N), 1e-3, "fp8t_e5m2")
