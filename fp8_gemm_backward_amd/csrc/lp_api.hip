@@ -8,6 +8,23 @@ namespace {
 
 constexpr int64_t kMaxUnits = (int64_t)1 << 31;    // kernels index 8-element units in 32 bits
 constexpr int64_t kMaxDim = ((int64_t)1 << 31) - 1;
+constexpr int64_t kMaxTiles = (int64_t)1 << 30;    // output tiles of one launch, counted in 32 bits
+
+// Element count of a [b][r][c] tensor (each size in [0, kMaxDim]) into *n;
+// false when it reaches 8 kMaxUnits.  r c stays below 2^62, and the product
+// with b is only formed once it is known to fit.
+bool count_ok(int64_t b, int64_t r, int64_t c, int64_t* n) {
+  const int64_t rc = r * c;
+  if (rc != 0 && b > (8 * kMaxUnits - 1) / rc) return false;
+  *n = b * rc;
+  return true;
+}
+
+// Output tiles of a result with `cols` columns whose rows make at most
+// `row_tiles` row tiles of 128, an upper bound for every tile shape the
+// kernels use (at least 128 x 128): the launches count them in 32 bits.
+// row_tiles < 2^35 here, so the product cannot overflow.
+bool tiles_ok(int64_t row_tiles, int64_t cols) { return row_tiles * (cols / 128 + 1) <= kMaxTiles; }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -28,8 +45,8 @@ lp_status check_tensor(const lp_qtensor* t) {
   if (t->cols % 16) return LP_ERR_SHAPE;
   if ((t->fmt == LP_MXFP4 || (t->fmt == LP_MXFP8 && axis == -1)) && t->cols % 32) return LP_ERR_SHAPE;
   if (t->fmt == LP_MXFP8 && axis == -2 && t->rows % 32) return LP_ERR_SHAPE;
-  const int64_t n = t->batch * t->rows * t->cols;
-  if (n / 8 >= kMaxUnits) return LP_ERR_SHAPE;
+  int64_t n = 0;
+  if (!count_ok(t->batch, t->rows, t->cols, &n)) return LP_ERR_SHAPE;
   if (n == 0) return LP_OK;
   if (t->codes == nullptr) return LP_ERR_NULL;
   if (has_block_scales(t->fmt) && t->scales == nullptr) return LP_ERR_NULL;
@@ -78,6 +95,9 @@ lp_status check_bwd(const lp_qtensor* grad, const lp_qtensor* x, const lp_qtenso
   for (const lp_qtensor* t : {grad_x ? w : nullptr, grad_w ? x : nullptr}) {
     if (t != nullptr && is_fp4(t->fmt) && t->cols % 32) return LP_ERR_SHAPE;
   }
+  const int64_t G = groups ? groups : 1;
+  if (grad_x != nullptr && !tiles_ok(M / 128 + G + 1, K)) return LP_ERR_SHAPE;   // a partial tile per group
+  if (grad_w != nullptr && !tiles_ok(G * (N / 128 + 1), K)) return LP_ERR_SHAPE;
   if (grad_x != nullptr && M * K > 0 && !aligned(grad_x, 16)) return LP_ERR_ALIGN;
   if (grad_w != nullptr && N * K > 0 && !aligned(grad_w, 16)) return LP_ERR_ALIGN;
   return LP_OK;
@@ -91,7 +111,7 @@ lp_status lp_dequant(const lp_qtensor* src, void* dst, void* stream) {
   lp_status st = check_tensor(src);
   if (st != LP_OK) return st;
   if (src->fmt == LP_BF16) return LP_ERR_FORMAT;
-  if (src->batch * src->rows * src->cols == 0) return LP_OK;
+  if (src->batch == 0 || src->rows == 0 || src->cols == 0) return LP_OK;
   if (dst == nullptr) return LP_ERR_NULL;
   if (!aligned(dst, 16)) return LP_ERR_ALIGN;
   return hip_status(lp::launch_dequant(*src, dst, static_cast<hipStream_t>(stream)));
@@ -104,8 +124,8 @@ lp_status lp_mx_quant(const void* src, int64_t batch, int64_t rows, int64_t cols
   if (dst_fmt != LP_MXFP8 && dst_fmt != LP_MXFP4) return LP_ERR_FORMAT;
   if (axis == -1 && cols % 32) return LP_ERR_SHAPE;
   if (axis == -2 && (rows % 32 || cols % 8)) return LP_ERR_SHAPE;
-  const int64_t n = batch * rows * cols;
-  if (n / 8 >= kMaxUnits) return LP_ERR_SHAPE;
+  int64_t n = 0;
+  if (!count_ok(batch, rows, cols, &n)) return LP_ERR_SHAPE;
   if (n == 0) return LP_OK;
   if (src == nullptr || codes == nullptr || scales == nullptr) return LP_ERR_NULL;
   if (!aligned(src, 16) || !aligned(codes, 16) || !aligned(scales, 16)) return LP_ERR_ALIGN;
@@ -118,8 +138,8 @@ lp_status lp_mx_quant_dual(const void* src, int64_t batch, int64_t rows, int64_t
   if (batch < 0 || rows < 0 || cols < 0 || batch > kMaxDim || rows > kMaxDim || cols > kMaxDim) return LP_ERR_SHAPE;
   if (dst_fmt != LP_MXFP8 && dst_fmt != LP_MXFP4) return LP_ERR_FORMAT;
   if (rows % 32 || cols % 32) return LP_ERR_SHAPE;
-  const int64_t n = batch * rows * cols;
-  if (n / 8 >= kMaxUnits) return LP_ERR_SHAPE;
+  int64_t n = 0;
+  if (!count_ok(batch, rows, cols, &n)) return LP_ERR_SHAPE;
   if (n == 0) return LP_OK;
   if (src == nullptr || codes_cols == nullptr || scales_cols == nullptr || codes_rows == nullptr ||
       scales_rows == nullptr)
@@ -248,6 +268,7 @@ static lp_status check_fwd(const lp_qtensor* x, const lp_qtensor* w, void* y, in
   if (x->scale_axis != -1 || w->scale_axis != -1) return LP_ERR_FORMAT;
   if (x->batch != 1 || w->batch != (groups ? groups : 1) || w->cols != x->cols) return LP_ERR_SHAPE;
   if (x->cols % (x->fmt == LP_MXFP4 ? 128 : 64) || w->rows % 16) return LP_ERR_SHAPE;
+  if (!tiles_ok(x->rows / 128 + (groups ? groups : 1) + 1, w->rows)) return LP_ERR_SHAPE;
   if (x->rows * w->rows > 0 && y == nullptr) return LP_ERR_NULL;
   if (!aligned(y, 16)) return LP_ERR_ALIGN;
   return LP_OK;

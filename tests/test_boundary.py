@@ -262,3 +262,29 @@ def test_linear_bwd_ws_rejects_misaligned_workspace():
     w = q("fp8_b128", 8192, 2048)
     assert lp.lib.lp_linear_bwd_ws(ctypes.byref(g), None, ctypes.byref(w), FAKE, None, FAKE + 16, 1 << 30,
                                    None) == ALIGN
+
+
+BIG = (1 << 31) - 32        # below 2^31 and a multiple of 32
+
+
+def test_element_counts_past_int64_are_rejected():
+    """batch x rows x cols of three sizes just below 2^31 overflows 64 bits;
+    the count is checked without forming the product."""
+    assert dq(q("mxfp8", BIG, BIG, batch=BIG)) == SHAPE
+    assert dq(q("mxfp8", 1 << 20, 1 << 14)) == SHAPE          # exactly 2^34 elements
+    assert lp.lib.lp_mx_quant(FAKE, BIG, BIG, BIG, -1, lp.FMT["mxfp8"], FAKE, FAKE, None) == SHAPE
+    assert lp.lib.lp_mx_quant_dual(FAKE, BIG, BIG, BIG, lp.FMT["mxfp8"], FAKE, FAKE, FAKE, FAKE, None) == SHAPE
+
+
+def test_outputs_with_too_many_tiles_are_rejected():
+    """Every operand fits its own limits, but the output has more tiles than
+    a launch counts in 32 bits."""
+    # grad_X of 2^24 tokens over a 2^29-wide input: about 2^39 tiles
+    assert lin(q("bf16", 1 << 24, 16), None, q("fp8_b128", 16, 1 << 29), FAKE, None) == SHAPE
+    # grad_W of 1024 groups of 16 x 2^29: 2^32 tiles
+    g, x, w = q("bf16", 16, 16), q("fp8_b128", 16, 1 << 29), q("fp8_b128", 16, 1 << 29, batch=1024)
+    assert lp.lib.lp_grouped_bwd(ctypes.byref(g), ctypes.byref(x), ctypes.byref(w), FAKE, 1024, None, FAKE,
+                                 None) == SHAPE
+    # forward of 2^24 tokens into 2^26 outputs
+    xf, wf = q("mxfp4", 1 << 24, 128), q("mxfp4", 1 << 26, 128)
+    assert lp.lib.lp_linear_fwd(ctypes.byref(xf), ctypes.byref(wf), FAKE, None) == SHAPE
