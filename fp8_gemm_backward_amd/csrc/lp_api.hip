@@ -9,6 +9,12 @@ namespace {
 constexpr int64_t kMaxUnits = (int64_t)1 << 31;    // kernels index 8-element units in 32 bits
 constexpr int64_t kMaxDim = ((int64_t)1 << 31) - 1;
 constexpr int64_t kMaxTiles = (int64_t)1 << 30;    // output tiles of one launch, counted in 32 bits
+// Products: a tile's 256 rows of any operand span fewer than 2^31 bytes (the
+// kernels address them with 32-bit offsets and buffer windows), and the
+// contraction of grad_W (the token rows) runs a few slabs past its end in
+// 32-bit arithmetic.
+constexpr int64_t kMaxProductCols = (int64_t)1 << 22;
+constexpr int64_t kMaxProductRows = (int64_t)1 << 30;
 
 // Element count of a [b][r][c] tensor (each size in [0, kMaxDim]) into *n;
 // false when it reaches 8 kMaxUnits.  r c stays below 2^62, and the product
@@ -95,6 +101,7 @@ lp_status check_bwd(const lp_qtensor* grad, const lp_qtensor* x, const lp_qtenso
   for (const lp_qtensor* t : {grad_x ? w : nullptr, grad_w ? x : nullptr}) {
     if (t != nullptr && is_fp4(t->fmt) && t->cols % 32) return LP_ERR_SHAPE;
   }
+  if (M >= kMaxProductRows || N >= kMaxProductCols || K >= kMaxProductCols) return LP_ERR_SHAPE;
   const int64_t G = groups ? groups : 1;
   if (grad_x != nullptr && !tiles_ok(M / 128 + G + 1, K)) return LP_ERR_SHAPE;   // a partial tile per group
   if (grad_w != nullptr && !tiles_ok(G * (N / 128 + 1), K)) return LP_ERR_SHAPE;
@@ -268,6 +275,7 @@ static lp_status check_fwd(const lp_qtensor* x, const lp_qtensor* w, void* y, in
   if (x->scale_axis != -1 || w->scale_axis != -1) return LP_ERR_FORMAT;
   if (x->batch != 1 || w->batch != (groups ? groups : 1) || w->cols != x->cols) return LP_ERR_SHAPE;
   if (x->cols % (x->fmt == LP_MXFP4 ? 128 : 64) || w->rows % 16) return LP_ERR_SHAPE;
+  if (x->rows >= kMaxProductRows || x->cols >= kMaxProductCols || w->rows >= kMaxProductCols) return LP_ERR_SHAPE;
   if (!tiles_ok(x->rows / 128 + (groups ? groups : 1) + 1, w->rows)) return LP_ERR_SHAPE;
   if (x->rows * w->rows > 0 && y == nullptr) return LP_ERR_NULL;
   if (!aligned(y, 16)) return LP_ERR_ALIGN;

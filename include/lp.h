@@ -30,6 +30,9 @@
  *   4-byte aligned.  A pointer may be NULL only when its tensor is empty.
  * - A tensor holds fewer than 2^34 elements and each of batch, rows, cols is
  *   below 2^31 (LP_ERR_SHAPE otherwise).
+ * - In the products (lp_linear_bwd*, lp_grouped_bwd, lp_*_fwd) the token
+ *   count M is below 2^30 and every other dimension (N, K) below 2^22
+ *   (LP_ERR_SHAPE otherwise).
  * - The output of a product must have few enough tiles to count in 32 bits:
  *   R * (cols/128 + 1) <= 2^30 (LP_ERR_SHAPE otherwise), with R =
  *   rows/128 + G + 1 for grad_X and the forward (rows: tokens) and

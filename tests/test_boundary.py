@@ -279,12 +279,20 @@ def test_element_counts_past_int64_are_rejected():
 def test_outputs_with_too_many_tiles_are_rejected():
     """Every operand fits its own limits, but the output has more tiles than
     a launch counts in 32 bits."""
-    # grad_X of 2^24 tokens over a 2^29-wide input: about 2^39 tiles
-    assert lin(q("bf16", 1 << 24, 16), None, q("fp8_b128", 16, 1 << 29), FAKE, None) == SHAPE
-    # grad_W of 1024 groups of 16 x 2^29: 2^32 tiles
-    g, x, w = q("bf16", 16, 16), q("fp8_b128", 16, 1 << 29), q("fp8_b128", 16, 1 << 29, batch=1024)
-    assert lp.lib.lp_grouped_bwd(ctypes.byref(g), ctypes.byref(x), ctypes.byref(w), FAKE, 1024, None, FAKE,
-                                 None) == SHAPE
-    # forward of 2^24 tokens into 2^26 outputs
-    xf, wf = q("mxfp4", 1 << 24, 128), q("mxfp4", 1 << 26, 128)
+    # grad_X of 2^29 tokens over a 2^21-wide input: about 2^36 tiles
+    assert lin(q("bf16", 1 << 29, 16), None, q("fp8_b128", 16, 1 << 21), FAKE, None) == SHAPE
+    # grad_W of 1024 groups of 2^21 x 2^21: about 2^38 tiles
+    g, x = q("bf16", 16, 1 << 21), q("fp8_b128", 16, 1 << 21)
+    assert lp.lib.lp_grouped_bwd(ctypes.byref(g), ctypes.byref(x), None, FAKE, 1024, None, FAKE, None) == SHAPE
+    # forward of 2^24 tokens into 2^21 outputs
+    xf, wf = q("mxfp4", 1 << 24, 128), q("mxfp4", 1 << 21, 128)
+    assert lp.lib.lp_linear_fwd(ctypes.byref(xf), ctypes.byref(wf), FAKE, None) == SHAPE
+
+
+def test_product_dimensions_beyond_the_kernels_addressing_are_rejected():
+    """Rows of 2^22 or more elements, or 2^30 or more tokens."""
+    assert lin(q("bf16", 16, 1 << 22), None, q("fp8_b128", 1 << 22, 16), FAKE, None) == SHAPE     # N
+    assert lin(q("bf16", 16, 16), None, q("fp8_b128", 16, 1 << 22), FAKE, None) == SHAPE          # K
+    assert lin(q("bf16", 1 << 30, 16), q("fp8_b128", 1 << 30, 16), None, None, FAKE) == SHAPE     # M
+    xf, wf = q("mxfp4", 16, 1 << 22), q("mxfp4", 16, 1 << 22)
     assert lp.lib.lp_linear_fwd(ctypes.byref(xf), ctypes.byref(wf), FAKE, None) == SHAPE
