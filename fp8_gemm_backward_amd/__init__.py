@@ -73,6 +73,41 @@ def _load() -> ctypes.CDLL:
 lib = _load()
 
 
+_CODE_BITS = {"bf16": 16, "mxfp4": 4, "nvfp4": 4, "fp8_b128": 8, "mxfp8": 8, "fp8t_e4m3": 8, "fp8t_e5m2": 8}
+
+
+def _scale_bytes(fmt: str, axis: int, b: int, r: int, c: int) -> int:
+    """Bytes of a tensor's block scales (include/lp.h, formats)."""
+    if fmt == "mxfp4" or (fmt == "mxfp8" and axis == -1):
+        return b * r * (c // 32)
+    if fmt == "mxfp8":
+        return b * (r // 32) * c
+    if fmt == "nvfp4":
+        return b * r * (c // 16)
+    if fmt == "fp8_b128":
+        return b * (-(-r // 128)) * (-(-c // 128)) * 4
+    return 0
+
+
+def _device(t: Optional[torch.Tensor], name: str, nbytes: int, dtype=None) -> None:
+    """A tensor the library reads or writes `nbytes` of: on the GPU,
+    contiguous, large enough (and of `dtype` where its element count is what
+    the call passes).  Checked here because the C calls take bare pointers:
+    a host pointer or a short buffer would reach a kernel as it is."""
+    if nbytes <= 0:
+        return
+    if t is None:
+        raise ValueError(f"{name}: a device tensor of {nbytes} bytes is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor, not on {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, not {t.dtype}")
+    if t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, the call needs {nbytes}")
+
+
 def header_functions() -> list[str]:
     """Names of the functions declared in include/lp.h."""
     text = open(HEADER_PATH).read()
@@ -112,6 +147,13 @@ class QTensor:
         return self.shape[2]
 
     def c(self) -> _QTensorC:
+        b, r, c = self.shape
+        n = b * r * c
+        _device(self.codes, f"{self.fmt} codes", n * _CODE_BITS[self.fmt] // 8)
+        _device(self.scales, f"{self.fmt} scales", _scale_bytes(self.fmt, self.axis, b, r, c))
+        if self.fmt in ("nvfp4", "fp8t_e4m3", "fp8t_e5m2"):
+            _device(self.tensor_scale, f"{self.fmt} tensor scale", 4 if n else 0, torch.float32)
+
         def ptr(t):
             return None if t is None else t.data_ptr()
         return _QTensorC(FMT[self.fmt], self.axis, self.shape[0], self.shape[1], self.shape[2],
@@ -134,6 +176,7 @@ def lp_dequant(src: QTensor, out: Optional[torch.Tensor] = None, stream=None) ->
     if out is None:
         out = torch.empty(src.shape, dtype=torch.bfloat16, device=src.codes.device)
     q = src.c()
+    _device(out, "out", 2 * src.shape[0] * src.shape[1] * src.shape[2])
     _check(lib.lp_dequant(ctypes.byref(q), out.data_ptr(), _stream(stream)), "lp_dequant")
     return out
 
@@ -150,6 +193,10 @@ def lp_mx_quant(src: torch.Tensor, axis: int, fmt: str = "mxfp8", codes: Optiona
     if scales is None:
         sshape = (b, r, c // 32) if axis == -1 else (b, r // 32, c)
         scales = torch.empty(sshape, dtype=torch.uint8, device=dev)
+    n = b * r * c
+    _device(src, "src", 2 * n, torch.bfloat16)
+    _device(codes, "codes", n if fmt == "mxfp8" else n // 2)
+    _device(scales, "scales", _scale_bytes(fmt, axis, b, r, c))
     _check(lib.lp_mx_quant(src.data_ptr(), b, r, c, axis, FMT[fmt], codes.data_ptr(), scales.data_ptr(),
                            _stream(stream)), "lp_mx_quant")
     return QTensor(fmt, codes, scales, None, shape, axis)
@@ -162,6 +209,7 @@ def lp_mx_quant_dual(src: torch.Tensor, fmt: str = "mxfp8", stream=None) -> tupl
     b, r, c = shape
     dev = src.device
     cb = c if fmt == "mxfp8" else c // 2
+    _device(src, "src", 2 * b * r * c, torch.bfloat16)
     codes_c = torch.empty((b, r, cb), dtype=torch.uint8, device=dev)
     scales_c = torch.empty((b, r, c // 32), dtype=torch.uint8, device=dev)
     codes_r = torch.empty((b, r, cb), dtype=torch.uint8, device=dev)
@@ -176,6 +224,8 @@ def lp_tensor_amax(src: torch.Tensor, amax: Optional[torch.Tensor] = None, strea
     one-element view into an amax history)."""
     if amax is None:
         amax = torch.empty(1, dtype=torch.float32, device=src.device)
+    _device(src, "src", 2 * src.numel(), torch.bfloat16)
+    _device(amax, "amax", 4, torch.float32)
     _check(lib.lp_tensor_amax(src.data_ptr(), src.numel(), amax.data_ptr(), _stream(stream)), "lp_tensor_amax")
     return amax
 
@@ -188,6 +238,11 @@ def lp_tensor_quant(src: torch.Tensor, fmt: str, scale: torch.Tensor, amax: Opti
     shape = tuple(src.shape) if src.dim() == 3 else (1,) + tuple(src.shape)
     if codes is None:
         codes = torch.empty(shape, dtype=torch.uint8, device=src.device)
+    _device(src, "src", 2 * src.numel(), torch.bfloat16)
+    _device(codes, "codes", src.numel())
+    _device(scale, "scale", 4, torch.float32)
+    if amax is not None:
+        _device(amax, "amax", 4, torch.float32)
     _check(lib.lp_tensor_quant(src.data_ptr(), src.numel(), FMT[fmt], scale.data_ptr(), codes.data_ptr(),
                                None if amax is None else amax.data_ptr(), _stream(stream)), "lp_tensor_quant")
     return QTensor(fmt, codes, None, scale, shape, -1)
@@ -203,6 +258,10 @@ def lp_tensor_quant_delayed(src: torch.Tensor, fmt: str, history: torch.Tensor, 
         codes = torch.empty(shape, dtype=torch.uint8, device=src.device)
     if scale is None:
         scale = torch.empty(1, dtype=torch.float32, device=src.device)
+    _device(src, "src", 2 * src.numel(), torch.bfloat16)
+    _device(codes, "codes", src.numel())
+    _device(history, "history", 4 * max(history.numel(), 1), torch.float32)
+    _device(scale, "scale", 4, torch.float32)
     _check(lib.lp_tensor_quant_delayed(src.data_ptr(), src.numel(), FMT[fmt], history.data_ptr(), history.numel(),
                                        slot, margin, codes.data_ptr(), scale.data_ptr(), _stream(stream)),
            "lp_tensor_quant_delayed")
@@ -214,6 +273,8 @@ def lp_scale_from_history(history: torch.Tensor, fmt: str, margin: int = 0, scal
     """Per-tensor scale (float32 device scalar) from a float32 amax history."""
     if scale is None:
         scale = torch.empty(1, dtype=torch.float32, device=history.device)
+    _device(history, "history", 4 * max(history.numel(), 1), torch.float32)
+    _device(scale, "scale", 4, torch.float32)
     _check(lib.lp_scale_from_history(history.data_ptr(), history.numel(), FMT[fmt], margin, scale.data_ptr(),
                                      _stream(stream)), "lp_scale_from_history")
     return scale
@@ -233,6 +294,12 @@ def lp_linear_bwd(grad_out: QTensor, x: Optional[QTensor], w: Optional[QTensor],
         grad_x = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
     if need_dw and grad_w is None:
         grad_w = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    if need_dx:
+        _device(grad_x, "grad_x", 2 * M * K)
+    if need_dw:
+        _device(grad_w, "grad_w", 2 * N * K)
+    if workspace is not None:
+        _device(workspace, "workspace", 1)
     g = grad_out.c()
     xc = x.c() if x is not None else None
     wc = w.c() if w is not None else None
@@ -275,6 +342,11 @@ def lp_grouped_bwd(grad_out: QTensor, x: Optional[QTensor], w: Optional[QTensor]
         grad_x = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
     if need_dw and grad_w is None:
         grad_w = torch.empty((G, N, K), dtype=torch.bfloat16, device=dev)
+    if need_dx:
+        _device(grad_x, "grad_x", 2 * M * K)
+    if need_dw:
+        _device(grad_w, "grad_w", 2 * G * N * K)
+    _device(offsets, "offsets", 4 * G, torch.int32)
     g = grad_out.c()
     xc = x.c() if x is not None else None
     wc = w.c() if w is not None else None
@@ -290,6 +362,7 @@ def lp_linear_fwd(x: QTensor, w: QTensor, y: Optional[torch.Tensor] = None, stre
     both "mxfp8")."""
     if y is None:
         y = torch.empty((x.rows, w.rows), dtype=torch.bfloat16, device=x.codes.device)
+    _device(y, "y", 2 * x.rows * w.rows)
     xc, wc = x.c(), w.c()
     _check(lib.lp_linear_fwd(ctypes.byref(xc), ctypes.byref(wc), y.data_ptr(), _stream(stream)), "lp_linear_fwd")
     return y
@@ -301,6 +374,8 @@ def lp_grouped_fwd(x: QTensor, w: QTensor, offsets: torch.Tensor, y: Optional[to
     offsets[-1] are left as they were in `y`."""
     if y is None:
         y = torch.empty((x.rows, w.rows), dtype=torch.bfloat16, device=x.codes.device)
+    _device(y, "y", 2 * x.rows * w.rows)
+    _device(offsets, "offsets", 4 * offsets.numel(), torch.int32)
     xc, wc = x.c(), w.c()
     _check(lib.lp_grouped_fwd(ctypes.byref(xc), ctypes.byref(wc), offsets.data_ptr(), offsets.numel(), y.data_ptr(),
                               _stream(stream)), "lp_grouped_fwd")

@@ -4,6 +4,7 @@ before touching the GPU (CPU only; no kernel is launched)."""
 import ctypes
 
 import pytest
+import torch
 
 import fp8_gemm_backward_amd as lp
 from fp8_gemm_backward_amd import _QTensorC
@@ -296,3 +297,16 @@ def test_product_dimensions_beyond_the_kernels_addressing_are_rejected():
     assert lin(q("bf16", 1 << 30, 16), q("fp8_b128", 1 << 30, 16), None, None, FAKE) == SHAPE     # M
     xf, wf = q("mxfp4", 16, 1 << 22), q("mxfp4", 16, 1 << 22)
     assert lp.lib.lp_linear_fwd(ctypes.byref(xf), ctypes.byref(wf), FAKE, None) == SHAPE
+
+
+def test_binding_rejects_host_tensors():
+    """The binding passes bare pointers to kernels: a host tensor must be
+    refused before any C call (CPU only)."""
+    src = torch.zeros(64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device tensor"):
+        lp.lp_tensor_amax(src)
+    with pytest.raises(ValueError, match="device tensor"):
+        lp.lp_mx_quant(src.view(2, 32), -1)
+    qt = lp.QTensor("mxfp8", torch.zeros((1, 4, 64), dtype=torch.uint8), torch.zeros((1, 4, 2), dtype=torch.uint8))
+    with pytest.raises(ValueError, match="device tensor"):
+        lp.lp_dequant(qt)

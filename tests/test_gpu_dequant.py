@@ -111,3 +111,23 @@ def test_ragged_sizes(lp, fmt, shape, axis):
     out = lp.lp_dequant(q)
     torch.cuda.synchronize()
     assert_bits_equal(bits_host(out), ref, f"{fmt} {shape}")
+
+
+def test_binding_rejects_short_and_strided_buffers(lp):
+    """A device buffer too small for the call, or a strided view, is refused
+    by the binding before any kernel runs (the C calls take bare pointers)."""
+    codes = torch.zeros((1, 64, 64), dtype=torch.uint8, device="cuda")
+    scales = torch.full((1, 64, 2), 127, dtype=torch.uint8, device="cuda")
+    q = lp.QTensor("mxfp8", codes, scales)
+    with pytest.raises(ValueError, match="needs"):
+        lp.lp_dequant(q, torch.empty((64, 63), dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(ValueError, match="needs"):
+        lp.lp_dequant(lp.QTensor("mxfp8", codes, scales[:, :32], shape=(1, 64, 64)))
+    with pytest.raises(ValueError, match="contiguous"):
+        lp.lp_dequant(q, torch.empty((64, 128), dtype=torch.bfloat16, device="cuda")[:, ::2])
+    src = torch.zeros((64, 64), dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError, match="bfloat16"):
+        lp.lp_tensor_amax(src)
+    out = lp.lp_dequant(q)                                   # and the well-formed call still runs
+    torch.cuda.synchronize()
+    assert out.shape == (1, 64, 64) and not out.float().abs().any()
