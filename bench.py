@@ -17,6 +17,12 @@ synthetic input already resident in HBM:
 Input sets are rotated through about 1 GB so that the 256 MiB Infinity Cache
 cannot serve a repeated step.  Prints one JSON line (rank 0).
 
+The default warmup is long (1000 steps, about 0.2 s of GPU work for the
+default workload): the GPU reaches its sustained clock only after some
+hundreds of milliseconds of load, and a training step runs in that steady
+state.  Measured on the default workload, the GEMM's launch time was 160 us
+after 5 warmup steps, 148 us after 100, 139-143 us after 1000 to 10000.
+
 Inputs are drawn on the GPU by torch and quantized there: FP8 blocks and
 NVFP4 with plain torch ops (input preparation only), MXFP4 with the
 library's own lp_mx_quant.  The CPU-baseline leg runs the CPU oracle on a
@@ -467,8 +473,8 @@ def cpu_baseline(name: str, budget_s: float = 12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--workload", default="fp8_frozen", choices=sorted(W.WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
     a = ap.parse_args()
