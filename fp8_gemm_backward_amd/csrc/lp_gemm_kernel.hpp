@@ -143,25 +143,23 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* base, int64_t bytes) {
 // cannot tell apart the LDS stages that such loads fill across loop
 // iterations, and would make every LDS read wait for all of them; the
 // kernels that use this wait for their loads themselves (barrier_vm) before
-// reading what they wrote.  The loads carry the sc0 sc1 cache policy: a
-// workgroup reads each byte once.  Measured on the MXFP4 forward of 8192 x
-// 4096 x 4096: with its operands resident in the last-level cache 110 -> 97
-// us; streamed from HBM, unchanged; the nt policy instead made it slower
-// (165 us).
+// reading what they wrote.  Default cache policy: the streaming policies
+// (sc0 sc1, nt) measured no faster on the MXFP4 forward and the MXFP8 dX in
+// steady state (nt slower).
 template <int kSize>
 __device__ __forceinline__ void dma(Rsrc r, lds_void* dst, int32_t voff, int32_t soff) {
   const uint32_t m0 = (uint32_t)(size_t)dst;
   if constexpr (kSize == 16)
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen sc0 sc1 lds" ::"s"(m0), "v"(voff), "s"(r), "s"(soff)
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(m0), "v"(voff), "s"(r), "s"(soff)
                  : "memory", "m0");
   else if constexpr (kSize == 4)
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen sc0 sc1 lds" ::"s"(m0), "v"(voff), "s"(r), "s"(soff)
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds" ::"s"(m0), "v"(voff), "s"(r), "s"(soff)
                  : "memory", "m0");
   else if constexpr (kSize == 2)
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_ushort %1, %2, %3 offen sc0 sc1 lds" ::"s"(m0), "v"(voff), "s"(r), "s"(soff)
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_ushort %1, %2, %3 offen lds" ::"s"(m0), "v"(voff), "s"(r), "s"(soff)
                  : "memory", "m0");
   else
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_ubyte %1, %2, %3 offen sc0 sc1 lds" ::"s"(m0), "v"(voff), "s"(r), "s"(soff)
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_ubyte %1, %2, %3 offen lds" ::"s"(m0), "v"(voff), "s"(r), "s"(soff)
                  : "memory", "m0");
 }
 
