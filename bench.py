@@ -4,7 +4,8 @@
 
 A step is one pass of the workload's whole backward path over one batch of
 synthetic input already resident in HBM:
-  fp8_frozen      lp_linear_bwd: dX of a frozen FP8 128x128-block weight (default)
+  fp8_frozen      lp_dequant of a frozen FP8 128x128-block weight to bf16, then
+                  lp_linear_bwd: dX against the bf16 copy (default)
   nvfp4_linear    lp_linear_bwd: dX and dW, NVFP4 X and W
   mxfp4_grouped   lp_grouped_bwd: dX and dW over 8 experts, MXFP4 X and W
   mxfp8_deferred  lp_mx_quant(grad, -1) + lp_mx_quant(W, -2) + lp_grouped_bwd dX
@@ -130,17 +131,38 @@ def build(lp, name: str):
             dw = torch.empty((N, K), dtype=torch.bfloat16, device="cuda") if w.need_dw else None
             sets.append((gq, xq, wq, dx, dw))
         flops = 2.0 * M * N * K * (2 if w.need_dw else 1)
-        phases.append(Phase("linear_bwd", "gemm_kernel", flops=flops))
-        # One workspace serves every input set: steps run in order on one stream.
-        gq, xq, wq = sets[0][:3]
-        nws = lp.lp_linear_bwd_workspace(gq, xq, wq, True, w.need_dw)
-        ws = torch.zeros(nws, dtype=torch.uint8, device="cuda") if nws else None
+        if name == "fp8_frozen":
+            # The weight is decoded once per step into a bf16 copy (lp_dequant), then dX
+            # contracts bf16 with bf16, both operands loaded straight into LDS: the
+            # order of "Train adapters on top of FP8 weights", FP8LinearFunction.backward
+            # (dequantize the weight, then matmul).  At this shape it is faster than
+            # decoding inside the GEMM, where each of the 16 row tiles decodes the
+            # weight again; the results are bit-identical.
+            wbf = torch.empty((1, N, K), dtype=torch.bfloat16, device="cuda")
+            wbq = lp.QTensor("bf16", wbf, shape=(1, N, K))
+            # Events bracket the GEMM only: a pair around the decode as well costs a
+            # few microseconds of queue time per step.  The decode's own rate is
+            # reported under standalone_hbm.
+            phases.append(Phase("linear_bwd dX (bf16 W)", "gemm_kernel", flops=flops))
 
-        def step(i, stream):
-            gq, xq, wq, dx, dw = sets[i % len(sets)]
-            ev = _events(stream)
-            lp.lp_linear_bwd(gq, xq, wq, need_dw=w.need_dw, grad_x=dx, grad_w=dw, stream=stream, workspace=ws)
-            return [ev.stop(stream)]
+            def step(i, stream):
+                gq, xq, wq, dx, dw = sets[i % len(sets)]
+                lp.lp_dequant(wq, wbf, stream=stream)
+                ev = _events(stream)
+                lp.lp_linear_bwd(gq, None, wbq, need_dw=False, grad_x=dx, stream=stream)
+                return [ev.stop(stream)]
+        else:
+            phases.append(Phase("linear_bwd", "gemm_kernel", flops=flops))
+            # One workspace serves every input set: steps run in order on one stream.
+            gq, xq, wq = sets[0][:3]
+            nws = lp.lp_linear_bwd_workspace(gq, xq, wq, True, w.need_dw)
+            ws = torch.zeros(nws, dtype=torch.uint8, device="cuda") if nws else None
+
+            def step(i, stream):
+                gq, xq, wq, dx, dw = sets[i % len(sets)]
+                ev = _events(stream)
+                lp.lp_linear_bwd(gq, xq, wq, need_dw=w.need_dw, grad_x=dx, grad_w=dw, stream=stream, workspace=ws)
+                return [ev.stop(stream)]
         standalone = [("W", sets[0][2])] + ([("X", sets[0][1])] if sets[0][1] is not None else [])
     elif name == "mxfp4_grouped":
         offsets = torch.from_numpy(W.cumulative_ends(W.group_sizes(w))).cuda()

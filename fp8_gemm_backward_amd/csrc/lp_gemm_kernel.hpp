@@ -779,20 +779,27 @@ template <class C, int PF, int PA, int QF, int QA, bool kDW>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_kernel(Params p) {
   constexpr bool PK = !kDW;                                      // P k-major in dx, mn-major in dw
   constexpr bool PD = PF == BF16;                                // P loaded straight into LDS
+  // Q straight into LDS too when both operands are bf16 and three Q stages fit.
+  constexpr bool QD = PD && QF == BF16 && 3 * Direct<PK, C::BP>::BUF_BYTES + 3 * Direct<false, C::BQ>::BUF_BYTES <= kMaxLds;
   using LP = std::conditional_t<PD, Direct<PK, C::BP>, Decoded<PF, PA, PK, C::BP>>;
-  using LQ = Decoded<QF, QA, false, C::BQ>;
+  using LQ = std::conditional_t<QD, Direct<false, C::BQ>, Decoded<QF, QA, false, C::BQ>>;
   constexpr int PERIOD = PD ? 3 : 2;                             // slabs per iteration = register stages
   constexpr int PBUF = LP::BUF_BYTES, QBUF = LQ::BUF_BYTES;
-  static_assert((PD ? 3 * PBUF : 2 * PBUF) + 2 * QBUF <= kMaxLds, "LDS budget");
+  constexpr int SB = C::WP * C::WQ * 2;                          // epilogue staging bytes per wave
+  constexpr int QBUF0 = QD ? (QBUF > SB ? QBUF : SB) : 2 * QBUF; // Q buffer 0 (also wave 3's staging)
+  static_assert((PD ? 3 * PBUF : 2 * PBUF) + QBUF0 + (QD ? 2 * QBUF : 0) <= kMaxLds, "LDS budget");
   static_assert(kMaxGroups * 4 <= PBUF, "group ends alias P buffer 0");
   __shared__ __attribute__((aligned(1024))) uint8_t sp0[PD ? PBUF : 2 * PBUF];
   __shared__ __attribute__((aligned(1024))) uint8_t sp1[PD ? PBUF : 16];
   __shared__ __attribute__((aligned(1024))) uint8_t sp2[PD ? PBUF : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t sq[2 * QBUF];
+  __shared__ __attribute__((aligned(1024))) uint8_t sq0[QBUF0];
+  __shared__ __attribute__((aligned(1024))) uint8_t sq1[QD ? QBUF : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t sq2[QD ? QBUF : 16];
 
-  // Per slab, in issue order: direct P loads, register loads (P, then Q).
-  constexpr int nDP = PD ? LP::VMEM : 0;
-  constexpr int nL = (PD ? 0 : LP::VMEM) + LQ::VMEM;
+  // Per slab, in issue order: direct loads (P, then Q), register loads (P,
+  // then Q).
+  constexpr int nDP = (PD ? LP::VMEM : 0) + (QD ? LQ::VMEM : 0);
+  constexpr int nL = (PD ? 0 : LP::VMEM) + (QD ? 0 : LQ::VMEM);
   constexpr int NIS = LP::ITEMS + LQ::ITEMS;
   constexpr int ND = LP::DECODES + LQ::DECODES;
   constexpr int DS0 = C::FP * C::FQ / 2;                         // first decode slot
@@ -820,7 +827,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   LQ lq;
   if constexpr (PD) lp.init(p.P, 0, t.p0, kDW ? 0 : p.P.rows, wave, lane);
   else lp.init(p.P, 0, t.p0, kDW ? 0 : p.P.rows, tid);
-  lq.init(p.Q, kDW ? 0 : t.g, t.q0, 0, tid);
+  if constexpr (QD) lq.init(p.Q, kDW ? 0 : t.g, t.q0, 0, wave, lane);
+  else lq.init(p.Q, kDW ? 0 : t.g, t.q0, 0, tid);
   FAP fap;
   FAQ faq;
   fap.init(wp * C::WP, lane);
@@ -834,7 +842,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     else if constexpr (B == 1) return sp1;
     else return sp2;
   };
-  auto qbuf = [&](int k) -> uint8_t* { return sq + (k & 1) * QBUF; };
+  // Q buffer of slab k (B = k mod 3 when direct, else k's parity).
+  auto qbuf = [&](auto bi, int k) -> uint8_t* {
+    constexpr int B = decltype(bi)::value % 3;
+    if constexpr (!QD) return sq0 + (k & 1) * QBUF;
+    else if constexpr (B == 0) return sq0;
+    else if constexpr (B == 1) return sq1;
+    else return sq2;
+  };
 
   f32x16 acc[FP][FQ];
 #pragma unroll
@@ -846,12 +861,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   typename LP::Stage ps[PERIOD];
   typename LQ::Stage qs[PERIOD];
 
-  // Load item n into register stage ST (direct P items: into LDS buffer pb).
-  auto issue = [&](auto ni, auto sti, const typename LP::Win& pw, const typename LQ::Win& qw, uint8_t* pb) {
+  // Load item n into register stage ST (direct items: into LDS buffers pb,
+  // qb; direct Q items take window qwd, register Q items window qw).
+  auto issue = [&](auto ni, auto sti, const typename LP::Win& pw, const typename LQ::Win& qwd,
+                   const typename LQ::Win& qw, uint8_t* pb, uint8_t* qb) {
     constexpr int n = decltype(ni)::value, ST = decltype(sti)::value;
     if constexpr (n < LP::ITEMS) {
       if constexpr (PD) lp.template load<n>(pb, pw);
       else lp.template load<n>(ps[ST], pw, p.P);
+    } else if constexpr (QD) {
+      lq.template load<n - LP::ITEMS>(qb, qwd);
     } else {
       lq.template load<n - LP::ITEMS>(qs[ST], qw, p.Q);
     }
@@ -865,7 +884,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         constexpr int QU = LP::QUARTERS, piece = n / QU;
         lp.template decode<piece / LP::PIECES, piece % LP::PIECES, n % QU>(ps[ST], pb, dst);
       }
-    } else {
+    } else if constexpr (!QD) {
       constexpr int m = n - LP::DECODES, QU = LQ::QUARTERS, piece = m / QU;
       lq.template decode<piece / LQ::PIECES, piece % LQ::PIECES, m % QU>(qs[ST], qb, dst);
     }
@@ -902,15 +921,18 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
       constexpr int s = decltype(si)::value;
       const auto pw = lp.window(p.P, kbeg + s * BK, kend);
       const auto qw = lq.window(p.Q, kbeg + s * BK, kend);
-      static_for<NIS>([&](auto n) {
-        constexpr int v = decltype(n)::value;
-        constexpr int item = PD ? (v + LP::ITEMS) % NIS : v;         // direct items last
-        if constexpr (!(PD && item < LP::ITEMS && s >= 2)) issue(IC<item>{}, si, pw, qw, pbuf(si, s));
+      static_for<2>([&](auto pass) {                                 // register items, then direct items
+        static_for<NIS>([&](auto n) {
+          constexpr int item = decltype(n)::value;
+          constexpr bool dir = (PD && item < LP::ITEMS) || (QD && item >= LP::ITEMS);
+          if constexpr (dir == (decltype(pass)::value == 1) && !(dir && s >= 2))
+            issue(IC<item>{}, si, pw, qw, qw, pbuf(si, s), qbuf(si, s));
+        });
       });
     });
-    static_for<ND>([&](auto n) { decode(n, IC<0>{}, pbuf(IC<0>{}, 0), qbuf(0)); });
+    static_for<ND>([&](auto n) { decode(n, IC<0>{}, pbuf(IC<0>{}, 0), qbuf(IC<0>{}, 0)); });
     barrier_vm<NV_PRO>();
-    static_for<NR>([&](auto r) { read(r, IC<0>{}, IC<0>{}, pbuf(IC<0>{}, 0), qbuf(0)); });
+    static_for<NR>([&](auto r) { read(r, IC<0>{}, IC<0>{}, pbuf(IC<0>{}, 0), qbuf(IC<0>{}, 0)); });
   }
 
   // Slab k = kt + J: multiply P buffer (k) and Q buffer (k); issue the
@@ -920,12 +942,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     constexpr int J = decltype(ji)::value;
     constexpr int JN = (J + 1) % PERIOD;
     const uint8_t* const pcur = pbuf(ji, k);
-    const uint8_t* const qcur = qbuf(k);
+    const uint8_t* const qcur = qbuf(ji, k);
     uint8_t* const pnxt = pbuf(IC<J + 1>{}, k + 1);
-    uint8_t* const qnxt = qbuf(k + 1);
+    uint8_t* const qnxt = qbuf(IC<J + 1>{}, k + 1);
     uint8_t* const pdst = pbuf(IC<J + 2>{}, k + 2);
+    uint8_t* const qdst = qbuf(IC<J + 2>{}, k + 2);
     const auto pw = lp.window(p.P, kbeg + (k + (PD ? 2 : PERIOD)) * BK, kend);
-    const auto qw = lq.window(p.Q, kbeg + (k + PERIOD) * BK, kend);
+    const auto qw = lq.window(p.Q, kbeg + (k + (QD ? 2 : PERIOD)) * BK, kend);
 
     static_for<4>([&](auto si) {
       constexpr int S = decltype(si)::value;
@@ -945,7 +968,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         }
         if constexpr (S < 3) {                                       // loads spread over substeps 0-2
           static_for<NIS>([&](auto ni) {
-            if constexpr (decltype(ni)::value * 3 * NM / NIS == S * NM + m) issue(ni, ji, pw, qw, pdst);
+            if constexpr (decltype(ni)::value * 3 * NM / NIS == S * NM + m) issue(ni, ji, pw, qw, qw, pdst, qdst);
           });
         }
         if constexpr (S < 3) {                                       // decode from mid substep 0 on
@@ -965,11 +988,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   // wave may still read a buffer the staging below overwrites.
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   __syncthreads();
-  constexpr int SB = C::WP * C::WQ * 2;                          // staging bytes per wave
-  static_assert(PD ? (PBUF >= SB && 2 * QBUF >= SB) : (2 * PBUF >= 2 * SB && 2 * QBUF >= 2 * SB), "staging fits");
-  if (p.splits > 1 && !reduce_split<C>(p, t, acc, wave, lane, reinterpret_cast<uint32_t*>(sq))) return;
-  uint8_t* stage = PD ? (wave == 0 ? sp0 : wave == 1 ? sp1 : wave == 2 ? sp2 : sq)
-                      : (wave < 2 ? sp0 + wave * SB : sq + (wave - 2) * SB);
+  static_assert(PD ? (PBUF >= SB && QBUF0 >= SB) : (2 * PBUF >= 2 * SB && QBUF0 >= 2 * SB), "staging fits");
+  if (p.splits > 1 && !reduce_split<C>(p, t, acc, wave, lane, reinterpret_cast<uint32_t*>(sq0))) return;
+  uint8_t* stage = PD ? (wave == 0 ? sp0 : wave == 1 ? sp1 : wave == 2 ? sp2 : sq0)
+                      : (wave < 2 ? sp0 + wave * SB : sq0 + (wave - 2) * SB);
   store_acc<C, kDW>(p, t, acc, wp, wq, lane, stage);
 }
 

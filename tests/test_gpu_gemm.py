@@ -352,6 +352,24 @@ def test_fp8_frozen_full_size(lp):
     assert_close(dx[torch.from_numpy(rows).cuda()], O.rows_dx(G, wd[0], rows), "fp8 frozen dX")
 
 
+def test_fp8_frozen_full_size_two_step(lp):
+    """The benchmark's form of the same step: lp_dequant of the weight to a
+    bf16 copy, then dX against it (bf16 x bf16, both operands loaded straight
+    into LDS).  Bit-identical to the fused decode, and 64 sampled rows against
+    the oracle."""
+    w = W.WORKLOADS["fp8_frozen"]
+    X, Wt, G = W.dense_inputs(w)
+    wq, wd = quantize(lp, "fp8_b128", Wt)
+    g = lp.QTensor("bf16", bf16_dev(G), shape=(1, w.M, w.N))
+    wbf = lp.lp_dequant(wq)
+    dx2, _ = lp.lp_linear_bwd(g, None, lp.QTensor("bf16", wbf, shape=(1, w.N, w.K)), need_dw=False)
+    dx1, _ = lp.lp_linear_bwd(g, None, wq, need_dw=False)
+    torch.cuda.synchronize()
+    assert torch.equal(dx1, dx2), "two-step dX differs from the fused decode"
+    rows = _sample_rows(w.M, 64, 41)
+    assert_close(dx2[torch.from_numpy(rows).cuda()], O.rows_dx(G, wd[0], rows), "fp8 frozen dX, two-step")
+
+
 def test_split_dw_full_contraction(lp):
     """A low-rank-adapter-sized dW: N = 256, K = 512 over all 16384 tokens of
     an NVFP4 input (two 256 x 256 tiles, 256 slabs in 16 splits); 32 sampled
