@@ -296,6 +296,11 @@ lp_status lp_tensor_quant_delayed(const void* src_bf16, int64_t n, int32_t dst_f
  * fp32 summation order.  Per-tensor scaled operands run on the same MFMA
  * with unit block scales: the fp32 sum of exact code products is multiplied
  * by fp32(scale_grad * scale_other), then rounded to bf16.
+ * A quantized x or w is decoded inside the contraction, once per output
+ * tile that reads it.  Decoding it beforehand with lp_dequant and passing
+ * the bf16 copy (fmt LP_BF16) gives bit-identical outputs; when many output
+ * tiles share the operand (grad_X of many tokens against one weight) that
+ * is faster, at the cost of the copy's memory.
  */
 lp_status lp_linear_bwd(const lp_qtensor* grad_out, const lp_qtensor* x, const lp_qtensor* w,
                         void* grad_x, void* grad_w, void* stream);
