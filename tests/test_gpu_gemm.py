@@ -246,10 +246,11 @@ def _sentinel(shape):
     return torch.full(shape, -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)   # 0xFFFF (NaN)
 
 
-@pytest.mark.parametrize("fmt,axis", [("mxfp4", -1), ("fp8_b128", -1), ("nvfp4", -1), ("mxfp8", -2)])
+@pytest.mark.parametrize("fmt,axis", [("bf16", -1), ("mxfp4", -1), ("fp8_b128", -1), ("nvfp4", -1), ("mxfp8", -2)])
 def test_grouped_edges(lp, fmt, axis):
     """Five groups: an empty one, one smaller than a tile, ragged ends, and
-    rows past the last offset that must keep their sentinel value."""
+    rows past the last offset that must keep their sentinel value.  bf16
+    operands take the path that loads both tiles straight into LDS."""
     M, N, K, G = 700, 256, 320, 5
     sizes = [130, 0, 17, 300, 203]            # sum 650 < M: rows 650.. untouched
     offsets = W.cumulative_ends(sizes)
