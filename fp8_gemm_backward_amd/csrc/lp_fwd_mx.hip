@@ -197,8 +197,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   }
 
   // Slab k = kt + J (stage J % 4): publish slab k+1, issue slab k+3 into the
-  // stage of slab k-1 (all at once: measured faster than spreading them over
-  // the MFMAs), multiply slab k while reading slab k+1's fragments.
+  // stage of slab k-1 (all at once; spreading them over the MFMAs measured
+  // the same in steady state), multiply slab k while reading slab k+1's
+  // fragments.
   auto slab = [&](auto ji, int k) {
     constexpr int J = decltype(ji)::value;
     constexpr int CUR = J & 1, NXT = CUR ^ 1;
