@@ -23,7 +23,7 @@ Pins (tests/test_oracle_*.py, all CPU):
   brute-force nearest search, the scale formula and ring update of the
   AstrAI page, triple-loop GEMMs with the scales applied to the sums.
 
-Parity unpinned by the pages: the E2M1 nibble order and the NVFP4
+Parity unpinned by the source documents: the E2M1 nibble order and the NVFP4
 tensor-scale reading (see formats.py).
 """
 from . import formats, gemm, pertensor  # noqa: F401

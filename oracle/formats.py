@@ -20,17 +20,17 @@ Sources:
   (`float8_e8m0fnu`) per group of 32 (`group_sizes=[1, 1, 32]`).
 * "AstrAI fp8.py", `FP8_MAX`: the E4M3 maximum is 448.
 
-Readings taken where the pages are silent (each is listed in the design
-notes with its pin):
+Readings taken where the source documents are silent (each with the test
+that pins it under tests/):
 * E2M1, E4M3 (OCP "FN": no infinities, S.1111.111 is NaN) and E8M0
   (2^(b-127), 0xFF = NaN) follow the OCP MX v1.0 element definitions.
 * Packed E2M1: element 2j in the low nibble, 2j+1 in the high nibble.
-  Parity unpinned by the pages (no packed example is printed).
+  Parity unpinned by the source documents (no packed example is printed).
 * Scales are plain row-major, unswizzled.
 * Every decode is RNE_bf16(RNE_fp32(code_value * S)) with S an fp32 block
   multiplier; for NVFP4, S = RNE_fp32(E4M3(s_b) * tensor_scale), the tensor
   scale being a decode multiplier.  Parity of the NVFP4 tensor-scale reading
-  is unpinned by the pages.
+  is unpinned by the source documents.
 * A NaN result is the bf16 quiet NaN 0x7FC0 carrying the code's sign bit.
 * MX scale: e = floor(log2(amax)) - emax_elem (8 for E4M3, 2 for E2M1),
   clamped to [-127, 127]; elements rounded to nearest, ties to even, and

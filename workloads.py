@@ -6,7 +6,7 @@ products.  Values that the method consumes in bf16 are rounded from fp32 by
 torch's CPU cast (a library conversion, neither the oracle nor the HIP path).
 
 Workloads (the shapes and value distributions of the backward passes that
-the pages describe: a frozen FP8-E4M3 128x128-block linear as in "Train
+the source documents describe: a frozen FP8-E4M3 128x128-block linear as in "Train
 adapters on top of FP8 weights", FP4 linear / grouped backward as in "Add
 Autograd Backward Support for FP4 GEMM Custom Ops", and the deferred MXFP8
 grouped backward of "perf: defer mxfp8 backward quantization"):
