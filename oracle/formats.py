@@ -209,8 +209,9 @@ def _dequant_one(fmt, codes, scales, tensor_scale, axis):
 def dequant(fmt: str, codes, scales=None, tensor_scale=None, axis: int = -1,
             chunk_rows: int = 512) -> np.ndarray:
     """Dispatch on the format; returns bf16 bits [b,R,C].  Large tensors are
-    processed in slabs of rows (a multiple of every block height), which
-    changes nothing in the result."""
+    processed in slabs of about `chunk_rows` rows, rounded up to a whole
+    number of scale-block rows so that every slab starts on a block
+    boundary; the slabs change nothing in the result."""
     if fmt == FMT_BF16:
         return _as3d(np.asarray(codes, dtype=np.uint16))
     codes = _as3d(np.asarray(codes))
@@ -219,13 +220,20 @@ def dequant(fmt: str, codes, scales=None, tensor_scale=None, axis: int = -1,
     C = codes.shape[2] * (2 if fmt in (FMT_MXFP4, FMT_NVFP4) else 1)
     out = np.empty((b, R, C), dtype=np.uint16)
     srow = {FMT_FP8_B128: FP8_BLOCK, FMT_MXFP8: MX_BLOCK if axis == -2 else 1}.get(fmt, 1)
+    step = -(-max(1, chunk_rows) // srow) * srow        # slabs start on a scale-block boundary
     for bi in range(b):
-        for r0 in range(0, R, chunk_rows):
-            r1 = min(R, r0 + chunk_rows)
+        for r0 in range(0, R, step):
+            r1 = min(R, r0 + step)
             out[bi, r0:r1] = _dequant_one(fmt, codes[bi:bi + 1, r0:r1],
-                                          scales[bi:bi + 1, r0 // srow:-(-r1 // srow)],
+                                          scales[bi:bi + 1, _scale_rows(r0, r1, srow)],
                                           tensor_scale, axis)[0]
     return out
+
+
+def _scale_rows(r0: int, r1: int, srow: int) -> slice:
+    """Rows of the scale grid that cover tensor rows [r0, r1) when one scale
+    row spans `srow` tensor rows (r0 a multiple of srow)."""
+    return slice(r0 // srow, -(-r1 // srow))
 
 
 # ---------------------------------------------------------------- rounding onto a grid
@@ -289,6 +297,12 @@ def _mx_quant_blocks(blocks: np.ndarray, elem: str):
     return codes.astype(np.uint8), scale
 
 
+def _block_chunks(n: int, size: int) -> list[tuple[int, int]]:
+    """[start, stop) ranges of at most `size` blocks covering blocks 0..n-1."""
+    size = max(1, size)
+    return [(i, min(n, i + size)) for i in range(0, n, size)]
+
+
 def mx_quant(bits: np.ndarray, axis: int, elem: str, chunk_blocks: int = 1 << 16):
     """Dynamic MX quantization of bf16 bits [b,R,C] along `axis` (-1: blocks of
     32 run along the columns, -2: along the rows).
@@ -301,12 +315,12 @@ def mx_quant(bits: np.ndarray, axis: int, elem: str, chunk_blocks: int = 1 << 16
         x = np.swapaxes(x, -1, -2)
     b, R, C = x.shape
     flat = np.ascontiguousarray(x).reshape(-1, MX_BLOCK)
-    codes = np.empty(flat.shape, dtype=np.uint8)
-    scale = np.empty(flat.shape[0], dtype=np.uint8)
-    for i in range(0, flat.shape[0], chunk_blocks):
-        c, s = _mx_quant_blocks(bf16_bits_to_f64(flat[i:i + chunk_blocks]), elem)
-        codes[i:i + chunk_blocks] = c
-        scale[i:i + chunk_blocks] = s
+    codes = np.zeros(flat.shape, dtype=np.uint8)
+    scale = np.zeros(flat.shape[0], dtype=np.uint8)
+    for i, j in _block_chunks(flat.shape[0], chunk_blocks):
+        c, s = _mx_quant_blocks(bf16_bits_to_f64(flat[i:j]), elem)
+        codes[i:j] = c
+        scale[i:j] = s
     codes = codes.reshape(b, R, C)
     scale = scale.reshape(b, R, C // MX_BLOCK)
     if axis == -2:

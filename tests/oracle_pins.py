@@ -551,4 +551,77 @@ def pin_grouped_forward_equals_dense():
     assert np.allclose(y[9:25], O.linear_fwd(x[9:25], w[2]), rtol=1e-13)
 
 
+# ------------------------------------------------------------------ sampled and chunked paths
+
+def pin_rows_dx_dw_brute_force():
+    """The sampled contractions that full-size checks use: rows_dx on an
+    unsorted row subset (one row twice) and rows_dw on an unsorted subset of
+    n, against pure-Python triple loops and against the rows of the whole
+    products."""
+    M, N, K = 9, 7, 5
+    g = _tiny_bf16(104, "grad", (M, N))
+    w = _tiny_bf16(104, "w", (N, K))
+    x = _tiny_bf16(104, "x", (M, K))
+    gv, wv, xv = (F.bf16_bits_to_f64(a).tolist() for a in (g, w, x))
+    rows = np.array([8, 0, 3, 3])
+    ns = np.array([6, 1, 0])
+    dx = [[sum(gv[m][n] * wv[n][k] for n in range(N)) for k in range(K)] for m in rows.tolist()]
+    dw = [[sum(gv[m][n] * xv[m][k] for m in range(M)) for k in range(K)] for n in ns.tolist()]
+    got_dx, got_dw = O.rows_dx(g, w, rows), O.rows_dw(g, x, ns)
+    assert got_dx.shape == (len(rows), K) and got_dw.shape == (len(ns), K)
+    assert np.allclose(got_dx, dx, rtol=1e-13, atol=0), "rows_dx differs from the triple loop"
+    assert np.allclose(got_dw, dw, rtol=1e-13, atol=0), "rows_dw differs from the triple loop"
+    assert np.allclose(got_dx, O.linear_dx(g, w)[rows], rtol=1e-13, atol=0)
+    assert np.allclose(got_dw, O.linear_dw(g, x)[ns], rtol=1e-13, atol=0)
+
+
+def pin_dequant_row_slabs():
+    """Dequantization in row slabs: slabs of 32, 100 (rounded up to whole
+    scale-block rows) and 128 rows give the same bits as one pass, and the
+    slabbed FP8 block result equals the FP8-adapter page's formulation in
+    torch (scale grid repeated over 128 x 128 blocks, cut at the edge) on a
+    300-row tensor whose last block row is partial; MXFP8 scaled along the
+    rows is checked against torch on 96 rows in slabs of 32."""
+    g = W.rng(105, "w")
+    R, C = 300, 200
+    codes = g.integers(0, 256, size=(R, C), dtype=np.uint8)
+    codes[codes & 0x7F == 0x7F] = 0x10
+    scale = (g.random((3, 2), dtype=np.float32) * 2 + 0.5).astype(np.float32)
+    whole = F.dequant(F.FMT_FP8_B128, codes, scale, chunk_rows=1 << 30)[0]
+    s = torch.from_numpy(scale).repeat_interleave(128, dim=0)[:R].repeat_interleave(128, dim=1)[:, :C]
+    ref = (_torch_decode_e4m3(codes) * s).bfloat16().view(torch.int16).numpy().view(np.uint16)
+    for rows in (32, 100, 128):
+        got = F.dequant(F.FMT_FP8_B128, codes, scale, chunk_rows=rows)[0]
+        assert np.array_equal(got, whole), f"FP8 block dequant in slabs of {rows} rows differs"
+        assert _bits_equal_nan_aware(got, ref), f"FP8 block dequant in slabs of {rows} rows differs from torch"
+    R8, C8 = 96, 64
+    c8 = g.integers(0, 256, size=(R8, C8), dtype=np.uint8)
+    sc8 = g.integers(100, 150, size=(R8 // 32, C8), dtype=np.uint8)
+    got8 = F.dequant(F.FMT_MXFP8, c8, sc8, axis=-2, chunk_rows=32)[0]
+    ref8 = (_torch_decode_e4m3(c8) * _torch_decode_e8m0(sc8).repeat_interleave(32, dim=0))
+    ref8 = ref8.bfloat16().view(torch.int16).numpy().view(np.uint16)
+    assert _bits_equal_nan_aware(got8, ref8), "MXFP8 axis -2 dequant in slabs differs from torch"
+    for fmt, ncols_s in ((F.FMT_MXFP4, 32), (F.FMT_NVFP4, 16)):
+        packed = g.integers(0, 256, size=(70, 32), dtype=np.uint8)
+        sc = g.integers(0, 0x7F if fmt == F.FMT_NVFP4 else 140, size=(70, 64 // ncols_s), dtype=np.uint8)
+        ts = np.float32(0.37) if fmt == F.FMT_NVFP4 else None
+        a = F.dequant(fmt, packed, sc, ts, chunk_rows=7)
+        b = F.dequant(fmt, packed, sc, ts, chunk_rows=1 << 30)
+        assert np.array_equal(a, b), f"{fmt} dequant in slabs of 7 rows differs"
+
+
+def pin_mx_quant_chunks():
+    """MX quantization in chunks of 3 blocks (the last one partial) gives
+    the same codes and scales as one pass, on both axes and both element
+    formats, with magnitudes spread over many binades."""
+    g = W.rng(106, "x")
+    mags = np.exp2(g.integers(-30, 30, size=(64, 1))).astype(np.float32)
+    bits = W.bf16_bits(g.standard_normal((64, 160)).astype(np.float32) * mags)
+    for axis in (-1, -2):
+        for elem in ("e4m3", "e2m1"):
+            q1, s1 = F.mx_quant(bits, axis, elem)
+            q3, s3 = F.mx_quant(bits, axis, elem, chunk_blocks=3)
+            assert np.array_equal(q1, q3) and np.array_equal(s1, s3), (axis, elem)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -118,7 +118,34 @@ def _fwd_no_transpose(x_bits, w_bits):
     return O._f64(x_bits) @ O._f64(w_bits).reshape(O._f64(w_bits).shape[::-1])
 
 
+_orig_rows_dx = O.rows_dx
+_orig_rows_dw = O.rows_dw
+
+
+def _rows_dx_next_row(grad_bits, w_bits, rows):
+    r = np.minimum(np.asarray(rows) + 1, np.asarray(grad_bits).shape[0] - 1)
+    return _orig_rows_dx(grad_bits, w_bits, r)
+
+
+def _rows_dw_next_n(grad_bits, x_bits, n_rows):
+    n = np.minimum(np.asarray(n_rows) + 1, np.asarray(grad_bits).shape[1] - 1)
+    return _orig_rows_dw(grad_bits, x_bits, n)
+
+
+def _scale_rows_lag(r0, r1, srow):
+    return slice(max(r0 - 1, 0) // srow, -(-r1 // srow))
+
+
+def _chunks_drop_last_block(n, size):
+    size = max(1, size)
+    return [(i, min(n, i + size) - (1 if min(n, i + size) - i > 1 else 0)) for i in range(0, n, size)]
+
+
 MUTATIONS = {
+    "sampled dX takes the next row": (O, "rows_dx", _rows_dx_next_row),
+    "sampled dW takes the next n": (O, "rows_dw", _rows_dw_next_n),
+    "dequant row slab lags one scale row": (F, "_scale_rows", _scale_rows_lag),
+    "MX quant chunks skip their last block": (F, "_block_chunks", _chunks_drop_last_block),
     "forward multiplies W untransposed": (O, "linear_fwd", _fwd_no_transpose),
     "per-tensor quantization multiplies by the scale": (PT, "quantize", _pt_quant_multiplies),
     "per-tensor quantization without saturation": (PT, "round_to_fp8", _pt_no_saturation),
