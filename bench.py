@@ -4,11 +4,12 @@
 
 A step is one pass of the workload's whole backward path over one batch of
 synthetic input already resident in HBM:
+  mxfp8_deferred  lp_mx_quant(grad, -1) + lp_mx_quant(W, -2) + lp_grouped_bwd dX over
+                  64 experts (default: the largest workload, 962 GFLOP per step)
   fp8_frozen      lp_dequant of a frozen FP8 128x128-block weight to bf16, then
-                  lp_linear_bwd: dX against the bf16 copy (default)
+                  lp_linear_bwd: dX against the bf16 copy
   nvfp4_linear    lp_linear_bwd: dX and dW, NVFP4 X and W
   mxfp4_grouped   lp_grouped_bwd: dX and dW over 8 experts, MXFP4 X and W
-  mxfp8_deferred  lp_mx_quant(grad, -1) + lp_mx_quant(W, -2) + lp_grouped_bwd dX
   mxfp8_dense     lp_mx_quant_dual(grad) + lp_mx_quant(W, -2) + lp_mx_quant(X, -2) + lp_linear_bwd dX, dW
   fp8_hybrid      lp_tensor_quant_delayed(grad -> E5M2 with the ring's scale, amax into the ring)
                   + lp_linear_bwd dX, dW against E4M3 X and W (per-tensor scales)
@@ -18,11 +19,16 @@ synthetic input already resident in HBM:
 Input sets are rotated through about 1 GB so that the 256 MiB Infinity Cache
 cannot serve a repeated step.  Prints one JSON line (rank 0).
 
-The default warmup is long (1000 steps, about 0.2 s of GPU work for the
-default workload): the GPU reaches its sustained clock only after some
-hundreds of milliseconds of load, and a training step runs in that steady
-state.  Measured on the default workload, the GEMM's launch time was 160 us
-after 5 warmup steps, 148 us after 100, 139-143 us after 1000 to 10000.
+The default warmup is long (1000 steps): the GPU reaches its sustained
+clock only after some hundreds of milliseconds of load, and a training step
+runs in that steady state.  Measured on the FP8 frozen-weight workload, its
+GEMM's launch time was 160 us after 5 warmup steps, 148 us after 100 and
+139-143 us after 1000 to 10000; the deferred MXFP8 step, about 1.2 ms long,
+moves by about 1%.
+
+The CPU-baseline leg times the oracle kernel by kernel (decode, quantize,
+products) on bounded samples, on one thread and on all of BLAS's threads,
+and scales each to the whole step.
 
 Inputs are drawn on the GPU by torch and quantized there: FP8 blocks and
 NVFP4 with plain torch ops (input preparation only), MXFP4 with the
@@ -338,19 +344,29 @@ def dequant_bytes(q) -> float:
     return n * (per[q.fmt] + 2.0)
 
 
-def time_standalone(lp, stream, q, reps=20):
-    out = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
-    for _ in range(3):
-        lp.lp_dequant(q, out, stream=stream)
+def time_standalone(lp, stream, q, reps=50):
+    """Median time of lp_dequant of `q` (5 warmups, `reps` timed calls), with
+    copies of the operand and of the output rotated through more than 1 GB
+    so that no call finds its input or output in the 256 MiB Infinity Cache."""
+    per = dequant_bytes(q)
+    n = max(2, math.ceil(ROTATE_BYTES / per) + 1)
+    copies = [q] + [lp.QTensor(q.fmt, q.codes.clone(), None if q.scales is None else q.scales.clone(),
+                               q.tensor_scale, shape=q.shape, axis=q.axis) for _ in range(n - 1)]
+    outs = [torch.empty(q.shape, dtype=torch.bfloat16, device="cuda") for _ in range(n)]
+    for i in range(5):
+        lp.lp_dequant(copies[i % n], outs[i % n], stream=stream)
     evs = []
-    for _ in range(reps):
+    for i in range(reps):
         ev = _events(stream)
-        lp.lp_dequant(q, out, stream=stream)
+        lp.lp_dequant(copies[(i + 5) % n], outs[(i + 5) % n], stream=stream)
         evs.append(ev.stop(stream))
     torch.cuda.synchronize()
-    ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
-    gbs = dequant_bytes(q) / (ms * 1e-3) / 1e9
-    return {"ms": round(ms, 5), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    med = float(np.median(ms))
+    gbs = per / (med * 1e-3) / 1e9
+    return {"ms": round(med, 5), "p10_ms": round(float(np.percentile(ms, 10)), 5),
+            "p90_ms": round(float(np.percentile(ms, 90)), 5), "GB/s": round(gbs, 1),
+            "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "rotated_copies": n}
 
 
 # ------------------------------------------------------------------ HBM traffic from committed counters
@@ -379,134 +395,195 @@ def committed_traffic(workload: str):
 
 # ------------------------------------------------------------------ CPU baseline (oracle)
 
-def cpu_baseline(name: str, budget_s: float = 12.0):
-    """The oracle on a bounded sample of the workload: decode of the saved
-    operands the sample needs plus the fp64 contraction of sampled rows,
-    extrapolated linearly to the whole step."""
-    from oracle import formats as F
-    from oracle import gemm as O
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [os.cpu_count()])
+        return max([p.get("num_threads", 1) for p in threadpool_info()] or [os.cpu_count() or 1])
     except Exception:  # noqa: BLE001
-        cores = os.cpu_count()
+        return os.cpu_count() or 1
+
+
+class _Part:
+    """One oracle kernel of the step on a sample: `fn` runs the sample, the
+    whole step's share is `scale` times its time.  `blas` parts (the fp64
+    contractions) are timed on one thread and on all of BLAS's threads; the
+    others are numpy element-wise code, which runs on one thread either way,
+    and are timed once."""
+
+    def __init__(self, name, fn, scale, blas, sample):
+        self.name, self.fn, self.scale, self.blas, self.sample = name, fn, scale, blas, sample
+
+
+def _oracle_parts(name: str):
+    """The step of workload `name` as oracle kernels on bounded samples."""
+    from oracle import formats as F
+    from oracle import gemm as O
     w = W.WORKLOADS[name]
     M, N, K = w.M, w.N, w.K
-    if name == "mxfp4_forward":
-        # W quantized and decoded once; a slab of token rows quantized,
-        # decoded and multiplied; extrapolated to all rows.
-        rows = 256
-        x = W.normal_f32(w.number, "x", (rows, K), w.x_sigma)
-        wt = W.normal_f32(w.number, "w", (N, K), w.w_sigma)
-        t0 = time.perf_counter()
-        wd = F.dequant("mxfp4", *F.quant_mxfp4_f32(wt[None]))[0]
-        t_w = time.perf_counter() - t0
-        t1 = time.perf_counter()
-        xd = F.dequant("mxfp4", *F.quant_mxfp4_f32(x[None]))[0]
-        O.linear_fwd(xd, wd)
-        t_rows = time.perf_counter() - t1
-        total = t_w + t_rows * (M / rows)
-        flops = 2.0 * M * N * K
-        sample = f"W quantized+decoded once; {rows} token rows quantized, decoded and multiplied (fp64); extrapolated to {M}"
-    elif name == "fp8_hybrid":
-        # a slab of token rows: the gradient's amax and E5M2 quantization, the
-        # saved operands' E4M3 quantization, and the fp64 dX / dW over the slab;
-        # extrapolated to all rows (W's quantization counted once).
-        from oracle import pertensor as PT
-        rows = 256
+    rows = min(M, 256)
+    parts = []
+    if name == "mxfp8_deferred":
+        gb = W.bf16_bits(W.normal_f32(w.number, "grad", (rows, N), 1.0))
+        wb = W.bf16_bits(W.normal_f32(w.number, "w", (N, K), w.w_sigma))
+        st = {}
+
+        def qg():
+            st["g"] = F.mx_quant(gb[None], -1, "e4m3")
+
+        def qw():
+            st["w"] = F.mx_quant(wb[None], -2, "e4m3")
+
+        def dec_w():
+            st["wd"] = F.dequant("mxfp8", *st["w"], axis=-2)[0]
+
+        def dx():
+            O.linear_dx(F.dequant("mxfp8", *st["g"], axis=-1)[0], st["wd"])
+        parts += [_Part("mx_quant grad", qg, M / rows, False, f"{rows} of {M} gradient rows"),
+                  _Part("mx_quant W", qw, w.groups, False, f"1 of {w.groups} experts' weights"),
+                  _Part("decode W", dec_w, w.groups, False, f"1 of {w.groups} experts' weights"),
+                  _Part("grouped dX (gradient decode + fp64 product)", dx, M / rows, True,
+                        f"{rows} token rows against one expert's weight")]
+        return parts, 2.0 * M * N * K
+    if name == "mxfp8_dense":
         gb = W.bf16_bits(W.normal_f32(w.number, "grad", (rows, N), 1.0))
         xb = W.bf16_bits(W.normal_f32(w.number, "x", (rows, K), w.x_sigma))
         wb = W.bf16_bits(W.normal_f32(w.number, "w", (N, K), w.w_sigma))
-        t0 = time.perf_counter()
+        st = {}
+
+        def qg():
+            st["g1"] = F.mx_quant(gb[None], -1, "e4m3")
+            st["g2"] = F.mx_quant(gb[None], -2, "e4m3")
+
+        def qw():
+            st["w"] = F.mx_quant(wb[None], -2, "e4m3")
+
+        def qx():
+            st["x"] = F.mx_quant(xb[None], -2, "e4m3")
+
+        def dec_w():
+            st["wd"] = F.dequant("mxfp8", *st["w"], axis=-2)[0]
+
+        def dx():
+            O.linear_dx(F.dequant("mxfp8", *st["g1"], axis=-1)[0], st["wd"])
+
+        def dw():
+            O.linear_dw(F.dequant("mxfp8", *st["g2"], axis=-2)[0], F.dequant("mxfp8", *st["x"], axis=-2)[0])
+        parts += [_Part("mx_quant grad, both axes", qg, M / rows, False, f"{rows} of {M} gradient rows"),
+                  _Part("mx_quant W", qw, 1, False, "whole weight"),
+                  _Part("mx_quant X", qx, M / rows, False, f"{rows} of {M} input rows"),
+                  _Part("decode W", dec_w, 1, False, "whole weight"),
+                  _Part("dX (decode + fp64 product)", dx, M / rows, True, f"{rows} token rows"),
+                  _Part("dW (decode + fp64 product)", dw, M / rows, True, f"{rows} token rows of the contraction")]
+        return parts, 4.0 * M * N * K
+    if name == "fp8_hybrid":
+        from oracle import pertensor as PT
+        gb = W.bf16_bits(W.normal_f32(w.number, "grad", (rows, N), 1.0))
+        xb = W.bf16_bits(W.normal_f32(w.number, "x", (rows, K), w.x_sigma))
+        wb = W.bf16_bits(W.normal_f32(w.number, "w", (N, K), w.w_sigma))
         ws_ = PT.scale_from_history([PT.amax(wb)], "e4m3")
         wc = PT.quantize(wb, "e4m3", ws_)
-        t_w = time.perf_counter() - t0
-        t1 = time.perf_counter()
-        hist = np.full(W.AMAX_RING, PT.amax(gb), np.float32)
-        gs = PT.scale_from_history(hist, "e5m2")
-        gc = PT.quantize(gb, "e5m2", gs)
-        PT.record(hist, 0, PT.amax(gb))
         xs = PT.scale_from_history([PT.amax(xb)], "e4m3")
         xc = PT.quantize(xb, "e4m3", xs)
-        PT.linear_dx(gc, "e5m2", gs, wc, "e4m3", ws_)
-        PT.linear_dw(gc, "e5m2", gs, xc, "e4m3", xs)
-        t_rows = time.perf_counter() - t1
-        total = t_w + t_rows * (M / rows)
-        flops = 4.0 * M * N * K
-        sample = (f"W quantized once; {rows} token rows: gradient amax, E5M2 quantization, X quantization, fp64 "
-                  f"dX and dW over the rows; extrapolated to {M} rows")
-    elif name == "mxfp8_dense":
-        # a slab of token rows: quantize grad both ways and X, W along -2,
-        # decode, contract dX and dW over the slab; extrapolate to all rows.
-        rows = 256
-        gb = W.bf16_bits(W.normal_f32(w.number, "grad", (rows, N), 1.0))
-        xb = W.bf16_bits(W.normal_f32(w.number, "x", (rows, K), w.x_sigma))
-        wb = W.bf16_bits(W.normal_f32(w.number, "w", (N, K), w.w_sigma))
-        t0 = time.perf_counter()
-        wc, ws = F.mx_quant(wb[None], -2, "e4m3")
-        wd = F.dequant("mxfp8", wc, ws, axis=-2)[0]
-        t_w = time.perf_counter() - t0
-        t1 = time.perf_counter()
-        gc1, gs1 = F.mx_quant(gb[None], -1, "e4m3")
-        gc2, gs2 = F.mx_quant(gb[None], -2, "e4m3")
-        xc, xs = F.mx_quant(xb[None], -2, "e4m3")
-        O.linear_dx(F.dequant("mxfp8", gc1, gs1, axis=-1)[0], wd)
-        O.linear_dw(F.dequant("mxfp8", gc2, gs2, axis=-2)[0], F.dequant("mxfp8", xc, xs, axis=-2)[0])
-        t_rows = time.perf_counter() - t1
-        total = t_w + t_rows * (M / rows)
-        flops = 4.0 * M * N * K
-        sample = (f"weight quantized+decoded once; {rows} token rows quantized both ways, decoded and contracted "
-                  f"(dX and dW); extrapolated to {M} rows")
-    elif name == "mxfp8_deferred":
-        # one expert: quantize its weight along -2 and a slab of gradient rows
-        # along -1, decode both, contract.
-        rows = 256
-        gb = W.bf16_bits(W.normal_f32(w.number, "grad", (rows, N), 1.0))
-        wb = W.bf16_bits(W.normal_f32(w.number, "w", (N, K), w.w_sigma))
-        t0 = time.perf_counter()
-        gc, gs = F.mx_quant(gb[None], -1, "e4m3")
-        wc, ws = F.mx_quant(wb[None], -2, "e4m3")
-        gd = F.dequant("mxfp8", gc, gs, axis=-1)[0]
-        wd = F.dequant("mxfp8", wc, ws, axis=-2)[0]
-        t_w = time.perf_counter() - t0
-        t1 = time.perf_counter()
-        O.linear_dx(gd, wd)
-        t_rows = time.perf_counter() - t1
-        total = t_w * w.groups + t_rows * (M / rows)
-        flops = 2.0 * M * N * K
-        sample = f"1 of {w.groups} experts' weight quantized+decoded, {rows} grad rows quantized+decoded+contracted; extrapolated"
-    else:
-        X, Wt, G = W.dense_inputs(w)
-        fmt = w.fmt
-        quant = {"fp8_b128": F.quant_fp8_b128, "nvfp4": lambda a: F.quant_nvfp4(a),
-                 "mxfp4": F.quant_mxfp4_f32}[fmt]
-        wq = quant(Wt)
-        xq = quant(X) if X is not None else None
+        st = {}
 
-        def deq(q):
-            if fmt == "nvfp4":
-                return F.dequant(fmt, q[0], q[1], q[2])
-            return F.dequant(fmt, q[0], q[1])
-        t0 = time.perf_counter()
-        wd = deq(wq)
-        xd = deq(xq)[0] if xq is not None else None
-        t_dec = time.perf_counter() - t0
-        rows = min(M, 64)
-        while True:
-            t1 = time.perf_counter()
-            O.rows_dx(G, wd[0] if not w.grouped else wd[0], np.arange(rows))
-            if xd is not None:
-                O.rows_dw(G[:rows], xd[:rows], np.arange(N))
-            t_rows = time.perf_counter() - t1
-            if t_rows > budget_s / 4 or rows >= M:
-                break
-            rows = min(M, rows * 4)
-        total = t_dec + t_rows * (M / rows)
-        flops = 2.0 * M * N * K * (2 if w.need_dw else 1)
-        sample = (f"whole-operand decode, then dX{' and dW' if w.need_dw else ''} over {rows} of {M} token rows "
-                  f"(fp64), time extrapolated to all rows")
-    return {"value": round(flops / total / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": sample, "seconds": round(total, 3)}
+        def q():
+            hist = np.full(W.AMAX_RING, PT.amax(gb), np.float32)
+            gs = PT.scale_from_history(hist, "e5m2")
+            st["g"] = (PT.quantize(gb, "e5m2", gs), gs)
+            PT.record(hist, 0, PT.amax(gb))
+
+        def prod():
+            gc, gs = st["g"]
+            PT.linear_dx(gc, "e5m2", gs, wc, "e4m3", ws_)
+            PT.linear_dw(gc, "e5m2", gs, xc, "e4m3", xs)
+        parts += [_Part("tensor_quant_delayed grad E5M2", q, M / rows, False, f"{rows} of {M} gradient rows"),
+                  _Part("dX + dW (fp64 products)", prod, M / rows, True, f"{rows} token rows")]
+        return parts, 4.0 * M * N * K
+    if name == "mxfp4_forward":
+        x = W.normal_f32(w.number, "x", (rows, K), w.x_sigma)
+        wt = W.normal_f32(w.number, "w", (N, K), w.w_sigma)
+        xq, wq = F.quant_mxfp4_f32(x[None]), F.quant_mxfp4_f32(wt[None])
+        st = {}
+
+        def dec_w():
+            st["w"] = F.dequant("mxfp4", *wq)[0]
+
+        def dec_x():
+            st["x"] = F.dequant("mxfp4", *xq)[0]
+
+        def fwd():
+            O.linear_fwd(st["x"], st["w"])
+        parts += [_Part("dequant W", dec_w, 1, False, "whole weight"),
+                  _Part("dequant X", dec_x, M / rows, False, f"{rows} of {M} input rows"),
+                  _Part("forward (fp64 product)", fwd, M / rows, True, f"{rows} token rows")]
+        return parts, 2.0 * M * N * K
+    # Saved packed operands (fp8_frozen, nvfp4_linear, mxfp4_grouped, mxfp4_tiny):
+    # decode, then the fp64 products over sampled token rows.
+    X, Wt, G = W.dense_inputs(w, M=rows)
+    fmt = w.fmt
+    quant = {"fp8_b128": F.quant_fp8_b128, "nvfp4": F.quant_nvfp4, "mxfp4": F.quant_mxfp4_f32}[fmt]
+    wq = quant(Wt)
+    xq = quant(X) if X is not None else None
+    st = {}
+
+    def deq(q):
+        return F.dequant(fmt, q[0], q[1], q[2]) if fmt == "nvfp4" else F.dequant(fmt, q[0], q[1])
+
+    def dw_dec():
+        st["w"] = deq(wq)
+
+    parts.append(_Part("dequant W", dw_dec, 1, False, "whole weight" + (f"s of {w.groups} experts" if w.grouped else "")))
+    if xq is not None:
+        def dx_dec():
+            st["x"] = deq(xq)[0]
+        parts.append(_Part("dequant X", dx_dec, M / rows, False, f"{rows} of {M} input rows"))
+
+    def dx():
+        O.rows_dx(G, st["w"][0], np.arange(rows))
+    parts.append(_Part("dX (fp64 product)", dx, M / rows, True, f"{rows} token rows"))
+    if w.need_dw:
+        def dw():
+            O.rows_dw(G, st["x"], np.arange(N))
+        parts.append(_Part("dW (fp64 product)", dw, M / rows, True, f"{rows} token rows of the contraction"))
+    return parts, 2.0 * M * N * K * (2 if w.need_dw else 1)
+
+
+def cpu_baseline(name: str):
+    """The oracle on a bounded sample of the workload's step, kernel by
+    kernel: each kernel's sample time is scaled linearly to the whole step
+    (token rows, or experts' weights).  The contractions run on one thread
+    and on all of BLAS's threads; `value` is the whole step at all threads."""
+    from threadpoolctl import threadpool_limits
+    parts, flops = _oracle_parts(name)
+    cores = _blas_threads()
+    per = {}
+    tot1 = totn = 0.0
+    for part in parts:
+        times = {}
+        for nthreads in ((1, cores) if part.blas else (1,)):
+            with threadpool_limits(limits=nthreads):
+                t0 = time.perf_counter()
+                part.fn()
+                times[nthreads] = (time.perf_counter() - t0) * part.scale
+        s1, sn = times[1], times.get(cores, times[1])
+        tot1 += s1
+        totn += sn
+        per[part.name] = {"s_1_thread": round(s1, 3), f"s_{cores}_threads": round(sn, 3), "sample": part.sample,
+                          "threads": "1 and all (BLAS)" if part.blas else "1 (numpy element-wise)"}
+    return {"value": round(flops / totn / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": "; ".join(f"{p.name}: {p.sample}" for p in parts) + "; each scaled to the whole step",
+            "seconds": round(totn, 3), "seconds_1_thread": round(tot1, 3),
+            "value_1_thread": round(flops / tot1 / 1e12, 6), "cpu_model": _cpu_model(), "per_kernel": per}
 
 
 # ------------------------------------------------------------------ main
@@ -516,7 +593,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=1000)
-    ap.add_argument("--workload", default="fp8_frozen", choices=sorted(W.WORKLOADS))
+    ap.add_argument("--workload", default="mxfp8_deferred", choices=sorted(W.WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
