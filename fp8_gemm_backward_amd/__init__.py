@@ -55,6 +55,7 @@ def _load() -> ctypes.CDLL:
     lib.lp_grouped_bwd.argtypes = [P, P, P, v, i64, v, v, v]
     lib.lp_linear_bwd_workspace.argtypes = [P, P, P, v, v, ctypes.POINTER(ctypes.c_size_t)]
     lib.lp_linear_bwd_ws.argtypes = [P, P, P, v, v, v, ctypes.c_size_t, v]
+    lib.lp_linear_bwd_noalloc.argtypes = [P, P, P, v, v, v]
     lib.lp_tensor_amax.argtypes = [v, i64, v, v]
     lib.lp_tensor_quant.argtypes = [v, i64, i32, v, v, v, v]
     lib.lp_scale_from_history.argtypes = [v, i32, i32, i32, v, v]
@@ -64,7 +65,7 @@ def _load() -> ctypes.CDLL:
     lib.lp_status_string.argtypes = [i32]
     lib.lp_status_string.restype = ctypes.c_char_p
     for f in ("lp_dequant", "lp_mx_quant", "lp_mx_quant_dual", "lp_linear_bwd", "lp_grouped_bwd",
-              "lp_linear_bwd_workspace", "lp_linear_bwd_ws", "lp_tensor_amax", "lp_tensor_quant",
+              "lp_linear_bwd_workspace", "lp_linear_bwd_ws", "lp_linear_bwd_noalloc", "lp_tensor_amax", "lp_tensor_quant",
               "lp_scale_from_history", "lp_linear_fwd", "lp_grouped_fwd", "lp_tensor_quant_delayed"):
         getattr(lib, f).restype = ctypes.c_int32
     return lib
@@ -312,6 +313,33 @@ def lp_linear_bwd(grad_out: QTensor, x: Optional[QTensor], w: Optional[QTensor],
         st = lib.lp_linear_bwd_ws(*args, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                   _stream(stream))
         _check(st, "lp_linear_bwd_ws")
+    return (grad_x if need_dx else None), (grad_w if need_dw else None)
+
+
+def lp_linear_bwd_noalloc(grad_out: QTensor, x: Optional[QTensor], w: Optional[QTensor], need_dx: bool = True,
+                          need_dw: bool = True, grad_x: Optional[torch.Tensor] = None,
+                          grad_w: Optional[torch.Tensor] = None, stream=None):
+    """lp_linear_bwd with the split workspace held inside the library (no
+    device allocation by the call; outputs are allocated here only when not
+    given)."""
+    M, N = grad_out.rows, grad_out.cols
+    K = (w if need_dx else x).cols
+    dev = grad_out.codes.device
+    if need_dx and grad_x is None:
+        grad_x = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    if need_dw and grad_w is None:
+        grad_w = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    if need_dx:
+        _device(grad_x, "grad_x", 2 * M * K)
+    if need_dw:
+        _device(grad_w, "grad_w", 2 * N * K)
+    g = grad_out.c()
+    xc = x.c() if x is not None else None
+    wc = w.c() if w is not None else None
+    st = lib.lp_linear_bwd_noalloc(ctypes.byref(g), ctypes.byref(xc) if xc else None,
+                                   ctypes.byref(wc) if wc else None, grad_x.data_ptr() if need_dx else None,
+                                   grad_w.data_ptr() if need_dw else None, _stream(stream))
+    _check(st, "lp_linear_bwd_noalloc")
     return (grad_x if need_dx else None), (grad_w if need_dw else None)
 
 

@@ -2,6 +2,8 @@
 // Every rule checked here is stated next to the entry point in lp.h.
 #include <stdint.h>
 
+#include <mutex>
+
 #include "lp_internal.hpp"
 
 namespace {
@@ -264,6 +266,80 @@ lp_status lp_linear_bwd_ws(const lp_qtensor* grad_out, const lp_qtensor* x, cons
   if (workspace != nullptr && !aligned(workspace, 256)) return LP_ERR_ALIGN;
   return run_bwd(grad_out, x, w, nullptr, 0, grad_x, grad_w, workspace, workspace_bytes, stream);
 }
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- no-allocation variant
+// The split-contraction workspace of lp_linear_bwd_noalloc: a file-scope
+// device array, one copy per GPU the library runs on, held until the process
+// ends.  A split plan uses at most 256 partial tiles of 256 x 256 fp32
+// (64 MiB: splitting only happens when the output has fewer tiles than the
+// GPU has compute units, and a tile splits at most 256 / tiles ways) plus
+// one u32 counter per tile (at most 64 tiles: 256 bytes); the array adds
+// 4 KiB of headroom for the counters.  Host code never passes `scratch`
+// itself to a kernel (in host code the name is a stand-in, not a device
+// address): it uses the address hipGetSymbolAddress returns for the current
+// device.
+namespace {
+
+constexpr size_t kScratchBytes = ((size_t)64 << 20) + 4096;
+constexpr size_t kScratchCounterBytes = 4096;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+void* g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's copy of `scratch`, looked up once per device.
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return hipSuccess;
+}
+
+// Zero n words: the per-tile counters must start at zero.  A kernel rather
+// than hipMemsetAsync, so that the call can be captured in a graph.
+__global__ void clear_words(uint32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+}  // namespace
+
+extern "C" {
+
+lp_status lp_linear_bwd_noalloc(const lp_qtensor* grad_out, const lp_qtensor* x, const lp_qtensor* w,
+                                void* grad_x, void* grad_w, void* stream) {
+  size_t need = 0;
+  lp_status st = lp_linear_bwd_workspace(grad_out, x, w, grad_x, grad_w, &need);
+  if (st != LP_OK) return st;
+  if (grad_x == nullptr && grad_w == nullptr) return LP_OK;
+  if ((st = check_bwd(grad_out, x, w, grad_x, grad_w, 0)) != LP_OK) return st;
+  if (need > kScratchBytes) return LP_ERR_SHAPE;
+  void* ws = nullptr;
+  if (need > 0) {
+    if (scratch_address(&ws) != hipSuccess) return LP_ERR_HIP;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    constexpr int kWords = (int)(kScratchCounterBytes / 4);
+    clear_words<<<dim3(kWords / 256), dim3(256), 0, s>>>(static_cast<uint32_t*>(ws), kWords);
+    if (hipGetLastError() != hipSuccess) return LP_ERR_HIP;
+  }
+  return run_bwd(grad_out, x, w, nullptr, 0, grad_x, grad_w, ws, need > 0 ? kScratchBytes : 0, stream);
+}
+
+}  // extern "C"
+
+extern "C" {
 
 // Checks of the forward: x [M][K] and w [G][N][K], both MXFP4 or both
 // MXFP8 scaled along k; K % 128 (MXFP4) or K % 64 (MXFP8); N % 16.

@@ -345,6 +345,31 @@ lp_status lp_linear_bwd_ws(const lp_qtensor* grad_out, const lp_qtensor* x, cons
                            void* stream);
 
 /*
+ * lp_linear_bwd_noalloc - lp_linear_bwd_ws for callers that cannot allocate
+ * device memory (code under graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).
+ *
+ * Same operation, arguments, results and errors as lp_linear_bwd_ws, with the
+ * workspace taken from a device array inside the library instead of from the
+ * caller: 64 MiB + 4 KiB per GPU, set aside when the library is loaded and
+ * held until the process ends.  Every contraction that splits fits in it (a
+ * split plan uses at most 256 partial tiles of 256 x 256 fp32); the call
+ * returns LP_ERR_SHAPE if a plan ever needed more.  The call itself allocates
+ * nothing: no hipMalloc, no hipFree, no allocating library routine.  The
+ * array's address on the current device is looked up once (the first call on
+ * that device); LP_ERR_HIP if that lookup fails.  Each call first clears the
+ * array's per-tile counters with a small kernel on `stream` (no memset, so it
+ * can be captured).
+ *
+ * All calls on one GPU share the array, which keeps the last call's partial
+ * tiles: calls that may run at the same time on one GPU (other streams,
+ * other threads) race and must be serialized by the caller.  `stream` must
+ * belong to the current device.
+ */
+lp_status lp_linear_bwd_noalloc(const lp_qtensor* grad_out, const lp_qtensor* x, const lp_qtensor* w,
+                                void* grad_x, void* grad_w, void* stream);
+
+/*
  * lp_grouped_bwd - backward of a grouped (per-expert) matmul.
  *
  * Cites: "Train adapters on top of FP8 weights", FP8GroupedMatmulFunction.

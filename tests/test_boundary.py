@@ -18,7 +18,7 @@ def test_library_exports_every_header_function():
     assert set(names) == {"lp_dequant", "lp_mx_quant", "lp_linear_bwd", "lp_grouped_bwd", "lp_status_string",
                           "lp_linear_bwd_workspace", "lp_linear_bwd_ws", "lp_mx_quant_dual", "lp_tensor_amax",
                           "lp_tensor_quant", "lp_scale_from_history", "lp_linear_fwd", "lp_grouped_fwd",
-                          "lp_tensor_quant_delayed"}
+                          "lp_tensor_quant_delayed", "lp_linear_bwd_noalloc"}
     for n in names:
         assert hasattr(lp.lib, n), n
 
@@ -263,6 +263,19 @@ def test_linear_bwd_ws_rejects_misaligned_workspace():
     w = q("fp8_b128", 8192, 2048)
     assert lp.lib.lp_linear_bwd_ws(ctypes.byref(g), None, ctypes.byref(w), FAKE, None, FAKE + 16, 1 << 30,
                                    None) == ALIGN
+
+
+def test_linear_bwd_noalloc_rejects_before_any_launch():
+    """Argument errors of the no-allocation variant, reported as for
+    lp_linear_bwd, before the library looks up its scratch array."""
+    g = q("bf16", 4096, 8192)
+    w = q("fp8_b128", 8192, 2048)
+    f = lp.lib.lp_linear_bwd_noalloc
+    assert f(ctypes.byref(g), None, None, FAKE, None, None) == NULL                 # dX without a weight
+    assert f(ctypes.byref(g), None, ctypes.byref(w), FAKE + 8, None, None) == ALIGN
+    bad = q("fp8_b128", 8000, 2048)
+    assert f(ctypes.byref(g), None, ctypes.byref(bad), FAKE, None, None) == SHAPE
+    assert f(ctypes.byref(g), None, ctypes.byref(w), None, None, None) == OK          # nothing asked for
 
 
 BIG = (1 << 31) - 32        # below 2^31 and a multiple of 32
