@@ -542,17 +542,20 @@ struct Tile {
 // Map the workgroup to its tile.  s_ends: LDS for the group offsets.  hw:
 // the workgroup's index among the p.ntiles of this contraction, in dispatch
 // order (blockIdx.x unless several contractions share a launch).
+// persistent = true: hw is already the logical tile index (a persistent
+// workgroup's own tile order), and s_ends already holds the group ends.
 template <class C, bool kDW>
-__device__ __forceinline__ Tile select_tile(const Params& p, int32_t* s_ends, int hw = blockIdx.x) {
+__device__ __forceinline__ Tile select_tile(const Params& p, int32_t* s_ends, int hw = blockIdx.x,
+                                            bool persistent = false) {
   const int tid = threadIdx.x;
-  int tile = xcd_remap(hw, p.ntiles);
+  int tile = persistent ? hw : xcd_remap(hw, p.ntiles);
   int split = 0;
   if (p.splits > 1) {                                          // the splits of a tile are neighbours
     split = tile % p.splits;
     tile /= p.splits;
   }
   Tile t{0, 0, 0, 0, 0, p.Ktot, tile, split, true};
-  if (p.offsets != nullptr) {
+  if (p.offsets != nullptr && !persistent) {
     for (int i = tid; i < p.groups; i += NT) s_ends[i] = p.offsets[i];
     __syncthreads();
   }

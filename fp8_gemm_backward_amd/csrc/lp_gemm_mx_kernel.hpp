@@ -107,13 +107,40 @@ constexpr int chunk_bytes() { return kMode == kChunkMode ? kChunkBytes : 16; }
   __shared__ __attribute__((aligned(1024))) uint8_t sc0[chunk_bytes<kMode>()];             \
   __shared__ __attribute__((aligned(1024))) uint8_t sc1[chunk_bytes<kMode>()]
 
+// Persistent grad_X (kPersist): a workgroup runs several tiles in turn, and
+// the loads of a tile's prologue (its first scale chunk and first three
+// slabs) are issued before the previous tile's results are written, so that
+// their latency hides behind that epilogue.  The epilogue then stages
+// through stage 3 only (the prologue fills stages 0..2 and chunk buffer 0)
+// and writes with buffer stores whose masked elements take an out-of-range
+// offset: every wave issues exactly kEpiStores store instructions per tile
+// (and as many stores that write nothing after a prologue it issues
+// itself), so that the barriers of a tile's prologue and first two slabs,
+// which wait for loads issued before those stores (vector memory
+// operations complete in issue order), can count them.
+constexpr int kEpiStores = XWP * XWQ * 2 / (64 * 16);     // 16-byte stores per wave and tile
+constexpr int kEpiRows = 32;                              // rows per epilogue pass
+static_assert(XWQ * 2 * kEpiRows * 4 <= kTileBytes, "four waves' epilogue passes fit one stage");
+
+// What a persistent workgroup carries from one tile to the next.
+struct Persist {
+  int32_t* ends;     // LDS holding the group ends (a stage may hold the next prologue)
+  int next;          // the workgroup's next tile (>= ntiles: none)
+  bool issued;       // this tile's prologue was issued by the previous tile
+};
+
 // One output tile.  hw: the workgroup's index among p.ntiles (see
 // select_tile); indices at or past p.ntiles have no tile.  kFP, kFQ: MFMA
 // format codes of the gradient and the other operand (0 E4M3, 1 E5M2); the
-// MX modes take E4M3 only.
-template <bool kDW, int kMode, int kFP = 0, int kFQ = 0>
-__device__ __forceinline__ void mx_tile(const Params& p, int hw, uint8_t* st0, uint8_t* st1, uint8_t* st2,
-                                        uint8_t* st3, uint8_t* sc0, uint8_t* sc1) {
+// MX modes take E4M3 only.  kPersist (grad_X, chunk mode): hw is the
+// logical tile index, `pst` the workgroup's state.  Returns kNoTile when hw
+// names no tile, else kDone, or kDoneNextIssued when the next tile's
+// prologue has been issued.
+enum : int { kNoTile = 0, kDone = 1, kDoneNextIssued = 2 };
+template <bool kDW, int kMode, int kFP = 0, int kFQ = 0, bool kPersist = false>
+__device__ __forceinline__ int mx_tile(const Params& p, int hw, uint8_t* st0, uint8_t* st1, uint8_t* st2,
+                                        uint8_t* st3, uint8_t* sc0, uint8_t* sc1, Persist* pst = nullptr) {
+  static_assert(!kPersist || (!kDW && kMode == kChunkMode), "persistent tiles: grad_X in chunk mode");
   constexpr bool kChunk = kMode == kChunkMode, kGather = kMode == kGatherMode;
   static_assert(!kDW || !kGather, "dW scale rows (N or K bytes, multiples of 16) always load in chunks");
   static_assert(kMode == kTensorMode || (kFP == 0 && kFQ == 0), "MX operands are E4M3");
@@ -124,12 +151,19 @@ __device__ __forceinline__ void mx_tile(const Params& p, int hw, uint8_t* st0, u
   static_assert(kMaxGroups * 4 <= kStage, "group ends alias stage 0");
   static_assert(XWP * XWQ * 2 <= kStage, "epilogue staging fits a stage");
 
-  const int tid = threadIdx.x, lane = tid & 63;
+  // Persistent tiles: the thread index goes through an empty asm statement
+  // so that the per-lane offsets are formed per tile instead of being held
+  // (and spilled) across the whole walk; a spill reload here would make the
+  // wave wait for the loads the previous tile left in flight.
+  int tid = threadIdx.x;
+  if constexpr (kPersist) asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wp = wave >> 1, wq = wave & 1;
-  if (hw >= p.ntiles) return;
-  const Tile t = select_tile<XCfg, kDW>(p, reinterpret_cast<int32_t*>(st0), hw);
-  if (!t.valid) return;
+  if (hw >= p.ntiles) return kNoTile;
+  const Tile t = kPersist ? select_tile<XCfg, kDW>(p, pst->ends, hw, true)
+                          : select_tile<XCfg, kDW>(p, reinterpret_cast<int32_t*>(st0), hw);
+  if (!t.valid) return kNoTile;
   __syncthreads();                                               // group ends read; stage 0 reusable
 
   const int ldp = p.P.code_ld;                                   // N bytes per gradient row
@@ -347,15 +381,27 @@ __device__ __forceinline__ void mx_tile(const Params& p, int hw, uint8_t* st0, u
   constexpr int NM = XFP * XFQ;
 
   const int nk = (kend - kbeg + XBK - 1) / XBK;
+  // Persistent tiles: kEpiStores stores that write nothing (inline
+  // assembly: the compiler would merge identical stores into one).
+  auto no_stores = [&]() {
+    const Rsrc none = make_rsrc(p.C, 0);
+    const int32_t oob = kOOB;
+#pragma unroll
+    for (int i = 0; i < kEpiStores; ++i)
+      asm volatile("buffer_store_dword %0, %1, %2, 0 offen" ::"v"(0), "v"(oob), "s"(none) : "memory");
+  };
   if (nk > 0) {
     // Prologue: (chunk 0,) slabs 0, 1, 2 in flight; slab 0 landed and
     // published; its fragments read.
-    if constexpr (kChunk) issue_chunk(chunkbuf(IC<0>{}), kbeg);
-    static_for<3>([&](auto si) {
-      constexpr int s = decltype(si)::value;
-      static_for<T>([&](auto u) { issue(u, stage(si), kbeg + s * XBK); });
-    });
-    barrier_vm<2 * T>();
+    if (!kPersist || !pst->issued) {
+      if constexpr (kChunk) issue_chunk(chunkbuf(IC<0>{}), kbeg);
+      static_for<3>([&](auto si) {
+        constexpr int s = decltype(si)::value;
+        static_for<T>([&](auto u) { issue(u, stage(si), kbeg + s * XBK); });
+      });
+      if constexpr (kPersist) no_stores();
+    }
+    barrier_vm<2 * T + (kPersist ? kEpiStores : 0)>();
     static_for<NREAD>([&](auto r) { read(r, IC<0>{}, IC<0>{}, stage(IC<0>{}), chunkbuf(IC<0>{}), kbeg); });
   }
 
@@ -367,8 +413,14 @@ __device__ __forceinline__ void mx_tile(const Params& p, int hw, uint8_t* st0, u
     constexpr int CUR = J & 1, NXT = CUR ^ 1;
     constexpr int S8 = J % kChunkSlabs, S8N = (J + 1) % kChunkSlabs;
     // Loads issued after slab k+1's tiles: slab k+2's, plus a scale chunk
-    // issued at chunk position 4 of slab k-1.
-    barrier_vm<T + ((kChunk && S8 == 5) ? S : 0)>();
+    // issued at chunk position 4 of slab k-1 (persistent tiles: plus the
+    // previous epilogue's stores, issued after slabs 1 and 2).
+    if constexpr (kPersist && J < 2) {
+      if (k < 2) barrier_vm<T + kEpiStores>();
+      else barrier_vm<T>();
+    } else {
+      barrier_vm<T + ((kChunk && S8 == 5) ? S : 0)>();
+    }
     uint8_t* const nxt = stage(IC<J + 1>{});
     uint8_t* const dst = stage(IC<J + 3>{});
     const uint8_t* const cnxt = chunkbuf(IC<(J + 1) / kChunkSlabs>{});
@@ -396,17 +448,125 @@ __device__ __forceinline__ void mx_tile(const Params& p, int hw, uint8_t* st0, u
   }
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   __syncthreads();
-  uint8_t* stg = wave == 0 ? st0 : wave == 1 ? st1 : wave == 2 ? st2 : st3;
-  if constexpr (kMode == kTensorMode)
-    store_acc<XCfg, kDW, true>(p, t, acc, wp, wq, lane, stg, *p.P.tensor_scale * *p.Q.tensor_scale);
-  else
-    store_acc<XCfg, kDW>(p, t, acc, wp, wq, lane, stg);
+  if constexpr (kPersist) {
+    // The next tile's prologue, then this tile's results.
+    bool issued = false;
+    if (pst->next < p.ntiles) {
+      const Tile tn = select_tile<XCfg, kDW>(p, pst->ends, pst->next, true);
+      if (tn.valid && tn.kend > tn.kbeg) {
+        const uint8_t* const npc = p.P.codes + (int64_t)tn.p0 * ldp;
+        const int64_t nprow = (int64_t)(M - tn.p0) * ldp;
+        const uint8_t* const nqc = p.Q.codes + (int64_t)tn.g * p.Q.code_batch;
+        const Rsrc nps_r = make_rsrc(p.P.scales + (int64_t)tn.p0 * sldp, (int64_t)(M - tn.p0) * sldp);
+        const Rsrc nqs_r = make_rsrc(p.Q.scales + (int64_t)tn.g * p.Q.scale_batch, p.Q.scale_bytes);
+        const int32_t nq_base = (16 * wave + lane / 16) * ldq + tn.q0;
+        dma<16>(nps_r, (lds_void*)(sc0 + 1024 * wave), (64 * wave + lane) * sldp, 0);
+        dma<16>(nqs_r, (lds_void*)(sc0 + XBP * 16 + 1024 * wave), (4 * wave + lane / 16) * sldq + tn.q0 + 16 * (lane & 15), 0);
+        static_for<3>([&](auto si) {
+          constexpr int sl = decltype(si)::value;
+          const int k0 = sl * XBK;
+          uint8_t* const sb = stage(si);
+          static_for<4>([&](auto ui) {
+            constexpr int u = decltype(ui)::value;
+            const Rsrc r = make_rsrc(npc + k0, nprow - k0);
+            dma<16>(r, (lds_void*)(sb + 1024 * (4 * wave + u)), k0 + p_col >= tn.kend ? kOOB : p_off, 16 * u * ldp);
+          });
+          static_for<4>([&](auto vi) {
+            constexpr int v = decltype(vi)::value;
+            const Rsrc r = make_rsrc(nqc + (int64_t)k0 * ldq, (int64_t)(tn.kend - k0) * ldq);
+            dma<16>(r, (lds_void*)(sb + kPBytes + 1024 * (4 * wave + v)), nq_base + 16 * ((v & 1) ? (qc0 ^ 8) : qc0),
+                    4 * v * ldq);
+          });
+        });
+        issued = true;
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // Results through stage 3: four passes of 32 rows per wave, 8 KiB each.
+    // The lane index goes through an empty asm statement so that the
+    // staging addresses are formed here, not held from the kernel's start;
+    // scheduling fences keep the passes apart (converting every result at
+    // once would hold all of them in registers).
+    constexpr int ROWB = XWQ * 2;
+    int el = lane;
+    asm volatile("" : "+v"(el));
+    uint8_t* const stg = st3 + wave * (ROWB * kEpiRows);
+    const int row0 = t.p0 + wp * XWP, col0 = t.q0 + wq * XWQ;
+    const Rsrc orsrc = make_rsrc(p.C + (int64_t)row0 * p.ldc + col0, ((int64_t)(M - row0) * p.ldc - col0) * 2);
+    const int c16 = el & 15;
+    const bool col_ok = col0 + 8 * c16 < p.Qtot;
+#pragma unroll
+    for (int i = 0; i < XFP; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int r = el & 31;
+#pragma unroll
+      for (int j = 0; j < XFQ; ++j) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int sl = (j * 32 + 8 * r4 + 4 * (el >> 5)) / 4;
+          const u32x2 v = {pack_bf16x2(acc[i][j][4 * r4], acc[i][j][4 * r4 + 1]),
+                           pack_bf16x2(acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3])};
+          *reinterpret_cast<u32x2*>(stg + r * ROWB + 8 * (sl ^ (r & 15))) = v;
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);                        // lgkmcnt(0): the pass is staged
+#pragma unroll
+      for (int it = 0; it < kEpiRows / 4; ++it) {
+        const int rr = it * 4 + el / 16;
+        const uint8_t* src = stg + rr * ROWB;
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(src + 8 * ((2 * c16) ^ (rr & 15)));
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(src + 8 * ((2 * c16 + 1) ^ (rr & 15)));
+        const int32_t off = (row0 + i * kEpiRows + rr < t.pend && col_ok)
+                                ? ((i * kEpiRows + rr) * p.ldc + 8 * c16) * 2 : kOOB;
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{lo[0], lo[1], hi[0], hi[1]}, orsrc, off, 0, 0);
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);                        // read back before the next pass overwrites
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return issued ? kDoneNextIssued : kDone;
+  } else {
+    uint8_t* stg = wave == 0 ? st0 : wave == 1 ? st1 : wave == 2 ? st2 : st3;
+    if constexpr (kMode == kTensorMode)
+      store_acc<XCfg, kDW, true>(p, t, acc, wp, wq, lane, stg, *p.P.tensor_scale * *p.Q.tensor_scale);
+    else
+      store_acc<XCfg, kDW>(p, t, acc, wp, wq, lane, stg);
+    return kDone;
+  }
 }
 
 template <bool kDW, int kMode, int kFP = 0, int kFQ = 0>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void fp8_mfma_kernel(Params p) {
   LP_MX_LDS(kMode);
   mx_tile<kDW, kMode, kFP, kFQ>(p, blockIdx.x, st0, st1, st2, st3, sc0, sc1);
+}
+
+// Persistent grad_X (MXFP8, chunk mode): one workgroup per compute unit
+// walks the tile list.  Workgroup b runs on XCD b % 8 (the hardware deals
+// workgroups to the XCDs in turn); at each step the 32 workgroups of an XCD
+// take 32 consecutive tiles (the column tiles of about one gradient row
+// tile, which that XCD's L2 then holds once), and the eight XCDs take
+// neighbouring row tiles, so that row tiles of one large expert share that
+// expert's weight slices in the Infinity Cache.  The grouped tile list ends
+// with its unused entries, so the first missing tile ends the walk.  Tiles
+// with an empty contraction issue no loads; the next tile then issues its
+// own prologue.
+template <int kFP = 0, int kFQ = 0>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void fp8_mfma_persistent(Params p) {
+  LP_MX_LDS(kChunkMode);
+  __shared__ int32_t s_ends[kMaxGroups];
+  const int nwg = gridDim.x, xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  Persist ps{s_ends, 0, false};
+  if (p.offsets != nullptr) {
+    for (int i = threadIdx.x; i < p.groups; i += NT) s_ends[i] = p.offsets[i];
+    __syncthreads();
+  }
+  for (int l = xcd * (nwg / 8) + slot; l < p.ntiles; l += nwg) {
+    ps.next = l + nwg;
+    const int r = mx_tile<false, kChunkMode, kFP, kFQ, true>(p, l, st0, st1, st2, st3, sc0, sc1, &ps);
+    if (r == kNoTile) break;
+    ps.issued = r == kDoneNextIssued;
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // grad_X and grad_W of one per-tensor scaled gradient in one launch: the

@@ -163,6 +163,63 @@ def test_native_mx_grouped_edges(lp, N):
     assert np.all(bits_host(dx[end:]) == 0xFFFF), "rows past the last offset were written"
 
 
+def _mx_grad_with_nan_rows(lp, number, M, N, nan_rows):
+    """MXFP8 gradient (scales along -1) whose listed rows each get one NaN
+    scale block; returns the descriptor and the oracle's decoded bits."""
+    gbits = W.bf16_bits(W.normal_f32(number, "grad", (1, M, N), 1.0))
+    gc, gs = F.mx_quant(gbits, -1, "e4m3")
+    gs = gs.copy()
+    for i, r in enumerate(nan_rows):
+        gs[0, r, (7 * i) % (N // 32)] = 0xFF
+    g = lp.QTensor("mxfp8", dev(gc[0]), dev(gs[0]), shape=(1, M, N), axis=-1)
+    return g, F.dequant("mxfp8", gc, gs, axis=-1)[0]
+
+
+def test_native_mx_persistent_grouped(lp):
+    """More tiles than compute units: one workgroup per compute unit walks the
+    tile list, issuing each tile's first loads before the previous tile's
+    results are written (about 2.5 tiles per workgroup here).  37 groups
+    (empty ones, groups of a few rows, groups spanning several row tiles),
+    rows past the last offset kept, a contraction of 24 slabs (N = 1536, not
+    a whole number of 16-slab passes), a partial last column tile (K =
+    2064), and two gradient rows
+    with a NaN scale block, which must come out NaN and leave every other
+    row finite."""
+    M, N, K, G = 10000, 1536, 2064, 37
+    sizes = W.rng(48, "route").integers(0, 400, size=G)
+    sizes[10] = 900
+    sizes = (sizes * (M - 150) // sizes.sum()).astype(np.int64)
+    sizes[[3, 4, 20]] = 0
+    sizes[[5, 6]] = [1, 31]
+    assert 0 < sizes.sum() < M
+    offsets = W.cumulative_ends(sizes)
+    end = int(offsets[-1])
+    nan_rows = [int(offsets[9]) + 3, end - 1]
+    g, gd = _mx_grad_with_nan_rows(lp, 48, M, N, nan_rows)
+    w, wd = _operand(lp, 48, "w", (G, N, K), "mxfp8", -2, sigma=0.02)
+    dx0 = _sentinel((M, K))
+    dx, _ = lp.lp_grouped_bwd(g, None, w, torch.from_numpy(offsets).cuda(), need_dw=False, grad_x=dx0)
+    torch.cuda.synchronize()
+    got = dx.float().cpu().numpy()
+    assert np.all(bits_host(dx[end:]) == 0xFFFF), "rows past the last offset were written"
+    assert np.isnan(got[nan_rows]).all(), "a NaN scale block must make its output row NaN"
+    fin = np.setdiff1d(np.arange(end), nan_rows)
+    assert not np.isnan(got[fin]).any(), "NaN outside the rows with a NaN scale block"
+    ref, _ = O.grouped_dx(gd, wd, offsets)
+    assert_close(dx[torch.from_numpy(fin).cuda()], ref[fin], "persistent grouped dX")
+
+
+def test_native_mx_persistent_dense(lp):
+    """Dense dX with 17 x 17 output tiles (ragged M, partial tiles on both
+    sides) through the persistent walk."""
+    M, N, K = 4100, 1024, 4336
+    g, gd = _grad(lp, 49, M, N, fmt="mxfp8")
+    w, wd = _operand(lp, 49, "w", (N, K), "mxfp8", -2, sigma=0.02)
+    dx, _ = lp.lp_linear_bwd(g, None, w, need_dw=False)
+    torch.cuda.synchronize()
+    assert_close(dx, O.linear_dx(gd, wd[0]), "persistent dense dX")
+
+
 def test_native_mx_matches_decode_path_with_nan_blocks(lp):
     """The block-scaled MFMA and the decode-to-bf16 path agree: on finite
     blocks within the tolerance, and a gradient block with scale 0xFF (NaN)
@@ -424,9 +481,11 @@ def test_mxfp4_grouped_full_size(lp):
 
 def test_mxfp8_deferred_full_size(lp):
     """64 experts, 32768 tokens with Zipf(1.1) sizes: the GPU quantizes grad
-    (along -1) and W (along the reduction axis) and runs grouped dX; sampled
-    rows are checked against the oracle's own quantization of the same bf16
-    inputs."""
+    (along -1) and W (along the reduction axis) and runs grouped dX.  Every
+    non-empty expert is checked on 3 sampled rows x 96 sampled output
+    columns against the oracle's own quantization of the same bf16 inputs
+    (a column of W quantized along the reduction axis depends on that
+    column alone), and the two largest experts on 8 whole rows."""
     w = W.WORKLOADS["mxfp8_deferred"]
     offsets = W.cumulative_ends(W.group_sizes(w))
     Wt = W.torch_normal_bf16((w.groups, w.N, w.K), w.w_sigma, seed=5005, device="cuda")
@@ -437,19 +496,28 @@ def test_mxfp8_deferred_full_size(lp):
     dx, _ = lp.lp_grouped_bwd(gq, None, wq, torch.from_numpy(offsets).cuda(), need_dw=False)
     torch.cuda.synchronize()
     bounds = O.group_bounds(offsets)
-    experts = [int(np.argmax(np.diff([0] + list(offsets))))] + [int(e) for e in W.rng(44, "x").choice(w.groups, 3)]
-    for gi in experts:
-        s, e = bounds[gi]
+    sizes = np.diff([0] + list(offsets))
+    biggest = set(int(i) for i in np.argsort(-sizes)[:2])
+    cols = np.sort(W.rng(44, "x").choice(w.K, 96, replace=False))
+    tcols = torch.from_numpy(cols).cuda()
+    checked = 0
+    for gi, (s, e) in enumerate(bounds):
         if e == s:
             continue
-        rows = s + _sample_rows(e - s, 8, 45 + gi)
-        gbits = Gt[torch.from_numpy(rows).cuda()].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        full = gi in biggest
+        rows = s + _sample_rows(e - s, 8 if full else 3, 45 + gi)
+        trows = torch.from_numpy(rows).cuda()
+        gbits = Gt[trows].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
         gc, gs = F.mx_quant(gbits[None], -1, "e4m3")
         g_deq = F.dequant("mxfp8", gc, gs, axis=-1)[0]
-        wbits = Wt[gi].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        wsel = Wt[gi] if full else Wt[gi][:, tcols]
+        wbits = wsel.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
         wc, ws = F.mx_quant(wbits[None], -2, "e4m3")
         w_deq = F.dequant("mxfp8", wc, ws, axis=-2)[0]
-        assert_close(dx[torch.from_numpy(rows).cuda()], O.linear_dx(g_deq, w_deq), f"expert {gi} dX")
+        got = dx[trows] if full else dx[trows][:, tcols]
+        assert_close(got, O.linear_dx(g_deq, w_deq), f"expert {gi} dX")
+        checked += 1
+    assert checked == int((sizes > 0).sum())
 
 
 def test_mxfp8_dense_full_size(lp):
