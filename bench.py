@@ -4,8 +4,11 @@
 
 A step is one pass of the workload's whole backward path over one batch of
 synthetic input already resident in HBM:
-  mxfp8_deferred  lp_mx_quant(grad, -1) + lp_mx_quant(W, -2) + lp_grouped_bwd dX over
-                  64 experts (default: the largest workload, 962 GFLOP per step)
+  mxfp8_deferred  lp_mx_quant(grad, -1) + lp_grouped_dx_deferred: grouped dX over 64 experts
+                  against the bf16 weight quantized to MXFP8 along its reduction axis, inside
+                  the product for experts of at most 256 tokens (default: the largest
+                  workload, 962 GFLOP per step; --unfused: lp_mx_quant(W, -2) then
+                  lp_grouped_bwd)
   fp8_frozen      lp_dequant of a frozen FP8 128x128-block weight to bf16, then
                   lp_linear_bwd: dX against the bf16 copy
   nvfp4_linear    lp_linear_bwd: dX and dW, NVFP4 X and W
@@ -59,6 +62,7 @@ PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA (the block-scaled MXFP8 c
 PEAK_FP4_TFLOPS = 10100.0      # MI355X dense fp4 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 ROTATE_BYTES = 1 << 30
+UNFUSED = False                # mxfp8_deferred: the three-call step instead of lp_grouped_dx_deferred
 
 
 # ------------------------------------------------------------------ input preparation (torch, GPU)
@@ -196,25 +200,43 @@ def build(lp, name: str):
         wt = W.torch_normal_bf16((w.groups, N, K), w.w_sigma, 7601, "cuda")
         gq = lp.lp_mx_quant(g, -1, "mxfp8")
         wq = lp.lp_mx_quant(wt, -2, "mxfp8")
+        gq.shape = (1, M, N)
         dx = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
         sets.append((g, wt, gq, wq, dx))
         phases.append(Phase("mx_quant grad", "mx_quant_cols", nbytes=M * N * (2 + 1 + 1 / 32)))
-        phases.append(Phase("mx_quant W", "mx_quant_rows", nbytes=w.groups * N * K * (2 + 1 + 1 / 32)))
-        # MXFP8 x MXFP8 with both scales along the contraction: block-scaled FP8 MFMA
-        phases.append(Phase("grouped_bwd dX", "fp8_mfma_kernel", flops=2.0 * M * N * K, peak=PEAK_FP8_TFLOPS))
+        if UNFUSED:
+            phases.append(Phase("mx_quant W", "mx_quant_tile", nbytes=w.groups * N * K * (2 + 1 + 1 / 32)))
+            # MXFP8 x MXFP8 with both scales along the contraction: block-scaled FP8 MFMA
+            phases.append(Phase("grouped_bwd dX", "fp8_mfma_persistent", flops=2.0 * M * N * K,
+                                peak=PEAK_FP8_TFLOPS))
 
-        def step(i, stream):
-            g, wt, gq, wq, dx = sets[0]
-            ev = _events(stream)
-            lp.lp_mx_quant(g, -1, "mxfp8", codes=gq.codes, scales=gq.scales, stream=stream)
-            t0 = ev.stop(stream)
-            ev = _events(stream)
-            lp.lp_mx_quant(wt, -2, "mxfp8", codes=wq.codes, scales=wq.scales, stream=stream)
-            t1 = ev.stop(stream)
-            ev = _events(stream)
-            gq.shape = (1, M, N)
-            lp.lp_grouped_bwd(gq, None, wq, offsets, need_dw=False, grad_x=dx, stream=stream)
-            return [t0, t1, ev.stop(stream)]
+            def step(i, stream):
+                g, wt, gq, wq, dx = sets[0]
+                ev = _events(stream)
+                lp.lp_mx_quant(g, -1, "mxfp8", codes=gq.codes, scales=gq.scales, stream=stream)
+                t0 = ev.stop(stream)
+                ev = _events(stream)
+                lp.lp_mx_quant(wt, -2, "mxfp8", codes=wq.codes, scales=wq.scales, stream=stream)
+                t1 = ev.stop(stream)
+                ev = _events(stream)
+                lp.lp_grouped_bwd(gq, None, wq, offsets, need_dw=False, grad_x=dx, stream=stream)
+                return [t0, t1, ev.stop(stream)]
+        else:
+            # One call: the weight is quantized inside the product for experts
+            # of at most 256 tokens, first (into wq) for the others.
+            phases.append(Phase("grouped_dx_deferred (W quant + dX)",
+                                "mx_quant_rows_groups + fp8_mfma_persistent + fp8_mfma_wquant_kernel",
+                                flops=2.0 * M * N * K, peak=PEAK_FP8_TFLOPS))
+
+            def step(i, stream):
+                g, wt, gq, wq, dx = sets[0]
+                ev = _events(stream)
+                lp.lp_mx_quant(g, -1, "mxfp8", codes=gq.codes, scales=gq.scales, stream=stream)
+                t0 = ev.stop(stream)
+                ev = _events(stream)
+                lp.lp_grouped_dx_deferred(gq, wt, offsets, fuse_rows=256, grad_x=dx, w_codes=wq.codes,
+                                          w_scales=wq.scales, stream=stream)
+                return [t0, ev.stop(stream)]
         standalone = []
     elif name == "mxfp8_dense":
         g = W.torch_normal_bf16((M, N), 1.0, 7700, "cuda")
@@ -595,7 +617,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--workload", default="mxfp8_deferred", choices=sorted(W.WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
+    ap.add_argument("--unfused", action="store_true",
+                    help="mxfp8_deferred: quantize the whole weight first (three calls) instead of lp_grouped_dx_deferred")
     a = ap.parse_args()
+    global UNFUSED
+    UNFUSED = a.unfused
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
@@ -666,7 +692,9 @@ def main():
         "vs_baseline": None, "data": "synthetic",
         "dtype": "fp4" if w.name == "mxfp4_forward" else ("fp8" if w.fmt in ("mxfp8", "fp8t") else "bf16"),
         "config": {"workload": w.name, "format": w.fmt, "M": w.M, "N": w.N, "K": w.K, "groups": w.groups,
-                   "grad_x": w.need_dx, "grad_w": w.need_dw, "global_batch": w.M, "parallelism": "none (1 GPU)"},
+                   "grad_x": w.need_dx, "grad_w": w.need_dw, "global_batch": w.M, "parallelism": "none (1 GPU)",
+                   **({"weight_quant": "three calls" if UNFUSED else "inside the product for experts <= 256 tokens"}
+                      if w.name == "mxfp8_deferred" else {})},
         "roofline": roof, "phases": phase_rec, "standalone_hbm": hbm,
     }
     if not a.no_cpu:

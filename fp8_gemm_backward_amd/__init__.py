@@ -56,6 +56,7 @@ def _load() -> ctypes.CDLL:
     lib.lp_linear_bwd_workspace.argtypes = [P, P, P, v, v, ctypes.POINTER(ctypes.c_size_t)]
     lib.lp_linear_bwd_ws.argtypes = [P, P, P, v, v, v, ctypes.c_size_t, v]
     lib.lp_linear_bwd_noalloc.argtypes = [P, P, P, v, v, v]
+    lib.lp_grouped_dx_deferred.argtypes = [P, v, i64, v, i64, i64, v, v, v, v]
     lib.lp_tensor_amax.argtypes = [v, i64, v, v]
     lib.lp_tensor_quant.argtypes = [v, i64, i32, v, v, v, v]
     lib.lp_scale_from_history.argtypes = [v, i32, i32, i32, v, v]
@@ -65,7 +66,7 @@ def _load() -> ctypes.CDLL:
     lib.lp_status_string.argtypes = [i32]
     lib.lp_status_string.restype = ctypes.c_char_p
     for f in ("lp_dequant", "lp_mx_quant", "lp_mx_quant_dual", "lp_linear_bwd", "lp_grouped_bwd",
-              "lp_linear_bwd_workspace", "lp_linear_bwd_ws", "lp_linear_bwd_noalloc", "lp_tensor_amax", "lp_tensor_quant",
+              "lp_linear_bwd_workspace", "lp_linear_bwd_ws", "lp_linear_bwd_noalloc", "lp_grouped_dx_deferred", "lp_tensor_amax", "lp_tensor_quant",
               "lp_scale_from_history", "lp_linear_fwd", "lp_grouped_fwd", "lp_tensor_quant_delayed"):
         getattr(lib, f).restype = ctypes.c_int32
     return lib
@@ -341,6 +342,37 @@ def lp_linear_bwd_noalloc(grad_out: QTensor, x: Optional[QTensor], w: Optional[Q
                                    grad_w.data_ptr() if need_dw else None, _stream(stream))
     _check(st, "lp_linear_bwd_noalloc")
     return (grad_x if need_dx else None), (grad_w if need_dw else None)
+
+
+def lp_grouped_dx_deferred(grad_out: QTensor, w: torch.Tensor, offsets: torch.Tensor, fuse_rows: int = 256,
+                           grad_x: Optional[torch.Tensor] = None, w_codes: Optional[torch.Tensor] = None,
+                           w_scales: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """grad_X of the deferred MXFP8 recipe: grad_out (MXFP8 along -1) times
+    the bf16 weight w [G, N, K] quantized to MXFP8 along N; groups of at most
+    fuse_rows rows quantize their weight inside the product.  w_codes /
+    w_scales (the weight's MXFP8 copy for the larger groups) are allocated
+    here when not given and fuse_rows < M."""
+    G, N, K = w.shape
+    M = grad_out.rows
+    dev = grad_out.codes.device
+    if grad_x is None:
+        grad_x = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    if fuse_rows < M or N % 512 or K % 32:
+        if w_codes is None:
+            w_codes = torch.empty((G, N, K), dtype=torch.uint8, device=dev)
+        if w_scales is None:
+            w_scales = torch.empty((G, N // 32, K), dtype=torch.uint8, device=dev)
+        _device(w_codes, "w_codes", G * N * K)
+        _device(w_scales, "w_scales", G * (N // 32) * K)
+    _device(w, "w", 2 * G * N * K, torch.bfloat16)
+    _device(offsets, "offsets", 4 * G, torch.int32)
+    _device(grad_x, "grad_x", 2 * M * K)
+    g = grad_out.c()
+    st = lib.lp_grouped_dx_deferred(ctypes.byref(g), w.data_ptr(), K, offsets.data_ptr(), G, fuse_rows,
+                                    grad_x.data_ptr(), None if w_codes is None else w_codes.data_ptr(),
+                                    None if w_scales is None else w_scales.data_ptr(), _stream(stream))
+    _check(st, "lp_grouped_dx_deferred")
+    return grad_x
 
 
 def lp_linear_bwd_workspace(grad_out: QTensor, x: Optional[QTensor], w: Optional[QTensor], need_dx: bool = True,

@@ -387,6 +387,29 @@ lp_status lp_grouped_bwd(const lp_qtensor* grad_out, const lp_qtensor* x, const 
   return run_bwd(grad_out, x, w, offsets, groups, grad_x, grad_w, nullptr, 0, stream);
 }
 
+lp_status lp_grouped_dx_deferred(const lp_qtensor* grad_out, const void* w, int64_t K, const int32_t* offsets,
+                                 int64_t groups, int64_t fuse_rows, void* grad_x, void* w_codes, void* w_scales,
+                                 void* stream) {
+  if (groups < 1 || groups > 1024 || fuse_rows < 0 || K < 0 || K > kMaxDim) return LP_ERR_SHAPE;
+  lp_status st = check_tensor(grad_out);
+  if (st != LP_OK) return st;
+  if (grad_out->fmt != LP_MXFP8 || grad_out->scale_axis != -1) return LP_ERR_FORMAT;
+  if (grad_out->batch != 1) return LP_ERR_SHAPE;
+  const int64_t M = grad_out->rows, N = grad_out->cols;
+  int64_t n = 0;
+  if (K % 16 || !count_ok(groups, N, K, &n)) return LP_ERR_SHAPE;
+  if (M >= kMaxProductRows || N >= kMaxProductCols || K >= kMaxProductCols) return LP_ERR_SHAPE;
+  if (!tiles_ok(M / 128 + groups + 1, K)) return LP_ERR_SHAPE;
+  if (offsets == nullptr) return LP_ERR_NULL;
+  if (!aligned(offsets, 4)) return LP_ERR_ALIGN;
+  if (M * K == 0) return LP_OK;
+  if (grad_x == nullptr || (n > 0 && w == nullptr)) return LP_ERR_NULL;
+  if ((fuse_rows < M || N % 512 || K % 32) && n > 0 && (w_codes == nullptr || w_scales == nullptr)) return LP_ERR_NULL;
+  if (!aligned(grad_x, 16) || !aligned(w, 16) || !aligned(w_codes, 16) || !aligned(w_scales, 16)) return LP_ERR_ALIGN;
+  return hip_status(lp::launch_grouped_dx_deferred(*grad_out, w, K, offsets, (int32_t)groups, fuse_rows, w_codes,
+                                                   w_scales, grad_x, static_cast<hipStream_t>(stream)));
+}
+
 const char* lp_status_string(int32_t s) {
   switch (s) {
     case LP_OK: return "ok";

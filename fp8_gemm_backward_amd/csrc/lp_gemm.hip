@@ -169,6 +169,8 @@ Params base_params(const GemmCall& call) {
   prm.offsets = call.offsets;
   prm.groups = call.groups;
   prm.splits = 1;
+  prm.fuse_rows = call.fuse_rows;
+  prm.fuse_side = call.fuse_side;
   if (!call.dw) {
     prm.Ptot = (int32_t)call.M;
     prm.Ktot = (int32_t)call.N;
@@ -242,6 +244,47 @@ hipError_t launch_fwd(const lp_qtensor& x, const lp_qtensor& w, const int32_t* o
   const int64_t ptiles = offsets ? (x.rows / Big::BP + groups) : (x.rows + Big::BP - 1) / Big::BP;
   prm.ntiles = (int32_t)(ptiles * prm.nq);
   return fwd_mx(prm, x.fmt == LP_MXFP4, stream);
+}
+
+hipError_t launch_grouped_dx_deferred(const lp_qtensor& grad, const void* w, int64_t K, const int32_t* offsets,
+                                      int32_t groups, int64_t fuse_rows, void* w_codes, void* w_scales,
+                                      void* grad_x, hipStream_t stream) {
+  const int64_t M = grad.rows, N = grad.cols;
+  // The fused kernel takes the gradient's scales in 16-byte chunks of its
+  // scale rows (N % 512 == 0), and the quantizer that leaves out the fused
+  // groups works on 32 x 32 tiles (K % 32 == 0); otherwise every weight is
+  // quantized first.
+  const bool can_fuse = N % 512 == 0 && K % 32 == 0;
+  const int32_t fr = can_fuse ? (int32_t)(fuse_rows < M ? fuse_rows : M) : 0;
+  // Groups of more than fr rows: weight quantized first, then the
+  // block-scaled product on its codes.
+  if (fr < M) {
+    hipError_t e = fr > 0 ? launch_mx_quant_rows_groups(w, groups, N, K, offsets, M, fr, w_codes, w_scales, stream)
+                          : launch_mx_quant(w, groups, N, K, -2, LP_MXFP8, w_codes, w_scales, stream);
+    if (e != hipSuccess) return e;
+    const lp_qtensor wq{LP_MXFP8, -2, groups, N, K, w_codes, w_scales, nullptr};
+    GemmCall c{false, &grad, &wq, offsets, groups, M, N, K, grad_x, nullptr, 0};
+    c.fuse_rows = fr;
+    c.fuse_side = fr > 0 ? 1 : 0;
+    if ((e = launch_gemm(c, stream)) != hipSuccess) return e;
+  }
+  // Groups of at most fr rows: the weight quantized inside the product.
+  if (fr > 0) {
+    const lp_qtensor wb{LP_BF16, -1, groups, N, K, w, nullptr, nullptr};
+    GemmCall c{false, &grad, &wb, offsets, groups, M, N, K, grad_x, nullptr, 0};
+    Params prm = base_params(c);
+    prm.fuse_rows = fr;
+    prm.fuse_side = 2;
+    prm.nq = (int32_t)((K + 255) / 256);
+    // Row tiles of the listed groups: at most M / 256 + G, and at most
+    // G ceil(fr / 256).
+    int64_t rt = M / 256 + groups;
+    const int64_t rt2 = (int64_t)groups * ((fr + 255) / 256);
+    rt = rt2 < rt ? rt2 : rt;
+    prm.ntiles = (int32_t)(rt * prm.nq);
+    return dx_wquant(prm, stream);
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_gemm_pair(const GemmCall& dx, const GemmCall& dw, hipStream_t stream) {

@@ -116,6 +116,12 @@ struct Params {
   int32_t split_len;     // multiple of BK
   float* ws;             // fp32 partial tiles [tile][split][BP * BQ]
   uint32_t* cnt;         // per-tile arrival counters, zero between calls
+  // Grouped grad_X split by group size (small groups quantize their weight
+  // inside the product, in a launch of their own): fuse_side 1 lists no
+  // tiles for groups of at most fuse_rows rows, 2 lists tiles for those
+  // only, 0 lists every group.
+  int32_t fuse_rows;
+  int32_t fuse_side;
 };
 
 template <int kBP, int kBQ>
@@ -574,10 +580,30 @@ __device__ __forceinline__ Tile select_tile(const Params& p, int32_t* s_ends, in
     } else {
       int start = 0, seen = 0;
       t.p0 = -1;
+      if (p.fuse_side != 0 && !persistent && p.splits == 1) {
+        // A filtered listing, whose tile count the host only bounds: deal
+        // the listed tiles themselves over the XCDs, or the bound's empty
+        // tail would leave whole XCDs idle.
+        int n = 0;
+        for (int gi = 0; gi < p.groups; ++gi) {
+          int e = s_ends[gi];
+          e = e < start ? start : (e > p.Ptot ? p.Ptot : e);
+          const bool listed = (e - start <= p.fuse_rows) == (p.fuse_side == 2);
+          n += listed ? (e - start + C::BP - 1) / C::BP : 0;
+          start = e;
+        }
+        const int nt = n * p.nq;
+        tile = hw < nt ? xcd_remap(hw, nt) : nt;                 // nt: past every listed tile
+        pidx = tile / p.nq;
+        t.q0 = (tile % p.nq) * C::BQ;
+        t.tile = tile;
+        start = 0;
+      }
       for (int gi = 0; gi < p.groups; ++gi) {
         int e = s_ends[gi];
         e = e < start ? start : (e > p.Ptot ? p.Ptot : e);        // end_g = clamp(o_g, end_{g-1}, M)
-        const int n = (e - start + C::BP - 1) / C::BP;
+        const bool listed = p.fuse_side == 0 || ((e - start <= p.fuse_rows) == (p.fuse_side == 2));
+        const int n = listed ? (e - start + C::BP - 1) / C::BP : 0;
         if (pidx < seen + n) {
           t.g = gi;
           t.p0 = start + (pidx - seen) * C::BP;
@@ -1035,6 +1061,10 @@ hipError_t dx_mx(const Params& prm, hipStream_t s);
 // Dense grad_W of an MXFP8 gradient and an MXFP8 input, both scaled along
 // their rows (the contraction), on the block-scaled MFMA.
 hipError_t dw_mx(const Params& prm, hipStream_t s);
+// Grouped grad_X of an MXFP8 gradient and a bf16 weight that the kernel
+// quantizes to MXFP8 along its rows (256 x 128 tiles; the groups that
+// prm.fuse_side / fuse_rows list).
+hipError_t dx_wquant(const Params& prm, hipStream_t s);
 // grad_X / grad_W of a per-tensor scaled FP8 gradient and a per-tensor
 // scaled FP8 operand (formats LP_FP8T_*), on the same MFMA with unit block
 // scales; grouped calls included.

@@ -65,6 +65,8 @@ struct GemmCall {
   void* out;
   void* ws;                 // workspace for split contractions, or nullptr
   size_t ws_bytes;
+  int32_t fuse_rows = 0;    // grouped dX: groups of at most this many rows are
+  int32_t fuse_side = 0;    // left out (1) or the only ones (2); 0: all groups
 };
 hipError_t launch_gemm(const GemmCall& call, hipStream_t stream);
 
@@ -81,5 +83,19 @@ hipError_t launch_gemm_pair(const GemmCall& dx, const GemmCall& dw, hipStream_t 
 // Workspace bytes the contraction would use to split its contraction
 // (0: it does not split).
 size_t gemm_workspace_bytes(const GemmCall& call);
+
+// grad_X of the deferred MXFP8 recipe: grad (MXFP8, scales along -1)
+// [M][N] times the bf16 weight w [G][N][K] quantized to MXFP8 along N.
+// Groups of at most fuse_rows rows quantize their weight inside the
+// product; the others' weights are first quantized into w_codes / w_scales
+// ([G][N][K], [G][N/32][K]; unused when fuse_rows >= M).
+hipError_t launch_grouped_dx_deferred(const lp_qtensor& grad, const void* w, int64_t K, const int32_t* offsets,
+                                      int32_t groups, int64_t fuse_rows, void* w_codes, void* w_scales,
+                                      void* grad_x, hipStream_t stream);
+// MXFP8 quantization along the rows of w [G][N][K] for the groups of more
+// than min_rows rows (lp_quant.hip).
+hipError_t launch_mx_quant_rows_groups(const void* src, int64_t groups, int64_t rows, int64_t cols,
+                                       const int32_t* offsets, int64_t M, int64_t min_rows, void* codes, void* scales,
+                                       hipStream_t stream);
 
 }  // namespace lp

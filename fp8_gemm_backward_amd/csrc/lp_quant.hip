@@ -5,72 +5,19 @@
 // last axis and the weight along its reduction axis, one E8M0 scale per 32
 // elements (group_sizes [1, 1, 32]).
 //
-// Per block of 32: amax over |v| is taken on the bf16 bit patterns (integer
-// max of the magnitude bits, which also flags NaN / infinity as >= 0x7F80);
-// e = floor(log2 amax) - emax, clamped to [-127, 127], comes exactly from
-// the exponent field (or the leading mantissa bit of a subnormal); each
-// element is multiplied by 2^-e (exact), clamped to the format's maximum
-// (saturation) and rounded to nearest even by the hardware conversion.
+// The element arithmetic (block amax, E8M0 scale, saturating nearest-even
+// conversion) is in lp_mxq.hpp.
 #include <type_traits>
 
 #include "lp_device.hpp"
 #include "lp_internal.hpp"
+#include "lp_mxq.hpp"
 
 namespace lp {
 
 namespace {
 
 constexpr int kThreads = 256;
-
-__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
-
-// floor(log2 |v|) of a non-zero finite bf16 magnitude (bits & 0x7FFF).
-__device__ __forceinline__ int floor_log2_bf16(uint32_t mag) {
-  uint32_t e = mag >> 7;
-  return e ? (int)e - 127 : (31 - __builtin_clz(mag)) - 133;
-}
-
-struct BlockScale {
-  uint32_t byte;   // E8M0 scale byte
-  float inv;       // 2^-e as fp32 (exact)
-  bool bad;        // NaN or infinity in the block
-};
-
-template <bool kFp4>
-__device__ __forceinline__ BlockScale block_scale(uint32_t amax_mag) {
-  constexpr int kEmax = kFp4 ? 2 : 8;
-  BlockScale s;
-  s.bad = amax_mag >= 0x7F80u;
-  int e = (amax_mag == 0u || s.bad) ? -127 : floor_log2_bf16(amax_mag) - kEmax;
-  e = e < -127 ? -127 : (e > 127 ? 127 : e);
-  s.byte = s.bad ? 0xFFu : (uint32_t)(e + 127);
-  s.inv = __builtin_bit_cast(float, (uint32_t)(127 - e) << 23);   // 127-e in [8, 254]
-  return s;
-}
-
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
-
-// Two scaled values -> two E4M3 codes (low byte first) in a 16-bit result.
-__device__ __forceinline__ uint32_t to_e4m3x2(float a, float b) {
-  a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
-  b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
-  i16x2 old = {0, 0};
-  i16x2 r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(old, a, b, 1.0f, false);
-  return (uint32_t)(uint16_t)r[0];
-}
-
-// Two scaled values -> one byte of two E2M1 codes (first in the low nibble).
-__device__ __forceinline__ uint32_t to_e2m1x2(float a, float b) {
-  a = __builtin_amdgcn_fmed3f(a, -6.0f, 6.0f);
-  b = __builtin_amdgcn_fmed3f(b, -6.0f, 6.0f);
-  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a, b, 1.0f, 0) & 0xFFu;
-}
-
-// NaN codes of a bad block: E4M3 0x7F with each element's sign; E2M1 0.
-__device__ __forceinline__ uint32_t nan_e4m3x2(uint32_t w) {
-  return 0x7F7Fu | ((w >> 8) & 0x80u) | ((w >> 16) & 0x8000u);
-}
 
 // Axis -1: the work unit is eight consecutive elements (16 bytes of bf16);
 // the four lanes of a quad hold one 32-element block and take its amax
@@ -206,19 +153,13 @@ __global__ __launch_bounds__(kThreads) void mx_quant_rows(const uint16_t* __rest
 // column strip (DPP row rotations by 4 and 8); a row's amax over 32 columns
 // combines the lanes of a quad (quad permutations).  Four times as many
 // threads as a 32 x 8 strip per thread, and a quarter of the registers.
-__device__ __forceinline__ uint32_t pk_umax16(uint32_t a, uint32_t b) {
-  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a), __builtin_bit_cast(u16x2, b)));
-}
-
+// One 32 x 32 tile (index `tile` over batch * rows / 32 row blocks of
+// tiles_per_row tiles each) by the 16 lanes of the calling lane group.
 template <bool kFp4, bool kDual>
-__global__ __launch_bounds__(kThreads) void mx_quant_tile(const uint16_t* __restrict__ src,
-                                                          uint8_t* __restrict__ codes_c, uint8_t* __restrict__ scales_c,
-                                                          uint8_t* __restrict__ codes_r, uint8_t* __restrict__ scales_r,
-                                                          uint32_t ntiles, FastDiv tiles_per_row, uint32_t cols) {
-  const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
-  const uint32_t tile = i >> 4;
-  if (tile >= ntiles) return;                            // whole 16-lane groups
+__device__ __forceinline__ void quant_tile32(const uint16_t* __restrict__ src, uint8_t* __restrict__ codes_c,
+                                             uint8_t* __restrict__ scales_c, uint8_t* __restrict__ codes_r,
+                                             uint8_t* __restrict__ scales_r, uint32_t tile, FastDiv tiles_per_row,
+                                             uint32_t cols) {
   const uint32_t l16 = threadIdx.x & 15, ci = l16 & 3, ri = l16 >> 2;
   const uint32_t rb = fdiv(tile, tiles_per_row);         // block of 32 rows over batch*rows
   const uint32_t tc = tile - rb * tiles_per_row.d;       // block of 32 columns
@@ -314,7 +255,76 @@ __global__ __launch_bounds__(kThreads) void mx_quant_tile(const uint16_t* __rest
   }
 }
 
+template <bool kFp4, bool kDual>
+__global__ __launch_bounds__(kThreads) void mx_quant_tile(const uint16_t* __restrict__ src,
+                                                          uint8_t* __restrict__ codes_c, uint8_t* __restrict__ scales_c,
+                                                          uint8_t* __restrict__ codes_r, uint8_t* __restrict__ scales_r,
+                                                          uint32_t ntiles, FastDiv tiles_per_row, uint32_t cols) {
+  const uint32_t tile = (blockIdx.x * kThreads + threadIdx.x) >> 4;
+  if (tile >= ntiles) return;                            // whole 16-lane groups
+  quant_tile32<kFp4, kDual>(src, codes_c, scales_c, codes_r, scales_r, tile, tiles_per_row, cols);
+}
+
+// Rows of group g from int32 cumulative ends, with the kernels' clamping:
+// end_g = min(max(0, o_0 .. o_g), M).  Called by a whole wave (lane-parallel
+// loads, then a maximum across the wave); every lane gets the result.
+__device__ __forceinline__ int group_rows(const int32_t* __restrict__ offsets, int g, int M) {
+  const int lane = threadIdx.x & 63;
+  int hi = 0, lo = 0;                                    // max over o_0..o_g, and over o_0..o_{g-1}
+  for (int j = lane; j <= g; j += 64) {
+    const int o = offsets[j];
+    hi = o > hi ? o : hi;
+    if (j < g) lo = o > lo ? o : lo;
+  }
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int h = __shfl_xor(hi, d), l = __shfl_xor(lo, d);
+    hi = h > hi ? h : hi;
+    lo = l > lo ? l : lo;
+  }
+  hi = hi < M ? hi : M;
+  lo = lo < M ? lo : M;
+  return g > 0 ? hi - lo : hi;
+}
+
+// MXFP8 quantization along the rows (-2) of a grouped weight [G][N][K], for
+// the groups with more than min_rows rows only (the others quantize their
+// weight inside the grad_X product).  Workgroup (x, g) takes tiles
+// 16 x .. 16 x + 15 of group g.
+__global__ __launch_bounds__(kThreads) void mx_quant_rows_groups(const uint16_t* __restrict__ src,
+                                                                 uint8_t* __restrict__ codes,
+                                                                 uint8_t* __restrict__ scales,
+                                                                 const int32_t* __restrict__ offsets, int32_t M,
+                                                                 int32_t min_rows, uint32_t tiles_per_group,
+                                                                 FastDiv tiles_per_row, uint32_t cols) {
+  __shared__ int s_rows;
+  const int g = blockIdx.y;
+  if (threadIdx.x < 64) {
+    const int rows = group_rows(offsets, g, M);
+    if (threadIdx.x == 0) s_rows = rows;
+  }
+  __syncthreads();
+  if (s_rows <= min_rows) return;
+  const uint32_t t = blockIdx.x * (kThreads / 16) + (threadIdx.x >> 4);
+  if (t >= tiles_per_group) return;
+  quant_tile32<false, false>(src, nullptr, nullptr, codes, scales, (uint32_t)g * tiles_per_group + t, tiles_per_row,
+                             cols);
+}
+
 }  // namespace
+
+hipError_t launch_mx_quant_rows_groups(const void* src, int64_t groups, int64_t rows, int64_t cols,
+                                       const int32_t* offsets, int64_t M, int64_t min_rows, void* codes, void* scales,
+                                       hipStream_t stream) {
+  if (groups * rows * cols == 0) return hipSuccess;
+  const uint32_t tpr = (uint32_t)(cols / 32);
+  const uint32_t tpg = (uint32_t)(rows / 32) * tpr;
+  const dim3 grid((tpg + kThreads / 16 - 1) / (kThreads / 16), (uint32_t)groups), block(kThreads);
+  mx_quant_rows_groups<<<grid, block, 0, stream>>>(static_cast<const uint16_t*>(src), static_cast<uint8_t*>(codes),
+                                                   static_cast<uint8_t*>(scales), offsets, (int32_t)M,
+                                                   (int32_t)min_rows, tpg, make_fastdiv(tpr), (uint32_t)cols);
+  return hipGetLastError();
+}
 
 hipError_t launch_mx_quant(const void* src, int64_t batch, int64_t rows, int64_t cols, int axis, int dst_fmt,
                            void* codes, void* scales, hipStream_t stream) {

@@ -402,6 +402,47 @@ lp_status lp_grouped_bwd(const lp_qtensor* grad_out, const lp_qtensor* x, const 
                          void* stream);
 
 /*
+ * lp_grouped_dx_deferred - grad_X of a grouped layer in the deferred MXFP8
+ * recipe, with the bf16 weight quantized as part of the call.
+ *
+ * Cites: "perf: defer mxfp8 backward quantization", MXFP8GMMFunction.op_dx
+ * (the weight is quantized in the backward along its reduction axis, one
+ * E8M0 scale per 32, and contracted with the MXFP8 gradient; the page trades
+ * this backward compute for saved memory).
+ *
+ * Computes exactly what lp_mx_quant(w, axis -2, LP_MXFP8) followed by
+ * lp_grouped_bwd(grad_out, NULL, that weight, offsets, groups, grad_x, NULL)
+ * computes, bit for bit.  A group of at most fuse_rows rows quantizes its
+ * weight slices inside the product, which then reads the bf16 weight once
+ * and never writes its quantized copy; the weights of larger groups are
+ * quantized first into w_codes / w_scales, then contracted.
+ *
+ * grad_out   LP_MXFP8 with scales along -1, [M][N] (N % 32 == 0).
+ * w          device bf16 [groups][N][K] (K % 16 == 0), 16-byte aligned.
+ * offsets    device int32 [groups], cumulative end rows, as for
+ *            lp_grouped_bwd (the group sizes that fuse_rows is compared with
+ *            are taken from it on the device, with its clamping).
+ * fuse_rows  >= 0; 0 quantizes every weight first, >= M none.  Weights are
+ *            quantized inside the product only when N % 512 == 0 (the
+ *            kernel reads the gradient's scale rows in 16-byte pieces) and
+ *            K % 32 == 0; otherwise every weight is quantized first.
+ * grad_x     device bf16 [M][K]; rows at or past offsets[groups-1] are not
+ *            written.
+ * w_codes    device u8 [groups][N][K] and w_scales u8 [groups][N/32][K]:
+ * w_scales   caller-owned, written for the groups whose weight is quantized
+ *            first (the others' slices are left as they are); may be NULL
+ *            when fuse_rows >= M, N % 512 == 0 and K % 32 == 0.
+ * Errors: LP_ERR_FORMAT unless grad_out is MXFP8 along -1; LP_ERR_SHAPE for
+ * sizes outside the rules (groups 1..1024, fuse_rows < 0, K % 16, the size
+ * limits of lp_grouped_bwd); LP_ERR_NULL / LP_ERR_ALIGN as usual; checked
+ * before anything is enqueued.  LP_ERR_HIP: a launch failed (earlier
+ * launches of the call may already be enqueued).
+ */
+lp_status lp_grouped_dx_deferred(const lp_qtensor* grad_out, const void* w, int64_t K, const int32_t* offsets,
+                                 int64_t groups, int64_t fuse_rows, void* grad_x, void* w_codes, void* w_scales,
+                                 void* stream);
+
+/*
  * lp_linear_fwd - forward of a linear layer y = x @ W^T whose operands are
  * both MX-quantized along the contraction.
  *

@@ -18,7 +18,7 @@ def test_library_exports_every_header_function():
     assert set(names) == {"lp_dequant", "lp_mx_quant", "lp_linear_bwd", "lp_grouped_bwd", "lp_status_string",
                           "lp_linear_bwd_workspace", "lp_linear_bwd_ws", "lp_mx_quant_dual", "lp_tensor_amax",
                           "lp_tensor_quant", "lp_scale_from_history", "lp_linear_fwd", "lp_grouped_fwd",
-                          "lp_tensor_quant_delayed", "lp_linear_bwd_noalloc"}
+                          "lp_tensor_quant_delayed", "lp_linear_bwd_noalloc", "lp_grouped_dx_deferred"}
     for n in names:
         assert hasattr(lp.lib, n), n
 
