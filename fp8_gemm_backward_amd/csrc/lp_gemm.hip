@@ -187,9 +187,12 @@ Params base_params(const GemmCall& call) {
 Params native_params(const GemmCall& call) {
   Params prm = base_params(call);
   prm.nq = (int32_t)((prm.Qtot + Big::BQ - 1) / Big::BQ);
-  if (call.offsets == nullptr)
+  // Dense calls order their tiles in blocks of gm row tiles; grouped grad_X
+  // does the same inside each group (a group of fewer row tiles is one
+  // block).
+  if (call.offsets == nullptr || !call.dw)
     prm.gm = tile_group(Big::BP * code_bytes2(call.grad->fmt), Big::BQ * code_bytes2(call.other->fmt),
-                        (prm.Ptot + Big::BP - 1) / Big::BP);
+                        call.offsets == nullptr ? (prm.Ptot + Big::BP - 1) / Big::BP : kCUsPerXcd);
   if (call.dw) {
     prm.ntiles = (int32_t)(((call.N + Big::BP - 1) / Big::BP) * prm.nq * call.groups);
   } else {

@@ -608,6 +608,14 @@ __device__ __forceinline__ Tile select_tile(const Params& p, int32_t* s_ends, in
           t.g = gi;
           t.p0 = start + (pidx - seen) * C::BP;
           t.pend = e;
+          if (p.gm > 1) {
+            // Inside the group, the dense order in blocks of gm row tiles
+            // (grouped_order): the tiles an XCD runs together share both
+            // gradient rows and weight columns in its L2.
+            const int2 pq = grouped_order(tile - seen * p.nq, n, p.nq, p.gm);
+            t.p0 = start + pq.x * C::BP;
+            t.q0 = pq.y * C::BQ;
+          }
           break;
         }
         seen += n;
@@ -1065,6 +1073,8 @@ hipError_t dw_mx(const Params& prm, hipStream_t s);
 // quantizes to MXFP8 along its rows (256 x 128 tiles; the groups that
 // prm.fuse_side / fuse_rows list).
 hipError_t dx_wquant(const Params& prm, hipStream_t s);
+// Compute units of the current device, looked up once per device.
+int compute_units();
 // grad_X / grad_W of a per-tensor scaled FP8 gradient and a per-tensor
 // scaled FP8 operand (formats LP_FP8T_*), on the same MFMA with unit block
 // scales; grouped calls included.

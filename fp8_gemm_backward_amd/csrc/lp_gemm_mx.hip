@@ -6,8 +6,6 @@
 namespace lp {
 namespace gk {
 
-namespace {
-
 // Compute units of the current device (one persistent workgroup each).
 int compute_units() {
   static std::atomic<int> cached[64];
@@ -19,8 +17,6 @@ int compute_units() {
   cached[dev].store(n, std::memory_order_relaxed);
   return n;
 }
-
-}  // namespace
 
 hipError_t dx_mx(const Params& prm, hipStream_t s) {
   if (prm.ntiles <= 0) return hipSuccess;

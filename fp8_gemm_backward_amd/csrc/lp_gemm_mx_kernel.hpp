@@ -174,8 +174,11 @@ __device__ __forceinline__ int mx_tile(const Params& p, int hw, uint8_t* st0, ui
   const int kbeg = t.kbeg, kend = t.kend;
   const uint8_t* pc = p.P.codes + (int64_t)t.p0 * ldp;
   const uint8_t* ps = p.P.scales + (int64_t)t.p0 * sldp;
-  const int64_t prow_bytes = (int64_t)(M - t.p0) * ldp;
-  const int64_t psrow_bytes = (int64_t)(M - t.p0) * sldp;
+  // dX reads only the rows of the tile's group (rows past them read as
+  // zeros: their results are never stored); dW reads to the end.
+  const int pend = kDW ? M : t.pend;
+  const int64_t prow_bytes = (int64_t)(pend - t.p0) * ldp;
+  const int64_t psrow_bytes = (int64_t)(pend - t.p0) * sldp;
   // dX: the weight of the tile's group; dW: the input X, one tensor for all
   // groups (its rows are the contraction).
   const int64_t qg = kDW ? 0 : t.g;
@@ -455,9 +458,10 @@ __device__ __forceinline__ int mx_tile(const Params& p, int hw, uint8_t* st0, ui
       const Tile tn = select_tile<XCfg, kDW>(p, pst->ends, pst->next, true);
       if (tn.valid && tn.kend > tn.kbeg) {
         const uint8_t* const npc = p.P.codes + (int64_t)tn.p0 * ldp;
-        const int64_t nprow = (int64_t)(M - tn.p0) * ldp;
+        const int npend = kDW ? M : tn.pend;
+        const int64_t nprow = (int64_t)(npend - tn.p0) * ldp;
         const uint8_t* const nqc = p.Q.codes + (int64_t)tn.g * p.Q.code_batch;
-        const Rsrc nps_r = make_rsrc(p.P.scales + (int64_t)tn.p0 * sldp, (int64_t)(M - tn.p0) * sldp);
+        const Rsrc nps_r = make_rsrc(p.P.scales + (int64_t)tn.p0 * sldp, (int64_t)(npend - tn.p0) * sldp);
         const Rsrc nqs_r = make_rsrc(p.Q.scales + (int64_t)tn.g * p.Q.scale_batch, p.Q.scale_bytes);
         const int32_t nq_base = (16 * wave + lane / 16) * ldq + tn.q0;
         dma<16>(nps_r, (lds_void*)(sc0 + 1024 * wave), (64 * wave + lane) * sldp, 0);

@@ -69,81 +69,151 @@ __device__ __forceinline__ uint32_t pk_add_u16(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, a) + __builtin_bit_cast(u16x2, b));
 }
 
+// The workgroup barrier for waves that issue no direct loads: their LDS
+// operations done, no wait on the memory counter (their stores).
+__device__ __forceinline__ void barrier_lgkm() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // bf16 weight slab [64 rows][512 B]: 16-byte chunk c of row n at physical
 // chunk c ^ 4 (n & 3).  A transposing read covers rows n0 .. n0 + 3 and
 // n0 + 16 .. n0 + 19 (n0 % 4 == 0) of one 64-byte segment: the swizzle puts
 // the four rows of each half on distinct banks.
 __device__ __forceinline__ int wb_swz(int n) { return 4 * (n & 3); }
 
+// One listed tile: its group, rows [p0, pend) and first output column; a
+// null tile (past a workgroup's list) has valid == false and empty ranges.
+struct WTile {
+  int g, p0, pend, q0;
+  bool valid;
+};
+
 template <int kDummy = 0>
 __global__ __launch_bounds__(NT8) __attribute__((amdgpu_waves_per_eu(2, 2))) void fp8_mfma_wquant_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kLds];
-  constexpr int TG = 2, TW = 4;                  // direct loads per wave and slab: gradient, weight
-  constexpr int S = 2;                           // scale chunk loads per wave
+  __shared__ int32_t s_ends[kMaxGroups];
+  // Waves 0 .. 3 issue every direct load, waves 4 .. 7 every store of
+  // results: a wave's memory counter covers loads and stores together, in
+  // issue order, so a loading wave that stored a tile's results would wait
+  // for those stores before it could count the next tile's loads as landed.
+  constexpr int TG = 4, TW = 8;                  // direct loads per loading wave and slab: gradient, weight
+  constexpr int S = 4;                           // scale chunk loads per loading wave
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if ((int)blockIdx.x >= p.ntiles) return;
-  const Tile t = select_tile<WCfg, false>(p, reinterpret_cast<int32_t*>(lds + kWBase));
-  if (!t.valid) return;
-  __syncthreads();                               // group ends read; the buffer is reusable
+  const int M = p.Ptot, K = p.Qtot, N = p.Ktot;
+  for (int i = tid; i < p.groups; i += NT8) s_ends[i] = p.offsets[i];
+  __syncthreads();
+
+  // The listed tiles (groups of 1 .. fuse_rows rows, ceil(rows / 256) row
+  // tiles each, nq column tiles per row tile), in order of group, row tile,
+  // column tile.  XCD x (workgroups b with b % 8 == x) takes the x-th
+  // eighth of the list and its workgroups deal it out in turn, so that the
+  // tiles one XCD runs together are neighbours: column tiles of the same
+  // rows, whose gradient rows its L2 then serves.
+  int nrt = 0;
+  {
+    int start = 0;
+    for (int gi = 0; gi < p.groups; ++gi) {
+      int e = s_ends[gi];
+      e = e < start ? start : (e > M ? M : e);
+      const int n = e - start;
+      nrt += (n > 0 && n <= p.fuse_rows) ? (n + WBP - 1) / WBP : 0;
+      start = e;
+    }
+  }
+  const int nlist = nrt * p.nq;
+  const int nslot = gridDim.x / 8, xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int per = (nlist + 7) / 8;
+  const int lo = xcd * per, hi = lo + per < nlist ? lo + per : nlist;
+  const int first = lo + slot;
+  const int mine = first < hi ? (hi - first + nslot - 1) / nslot : 0;
+  if (mine == 0) return;
+  auto tile_at = [&](int i) __attribute__((always_inline)) {
+    WTile t{0, 0, 0, 0, false};
+    if (i >= mine) return t;
+    const int l = first + i * nslot;
+    const int pidx = l / p.nq;
+    t.q0 = (l - pidx * p.nq) * WBQ;
+    int start = 0, seen = 0;
+    for (int gi = 0; gi < p.groups; ++gi) {
+      int e = s_ends[gi];
+      e = e < start ? start : (e > M ? M : e);
+      const int n = e - start;
+      const int c = (n > 0 && n <= p.fuse_rows) ? (n + WBP - 1) / WBP : 0;
+      if (pidx < seen + c) {
+        t.g = gi;
+        t.p0 = start + (pidx - seen) * WBP;
+        t.pend = e;
+        t.valid = true;
+        break;
+      }
+      seen += c;
+      start = e;
+    }
+    return t;
+  };
 
   const int ldp = p.P.code_ld;                   // N bytes per gradient row
   const int sldp = p.P.scale_ld;                 // N / 32
   const int ldw = p.Q.code_ld;                   // 2 K bytes per weight row
-  const int M = p.Ptot, kend = t.kend;           // kend = N
-  const uint8_t* const pc = p.P.codes + (int64_t)t.p0 * ldp;
-  const int64_t prow = (int64_t)(M - t.p0) * ldp;
-  const int32_t prange = (int32_t)(prow < 0x7FFFFFFF ? prow : 0x7FFFFFFF);
-  const Rsrc ps_r = make_rsrc(p.P.scales + (int64_t)t.p0 * sldp, (int64_t)(M - t.p0) * sldp);
-  const uint8_t* const wg = p.Q.codes + (int64_t)t.g * p.Q.code_batch + 2 * (int64_t)t.q0;
-  const int wrows_max = 0x7FFFFFFF / ldw;        // rows one 32-bit range can cover
+  const int nk = N / XBK;                        // a multiple of 8 (N % 512 == 0)
+  const int wrows_max = 0x7FFFFFFF / ldw;        // weight rows one 32-bit range covers
 
-  // Gradient codes: wave w fills blocks 2 w + u of 16 rows x 64 B; lane i
-  // takes row 16 (2 w + u) + i / 4, physical chunk i % 4, logical chunk
-  // (i % 4) ^ p_swz(row) = (i % 4) ^ ((i >> 4) & 3).
+  const bool loader = wave < 4;
+  const int lw = wave & 3;                       // index among the loading (or storing) waves
+  // Gradient codes: loading wave w fills blocks 4 w + u of 16 rows x 64 B;
+  // lane i takes row 16 (4 w + u) + i / 4, physical chunk i % 4, logical
+  // chunk (i % 4) ^ p_swz(row) = (i % 4) ^ ((i >> 4) & 3).
   const int pchunk = (lane & 3) ^ ((lane >> 4) & 3);
-  const int32_t p_off = (16 * 2 * wave + lane / 4) * ldp + 16 * pchunk;
-  // bf16 weight: wave w fills blocks 4 w + v of 2 rows x 512 B; lane i
-  // takes row n = 8 w + 2 v + i / 32, physical chunk i % 32, logical chunk
-  // (i % 32) ^ wb_swz(n); v and v + 2 share the swizzle.
+  const int32_t p_off = (16 * 4 * lw + lane / 4) * ldp + 16 * pchunk;
+  // bf16 weight: loading wave w fills blocks 8 w + v of 2 rows x 512 B;
+  // lane i takes row n = 16 w + 2 v + i / 32, physical chunk i % 32,
+  // logical chunk (i % 32) ^ wb_swz(n); the swizzle depends on v's parity
+  // only.
   auto w_off = [&](int v) __attribute__((always_inline)) {
-    const int n = 8 * wave + 2 * v + lane / 32;
-    return (int32_t)((8 * wave + lane / 32) * ldw + 16 * ((lane & 31) ^ wb_swz(n)));
+    const int n = 16 * lw + 2 * v + lane / 32;
+    return (int32_t)((16 * lw + lane / 32) * ldw + 16 * ((lane & 31) ^ wb_swz(n)));
   };
   const int32_t w_off0 = w_off(0), w_off1 = w_off(1);
+  const int32_t c_off = (16 * 4 * lw + lane / 4) * sldp + 4 * (lane & 3);   // scale chunk pieces
 
-  // Direct loads of gradient slab kk and of weight slab kk into their
-  // buffers.  The contraction is a whole number of scale chunks (N % 512 ==
-  // 0, which the launch checks), so every slab the products use is full;
-  // the loads past the end (prefetches nothing uses) stay inside the
-  // operands or read zeros.
-  auto issue_g = [&](int kk) __attribute__((always_inline)) {
+  // Direct loads of slab kk of tile t into the buffers of stream step sg
+  // (every slab of a workgroup's tiles is one step of a single stream; a
+  // null tile's loads read nothing and leave zeros).  The contraction is a
+  // whole number of scale chunks (N % 512 == 0, which the launch checks),
+  // so every slab is full.
+  auto issue_g = [&](const WTile& t, int kk, int sg) __attribute__((always_inline)) {
     const int k0 = kk * XBK;
-    const Rsrc r = make_rsrc(pc + k0, (int64_t)__builtin_amdgcn_readfirstlane(prange - k0 > 0 ? prange - k0 : 0));
-    uint8_t* const gb = lds + kGBase + kGTile * (kk % 3);
+    int64_t range = 0;
+    if (t.valid) {
+      const int64_t rb = (int64_t)(t.pend - t.p0) * ldp - k0;   // the group's rows only: the rest read as zeros
+      range = rb < 0 ? 0 : (rb > 0x7FFFFFFF ? 0x7FFFFFFF : rb);
+    }
+    const Rsrc r = make_rsrc(p.P.codes + (int64_t)t.p0 * ldp + k0, (int64_t)__builtin_amdgcn_readfirstlane((int)range));
+    uint8_t* const gb = lds + kGBase + kGTile * (sg % 3);
 #pragma unroll
-    for (int u = 0; u < TG; ++u) dma<16>(r, (lds_void*)(gb + 1024 * (2 * wave + u)), p_off, 16 * u * ldp);
+    for (int u = 0; u < TG; ++u) dma<16>(r, (lds_void*)(gb + 1024 * (4 * lw + u)), p_off, 16 * u * ldp);
   };
-  auto issue_w = [&](int kk) __attribute__((always_inline)) {
+  auto issue_w = [&](const WTile& t, int kk, int sg) __attribute__((always_inline)) {
     const int k0 = kk * XBK;
-    int rows = kend - k0;
+    int rows = t.valid ? N - k0 : 0;
     rows = rows < 0 ? 0 : (rows > wrows_max ? wrows_max : rows);
+    const uint8_t* const wg = p.Q.codes + (int64_t)t.g * p.Q.code_batch + 2 * (int64_t)t.q0;
     const Rsrc r = make_rsrc(wg + (int64_t)k0 * ldw, (int64_t)__builtin_amdgcn_readfirstlane(rows * ldw));
-    uint8_t* const wb = lds + kWBase + kWTile * (kk % 3);
+    uint8_t* const wb = lds + kWBase + kWTile * (sg % 3);
 #pragma unroll
     for (int v = 0; v < TW; ++v)
-      dma<16>(r, (lds_void*)(wb + 1024 * (4 * wave + v)), (v & 1) ? w_off1 : w_off0, 2 * v * ldw);
+      dma<16>(r, (lds_void*)(wb + 1024 * (8 * lw + v)), (v & 1) ? w_off1 : w_off0, 2 * v * ldw);
   };
-  // Gradient scales of the chunk at slab kk ([256 rows][16 B]): wave w
-  // fills 256-byte pieces 2 w + s, lane i taking 4 bytes of row
-  // 16 (2 w + s) + i / 4.
-  auto issue_chunk = [&](int kk) __attribute__((always_inline)) {
-    uint8_t* const cb = lds + kCBase + kGChunk * ((kk / kChunkSlabs) & 1);
+  // Gradient scales of the chunk at slab kk ([256 rows][16 B]) into the
+  // chunk buffer of step sg: loading wave w fills 256-byte pieces 4 w + s,
+  // lane i taking 4 bytes of row 16 (4 w + s) + i / 4.
+  auto issue_chunk = [&](const WTile& t, int kk, int sg) __attribute__((always_inline)) {
+    const int64_t rb = t.valid ? (int64_t)(t.pend - t.p0) * sldp : 0;
+    const Rsrc r = make_rsrc(p.P.scales + (int64_t)t.p0 * sldp, (int64_t)__builtin_amdgcn_readfirstlane((int)(rb < 0x7FFFFFFF ? rb : 0x7FFFFFFF)));
+    uint8_t* const cb = lds + kCBase + kGChunk * ((sg / kChunkSlabs) & 1);
 #pragma unroll
     for (int sp = 0; sp < S; ++sp)
-      dma<4>(ps_r, (lds_void*)(cb + 256 * (2 * wave + sp)), (16 * (2 * wave + sp) + lane / 4) * sldp + 4 * (lane & 3),
-             (kk * XBK) >> 5);
+      dma<4>(r, (lds_void*)(cb + 256 * (4 * lw + sp)), c_off, 16 * sp * sldp + ((kk * XBK) >> 5));
   };
 
   // Fragments.  Lane l = 32 h + r (h = l / 32, r = l % 32) of an MFMA
@@ -249,42 +319,55 @@ __global__ __launch_bounds__(NT8) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
   for (int f = 0; f < NF; ++f) acc[f] = f32x16{};
 
-  const int nk = (kend + XBK - 1) / XBK;
-  if (nk > 0) {
-    // Prologue: chunk 0, slabs 0, 1 (gradient and weight) and weight slab 2
-    // in flight; chunk 0 and slab 0 landed, weight slab 0 quantized.
-    issue_chunk(0);
-    issue_g(0);
-    issue_w(0);
-    issue_w(1);
-    issue_g(1);
-    issue_w(2);
+  // Prologue: the first tile's chunk 0, slabs 0, 1 (gradient and weight)
+  // and weight slab 2 in flight; chunk 0 and slab 0 landed, weight slab 0
+  // quantized.
+  WTile cur = tile_at(0), nxt = tile_at(1);
+  if (loader) {
+    issue_chunk(cur, 0, 0);
+    issue_g(cur, 0, 0);
+    issue_w(cur, 0, 0);
+    issue_w(cur, 1, 1);
+    issue_g(cur, 1, 1);
+    issue_w(cur, 2, 2);
     barrier_vm<TG + 2 * TW>();
-    q_read(lds + kWBase);
-    q_amax(IC<0>{});
-    q_amax(IC<1>{});
-    q_scale();
-    static_for<4>([&](auto pci) { q_codes(pci, qf[0]); });
-    qsc[0] = bsc >> hsh;
-    if (special) q_special(qf[0], qsc[0]);
+  } else {
+    barrier_lgkm();
   }
+  q_read(lds + kWBase);
+  q_amax(IC<0>{});
+  q_amax(IC<1>{});
+  q_scale();
+  static_for<4>([&](auto pci) { q_codes(pci, qf[0]); });
+  qsc[0] = bsc >> hsh;
+  if (special) q_special(qf[0], qsc[0]);
 
-  // Slab k (position S8 in its scale chunk): the barrier publishes
-  // gradient slab k and weight slab k + 1; issue gradient slab k + 2 and
-  // weight slab k + 3 (and at position 4 the next scale chunk), read weight
-  // slab k + 1, then run slab k's eight products with the quantization of
-  // slab k + 1 spread between them.  Slabs past the end quantize the zeros
-  // their loads read, into fragments nothing uses.
-  auto slab = [&](auto ji, int k) __attribute__((always_inline)) {
+  // Step sg = slab k of the current tile (position S8 in its scale chunk):
+  // the barrier publishes gradient slab sg and weight slab sg + 1 of the
+  // stream; issue gradient slab sg + 2 and weight
+  // slab sg + 3 (and at position 4 the next scale chunk), of this tile or,
+  // near its end, of the next; read weight slab sg + 1, then run slab sg's
+  // eight products with the quantization of slab sg + 1 spread between
+  // them.
+  auto slab = [&](auto ji, int k, int sg) __attribute__((always_inline)) {
     constexpr int S8 = decltype(ji)::value;
     constexpr int CUR = S8 & 1, NXT = CUR ^ 1;
-    barrier_vm<TG + TW + (S8 == 5 ? S : 0)>();
-    if constexpr (S8 == 4) issue_chunk(k + 4);
-    issue_g(k + 2);
-    issue_w(k + 3);
-    const uint8_t* const gb = lds + kGBase + kGTile * (k % 3);
-    const uint8_t* const cb = lds + kCBase + kGChunk * ((k / kChunkSlabs) & 1);
-    q_read(lds + kWBase + kWTile * ((k + 1) % 3));
+    if (loader) {
+      barrier_vm<TG + TW + (S8 == 5 ? S : 0)>();
+      if constexpr (S8 == 4) {
+        if (k + 4 < nk) issue_chunk(cur, k + 4, sg + 4);
+        else issue_chunk(nxt, k + 4 - nk, sg + 4);
+      }
+      if (k + 2 < nk) issue_g(cur, k + 2, sg + 2);
+      else issue_g(nxt, k + 2 - nk, sg + 2);
+      if (k + 3 < nk) issue_w(cur, k + 3, sg + 3);
+      else issue_w(nxt, k + 3 - nk, sg + 3);
+    } else {
+      barrier_lgkm();
+    }
+    const uint8_t* const gb = lds + kGBase + kGTile * (sg % 3);
+    const uint8_t* const cb = lds + kCBase + kGChunk * ((sg / kChunkSlabs) & 1);
+    q_read(lds + kWBase + kWTile * ((sg + 1) % 3));
     i32x8 pf[2];
     int32_t psc[2];
     auto read_p = [&](auto fi) __attribute__((always_inline)) {
@@ -324,44 +407,72 @@ __global__ __launch_bounds__(NT8) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       q_special(qf[NXT], qsc[NXT]);
     }
   };
-  for (int kt = 0; kt < nk; kt += kChunkSlabs) {
-    static_for<kChunkSlabs>([&](auto ji) {
-      constexpr int J = decltype(ji)::value;
-      if (kt + J < nk) slab(ji, kt + J);
-    });
-  }
-  // No direct load may still be writing LDS when the staging below reuses
-  // it or the workgroup ends, and no wave may still read a slab buffer.
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-  __syncthreads();
 
-  // Epilogue: fp32 -> bf16 (nearest even) through 16 KiB of staging per
-  // wave (256 rows x 64 B, 8-byte slot s of row r at s ^ (r & 7)), then 16
-  // bytes per lane to global memory, masked to the tile's group rows.
-  uint8_t* const stg = lds + wave * (WBP * kStageRow);
+  // Results of a tile: fp32 -> bf16 (nearest even) staged through the
+  // weight buffer that slab sg - 1 finished with (the stream refills it only
+  // at step sg), 64 rows at a time (16-byte chunk c of staged row r at
+  // c ^ (r % 32)), then stored by the storing waves as whole 512-byte row
+  // segments, 1 KiB per store (register-direct stores of 16-byte pieces
+  // cost far more).  Only rows of the tile's group are staged and stored
+  // (a column group past K is sent out of range).
+  auto store_tile = [&](const WTile& t, uint8_t* stg) __attribute__((always_inline)) {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // every wave done reading the buffer
+    const int nrows = t.pend - t.p0;
+    const Rsrc out = make_rsrc(p.C + (int64_t)t.p0 * p.ldc, (int64_t)nrows * p.ldc * 2);
+    const int ccol = t.q0 + 8 * (lane & 31);
+    const bool cok = ccol < K;
 #pragma unroll
-  for (int f = 0; f < NF; ++f) {
-    const int r = 32 * f + r32;
+    for (int rnd = 0; rnd < NF / 2; ++rnd) {
+      if (64 * rnd >= nrows) break;
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int slot = 2 * r4 + hh;
-      const u32x2 v = {pack_bf16x2(acc[f][4 * r4], acc[f][4 * r4 + 1]), pack_bf16x2(acc[f][4 * r4 + 2], acc[f][4 * r4 + 3])};
-      *reinterpret_cast<u32x2*>(stg + r * kStageRow + 8 * (slot ^ (r & 7))) = v;
+      for (int h = 0; h < 2; ++h) {
+        const int f = 2 * rnd + h;
+        const int r = 32 * h + r32;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int phys = (4 * wave + r4) ^ r32;
+          const u32x2 v = {pack_bf16x2(acc[f][4 * r4], acc[f][4 * r4 + 1]),
+                           pack_bf16x2(acc[f][4 * r4 + 2], acc[f][4 * r4 + 3])};
+          *reinterpret_cast<u32x2*>(stg + r * (WBQ * 2) + 16 * phys + 8 * hh) = v;
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (!loader) {
+        // Row r = 16 w + 2 j + h of the round: voffset per lane, the row
+        // step 2 j in soffset; r % 32 = (16 (w % 2) + h) | 2 j.
+        int y = (lane & 31) ^ (16 * (lw & 1) + hh);
+        int32_t voff = cok ? ((16 * lw + hh) * p.ldc + ccol) * 2 : kOOB;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          asm volatile("" : "+v"(y), "+v"(voff));             // recomputed per store, not held eight times
+          if (64 * rnd + 16 * lw + 2 * j < nrows) {
+            const int r = 16 * lw + 2 * j + hh;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * (WBQ * 2) + 16 * (y ^ (2 * j)));
+            __builtin_amdgcn_raw_buffer_store_b128(v, out, voff, (64 * rnd + 2 * j) * p.ldc * 2, 0);
+          }
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
-  }
-  __builtin_amdgcn_s_waitcnt(0xC07F);            // lgkmcnt(0): own staging writes done
-  const int c4 = lane & 3;
-  const int col = t.q0 + 32 * wave + 8 * c4;
 #pragma unroll
-  for (int it = 0; it < WBP / 16; ++it) {
-    const int r = 16 * it + lane / 4;
-    const uint8_t* src = stg + r * kStageRow;
-    const u32x2 lo = *reinterpret_cast<const u32x2*>(src + 8 * ((2 * c4) ^ (r & 7)));
-    const u32x2 hi = *reinterpret_cast<const u32x2*>(src + 8 * ((2 * c4 + 1) ^ (r & 7)));
-    const int row = t.p0 + r;
-    if (row < t.pend && col < p.Qtot)
-      *reinterpret_cast<u32x4*>(p.C + (int64_t)row * p.ldc + col) = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    for (int f = 0; f < NF; ++f) acc[f] = f32x16{};
+  };
+
+  int sg = 0;
+  for (int i = 0; i < mine; ++i) {
+    for (int kt = 0; kt < nk; kt += kChunkSlabs) {
+      static_for<kChunkSlabs>([&](auto ji) {
+        constexpr int J = decltype(ji)::value;
+        slab(ji, kt + J, sg + J);
+      });
+      sg += kChunkSlabs;
+    }
+    store_tile(cur, lds + kWBase + kWTile * (sg % 3));
+    cur = nxt;
+    nxt = tile_at(i + 2);
   }
+  // No direct load may still be writing LDS when the workgroup ends.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 }  // namespace
@@ -370,7 +481,12 @@ __global__ __launch_bounds__(NT8) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // p.fuse_rows rows); p.Q describes the bf16 weight [G][N][K].
 hipError_t dx_wquant(const Params& prm, hipStream_t s) {
   if (prm.ntiles <= 0) return hipSuccess;
-  fp8_mfma_wquant_kernel<><<<dim3(prm.ntiles), dim3(NT8), 0, s>>>(prm);
+  // Persistent: one workgroup per compute unit (a multiple of the 8 XCDs),
+  // fewer when the listed tiles (at most prm.ntiles) are fewer.
+  int wg = compute_units() / 8 * 8;
+  wg = wg < 8 ? 8 : wg;
+  const int cap = (prm.ntiles + 7) / 8 * 8;
+  fp8_mfma_wquant_kernel<><<<dim3(wg < cap ? wg : cap), dim3(NT8), 0, s>>>(prm);
   return hipGetLastError();
 }
 

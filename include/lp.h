@@ -17,13 +17,18 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * - Every pointer to tensor data is a DEVICE pointer.  The caller allocates
- *   and owns every buffer; the library allocates nothing, frees nothing and
- *   keeps no pointer after a call returns.  It holds no state between calls
- *   and is safe to call from several host threads.
+ *   and owns every buffer; the library calls no device allocator, frees
+ *   nothing and keeps no pointer after a call returns.  Between calls it
+ *   keeps only facts it looks up once per device (the compute-unit count,
+ *   the address of lp_linear_bwd_noalloc's workspace array), and it is safe
+ *   to call from several host threads.
  * - Work is enqueued on `stream` (a hipStream_t; NULL is the default
  *   stream) and runs asynchronously.  The status covers argument checking
- *   and the launch only.  On any error nothing is enqueued and no output
- *   is written.
+ *   and the launch only.  Argument errors (LP_ERR_NULL, LP_ERR_SHAPE,
+ *   LP_ERR_FORMAT, LP_ERR_ALIGN) are found before anything is enqueued:
+ *   nothing runs and no output is written.  LP_ERR_HIP reports a launch
+ *   that failed; launches of the same call made before it may already be
+ *   enqueued.
  * - Tensors are dense and row-major.  Element (b, r, c) of a [batch][rows][cols]
  *   tensor is at offset (b*rows + r)*cols + c, in units of elements.
  * - Codes, scales and outputs must be 16-byte aligned; a tensor scale

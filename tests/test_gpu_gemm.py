@@ -479,6 +479,34 @@ def test_mxfp4_grouped_full_size(lp):
         assert_close(dw[gi][torch.from_numpy(nrows).cuda()], ref, f"group {gi} dW")
 
 
+def test_mxfp4_grouped_forced_empty_full_size(lp):
+    """The 8-expert MXFP4 grouped layer at full size with one expert's
+    tokens all moved to the largest (an empty group inside the offsets):
+    its grad_W is all zeros, and sampled rows of every other group's dX and
+    dW (the grown group's included) match the oracle."""
+    w = W.WORKLOADS["mxfp4_grouped"]
+    X, Wt, G = W.dense_inputs(w)
+    sizes = W.group_sizes(w)
+    empty = int(np.argmin(sizes))
+    sizes = W.force_empty(sizes, empty)
+    assert sizes[empty] == 0 and sizes.sum() == w.M
+    offsets = W.cumulative_ends(sizes)
+    xq, xd = quantize(lp, "mxfp4", X)
+    wq, wd = quantize(lp, "mxfp4", Wt)
+    g = lp.QTensor("bf16", bf16_dev(G), shape=(1, w.M, w.N))
+    dx, dw = lp.lp_grouped_bwd(g, xq, wq, torch.from_numpy(offsets).cuda())
+    torch.cuda.synchronize()
+    assert not torch.any(dw[empty].view(torch.int16) != 0), "the emptied group's dW is not all zeros"
+    for gi, (s, e) in enumerate(O.group_bounds(offsets)):
+        if e == s:
+            continue
+        rows = s + _sample_rows(e - s, 8, 143 + gi)
+        assert_close(dx[torch.from_numpy(rows).cuda()], O.rows_dx(G, wd[gi], rows), f"group {gi} dX")
+        nrows = _sample_rows(w.N, 6, 160 + gi)
+        ref = O.rows_dw(G[s:e], xd[0][s:e], nrows)
+        assert_close(dw[gi][torch.from_numpy(nrows).cuda()], ref, f"group {gi} dW")
+
+
 def test_mxfp8_deferred_full_size(lp):
     """64 experts, 32768 tokens with Zipf(1.1) sizes: the GPU quantizes grad
     (along -1) and W (along the reduction axis) and runs grouped dX.  Every
