@@ -247,10 +247,10 @@ def build(lp, name: str):
         xq = lp.lp_mx_quant(xt, -2, "mxfp8")
         dx = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
         dw = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
-        phases.append(Phase("mx_quant_dual grad", "mx_quant_dual", nbytes=M * N * (2 + 2 * (1 + 1 / 32))))
-        phases.append(Phase("mx_quant W", "mx_quant_rows", nbytes=N * K * (2 + 1 + 1 / 32)))
-        phases.append(Phase("mx_quant X", "mx_quant_rows", nbytes=M * K * (2 + 1 + 1 / 32)))
-        phases.append(Phase("linear_bwd dX", "fp8_mfma_kernel", flops=2.0 * M * N * K, peak=PEAK_FP8_TFLOPS))
+        phases.append(Phase("mx_quant_dual grad", "mx_quant_tile<dual>", nbytes=M * N * (2 + 2 * (1 + 1 / 32))))
+        phases.append(Phase("mx_quant W", "mx_quant_tile", nbytes=N * K * (2 + 1 + 1 / 32)))
+        phases.append(Phase("mx_quant X", "mx_quant_tile", nbytes=M * K * (2 + 1 + 1 / 32)))
+        phases.append(Phase("linear_bwd dX", "fp8_mfma_persistent", flops=2.0 * M * N * K, peak=PEAK_FP8_TFLOPS))
         phases.append(Phase("linear_bwd dW", "fp8_mfma_kernel", flops=2.0 * M * N * K, peak=PEAK_FP8_TFLOPS))
 
         def step(i, stream):

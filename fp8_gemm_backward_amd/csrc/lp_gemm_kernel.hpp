@@ -545,6 +545,46 @@ struct Tile {
   bool valid;
 };
 
+// The group holding listed row tile pidx (row tiles of BP rows, groups in
+// order, a group listed or not by its row count), with the clamped group
+// ends end_g = clamp(o_g, end_{g-1}, M); pidx past every listed tile:
+// found = false and seen = the listed row tiles in all.  Each wave reads 64
+// group ends with one LDS read and walks them from registers (readlane), so
+// that no LDS round trip sits in the per-group chain: walking one group per
+// LDS read cost up to 20k cycles per tile with 64 groups.
+// A walk may resume from an earlier hit (hint) whose first row tile is at
+// or before pidx: a persistent workgroup's tiles come in increasing order,
+// and restarting from group 0 for each cost it more as its tiles moved to
+// later groups.
+struct GroupHit {
+  int g, start, end, seen;
+  bool found;
+};
+template <int BP, class Listed>
+__device__ __forceinline__ GroupHit find_row_tile(const int32_t* s_ends, int groups, int M, int pidx, Listed listed,
+                                                  const GroupHit* hint = nullptr) {
+  const int lane = threadIdx.x & 63;
+  int g0 = 0, start = 0, seen = 0;
+  if (hint != nullptr && hint->found && hint->seen <= pidx) {
+    g0 = hint->g;
+    start = hint->start;
+    seen = hint->seen;
+  }
+  for (int base = g0; base < groups; base += 64) {
+    const int v = base + lane < groups ? s_ends[base + lane] : 0;
+    const int cnt = groups - base < 64 ? groups - base : 64;
+    for (int j = 0; j < cnt; ++j) {
+      int e = __builtin_amdgcn_readlane(v, j);
+      e = e < start ? start : (e > M ? M : e);
+      const int n = listed(e - start) ? (e - start + BP - 1) / BP : 0;
+      if (pidx < seen + n) return GroupHit{base + j, start, e, seen, true};
+      seen += n;
+      start = e;
+    }
+  }
+  return GroupHit{0, 0, 0, seen, false};
+}
+
 // Map the workgroup to its tile.  s_ends: LDS for the group offsets.  hw:
 // the workgroup's index among the p.ntiles of this contraction, in dispatch
 // order (blockIdx.x unless several contractions share a launch).
@@ -552,7 +592,7 @@ struct Tile {
 // workgroup's own tile order), and s_ends already holds the group ends.
 template <class C, bool kDW>
 __device__ __forceinline__ Tile select_tile(const Params& p, int32_t* s_ends, int hw = blockIdx.x,
-                                            bool persistent = false) {
+                                            bool persistent = false, GroupHit* hint = nullptr) {
   const int tid = threadIdx.x;
   int tile = persistent ? hw : xcd_remap(hw, p.ntiles);
   int split = 0;
@@ -578,48 +618,35 @@ __device__ __forceinline__ Tile select_tile(const Params& p, int32_t* s_ends, in
       t.p0 = pidx * C::BP;
       t.pend = p.Ptot;
     } else {
-      int start = 0, seen = 0;
       t.p0 = -1;
+      // fuse_side 0 lists every group; 1 the groups of more than fuse_rows
+      // rows; 2 those of at most fuse_rows.
+      auto listed = [&](int n) { return p.fuse_side == 0 || ((n <= p.fuse_rows) == (p.fuse_side == 2)); };
       if (p.fuse_side != 0 && !persistent && p.splits == 1) {
         // A filtered listing, whose tile count the host only bounds: deal
         // the listed tiles themselves over the XCDs, or the bound's empty
         // tail would leave whole XCDs idle.
-        int n = 0;
-        for (int gi = 0; gi < p.groups; ++gi) {
-          int e = s_ends[gi];
-          e = e < start ? start : (e > p.Ptot ? p.Ptot : e);
-          const bool listed = (e - start <= p.fuse_rows) == (p.fuse_side == 2);
-          n += listed ? (e - start + C::BP - 1) / C::BP : 0;
-          start = e;
-        }
-        const int nt = n * p.nq;
+        const int nt = find_row_tile<C::BP>(s_ends, p.groups, p.Ptot, INT32_MAX, listed).seen * p.nq;
         tile = hw < nt ? xcd_remap(hw, nt) : nt;                 // nt: past every listed tile
         pidx = tile / p.nq;
         t.q0 = (tile % p.nq) * C::BQ;
         t.tile = tile;
-        start = 0;
       }
-      for (int gi = 0; gi < p.groups; ++gi) {
-        int e = s_ends[gi];
-        e = e < start ? start : (e > p.Ptot ? p.Ptot : e);        // end_g = clamp(o_g, end_{g-1}, M)
-        const bool listed = p.fuse_side == 0 || ((e - start <= p.fuse_rows) == (p.fuse_side == 2));
-        const int n = listed ? (e - start + C::BP - 1) / C::BP : 0;
-        if (pidx < seen + n) {
-          t.g = gi;
-          t.p0 = start + (pidx - seen) * C::BP;
-          t.pend = e;
-          if (p.gm > 1) {
-            // Inside the group, the dense order in blocks of gm row tiles
-            // (grouped_order): the tiles an XCD runs together share both
-            // gradient rows and weight columns in its L2.
-            const int2 pq = grouped_order(tile - seen * p.nq, n, p.nq, p.gm);
-            t.p0 = start + pq.x * C::BP;
-            t.q0 = pq.y * C::BQ;
-          }
-          break;
+      const GroupHit h = find_row_tile<C::BP>(s_ends, p.groups, p.Ptot, pidx, listed, hint);
+      if (hint != nullptr && h.found) *hint = h;
+      if (h.found) {
+        t.g = h.g;
+        t.p0 = h.start + (pidx - h.seen) * C::BP;
+        t.pend = h.end;
+        if (p.gm > 1) {
+          // Inside the group, the dense order in blocks of gm row tiles
+          // (grouped_order): the tiles an XCD runs together share both
+          // gradient rows and weight columns in its L2.
+          const int n = (h.end - h.start + C::BP - 1) / C::BP;
+          const int2 pq = grouped_order(tile - h.seen * p.nq, n, p.nq, p.gm);
+          t.p0 = h.start + pq.x * C::BP;
+          t.q0 = pq.y * C::BQ;
         }
-        seen += n;
-        start = e;
       }
     }
     t.valid = t.p0 >= 0 && t.p0 < t.pend;

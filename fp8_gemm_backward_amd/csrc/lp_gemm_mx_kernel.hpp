@@ -127,6 +127,7 @@ struct Persist {
   int32_t* ends;     // LDS holding the group ends (a stage may hold the next prologue)
   int next;          // the workgroup's next tile (>= ntiles: none)
   bool issued;       // this tile's prologue was issued by the previous tile
+  GroupHit hint;     // the group walk's last hit (the workgroup's tiles only move forward)
 };
 
 // One output tile.  hw: the workgroup's index among p.ntiles (see
@@ -161,7 +162,7 @@ __device__ __forceinline__ int mx_tile(const Params& p, int hw, uint8_t* st0, ui
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wp = wave >> 1, wq = wave & 1;
   if (hw >= p.ntiles) return kNoTile;
-  const Tile t = kPersist ? select_tile<XCfg, kDW>(p, pst->ends, hw, true)
+  const Tile t = kPersist ? select_tile<XCfg, kDW>(p, pst->ends, hw, true, &pst->hint)
                           : select_tile<XCfg, kDW>(p, reinterpret_cast<int32_t*>(st0), hw);
   if (!t.valid) return kNoTile;
   __syncthreads();                                               // group ends read; stage 0 reusable
@@ -455,7 +456,7 @@ __device__ __forceinline__ int mx_tile(const Params& p, int hw, uint8_t* st0, ui
     // The next tile's prologue, then this tile's results.
     bool issued = false;
     if (pst->next < p.ntiles) {
-      const Tile tn = select_tile<XCfg, kDW>(p, pst->ends, pst->next, true);
+      const Tile tn = select_tile<XCfg, kDW>(p, pst->ends, pst->next, true, &pst->hint);
       if (tn.valid && tn.kend > tn.kbeg) {
         const uint8_t* const npc = p.P.codes + (int64_t)tn.p0 * ldp;
         const int npend = kDW ? M : tn.pend;
@@ -559,7 +560,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   LP_MX_LDS(kChunkMode);
   __shared__ int32_t s_ends[kMaxGroups];
   const int nwg = gridDim.x, xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
-  Persist ps{s_ends, 0, false};
+  Persist ps{s_ends, 0, false, GroupHit{0, 0, 0, 0, false}};
   if (p.offsets != nullptr) {
     for (int i = threadIdx.x; i < p.groups; i += NT) s_ends[i] = p.offsets[i];
     __syncthreads();

@@ -109,45 +109,28 @@ __global__ __launch_bounds__(NT8) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // eighth of the list and its workgroups deal it out in turn, so that the
   // tiles one XCD runs together are neighbours: column tiles of the same
   // rows, whose gradient rows its L2 then serves.
-  int nrt = 0;
-  {
-    int start = 0;
-    for (int gi = 0; gi < p.groups; ++gi) {
-      int e = s_ends[gi];
-      e = e < start ? start : (e > M ? M : e);
-      const int n = e - start;
-      nrt += (n > 0 && n <= p.fuse_rows) ? (n + WBP - 1) / WBP : 0;
-      start = e;
-    }
-  }
-  const int nlist = nrt * p.nq;
+  auto listed = [&](int n) { return n <= p.fuse_rows; };
+  const int nlist = find_row_tile<WBP>(s_ends, p.groups, M, INT32_MAX, listed).seen * p.nq;
   const int nslot = gridDim.x / 8, xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
   const int per = (nlist + 7) / 8;
   const int lo = xcd * per, hi = lo + per < nlist ? lo + per : nlist;
   const int first = lo + slot;
   const int mine = first < hi ? (hi - first + nslot - 1) / nslot : 0;
   if (mine == 0) return;
+  GroupHit hint{0, 0, 0, 0, false};              // the walk's last hit: tiles come in increasing order
   auto tile_at = [&](int i) __attribute__((always_inline)) {
     WTile t{0, 0, 0, 0, false};
     if (i >= mine) return t;
     const int l = first + i * nslot;
     const int pidx = l / p.nq;
     t.q0 = (l - pidx * p.nq) * WBQ;
-    int start = 0, seen = 0;
-    for (int gi = 0; gi < p.groups; ++gi) {
-      int e = s_ends[gi];
-      e = e < start ? start : (e > M ? M : e);
-      const int n = e - start;
-      const int c = (n > 0 && n <= p.fuse_rows) ? (n + WBP - 1) / WBP : 0;
-      if (pidx < seen + c) {
-        t.g = gi;
-        t.p0 = start + (pidx - seen) * WBP;
-        t.pend = e;
-        t.valid = true;
-        break;
-      }
-      seen += c;
-      start = e;
+    const GroupHit h = find_row_tile<WBP>(s_ends, p.groups, M, pidx, listed, &hint);
+    if (h.found) {
+      hint = h;
+      t.g = h.g;
+      t.p0 = h.start + (pidx - h.seen) * WBP;
+      t.pend = h.end;
+      t.valid = true;
     }
     return t;
   };
