@@ -394,11 +394,11 @@ def time_standalone(lp, stream, q, reps=50):
 # ------------------------------------------------------------------ HBM traffic from committed counters
 
 def kernel_source_digest() -> str:
-    """Digest of the sources the fused GEMM kernels are built from."""
+    """Digest of every kernel source (the library's .hip and .hpp files)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "fp8_gemm_backward_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        if f.startswith("lp_gemm") or f in ("lp_device.hpp", "lp_internal.hpp"):
+        if f.endswith((".hip", ".hpp")):
             h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
