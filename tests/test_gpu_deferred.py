@@ -56,12 +56,25 @@ def test_deferred_matches_quantize_then_product(lp, fuse_rows):
     w = bf16_dev(wbits)
     offs = torch.from_numpy(offsets).cuda()
     ref = _two_calls(lp, g, w, offs, _sentinel((M, K)))
-    dx = lp.lp_grouped_dx_deferred(g, w, offs, fuse_rows=fuse_rows, grad_x=_sentinel((M, K)))
+    G = len(sizes)
+    codes = torch.full((G, N, K), 0xA5, dtype=torch.uint8, device="cuda")
+    scales = torch.full((G, N // 32, K), 0x5A, dtype=torch.uint8, device="cuda")
+    dx = lp.lp_grouped_dx_deferred(g, w, offs, fuse_rows=fuse_rows, grad_x=_sentinel((M, K)), w_codes=codes,
+                                   w_scales=scales)
     torch.cuda.synchronize()
     assert_bits_equal(bits_host(dx), bits_host(ref), f"fuse_rows={fuse_rows} vs quantize-then-product")
     end = int(offsets[-1])
     assert np.all(bits_host(dx[end:]) == 0xFFFF), "rows past the last offset were written"
     wc, ws = F.mx_quant(wbits, -2, "e4m3")
+    # The weight copy: written (the oracle's codes and scales) for the groups
+    # quantized first (all of them when fuse_rows is 0), left as it was for
+    # the groups quantized inside the product.
+    got_c, got_s = codes.cpu().numpy(), scales.cpu().numpy()
+    for gi, (s0, e0) in enumerate(O.group_bounds(offsets)):
+        if fuse_rows == 0 or e0 - s0 > fuse_rows:
+            assert np.array_equal(got_c[gi], wc[gi]) and np.array_equal(got_s[gi], ws[gi]), f"group {gi} codes"
+        else:
+            assert np.all(got_c[gi] == 0xA5) and np.all(got_s[gi] == 0x5A), f"group {gi} copy was written"
     wd = F.dequant("mxfp8", wc, ws, axis=-2)
     exp, _ = O.grouped_dx(gd, wd, offsets)
     got = dx[:end].float().cpu().numpy()
