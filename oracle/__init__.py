@@ -18,6 +18,10 @@ Pins (tests/test_oracle_*.py, all CPU):
 * MX quant: scale-exponent invariant, idempotence, special blocks.
 * GEMMs: pure-Python triple loops on tiny shapes, the ones-gradient closed
   forms of the FP8-adapter page's tests, grouped == per-group dense.
+* forwards: triple loops (the NVFP4 forward over scalar-decoded operands),
+  the FP8-adapter page's formulation on its grouped test shapes and on
+  partial 128-blocks, and the adjoint identity that ties each forward's
+  orientation to the backward's.
 * per-tensor FP8 (pertensor.py): the E5M2 table against torch's
   float8_e5m2, quantization against torch's casts below saturation and a
   brute-force nearest search, the scale formula and ring update of the

@@ -27,7 +27,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .formats import bf16_bits_to_f64
+from .formats import FMT_FP8_B128, FMT_NVFP4, bf16_bits_to_f64, dequant
 
 
 def _f64(bits) -> np.ndarray:
@@ -104,3 +104,35 @@ def rows_dx(grad_bits: np.ndarray, w_bits: np.ndarray, rows) -> np.ndarray:
 def rows_dw(grad_bits: np.ndarray, x_bits: np.ndarray, n_rows) -> np.ndarray:
     """Selected rows n of grad_W = grad.T @ X."""
     return _f64(np.asarray(grad_bits)[:, n_rows]).T @ _f64(x_bits)
+
+
+# ---------------------------------------------------------------- forwards of quantized layers
+# The forward ops that the backward pages pair with take the same saved
+# operands.  Neither page gives their arithmetic; the reading here is the
+# one the backward states for its own products: decode each quantized
+# operand to bf16 exactly as the backward does (formats.dequant), then
+# contract in fp64.
+
+def nvfp4_fwd(x_codes, x_scales, x_ts, w_codes, w_scales, w_ts, offsets=None) -> np.ndarray:
+    """NVFP4 forward ("Add Autograd Backward Support for FP4 GEMM Custom Ops":
+    the f4f4bf16 ops multiply FP4 inputs by FP4 weights into BF16, dense and
+    grouped).  x [M][K] and w [G][N][K] (G = 1 for the dense op) are NVFP4:
+    packed E2M1 codes, E4M3 scales per 16 along K, an fp32 tensor scale.
+    Dense: y = dec(x) @ dec(w)^T; grouped (offsets given): per group as
+    grouped_fwd, rows past the last offset NaN ("not written")."""
+    xb = dequant(FMT_NVFP4, x_codes, x_scales, x_ts)[0]
+    wb = dequant(FMT_NVFP4, w_codes, w_scales, w_ts)
+    return linear_fwd(xb, wb[0]) if offsets is None else grouped_fwd(xb, wb, offsets)
+
+
+def fp8_block_fwd(x_bits, w_codes, w_scale_inv, offsets=None) -> np.ndarray:
+    """Block-FP8 forward ("Train adapters on top of FP8 weights":
+    FP8LinearFunction.forward through fp8_linear, and
+    FP8GroupedMatmulFunction.forward through the kernel's
+    grouped_matmul(input, weight, weight_scale_inv, offsets, ...)): a bf16
+    input times an E4M3 weight [G][N][K] with fp32 inverse scales per 128 x
+    128 block.  The input stays bf16 (the page quantizes nothing else); the
+    weight is decoded as `_dequantize_fp8_weight` does for the backward.
+    Dense (offsets None, G = 1) or grouped as grouped_fwd."""
+    wb = dequant(FMT_FP8_B128, w_codes, w_scale_inv)
+    return linear_fwd(x_bits, wb[0]) if offsets is None else grouped_fwd(x_bits, wb, offsets)

@@ -551,6 +551,88 @@ def pin_grouped_forward_equals_dense():
     assert np.allclose(y[9:25], O.linear_fwd(x[9:25], w[2]), rtol=1e-13)
 
 
+def _nv_scalar_decode(packed, scales, ts):
+    """Element-by-element NVFP4 decode from the scalar code functions: low
+    nibble = even column, one E4M3 scale per 16 columns, S = fp32(s * ts),
+    value = bf16(fp32(code * S)) through torch's CPU casts."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    R, C = packed.shape[0], packed.shape[1] * 2
+    out = np.empty((R, C), dtype=np.float64)
+    for r in range(R):
+        for c in range(C):
+            byte = int(packed[r, c // 2])
+            code = byte & 0xF if c % 2 == 0 else byte >> 4
+            S = float(np.float32(F.e4m3_value(int(scales[r, c // 16])) * float(np.float32(ts))))
+            f = np.float32(F.e2m1_value(code) * S)
+            out[r, c] = float(torch.tensor(float(f), dtype=torch.float32).bfloat16().double())
+    return out
+
+
+def pin_nvfp4_forward_scalar_loop():
+    """NVFP4 forward against a triple loop over scalar-decoded operands, dense
+    and grouped (an empty group; rows past the last offset unwritten), with
+    distinct tensor scales so that dropping or swapping one shows."""
+    M, N, K, G = 6, 4, 32, 3
+    xc, xs, xts = F.quant_nvfp4(W.normal_f32(106, "x", (M, K), 1.0))
+    wc, ws, wts = F.quant_nvfp4(W.normal_f32(106, "w", (G, N, K), 3.0))
+    assert float(xts) != float(wts)
+    xv = _nv_scalar_decode(xc[0], xs[0], xts)
+    wv = [_nv_scalar_decode(wc[g], ws[g], wts) for g in range(G)]
+
+    def loop(rows, wg):
+        return np.array([[sum(xv[m, k] * wg[n, k] for k in range(K)) for n in range(N)] for m in rows])
+
+    dense = O.nvfp4_fwd(xc[0], xs[0], xts, wc[:1], ws[:1], wts)
+    assert dense.shape == (M, N)
+    assert np.allclose(dense, loop(range(M), wv[0]), rtol=1e-12, atol=0), "dense NVFP4 forward"
+    offsets = np.array([2, 2, 5], dtype=np.int32)
+    y = O.nvfp4_fwd(xc[0], xs[0], xts, wc, ws, wts, offsets)
+    assert np.allclose(y[0:2], loop(range(0, 2), wv[0]), rtol=1e-12, atol=0), "grouped NVFP4 forward, group 0"
+    assert np.allclose(y[2:5], loop(range(2, 5), wv[2]), rtol=1e-12, atol=0), "grouped NVFP4 forward, group 2"
+    assert np.all(np.isnan(y[5:]))
+
+
+def pin_fp8_block_forward_page_formulation():
+    """Block-FP8 forward on the FP8-adapter page's grouped test shapes (2
+    groups, weight 512 x 256 viewed as 2 x 256 x 256, scale grid 4 x 2) and on
+    a weight with partial 128-blocks: equal to the page's test formulation in
+    torch (codes decoded by torch's float8_e4m3fn, times the scale grid
+    repeated over 128 x 128 blocks and cut at the edge, rounded to bf16,
+    contracted in float64), and tied to the backward by the adjoint identity
+    sum(y * g) = sum(x * grad_X)."""
+    c = GOLDEN["fp8_grouped_test"]
+    G, tpg = c["groups"], c["tokens_per_group"]
+    codes, scale = _page_fp8_weight(107, c["out_features"], c["in_features"], tuple(c["scale_grid"]), c["scale_low"])
+    per = c["out_features"] // G
+    wc = codes.reshape(G, per, c["in_features"])
+    wsc = scale.reshape(G, per // 128, -1)
+    x = _tiny_bf16(107, "x", (G * tpg + 2, c["in_features"]))        # two rows past the last offset
+    offsets = np.arange(1, G + 1, dtype=np.int32) * tpg
+    y = O.fp8_block_fwd(x, wc, wsc, offsets)
+    s = torch.from_numpy(scale).repeat_interleave(128, 0).repeat_interleave(128, 1)
+    wt = (_torch_decode_e4m3(codes) * s).bfloat16().double().view(G, per, -1)
+    xt = torch.from_numpy(F.bf16_bits_to_f64(x))
+    for g in range(G):
+        ref = xt[g * tpg:(g + 1) * tpg] @ wt[g].T
+        assert np.allclose(y[g * tpg:(g + 1) * tpg], ref.numpy(), rtol=1e-12, atol=0), f"group {g}"
+    assert np.all(np.isnan(y[G * tpg:]))
+    gr = _tiny_bf16(107, "grad", (G * tpg, per))
+    wd = F.dequant(F.FMT_FP8_B128, wc, wsc)
+    dx, _ = O.grouped_dx(gr, wd, offsets)
+    lhs = float(np.sum(y[:G * tpg] * F.bf16_bits_to_f64(gr)))
+    rhs = float(np.sum(F.bf16_bits_to_f64(x)[:G * tpg] * dx[:G * tpg]))
+    assert abs(lhs - rhs) <= 1e-10 * max(1.0, abs(lhs)), "forward and backward disagree on orientation"
+    # dense, partial blocks: 300 x 200 weight, 3 x 2 grid
+    R, C = 300, 200
+    codes2, scale2 = _page_fp8_weight(108, R, C, (3, 2), 0.5)
+    x2 = _tiny_bf16(108, "x", (5, C))
+    y2 = O.fp8_block_fwd(x2, codes2, scale2)
+    s2 = torch.from_numpy(scale2).repeat_interleave(128, 0)[:R].repeat_interleave(128, 1)[:, :C]
+    w2 = (_torch_decode_e4m3(codes2) * s2).bfloat16().double()
+    ref2 = torch.from_numpy(F.bf16_bits_to_f64(x2)) @ w2.T
+    assert np.allclose(y2, ref2.numpy(), rtol=1e-12, atol=0), "dense block-FP8 forward with partial blocks"
+
+
 # ------------------------------------------------------------------ sampled and chunked paths
 
 def pin_rows_dx_dw_brute_force():

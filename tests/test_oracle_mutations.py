@@ -141,12 +141,32 @@ def _chunks_drop_last_block(n, size):
     return [(i, min(n, i + size) - (1 if min(n, i + size) - i > 1 else 0)) for i in range(0, n, size)]
 
 
+_orig_nv_fwd = O.nvfp4_fwd
+_orig_fp8_fwd = O.fp8_block_fwd
+_orig_grouped_fwd = O.grouped_fwd
+
+
+def _nv_fwd_without_w_tensor_scale(x_codes, x_scales, x_ts, w_codes, w_scales, w_ts, offsets=None):
+    return _orig_nv_fwd(x_codes, x_scales, x_ts, w_codes, w_scales, 1.0, offsets)
+
+
+def _fp8_fwd_unit_scales(x_bits, w_codes, w_scale_inv, offsets=None):
+    return _orig_fp8_fwd(x_bits, w_codes, np.ones_like(w_scale_inv), offsets)
+
+
+def _grouped_fwd_next_weight(x_bits, w_bits, offsets):
+    return _orig_grouped_fwd(x_bits, np.roll(np.asarray(w_bits), -1, axis=0), offsets)
+
+
 MUTATIONS = {
     "sampled dX takes the next row": (O, "rows_dx", _rows_dx_next_row),
     "sampled dW takes the next n": (O, "rows_dw", _rows_dw_next_n),
     "dequant row slab lags one scale row": (F, "_scale_rows", _scale_rows_lag),
     "MX quant chunks skip their last block": (F, "_block_chunks", _chunks_drop_last_block),
     "forward multiplies W untransposed": (O, "linear_fwd", _fwd_no_transpose),
+    "NVFP4 forward drops the weight tensor scale": (O, "nvfp4_fwd", _nv_fwd_without_w_tensor_scale),
+    "block-FP8 forward ignores the block scales": (O, "fp8_block_fwd", _fp8_fwd_unit_scales),
+    "grouped forward takes the next group's weight": (O, "grouped_fwd", _grouped_fwd_next_weight),
     "per-tensor quantization multiplies by the scale": (PT, "quantize", _pt_quant_multiplies),
     "per-tensor quantization without saturation": (PT, "round_to_fp8", _pt_no_saturation),
     "scale ignores the margin": (PT, "scale_from_history", _pt_scale_no_margin),
