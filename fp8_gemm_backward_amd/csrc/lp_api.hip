@@ -341,16 +341,21 @@ lp_status lp_linear_bwd_noalloc(const lp_qtensor* grad_out, const lp_qtensor* x,
 
 extern "C" {
 
-// Checks of the forward: x [M][K] and w [G][N][K], both MXFP4 or both
-// MXFP8 scaled along k; K % 128 (MXFP4) or K % 64 (MXFP8); N % 16.
+// Checks of the forward: x [M][K] and w [G][N][K], both MXFP4 or both MXFP8
+// scaled along k (K % 128 for MXFP4, K % 64 for MXFP8), both NVFP4 (K % 32),
+// or a bf16 x with a bf16 or block-FP8 weight (K % 16); N % 16.
 static lp_status check_fwd(const lp_qtensor* x, const lp_qtensor* w, void* y, int64_t groups) {
   lp_status st = check_tensor(x);
   if (st != LP_OK) return st;
   if ((st = check_tensor(w)) != LP_OK) return st;
-  if ((x->fmt != LP_MXFP4 && x->fmt != LP_MXFP8) || w->fmt != x->fmt) return LP_ERR_FORMAT;
-  if (x->scale_axis != -1 || w->scale_axis != -1) return LP_ERR_FORMAT;
+  const bool mx = (x->fmt == LP_MXFP4 || x->fmt == LP_MXFP8) && w->fmt == x->fmt;
+  const bool nv = x->fmt == LP_NVFP4 && w->fmt == LP_NVFP4;
+  const bool b16 = x->fmt == LP_BF16 && (w->fmt == LP_BF16 || w->fmt == LP_FP8_B128);
+  if (!mx && !nv && !b16) return LP_ERR_FORMAT;
+  if ((mx || nv) && (x->scale_axis != -1 || w->scale_axis != -1)) return LP_ERR_FORMAT;
   if (x->batch != 1 || w->batch != (groups ? groups : 1) || w->cols != x->cols) return LP_ERR_SHAPE;
-  if (x->cols % (x->fmt == LP_MXFP4 ? 128 : 64) || w->rows % 16) return LP_ERR_SHAPE;
+  const int64_t kmul = x->fmt == LP_MXFP4 ? 128 : x->fmt == LP_MXFP8 ? 64 : nv ? 32 : 16;
+  if (x->cols % kmul || w->rows % 16) return LP_ERR_SHAPE;
   if (x->rows >= kMaxProductRows || x->cols >= kMaxProductCols || w->rows >= kMaxProductCols) return LP_ERR_SHAPE;
   if (!tiles_ok(x->rows / 128 + (groups ? groups : 1) + 1, w->rows)) return LP_ERR_SHAPE;
   if (x->rows * w->rows > 0 && y == nullptr) return LP_ERR_NULL;

@@ -241,12 +241,18 @@ hipError_t launch_fwd(const lp_qtensor& x, const lp_qtensor& w, const int32_t* o
   prm.offsets = offsets;
   prm.groups = groups;
   prm.splits = 1;
-  prm.nq = (int32_t)((prm.Qtot + Big::BQ - 1) / Big::BQ);
+  // MX operands run on the block-scaled MFMA (256 x 256 tiles); the others
+  // through bf16 tiles: 256 x 256 when both are decoded (NVFP4), else
+  // 256 x 128 (three stages of a bf16 x tile and of the weight tile fit in
+  // LDS only at that width).
+  const bool mx = x.fmt == LP_MXFP4 || x.fmt == LP_MXFP8;
+  const int BP = 256, BQ = (mx || x.fmt == LP_NVFP4) ? 256 : 128;
+  prm.nq = (int32_t)((prm.Qtot + BQ - 1) / BQ);
   if (offsets == nullptr)
-    prm.gm = tile_group(Big::BP * code_bytes2(x.fmt), Big::BQ * code_bytes2(w.fmt), (prm.Ptot + Big::BP - 1) / Big::BP);
-  const int64_t ptiles = offsets ? (x.rows / Big::BP + groups) : (x.rows + Big::BP - 1) / Big::BP;
+    prm.gm = tile_group(BP * code_bytes2(x.fmt), BQ * code_bytes2(w.fmt), (prm.Ptot + BP - 1) / BP);
+  const int64_t ptiles = offsets ? (x.rows / BP + groups) : (x.rows + BP - 1) / BP;
   prm.ntiles = (int32_t)(ptiles * prm.nq);
-  return fwd_mx(prm, x.fmt == LP_MXFP4, stream);
+  return mx ? fwd_mx(prm, x.fmt == LP_MXFP4, stream) : fwd_dec(prm, x.fmt, w.fmt, stream);
 }
 
 hipError_t launch_grouped_dx_deferred(const lp_qtensor& grad, const void* w, int64_t K, const int32_t* offsets,

@@ -269,7 +269,8 @@ struct Decoded {
   static constexpr int VMEM = PER * (kScale ? 2 : 1);                // vector-memory loads per slab
   static constexpr int QUARTERS = F == BF16 ? 1 : 4;                 // decode items per piece
   static constexpr int DECODES = PER * PIECES * QUARTERS;            // decode items per slab
-  static_assert(kKMajor ? (F == MXFP8) : true, "k-major decode is for MXFP8 only");
+  static_assert(kKMajor ? ((F == MXFP8 && A == -1) || F == NVFP4 || F == FP8_B128) : true,
+                "k-major decode needs scales along the contraction");
 
   using Stage = Raw<F, A>[PER];
 
@@ -311,8 +312,9 @@ struct Decoded {
       }
     }
     if constexpr (kKMajor) {
-      cbase = op.codes + (int64_t)mn0 * op.code_ld;
-      sbase = op.scales + (int64_t)mn0 * op.scale_ld;
+      // Rows [mn0, mnend_rows) of group g (FP8 blocks: mn0 % 128 == 0).
+      cbase = op.codes + (int64_t)g * op.code_batch + (int64_t)mn0 * op.code_ld;
+      sbase = op.scales + (int64_t)g * op.scale_batch + (int64_t)(F == FP8_B128 ? mn0 >> 7 : mn0) * op.scale_ld;
       crows_bytes = (int64_t)(mnend_rows - mn0) * op.code_ld;
     } else {
       cbase = op.codes + (int64_t)g * op.code_batch;
@@ -330,8 +332,14 @@ struct Decoded {
     w.kend = kend;
     w.tail = k0 + BK > kend;
     if constexpr (kKMajor) {
+      // A slab (BK = 64 columns, k0 % 64 == 0) lies inside one 128-column
+      // FP8 block, so one scale column serves it.
+      constexpr int KS = F == NVFP4 ? 4 : (F == FP8_B128 ? 7 : 5);    // log2 columns per scale
+      const int64_t nrows = crows_bytes / op.code_ld;
+      const int64_t srows = F == FP8_B128 ? (nrows + 127) >> 7 : nrows;
+      const int soff = F == FP8_B128 ? (k0 >> 7) * 4 : (k0 >> KS);
       w.cr = make_rsrc(cbase + (int64_t)k0 * BPE2 / 2, crows_bytes - (int64_t)k0 * BPE2 / 2);
-      w.sr = make_rsrc(sbase + (k0 >> 5), crows_bytes / op.code_ld * op.scale_ld - (k0 >> 5));
+      w.sr = make_rsrc(sbase + soff, srows * op.scale_ld - soff);
     } else {
       const int64_t nrows = kend - k0;
       w.cr = make_rsrc(cbase + (int64_t)k0 * op.code_ld, nrows * op.code_ld);
@@ -349,7 +357,12 @@ struct Decoded {
     if constexpr (kKMajor) {
       const bool out = w.tail && w.k0 + mnc[I] >= w.kend;
       st[I].c = bload16(w.cr, out ? kOOB : voff[I]);
-      st[I].s = __builtin_amdgcn_raw_buffer_load_b8(w.sr, out ? kOOB : row[I] * op.scale_ld + (mnc[I] >> 5), 0, 0);
+      if constexpr (F == NVFP4)
+        st[I].s = __builtin_amdgcn_raw_buffer_load_b16(w.sr, out ? kOOB : row[I] * op.scale_ld + (mnc[I] >> 4), 0, 0);
+      else if constexpr (F == FP8_B128)
+        st[I].s = __builtin_amdgcn_raw_buffer_load_b32(w.sr, out ? kOOB : (row[I] >> 7) * op.scale_ld, 0, 0);
+      else
+        st[I].s = __builtin_amdgcn_raw_buffer_load_b8(w.sr, out ? kOOB : row[I] * op.scale_ld + (mnc[I] >> 5), 0, 0);
     } else {
       st[I].c = bload16(w.cr, voff[I]);
       if constexpr (F == MXFP4 || (F == MXFP8 && A == -1)) {
@@ -428,7 +441,7 @@ struct Direct {
       }
     }
     if constexpr (kKMajor) {
-      base = op.codes + (int64_t)mn0 * ld;
+      base = op.codes + (int64_t)g * op.code_batch + (int64_t)mn0 * ld;
       rows_bytes = (int64_t)(mnend_rows - mn0) * ld;
     } else {
       base = op.codes + (int64_t)g * op.code_batch;
@@ -839,14 +852,19 @@ __device__ __forceinline__ void barrier_vm() {
 // filled by direct loads and waits only for the load that filled it.  This
 // needs the buffer of each slab fixed at compile time: the main loop covers
 // three slabs, and decoded operands use three register stages to match.
-template <class C, int PF, int PA, int QF, int QA, bool kDW>
+//
+// kFwd: the forward y = x @ W^T (P = x rows, Q = W[g] rows, both k-major,
+// the contraction running along K, the columns of both).
+template <class C, int PF, int PA, int QF, int QA, bool kDW, bool kFwd = false>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_kernel(Params p) {
-  constexpr bool PK = !kDW;                                      // P k-major in dx, mn-major in dw
+  static_assert(!(kFwd && kDW), "the forward lists its tiles as grad_X does");
+  constexpr bool PK = !kDW;                                      // P k-major in dx and the forward, mn-major in dw
+  constexpr bool QK = kFwd;                                      // Q k-major in the forward only
   constexpr bool PD = PF == BF16;                                // P loaded straight into LDS
   // Q straight into LDS too when both operands are bf16 and three Q stages fit.
-  constexpr bool QD = PD && QF == BF16 && 3 * Direct<PK, C::BP>::BUF_BYTES + 3 * Direct<false, C::BQ>::BUF_BYTES <= kMaxLds;
+  constexpr bool QD = PD && QF == BF16 && 3 * Direct<PK, C::BP>::BUF_BYTES + 3 * Direct<QK, C::BQ>::BUF_BYTES <= kMaxLds;
   using LP = std::conditional_t<PD, Direct<PK, C::BP>, Decoded<PF, PA, PK, C::BP>>;
-  using LQ = std::conditional_t<QD, Direct<false, C::BQ>, Decoded<QF, QA, false, C::BQ>>;
+  using LQ = std::conditional_t<QD, Direct<QK, C::BQ>, Decoded<QF, QA, QK, C::BQ>>;
   constexpr int PERIOD = PD ? 3 : 2;                             // slabs per iteration = register stages
   constexpr int PBUF = LP::BUF_BYTES, QBUF = LQ::BUF_BYTES;
   constexpr int SB = C::WP * C::WQ * 2;                          // epilogue staging bytes per wave
@@ -869,8 +887,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   constexpr int DS0 = C::FP * C::FQ / 2;                         // first decode slot
   constexpr int FP = C::FP, FQ = C::FQ, NM = FP * FQ;
   using FAP = FragAddr<PK, PD, C::BP, FP>;
-  using FAQ = FragAddr<false, false, C::BQ, FQ>;
-  constexpr int NRP = FAP::NREAD, NR = FP * NRP + 2 * FQ;
+  using FAQ = FragAddr<QK, QD && QK, C::BQ, FQ>;
+  constexpr int NRP = FAP::NREAD, NRQ = FAQ::NREAD, NR = FP * NRP + NRQ * FQ;
   // The barrier of slab k needs this wave's direct loads of slab k+1 (issued
   // in slab k-1, ahead of its register loads); vmcnt lets the loads issued
   // after them stay outstanding (loads complete in order).
@@ -887,12 +905,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 
   // dx: P = grad rows [p0, pend) (k-major), Q = W[g] columns from q0.
   // dw: P = grad columns from p0, Q = X columns from q0, rows [kbeg, kend).
+  // forward: P = x rows [p0, pend), Q = W[g] rows from q0 (both k-major).
   LP lp;
   LQ lq;
   if constexpr (PD) lp.init(p.P, 0, t.p0, kDW ? 0 : p.P.rows, wave, lane);
   else lp.init(p.P, 0, t.p0, kDW ? 0 : p.P.rows, tid);
-  if constexpr (QD) lq.init(p.Q, kDW ? 0 : t.g, t.q0, 0, wave, lane);
-  else lq.init(p.Q, kDW ? 0 : t.g, t.q0, 0, tid);
+  if constexpr (QD) lq.init(p.Q, kDW ? 0 : t.g, t.q0, QK ? p.Q.rows : 0, wave, lane);
+  else lq.init(p.Q, kDW ? 0 : t.g, t.q0, QK ? p.Q.rows : 0, tid);
   FAP fap;
   FAQ faq;
   fap.init(wp * C::WP, lane);
@@ -959,11 +978,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     constexpr int r = decltype(ri)::value, S = decltype(si)::value, SET = decltype(seti)::value;
     if constexpr (r < NRP) {
       fap.template read<S, r, 0>(pb, fr[SET][0]);
-    } else if constexpr (r < NRP + 2 * FQ) {
-      constexpr int j = (r - NRP) / 2, h = (r - NRP) % 2;
+    } else if constexpr (r < NRP + NRQ * FQ) {
+      constexpr int j = (r - NRP) / NRQ, h = (r - NRP) % NRQ;
       faq.template read<S, h, j>(qb, fr[SET][FP + j]);
     } else {
-      constexpr int i = 1 + (r - NRP - 2 * FQ) / NRP, h = (r - NRP - 2 * FQ) % NRP;
+      constexpr int i = 1 + (r - NRP - NRQ * FQ) / NRP, h = (r - NRP - NRQ * FQ) % NRP;
       fap.template read<S, h, i>(pb, fr[SET][i]);
     }
   };
@@ -1059,10 +1078,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   store_acc<C, kDW>(p, t, acc, wp, wq, lane, stage);
 }
 
-template <class C, int PF, int PA, int QF, int QA, bool kDW>
+template <class C, int PF, int PA, int QF, int QA, bool kDW, bool kFwd = false>
 inline hipError_t run(const Params& prm, hipStream_t stream) {
   if (prm.ntiles <= 0) return hipSuccess;
-  gemm_kernel<C, PF, PA, QF, QA, kDW><<<dim3(prm.ntiles), dim3(NT), 0, stream>>>(prm);
+  gemm_kernel<C, PF, PA, QF, QA, kDW, kFwd><<<dim3(prm.ntiles), dim3(NT), 0, stream>>>(prm);
   return hipGetLastError();
 }
 
@@ -1110,6 +1129,10 @@ hipError_t dw_pt(const Params& prm, int fmt_p, int fmt_q, hipStream_t s);
 // Forward y = x @ w^T of MX operands scaled along k, both MXFP4 (fp4) or
 // both MXFP8.
 hipError_t fwd_mx(const Params& prm, bool fp4, hipStream_t s);
+// Forward y = x @ w^T through bf16 tiles (fused decode): bf16 x with a bf16
+// or block-FP8 weight (256 x 128 tiles), NVFP4 x with an NVFP4 weight
+// (256 x 256 tiles).
+hipError_t fwd_dec(const Params& prm, int fmt_x, int fmt_w, hipStream_t s);
 // Both of them in one launch (X and W in the same format fmt_q).
 hipError_t pt_pair(const Params& dx, const Params& dw, int fmt_p, int fmt_q, hipStream_t s);
 

@@ -448,32 +448,46 @@ lp_status lp_grouped_dx_deferred(const lp_qtensor* grad_out, const void* w, int6
                                  void* stream);
 
 /*
- * lp_linear_fwd - forward of a linear layer y = x @ W^T whose operands are
- * both MX-quantized along the contraction.
+ * lp_linear_fwd - forward of a linear layer y = x @ W^T with quantized (or
+ * bf16) operands.
  *
  * Cites: "Add Autograd Backward Support for FP4 GEMM Custom Ops" (the forward
  * ops that the backward pairs with multiply FP4 inputs by FP4 weights into
  * BF16); "perf: defer mxfp8 backward quantization", MXFP8MatMul.forward (x
  * quantized along its last axis, the weight along its reduction axis, one
- * E8M0 scale per 32).
+ * E8M0 scale per 32); "Train adapters on top of FP8 weights",
+ * FP8LinearFunction.forward (a bf16 input times an E4M3 weight with fp32
+ * inverse scales per 128 x 128 block).
  *
- * x  [M][K], w [N][K]: both LP_MXFP4 or both LP_MXFP8, scale_axis -1 (blocks
- *    of 32 along K).  K % 128 == 0 (LP_MXFP4) or K % 64 == 0 (LP_MXFP8);
+ * x  [M][K], w [N][K], one of:
+ *    - both LP_MXFP4 or both LP_MXFP8, scale_axis -1 (blocks of 32 along K);
+ *      K % 128 == 0 (LP_MXFP4) or K % 64 == 0 (LP_MXFP8);
+ *    - both LP_NVFP4 (E4M3 scales per 16 along K, each its own tensor
+ *      scale); K % 32 == 0;
+ *    - x LP_BF16 and w LP_BF16 or LP_FP8_B128; K % 16 == 0.
  *    N % 16 == 0; M >= 0 arbitrary.
  * y  device bf16 [M][N].
- * y[m][n] = sum_k dec(x)[m][k] * dec(w)[n][k] on the block-scaled MFMA: each
- * product code_x * code_w * 2^(sx + sw) is exact, the sum is fp32, the
- * result is rounded to bf16 (nearest even).  LP_ERR_FORMAT for other
- * formats.
+ * MX operands: y[m][n] = sum_k dec(x)[m][k] * dec(w)[n][k] on the
+ * block-scaled MFMA: each product code_x * code_w * 2^(sx + sw) is exact,
+ * the sum is fp32, the result is rounded to bf16 (nearest even).
+ * NVFP4 and block-FP8 operands are decoded to bf16 inside the contraction,
+ * exactly as lp_dequant decodes them (so a NaN code or scale gives NaN
+ * outputs in its row or column), then contracted on the bf16 MFMA with fp32
+ * sums; decoding them first with lp_dequant and passing the bf16 copies
+ * gives bit-identical results.
+ * LP_ERR_FORMAT for other format combinations.
  */
 lp_status lp_linear_fwd(const lp_qtensor* x, const lp_qtensor* w, void* y, void* stream);
 
 /*
- * lp_grouped_fwd - forward of a grouped (per-expert) matmul with MX operands.
+ * lp_grouped_fwd - forward of a grouped (per-expert) matmul.
  *
  * Cites: "Add Autograd Backward Support for FP4 GEMM Custom Ops" (grouped FP4
  * forward); "Train adapters on top of FP8 weights", FP8GroupedLinear.forward
- * (int32 cumulative end offsets; rows past the last offset are not written).
+ * and FP8GroupedMatmulFunction.forward (the kernel's grouped_matmul of a
+ * bf16 input with block-FP8 expert weights over int32 cumulative end
+ * offsets); the EP-sentinel comment of fp8_grouped_mm_experts_forward (rows
+ * past the last offset are not written).
  *
  * x        [M][K] rows grouped by offsets; w [groups][N][K]; formats and sizes
  *          as lp_linear_fwd.  offsets as lp_grouped_bwd (read on the device,

@@ -148,8 +148,12 @@ def fwd(x, w, y=FAKE):
     (None, q("mxfp4", 64, 128), FAKE, NULL),
     (q("mxfp4", 64, 128), q("mxfp4", 32, 128), None, NULL),
     (q("mxfp4", 64, 128), q("mxfp8", 32, 128), FAKE, FORMAT),       # formats must agree
-    (q("bf16", 64, 128), q("bf16", 32, 128), FAKE, FORMAT),
-    (q("nvfp4", 64, 128), q("nvfp4", 32, 128), FAKE, FORMAT),
+    (q("bf16", 64, 128), q("mxfp4", 32, 128), FAKE, FORMAT),        # bf16 x: bf16 or block-FP8 weight
+    (q("fp8_b128", 64, 128), q("bf16", 32, 128), FAKE, FORMAT),     # the block-FP8 operand is the weight
+    (q("nvfp4", 64, 128), q("bf16", 32, 128), FAKE, FORMAT),        # NVFP4 x: NVFP4 weight
+    (q("nvfp4", 64, 48), q("nvfp4", 32, 48), FAKE, SHAPE),          # NVFP4: K % 32
+    (q("bf16", 64, 128), q("fp8_b128", 40, 128), FAKE, SHAPE),      # N % 16
+    (q("bf16", 0, 128, codes=None), q("fp8_b128", 32, 128), None, OK),
     (q("mxfp8", 64, 128, axis=-2), q("mxfp8", 32, 128), FAKE, FORMAT),
     (q("mxfp4", 64, 96), q("mxfp4", 32, 96), FAKE, SHAPE),          # MXFP4: K % 128
     (q("mxfp8", 64, 96), q("mxfp8", 32, 96), FAKE, SHAPE),          # MXFP8: K % 64

@@ -36,6 +36,13 @@ grouped backward of "perf: defer mxfp8 backward quantization"):
   mxfp4_forward  the forward the FP4 backward pairs with ("Add Autograd Backward
                  Support for FP4 GEMM Custom Ops"): X 8192x4096 N(0,1) and W
                  4096x4096 N(0,1), both MXFP4 along K; y = X @ W^T
+  nvfp4_forward  the same forward with NVFP4 operands and nvfp4_linear's
+                 inputs (1% outliers x10); y = X @ W^T
+  fp8_grouped_forward  the block-FP8 grouped forward of "Train adapters on top
+                 of FP8 weights" (FP8GroupedMatmulFunction.forward): X bf16
+                 16384x4096 N(0,1), W 8x2048x4096 N(0,0.02) -> E4M3 with an
+                 fp32 scale per 128x128 block, group sizes as mxfp4_grouped
+                 (Multinomial(16384, Dirichlet(1)))
 
 Every tensor has its own PCG64 stream: SeedSequence(entropy=1000 + config
 number, spawn_key=(tensor id,)), so a tensor's values do not depend on which
@@ -86,6 +93,10 @@ WORKLOADS = {
     "mxfp8_dense": Workload("mxfp8_dense", 6, "mxfp8", M=8192, N=4096, K=4096, w_sigma=0.02),
     "fp8_hybrid": Workload("fp8_hybrid", 7, "fp8t", M=4096, N=6144, K=1536, w_sigma=0.02),
     "mxfp4_forward": Workload("mxfp4_forward", 8, "mxfp4", M=8192, N=4096, K=4096, need_dx=False, need_dw=False),
+    "nvfp4_forward": Workload("nvfp4_forward", 9, "nvfp4", M=8192, N=4096, K=4096, outliers=True,
+                              need_dx=False, need_dw=False),
+    "fp8_grouped_forward": Workload("fp8_grouped_forward", 10, "fp8_b128", M=16384, N=2048, K=4096, groups=8,
+                                    w_sigma=0.02, need_dx=False, need_dw=False, routing="dirichlet"),
 }
 
 AMAX_RING = 16               # amax history length of the delayed-scaling recipe
