@@ -6,7 +6,7 @@ A step is one pass of the workload's whole backward path over one batch of
 synthetic input already resident in HBM:
   mxfp8_deferred  lp_mx_quant(grad, -1) + lp_grouped_dx_deferred: grouped dX over 64 experts
                   against the bf16 weight quantized to MXFP8 along its reduction axis, inside
-                  the product for experts of at most 256 tokens (default: the largest
+                  the product for experts of at most 512 tokens (default: the largest
                   workload, 962 GFLOP per step; --unfused: lp_mx_quant(W, -2) then
                   lp_grouped_bwd)
   fp8_frozen      lp_dequant of a frozen FP8 128x128-block weight to bf16, then
@@ -18,6 +18,10 @@ synthetic input already resident in HBM:
                   + lp_linear_bwd dX, dW against E4M3 X and W (per-tensor scales)
   mxfp4_forward   lp_linear_fwd: y = X @ W^T, MXFP4 X 8192x4096 and W 4096x4096 (the forward
                   the FP4 backward pairs with, on the block-scaled FP4 MFMA)
+  nvfp4_forward   lp_linear_fwd: y = X @ W^T, NVFP4 X 8192x4096 and W 4096x4096, decoded to bf16
+                  inside the contraction
+  fp8_grouped_forward  lp_grouped_fwd: bf16 X 16384x4096 against 8 block-FP8 experts
+                  8x2048x4096 (the FP8-adapter page's grouped forward)
   mxfp4_tiny      lp_linear_bwd: dX and dW, 64 x 128 x 128
 Input sets are rotated through about 1 GB so that the 256 MiB Infinity Cache
 cannot serve a repeated step.  Prints one JSON line (rank 0).
@@ -63,6 +67,12 @@ PEAK_FP4_TFLOPS = 10100.0      # MI355X dense fp4 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 ROTATE_BYTES = 1 << 30
 UNFUSED = False                # mxfp8_deferred: the three-call step instead of lp_grouped_dx_deferred
+# mxfp8_deferred: experts of at most this many tokens (two 256-row tiles)
+# quantize their weight inside the product.  Interleaved steady-state sweep
+# of the whole call: 0 (every weight quantized first) 1046 us, 256 897-901,
+# 384 878, 512 873-879, 640 884, 768 904, 1024 898, 2048 908, every expert
+# 896.
+FUSE_ROWS = 512
 
 
 # ------------------------------------------------------------------ input preparation (torch, GPU)
@@ -223,10 +233,13 @@ def build(lp, name: str):
                 return [t0, t1, ev.stop(stream)]
         else:
             # One call: the weight is quantized inside the product for experts
-            # of at most 256 tokens, first (into wq) for the others.
+            # of at most FUSE_ROWS tokens, first (into wq) for the others.
+            # Algorithmic bytes: the bf16 weight, the gradient's codes and
+            # scales, the bf16 result.
             phases.append(Phase("grouped_dx_deferred (W quant + dX)",
                                 "mx_quant_rows_groups + fp8_mfma_persistent + fp8_mfma_wquant_kernel",
-                                flops=2.0 * M * N * K, peak=PEAK_FP8_TFLOPS))
+                                flops=2.0 * M * N * K, peak=PEAK_FP8_TFLOPS,
+                                nbytes=w.groups * N * K * 2 + M * N * (1 + 1 / 32) + M * K * 2))
 
             def step(i, stream):
                 g, wt, gq, wq, dx = sets[0]
@@ -234,7 +247,7 @@ def build(lp, name: str):
                 lp.lp_mx_quant(g, -1, "mxfp8", codes=gq.codes, scales=gq.scales, stream=stream)
                 t0 = ev.stop(stream)
                 ev = _events(stream)
-                lp.lp_grouped_dx_deferred(gq, wt, offsets, fuse_rows=256, grad_x=dx, w_codes=wq.codes,
+                lp.lp_grouped_dx_deferred(gq, wt, offsets, fuse_rows=FUSE_ROWS, grad_x=dx, w_codes=wq.codes,
                                           w_scales=wq.scales, stream=stream)
                 return [t0, ev.stop(stream)]
         standalone = []
@@ -324,6 +337,40 @@ def build(lp, name: str):
             xq, wq, y = sets[i % len(sets)]
             ev = _events(stream)
             lp.lp_linear_fwd(xq, wq, y=y, stream=stream)
+            return [ev.stop(stream)]
+        standalone = []
+    elif name == "nvfp4_forward":
+        per_set = (M * K + N * K) * (0.5 + 1 / 16) + M * N * 2
+        nsets = max(1, min(16, math.ceil(ROTATE_BYTES / per_set)))
+        for i in range(nsets):
+            c, s, ts = nvfp4_quant_torch(_randn((M, K), w.x_sigma, 8300 + i))
+            xq = lp.QTensor("nvfp4", c, s, ts, shape=(1, M, K))
+            c, s, ts = nvfp4_quant_torch(_randn((N, K), w.w_sigma, 8400 + i))
+            wq = lp.QTensor("nvfp4", c, s, ts, shape=(1, N, K))
+            sets.append((xq, wq, torch.empty((M, N), dtype=torch.bfloat16, device="cuda")))
+        phases.append(Phase("linear_fwd", "gemm_kernel", flops=2.0 * M * N * K))
+
+        def step(i, stream):
+            xq, wq, y = sets[i % len(sets)]
+            ev = _events(stream)
+            lp.lp_linear_fwd(xq, wq, y=y, stream=stream)
+            return [ev.stop(stream)]
+        standalone = []
+    elif name == "fp8_grouped_forward":
+        offsets = torch.from_numpy(W.cumulative_ends(W.group_sizes(w))).cuda()
+        per_set = M * K * 2 + w.groups * N * K + M * N * 2
+        nsets = max(1, min(8, math.ceil(ROTATE_BYTES / per_set)))
+        for i in range(nsets):
+            x = W.torch_normal_bf16((M, K), w.x_sigma, 8500 + i, "cuda")
+            c, s = fp8_b128_quant_torch(_randn((w.groups, N, K), w.w_sigma, 8600 + i))
+            sets.append((lp.QTensor("bf16", x, shape=(1, M, K)), lp.QTensor("fp8_b128", c, s, shape=(w.groups, N, K)),
+                         torch.empty((M, N), dtype=torch.bfloat16, device="cuda")))
+        phases.append(Phase("grouped_fwd", "gemm_kernel", flops=2.0 * M * N * K))
+
+        def step(i, stream):
+            xq, wq, y = sets[i % len(sets)]
+            ev = _events(stream)
+            lp.lp_grouped_fwd(xq, wq, offsets, y=y, stream=stream)
             return [ev.stop(stream)]
         standalone = []
     else:
@@ -549,6 +596,38 @@ def _oracle_parts(name: str):
                   _Part("dequant X", dec_x, M / rows, False, f"{rows} of {M} input rows"),
                   _Part("forward (fp64 product)", fwd, M / rows, True, f"{rows} token rows")]
         return parts, 2.0 * M * N * K
+    if name == "nvfp4_forward":
+        xq = F.quant_nvfp4(W.with_outliers(W.normal_f32(w.number, "x", (rows, K), w.x_sigma), w.number, "x")[None])
+        wq = F.quant_nvfp4(W.with_outliers(W.normal_f32(w.number, "w", (N, K), w.w_sigma), w.number, "w")[None])
+        st = {}
+
+        def dec_w():
+            st["w"] = F.dequant("nvfp4", *wq)[0]
+
+        def dec_x():
+            st["x"] = F.dequant("nvfp4", *xq)[0]
+
+        def fwd():
+            O.linear_fwd(st["x"], st["w"])
+        parts += [_Part("dequant W", dec_w, 1, False, "whole weight"),
+                  _Part("dequant X", dec_x, M / rows, False, f"{rows} of {M} input rows"),
+                  _Part("forward (fp64 product)", fwd, M / rows, True, f"{rows} token rows")]
+        return parts, 2.0 * M * N * K
+    if name == "fp8_grouped_forward":
+        xb = W.bf16_bits(W.normal_f32(w.number, "x", (rows, K), w.x_sigma))
+        wc, ws = F.quant_fp8_b128(W.normal_f32(w.number, "w", (1, N, K), w.w_sigma))
+        st = {}
+
+        def dec_w():
+            st["w"] = F.dequant("fp8_b128", wc, ws)[0]
+
+        def fwd():
+            O.linear_fwd(xb, st["w"])
+        # Every token row meets exactly one expert's weight: the cost per row
+        # is that of one dense row, whatever the group sizes.
+        parts += [_Part("dequant W", dec_w, w.groups, False, f"one of {w.groups} expert weights"),
+                  _Part("grouped forward (fp64 product)", fwd, M / rows, True, f"{rows} token rows, one expert")]
+        return parts, 2.0 * M * N * K
     # Saved packed operands (fp8_frozen, nvfp4_linear, mxfp4_grouped, mxfp4_tiny):
     # decode, then the fp64 products over sampled token rows.
     X, Wt, G = W.dense_inputs(w, M=rows)
@@ -660,7 +739,10 @@ def main():
     flops = sum(p.flops for p in phases)
     value = flops / (ms_step * 1e-3) / 1e12
     dom_ms = float(np.mean(dom.ms))
-    if dom.flops:
+    # The binding roof is the one that allows the longer time: MFMA
+    # (flops / peak) or HBM (algorithmic bytes / 8 TB/s).
+    hbm_bound = dom.nbytes and (not dom.flops or dom.nbytes / PEAK_HBM_GBS / 1e9 > dom.flops / dom.peak / 1e12)
+    if not hbm_bound:
         achieved = dom.flops / (dom_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": dom.peak, "unit": "TFLOP/s",
                 "frac": round(achieved / dom.peak, 4)}
@@ -695,7 +777,7 @@ def main():
         "dtype": "fp4" if w.name == "mxfp4_forward" else ("fp8" if w.fmt in ("mxfp8", "fp8t") else "bf16"),
         "config": {"workload": w.name, "format": w.fmt, "M": w.M, "N": w.N, "K": w.K, "groups": w.groups,
                    "grad_x": w.need_dx, "grad_w": w.need_dw, "global_batch": w.M, "parallelism": "none (1 GPU)",
-                   **({"weight_quant": "three calls" if UNFUSED else "inside the product for experts <= 256 tokens"}
+                   **({"weight_quant": "three calls" if UNFUSED else f"inside the product for experts <= {FUSE_ROWS} tokens"}
                       if w.name == "mxfp8_deferred" else {})},
         "roofline": roof, "phases": phase_rec, "standalone_hbm": hbm,
     }
