@@ -217,7 +217,7 @@ def build(lp, name: str):
         if UNFUSED:
             phases.append(Phase("mx_quant W", "mx_quant_tile", nbytes=w.groups * N * K * (2 + 1 + 1 / 32)))
             # MXFP8 x MXFP8 with both scales along the contraction: block-scaled FP8 MFMA
-            phases.append(Phase("grouped_bwd dX", "fp8_mfma_persistent", flops=2.0 * M * N * K,
+            phases.append(Phase("grouped_bwd dX", "fp8_mfma_paired", flops=2.0 * M * N * K,
                                 peak=PEAK_FP8_TFLOPS))
 
             def step(i, stream):
@@ -237,7 +237,7 @@ def build(lp, name: str):
             # Algorithmic bytes: the bf16 weight, the gradient's codes and
             # scales, the bf16 result.
             phases.append(Phase("grouped_dx_deferred (W quant + dX)",
-                                "mx_quant_rows_groups + fp8_mfma_persistent + fp8_mfma_wquant_kernel",
+                                "mx_quant_rows_groups + fp8_mfma_paired + fp8_mfma_wquant_kernel",
                                 flops=2.0 * M * N * K, peak=PEAK_FP8_TFLOPS,
                                 nbytes=w.groups * N * K * 2 + M * N * (1 + 1 / 32) + M * K * 2))
 
@@ -263,7 +263,7 @@ def build(lp, name: str):
         phases.append(Phase("mx_quant_dual grad", "mx_quant_tile<dual>", nbytes=M * N * (2 + 2 * (1 + 1 / 32))))
         phases.append(Phase("mx_quant W", "mx_quant_tile", nbytes=N * K * (2 + 1 + 1 / 32)))
         phases.append(Phase("mx_quant X", "mx_quant_tile", nbytes=M * K * (2 + 1 + 1 / 32)))
-        phases.append(Phase("linear_bwd dX", "fp8_mfma_persistent", flops=2.0 * M * N * K, peak=PEAK_FP8_TFLOPS))
+        phases.append(Phase("linear_bwd dX", "fp8_mfma_paired", flops=2.0 * M * N * K, peak=PEAK_FP8_TFLOPS))
         phases.append(Phase("linear_bwd dW", "fp8_mfma_kernel", flops=2.0 * M * N * K, peak=PEAK_FP8_TFLOPS))
 
         def step(i, stream):

@@ -242,11 +242,10 @@ hipError_t launch_fwd(const lp_qtensor& x, const lp_qtensor& w, const int32_t* o
   prm.groups = groups;
   prm.splits = 1;
   // MX operands run on the block-scaled MFMA (256 x 256 tiles); the others
-  // through bf16 tiles: 256 x 256 when both are decoded (NVFP4), else
-  // 256 x 128 (three stages of a bf16 x tile and of the weight tile fit in
-  // LDS only at that width).
+  // through bf16 tiles, 256 x 256 unless both are bf16 (256 x 128: three
+  // stages of both tiles fit in LDS only at that width).
   const bool mx = x.fmt == LP_MXFP4 || x.fmt == LP_MXFP8;
-  const int BP = 256, BQ = (mx || x.fmt == LP_NVFP4) ? 256 : 128;
+  const int BP = 256, BQ = w.fmt == LP_BF16 ? 128 : 256;
   prm.nq = (int32_t)((prm.Qtot + BQ - 1) / BQ);
   if (offsets == nullptr)
     prm.gm = tile_group(BP * code_bytes2(x.fmt), BQ * code_bytes2(w.fmt), (prm.Ptot + BP - 1) / BP);

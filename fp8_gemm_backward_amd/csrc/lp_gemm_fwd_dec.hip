@@ -17,7 +17,7 @@ namespace gk {
 
 hipError_t fwd_dec(const Params& prm, int fmt_x, int fmt_w, hipStream_t s) {
   if (fmt_x == LP_BF16 && fmt_w == LP_BF16) return run<Narrow, BF16, -1, BF16, -1, false, true>(prm, s);
-  if (fmt_x == LP_BF16 && fmt_w == LP_FP8_B128) return run<Narrow, BF16, -1, FP8_B128, -1, false, true>(prm, s);
+  if (fmt_x == LP_BF16 && fmt_w == LP_FP8_B128) return run<Big, BF16, -1, FP8_B128, -1, false, true>(prm, s);
   if (fmt_x == LP_NVFP4 && fmt_w == LP_NVFP4) return run<Big, NVFP4, -1, NVFP4, -1, false, true>(prm, s);
   return hipErrorInvalidValue;
 }

@@ -252,7 +252,9 @@ struct DecState {
 // kKMajor: the tile is BMN rows (mn) x BK columns (the contraction runs
 // along the tensor's columns); otherwise BK rows x BMN columns.  Per-thread
 // chunk positions are fixed for the whole k loop; only the window moves.
-template <int F, int A, bool kKMajor, int BMN>
+// kSwz (k-major only): unpadded rows with the chunk swizzle of direct
+// k-major tiles, read like them; otherwise rows padded by 16 bytes.
+template <int F, int A, bool kKMajor, int BMN, bool kSwz = false>
 struct Decoded {
   static constexpr bool kDirect = false;
   static constexpr int EPC = elems_per_chunk<F>();
@@ -261,7 +263,8 @@ struct Decoded {
   static constexpr int PER = CHUNKS / NT;                            // chunks per thread
   static_assert(CHUNKS % NT == 0, "tile not evenly divided among threads");
   static constexpr int PIECES = EPC / 8;                             // 16-byte LDS writes per chunk
-  static constexpr int PITCH = kKMajor ? BK + 8 : BMN;               // LDS row pitch, bf16 elements
+  static_assert(!kSwz || kKMajor, "the swizzle is for k-major tiles");
+  static constexpr int PITCH = kKMajor ? (kSwz ? BK : BK + 8) : BMN;  // LDS row pitch, bf16 elements
   static constexpr int BUF_BYTES = (kKMajor ? BMN : BK) * PITCH * 2;
   static constexpr int BPE2 = F == BF16 ? 4 : ((F == MXFP4 || F == NVFP4) ? 1 : 2);  // 2 x bytes per element
   static constexpr bool kScale = F != BF16;
@@ -301,7 +304,7 @@ struct Decoded {
 #pragma unroll
       for (int j = 0; j < PIECES; ++j) {
         const int q = col / 8 + j;                                   // logical 16-byte chunk
-        lds[i][j] = 2 * r * PITCH + 16 * (kKMajor ? q : (q ^ swz_mn(r)));
+        lds[i][j] = 2 * r * PITCH + 16 * (kKMajor ? (kSwz ? q ^ swz_k(r) : q) : (q ^ swz_mn(r)));
       }
       if constexpr (kKMajor) {
         mnc[i] = col;
@@ -864,7 +867,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   // Q straight into LDS too when both operands are bf16 and three Q stages fit.
   constexpr bool QD = PD && QF == BF16 && 3 * Direct<PK, C::BP>::BUF_BYTES + 3 * Direct<QK, C::BQ>::BUF_BYTES <= kMaxLds;
   using LP = std::conditional_t<PD, Direct<PK, C::BP>, Decoded<PF, PA, PK, C::BP>>;
-  using LQ = std::conditional_t<QD, Direct<QK, C::BQ>, Decoded<QF, QA, QK, C::BQ>>;
+  // A decoded k-major Q tile drops its row padding when two padded buffers
+  // would not fit beside P's.
+  constexpr bool QSWZ = QK && !QD && (PD ? 3 : 2) * LP::BUF_BYTES + 2 * C::BQ * (BK + 8) * 2 > kMaxLds;
+  using LQ = std::conditional_t<QD, Direct<QK, C::BQ>, Decoded<QF, QA, QK, C::BQ, QSWZ>>;
   constexpr int PERIOD = PD ? 3 : 2;                             // slabs per iteration = register stages
   constexpr int PBUF = LP::BUF_BYTES, QBUF = LQ::BUF_BYTES;
   constexpr int SB = C::WP * C::WQ * 2;                          // epilogue staging bytes per wave
@@ -887,7 +893,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   constexpr int DS0 = C::FP * C::FQ / 2;                         // first decode slot
   constexpr int FP = C::FP, FQ = C::FQ, NM = FP * FQ;
   using FAP = FragAddr<PK, PD, C::BP, FP>;
-  using FAQ = FragAddr<QK, QD && QK, C::BQ, FQ>;
+  using FAQ = FragAddr<QK, QK && (QD || QSWZ), C::BQ, FQ>;
   constexpr int NRP = FAP::NREAD, NRQ = FAQ::NREAD, NR = FP * NRP + NRQ * FQ;
   // The barrier of slab k needs this wave's direct loads of slab k+1 (issued
   // in slab k-1, ahead of its register loads); vmcnt lets the loads issued
@@ -1130,8 +1136,8 @@ hipError_t dw_pt(const Params& prm, int fmt_p, int fmt_q, hipStream_t s);
 // both MXFP8.
 hipError_t fwd_mx(const Params& prm, bool fp4, hipStream_t s);
 // Forward y = x @ w^T through bf16 tiles (fused decode): bf16 x with a bf16
-// or block-FP8 weight (256 x 128 tiles), NVFP4 x with an NVFP4 weight
-// (256 x 256 tiles).
+// weight (256 x 128 tiles) or a block-FP8 weight, NVFP4 x with an NVFP4
+// weight (256 x 256 tiles).
 hipError_t fwd_dec(const Params& prm, int fmt_x, int fmt_w, hipStream_t s);
 // Both of them in one launch (X and W in the same format fmt_q).
 hipError_t pt_pair(const Params& dx, const Params& dw, int fmt_p, int fmt_q, hipStream_t s);

@@ -25,7 +25,7 @@ hipError_t dx_mx(const Params& prm, hipStream_t s) {
   // compute unit (a multiple of the 8 XCDs) walks them.
   const int cus = compute_units() / 8 * 8;
   if (prm.P.scale_ld % 16 == 0 && prm.ntiles > cus && cus >= 8)
-    fp8_mfma_persistent<><<<dim3(cus), dim3(NT), 0, s>>>(prm);
+    fp8_mfma_paired<><<<dim3(cus), dim3(NT), 0, s>>>(prm);
   else if (prm.P.scale_ld % 16 == 0)
     fp8_mfma_kernel<false, kChunkMode><<<dim3(prm.ntiles), dim3(NT), 0, s>>>(prm);
   else

@@ -107,20 +107,13 @@ constexpr int chunk_bytes() { return kMode == kChunkMode ? kChunkBytes : 16; }
   __shared__ __attribute__((aligned(1024))) uint8_t sc0[chunk_bytes<kMode>()];             \
   __shared__ __attribute__((aligned(1024))) uint8_t sc1[chunk_bytes<kMode>()]
 
-// Persistent grad_X (kPersist): a workgroup runs several tiles in turn, and
-// the loads of a tile's prologue (its first scale chunk and first three
-// slabs) are issued before the previous tile's results are written, so that
-// their latency hides behind that epilogue.  The epilogue then stages
-// through stage 3 only (the prologue fills stages 0..2 and chunk buffer 0)
-// and writes with buffer stores whose masked elements take an out-of-range
-// offset: every wave issues exactly kEpiStores store instructions per tile
-// (and as many stores that write nothing after a prologue it issues
-// itself), so that the barriers of a tile's prologue and first two slabs,
-// which wait for loads issued before those stores (vector memory
-// operations complete in issue order), can count them.
+// Persistent grad_X (mx_tile_pair): the epilogue writes with buffer stores
+// whose masked elements take an out-of-range offset, so that every wave
+// issues exactly kEpiStores store instructions per tile and the next tile's
+// first barrier, which waits for loads issued before those stores (vector
+// memory operations complete in issue order), can count them.
 constexpr int kEpiStores = XWP * XWQ * 2 / (64 * 16);     // 16-byte stores per wave and tile
 constexpr int kEpiRows = 32;                              // rows per epilogue pass
-static_assert(XWQ * 2 * kEpiRows * 4 <= kTileBytes, "four waves' epilogue passes fit one stage");
 
 // What a persistent workgroup carries from one tile to the next.
 struct Persist {
@@ -133,15 +126,13 @@ struct Persist {
 // One output tile.  hw: the workgroup's index among p.ntiles (see
 // select_tile); indices at or past p.ntiles have no tile.  kFP, kFQ: MFMA
 // format codes of the gradient and the other operand (0 E4M3, 1 E5M2); the
-// MX modes take E4M3 only.  kPersist (grad_X, chunk mode): hw is the
-// logical tile index, `pst` the workgroup's state.  Returns kNoTile when hw
-// names no tile, else kDone, or kDoneNextIssued when the next tile's
-// prologue has been issued.
+// MX modes take E4M3 only.  Returns kNoTile when hw names no tile, else
+// kDone (mx_tile_pair: kDoneNextIssued when the next tile's prologue has
+// been issued).
 enum : int { kNoTile = 0, kDone = 1, kDoneNextIssued = 2 };
-template <bool kDW, int kMode, int kFP = 0, int kFQ = 0, bool kPersist = false>
+template <bool kDW, int kMode, int kFP = 0, int kFQ = 0>
 __device__ __forceinline__ int mx_tile(const Params& p, int hw, uint8_t* st0, uint8_t* st1, uint8_t* st2,
-                                        uint8_t* st3, uint8_t* sc0, uint8_t* sc1, Persist* pst = nullptr) {
-  static_assert(!kPersist || (!kDW && kMode == kChunkMode), "persistent tiles: grad_X in chunk mode");
+                                        uint8_t* st3, uint8_t* sc0, uint8_t* sc1) {
   constexpr bool kChunk = kMode == kChunkMode, kGather = kMode == kGatherMode;
   static_assert(!kDW || !kGather, "dW scale rows (N or K bytes, multiples of 16) always load in chunks");
   static_assert(kMode == kTensorMode || (kFP == 0 && kFQ == 0), "MX operands are E4M3");
@@ -152,18 +143,12 @@ __device__ __forceinline__ int mx_tile(const Params& p, int hw, uint8_t* st0, ui
   static_assert(kMaxGroups * 4 <= kStage, "group ends alias stage 0");
   static_assert(XWP * XWQ * 2 <= kStage, "epilogue staging fits a stage");
 
-  // Persistent tiles: the thread index goes through an empty asm statement
-  // so that the per-lane offsets are formed per tile instead of being held
-  // (and spilled) across the whole walk; a spill reload here would make the
-  // wave wait for the loads the previous tile left in flight.
-  int tid = threadIdx.x;
-  if constexpr (kPersist) asm volatile("" : "+v"(tid));
+  const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wp = wave >> 1, wq = wave & 1;
   if (hw >= p.ntiles) return kNoTile;
-  const Tile t = kPersist ? select_tile<XCfg, kDW>(p, pst->ends, hw, true, &pst->hint)
-                          : select_tile<XCfg, kDW>(p, reinterpret_cast<int32_t*>(st0), hw);
+  const Tile t = select_tile<XCfg, kDW>(p, reinterpret_cast<int32_t*>(st0), hw);
   if (!t.valid) return kNoTile;
   __syncthreads();                                               // group ends read; stage 0 reusable
 
@@ -385,27 +370,15 @@ __device__ __forceinline__ int mx_tile(const Params& p, int hw, uint8_t* st0, ui
   constexpr int NM = XFP * XFQ;
 
   const int nk = (kend - kbeg + XBK - 1) / XBK;
-  // Persistent tiles: kEpiStores stores that write nothing (inline
-  // assembly: the compiler would merge identical stores into one).
-  auto no_stores = [&]() {
-    const Rsrc none = make_rsrc(p.C, 0);
-    const int32_t oob = kOOB;
-#pragma unroll
-    for (int i = 0; i < kEpiStores; ++i)
-      asm volatile("buffer_store_dword %0, %1, %2, 0 offen" ::"v"(0), "v"(oob), "s"(none) : "memory");
-  };
   if (nk > 0) {
     // Prologue: (chunk 0,) slabs 0, 1, 2 in flight; slab 0 landed and
     // published; its fragments read.
-    if (!kPersist || !pst->issued) {
-      if constexpr (kChunk) issue_chunk(chunkbuf(IC<0>{}), kbeg);
-      static_for<3>([&](auto si) {
-        constexpr int s = decltype(si)::value;
-        static_for<T>([&](auto u) { issue(u, stage(si), kbeg + s * XBK); });
-      });
-      if constexpr (kPersist) no_stores();
-    }
-    barrier_vm<2 * T + (kPersist ? kEpiStores : 0)>();
+    if constexpr (kChunk) issue_chunk(chunkbuf(IC<0>{}), kbeg);
+    static_for<3>([&](auto si) {
+      constexpr int s = decltype(si)::value;
+      static_for<T>([&](auto u) { issue(u, stage(si), kbeg + s * XBK); });
+    });
+    barrier_vm<2 * T>();
     static_for<NREAD>([&](auto r) { read(r, IC<0>{}, IC<0>{}, stage(IC<0>{}), chunkbuf(IC<0>{}), kbeg); });
   }
 
@@ -417,14 +390,8 @@ __device__ __forceinline__ int mx_tile(const Params& p, int hw, uint8_t* st0, ui
     constexpr int CUR = J & 1, NXT = CUR ^ 1;
     constexpr int S8 = J % kChunkSlabs, S8N = (J + 1) % kChunkSlabs;
     // Loads issued after slab k+1's tiles: slab k+2's, plus a scale chunk
-    // issued at chunk position 4 of slab k-1 (persistent tiles: plus the
-    // previous epilogue's stores, issued after slabs 1 and 2).
-    if constexpr (kPersist && J < 2) {
-      if (k < 2) barrier_vm<T + kEpiStores>();
-      else barrier_vm<T>();
-    } else {
-      barrier_vm<T + ((kChunk && S8 == 5) ? S : 0)>();
-    }
+    // issued at chunk position 4 of slab k-1.
+    barrier_vm<T + ((kChunk && S8 == 5) ? S : 0)>();
     uint8_t* const nxt = stage(IC<J + 1>{});
     uint8_t* const dst = stage(IC<J + 3>{});
     const uint8_t* const cnxt = chunkbuf(IC<(J + 1) / kChunkSlabs>{});
@@ -452,84 +419,7 @@ __device__ __forceinline__ int mx_tile(const Params& p, int hw, uint8_t* st0, ui
   }
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   __syncthreads();
-  if constexpr (kPersist) {
-    // The next tile's prologue, then this tile's results.
-    bool issued = false;
-    if (pst->next < p.ntiles) {
-      const Tile tn = select_tile<XCfg, kDW>(p, pst->ends, pst->next, true, &pst->hint);
-      if (tn.valid && tn.kend > tn.kbeg) {
-        const uint8_t* const npc = p.P.codes + (int64_t)tn.p0 * ldp;
-        const int npend = kDW ? M : tn.pend;
-        const int64_t nprow = (int64_t)(npend - tn.p0) * ldp;
-        const uint8_t* const nqc = p.Q.codes + (int64_t)tn.g * p.Q.code_batch;
-        const Rsrc nps_r = make_rsrc(p.P.scales + (int64_t)tn.p0 * sldp, (int64_t)(npend - tn.p0) * sldp);
-        const Rsrc nqs_r = make_rsrc(p.Q.scales + (int64_t)tn.g * p.Q.scale_batch, p.Q.scale_bytes);
-        const int32_t nq_base = (16 * wave + lane / 16) * ldq + tn.q0;
-        dma<16>(nps_r, (lds_void*)(sc0 + 1024 * wave), (64 * wave + lane) * sldp, 0);
-        dma<16>(nqs_r, (lds_void*)(sc0 + XBP * 16 + 1024 * wave), (4 * wave + lane / 16) * sldq + tn.q0 + 16 * (lane & 15), 0);
-        static_for<3>([&](auto si) {
-          constexpr int sl = decltype(si)::value;
-          const int k0 = sl * XBK;
-          uint8_t* const sb = stage(si);
-          static_for<4>([&](auto ui) {
-            constexpr int u = decltype(ui)::value;
-            const Rsrc r = make_rsrc(npc + k0, nprow - k0);
-            dma<16>(r, (lds_void*)(sb + 1024 * (4 * wave + u)), k0 + p_col >= tn.kend ? kOOB : p_off, 16 * u * ldp);
-          });
-          static_for<4>([&](auto vi) {
-            constexpr int v = decltype(vi)::value;
-            const Rsrc r = make_rsrc(nqc + (int64_t)k0 * ldq, (int64_t)(tn.kend - k0) * ldq);
-            dma<16>(r, (lds_void*)(sb + kPBytes + 1024 * (4 * wave + v)), nq_base + 16 * ((v & 1) ? (qc0 ^ 8) : qc0),
-                    4 * v * ldq);
-          });
-        });
-        issued = true;
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // Results through stage 3: four passes of 32 rows per wave, 8 KiB each.
-    // The lane index goes through an empty asm statement so that the
-    // staging addresses are formed here, not held from the kernel's start;
-    // scheduling fences keep the passes apart (converting every result at
-    // once would hold all of them in registers).
-    constexpr int ROWB = XWQ * 2;
-    int el = lane;
-    asm volatile("" : "+v"(el));
-    uint8_t* const stg = st3 + wave * (ROWB * kEpiRows);
-    const int row0 = t.p0 + wp * XWP, col0 = t.q0 + wq * XWQ;
-    const Rsrc orsrc = make_rsrc(p.C + (int64_t)row0 * p.ldc + col0, ((int64_t)(M - row0) * p.ldc - col0) * 2);
-    const int c16 = el & 15;
-    const bool col_ok = col0 + 8 * c16 < p.Qtot;
-#pragma unroll
-    for (int i = 0; i < XFP; ++i) {
-      __builtin_amdgcn_sched_barrier(0);
-      const int r = el & 31;
-#pragma unroll
-      for (int j = 0; j < XFQ; ++j) {
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int sl = (j * 32 + 8 * r4 + 4 * (el >> 5)) / 4;
-          const u32x2 v = {pack_bf16x2(acc[i][j][4 * r4], acc[i][j][4 * r4 + 1]),
-                           pack_bf16x2(acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3])};
-          *reinterpret_cast<u32x2*>(stg + r * ROWB + 8 * (sl ^ (r & 15))) = v;
-        }
-      }
-      __builtin_amdgcn_s_waitcnt(0xC07F);                        // lgkmcnt(0): the pass is staged
-#pragma unroll
-      for (int it = 0; it < kEpiRows / 4; ++it) {
-        const int rr = it * 4 + el / 16;
-        const uint8_t* src = stg + rr * ROWB;
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(src + 8 * ((2 * c16) ^ (rr & 15)));
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(src + 8 * ((2 * c16 + 1) ^ (rr & 15)));
-        const int32_t off = (row0 + i * kEpiRows + rr < t.pend && col_ok)
-                                ? ((i * kEpiRows + rr) * p.ldc + 8 * c16) * 2 : kOOB;
-        __builtin_amdgcn_raw_buffer_store_b128(u32x4{lo[0], lo[1], hi[0], hi[1]}, orsrc, off, 0, 0);
-      }
-      __builtin_amdgcn_s_waitcnt(0xC07F);                        // read back before the next pass overwrites
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    return issued ? kDoneNextIssued : kDone;
-  } else {
+  {
     uint8_t* stg = wave == 0 ? st0 : wave == 1 ? st1 : wave == 2 ? st2 : st3;
     if constexpr (kMode == kTensorMode)
       store_acc<XCfg, kDW, true>(p, t, acc, wp, wq, lane, stg, *p.P.tensor_scale * *p.Q.tensor_scale);
@@ -545,6 +435,310 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   mx_tile<kDW, kMode, kFP, kFQ>(p, blockIdx.x, st0, st1, st2, st3, sc0, sc1);
 }
 
+// ---------------------------------------------------------------- paired stages
+// Persistent grad_X (MXFP8, chunk mode) with 128-deep stages.  A stage holds
+// two 64-deep halves: the gradient tile [256 m][128 B] and the weight tile
+// [128 n][256 B], 64 KiB together, in two LDS buffers.  Against the four
+// 64-deep stages of mx_tile this halves the barriers (one per stage) and
+// makes each gradient row's load one whole 128-byte line instead of two
+// halves of one in consecutive slabs.
+//
+// Schedule, in 64-deep halves h (stage j = h / 2 in buffer j % 2):
+// * the fragments of half h + 1 are read during the MFMAs of half h;
+// * at the start of every odd half 2j+1 one barrier (vmcnt(0)) publishes
+//   stage j+1, whose loads were issued at the start of half 2j-1; every wave
+//   then has its half-2j+1 fragments in registers, so buffer j % 2 is free
+//   and stage j+2's loads go into it, spread over the half's MFMAs;
+// * a scale chunk (8 halves) is issued at chunk position 3 and lands by the
+//   barrier of position 7, before position 8 reads it.
+// The load lead is thus two halves, as with mx_tile's three slabs ahead of
+// four stages.  A persistent workgroup issues the next tile's first scale
+// chunk and stage 0 before storing the current tile's results, which it
+// stages through buffer 1; stage 1 follows at the next tile's start.
+constexpr int YBK = 2 * XBK;                    // contraction per stage
+constexpr int kYPBytes = XBP * YBK;             // gradient codes per stage
+constexpr int kYStage = kYPBytes + YBK * XBQ;   // plus weight codes
+constexpr int TY = 16;                          // direct loads per wave and stage
+static_assert(XWQ * 2 * kEpiRows * 4 <= kYStage, "four waves' epilogue passes fit one stage");
+
+// Gradient tile [m][128 B]: chunk c of row m at c ^ ((m >> 1) & 7); the 16
+// rows a fragment read serves together hit 16 distinct slots mod 256 B.
+__device__ __forceinline__ int y_swz(int m) { return (m >> 1) & 7; }
+
+template <int kFP, int kFQ>
+__device__ __forceinline__ int mx_tile_pair(const Params& p, int hw, uint8_t* s0, uint8_t* s1, uint8_t* sc0,
+                                             uint8_t* sc1, Persist* pst) {
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wp = wave >> 1, wq = wave & 1;
+  if (hw >= p.ntiles) return kNoTile;
+  const Tile t = select_tile<XCfg, false>(p, pst->ends, hw, true, &pst->hint);
+  if (!t.valid) return kNoTile;
+  __syncthreads();                                               // the previous epilogue's staging read
+
+  const int ldp = p.P.code_ld, sldp = p.P.scale_ld;
+  const int ldq = p.Q.code_ld, sldq = p.Q.scale_ld;
+  const int M = p.Ptot;
+  const int kbeg = t.kbeg, kend = t.kend;
+  const uint8_t* pc = p.P.codes + (int64_t)t.p0 * ldp;
+  const int64_t prow_bytes = (int64_t)(t.pend - t.p0) * ldp;
+  const Rsrc ps_r = make_rsrc(p.P.scales + (int64_t)t.p0 * sldp, (int64_t)(t.pend - t.p0) * sldp);
+  const uint8_t* qc = p.Q.codes + (int64_t)t.g * p.Q.code_batch;
+  const Rsrc qs_r = make_rsrc(p.Q.scales + (int64_t)t.g * p.Q.scale_batch, p.Q.scale_bytes);
+
+  // Gradient codes: wave w fills blocks 8 w + u (u = 0..7) of 8 rows x
+  // 128 B; lane i takes row 64 w + 8 u + i / 8, physical chunk i % 8, whose
+  // logical chunk (i % 8) ^ y_swz(row) = (i % 8) ^ (4 (u & 1) + i / 16)
+  // depends on u's parity only.
+  const int pl_even = (lane & 7) ^ (lane >> 4), pl_odd = (lane & 7) ^ (4 + (lane >> 4));
+  const int32_t p_row = (64 * wave + lane / 8) * ldp;            // + 8 u ldp
+  const int32_t p_off_even = p_row + 16 * pl_even, p_off_odd = p_row + 16 * pl_odd;
+  // Weight codes: blocks 8 w + v of 4 rows x 256 B; lane i takes row
+  // 32 w + 4 v + i / 16, logical chunk (i % 16) ^ q_swz(row) = c0 ^ 8 (v & 1).
+  const int qc0 = (lane & 15) ^ (2 * (lane >> 4));
+  const int32_t q_base = (32 * wave + lane / 16) * ldq + t.q0;  // + 4 v ldq
+  const int32_t q_off_even = q_base + 16 * qc0, q_off_odd = q_base + 16 * (qc0 ^ 8);
+
+  auto stagebuf = [&](auto bi) -> uint8_t* {
+    if constexpr (decltype(bi)::value % 2 == 0) return s0;
+    else return s1;
+  };
+  auto chunkbuf = [&](auto ci) -> uint8_t* {
+    if constexpr (decltype(ci)::value % 2 == 0) return sc0;
+    else return sc1;
+  };
+  // Direct load u of the stage starting at contraction k0 into buffer sb:
+  // gradient codes (0..7), weight codes (8..15).  A gradient row runs on
+  // into the next row, so a 16-byte chunk at or past the end of the
+  // contraction (N % 16 == 0) is read as zeros.
+  auto issue = [&](auto ui, uint8_t* sb, int k0) {
+    constexpr int u = decltype(ui)::value;
+    if constexpr (u < 8) {
+      const Rsrc r = make_rsrc(pc + k0, prow_bytes - k0);
+      const bool out = k0 + 16 * ((u & 1) ? pl_odd : pl_even) >= kend;
+      dma<16>(r, (lds_void*)(sb + 1024 * (8 * wave + u)), out ? kOOB : ((u & 1) ? p_off_odd : p_off_even),
+              8 * u * ldp);
+    } else {
+      constexpr int v = u - 8;
+      const Rsrc r = make_rsrc(qc + (int64_t)k0 * ldq, (int64_t)(kend - k0) * ldq);
+      dma<16>(r, (lds_void*)(sb + kYPBytes + 1024 * (8 * wave + v)), (v & 1) ? q_off_odd : q_off_even,
+              4 * v * ldq);
+    }
+  };
+  // Scale blocks [kb, kb + 16) of the tile (kb = k0 / 32): gradient row
+  // 64 w + i, 16 bytes; weight block row 4 w + i / 16, 16 bytes at column
+  // 16 (i % 16).
+  auto issue_chunk = [&](uint8_t* cb, int k0) {
+    const int kb = k0 >> 5;
+    dma<16>(ps_r, (lds_void*)(cb + 1024 * wave), (64 * wave + lane) * sldp, kb);
+    dma<16>(qs_r, (lds_void*)(cb + XBP * 16 + 1024 * wave), (4 * wave + lane / 16) * sldq + t.q0 + 16 * (lane & 15),
+            kb * sldq);
+  };
+
+  // Fragment addresses inside a stage.  Gradient fragment f of lane l: row
+  // m = wp 128 + 32 f + l % 32 (y_swz(m) = y_swz(l % 32)), read e of half s:
+  // logical chunk 4 s + 2 e + l / 32.  Weight fragment j, read tt, half s:
+  // rows n = 64 s + 32 (tt / 2) + 16 h + 8 (tt % 2) + i / 2, as in mx_tile.
+  const int r32 = lane & 31, hh = lane >> 5;
+  int32_t pa[2][2];
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) pa[s2][e] = (wp * XWP + r32) * YBK + 16 * ((4 * s2 + 2 * e + hh) ^ y_swz(r32));
+  int32_t qa[XFQ];
+  {
+    const int i16 = lane & 15, c16 = (lane >> 4) & 1;
+    const int n0 = 16 * hh + i16 / 2;
+    const int32_t a0 = kYPBytes + n0 * XBQ + 16 * ((wq * (XWQ / 16) + c16) ^ q_swz(n0)) + 8 * (i16 & 1);
+#pragma unroll
+    for (int j = 0; j < XFQ; ++j) qa[j] = a0 ^ (32 * j);
+  }
+  const int32_t psa = 16 * (wp * XWP + r32) + hh;
+  const int32_t qsa = XBP * 16 + hh * XBQ + wq * XWQ + r32;
+
+  i32x8 pf[2][XFP], qf[2][XFQ];
+  int32_t psc[2][XFP], qsc[2][XFQ];
+  bool sval[2];
+  constexpr int NFRAG = 2 * XFP + 4 * XFQ;
+  constexpr int NREAD = NFRAG + XFP + XFQ;
+  // Read r of half SS of the stage in sb (scale-chunk position S8 in cb,
+  // the half starting at contraction k0) into register set SET.
+  auto read = [&](auto ri, auto seti, auto ssi, auto s8i, const uint8_t* sb, const uint8_t* cb, int k0) {
+    constexpr int r = decltype(ri)::value, SET = decltype(seti)::value;
+    constexpr int SS = decltype(ssi)::value, S8 = decltype(s8i)::value;
+    if constexpr (r < 2 * XFP) {
+      constexpr int f = r / 2, e = r % 2;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(sb + pa[SS][e] + f * 32 * YBK);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) pf[SET][f][4 * e + d] = (int)v[d];
+    } else if constexpr (r < NFRAG) {
+      constexpr int j = (r - 2 * XFP) / 4, tt = (r - 2 * XFP) % 4;
+      constexpr int toff = (64 * SS + 32 * (tt / 2) + 8 * (tt % 2)) * XBQ;
+      const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(sb + qa[j] + toff));
+      qf[SET][j][2 * tt] = v[0];
+      qf[SET][j][2 * tt + 1] = v[1];
+    } else {
+      if constexpr (r == NFRAG) sval[SET] = k0 + 32 * hh < kend;
+      if constexpr (r < NFRAG + XFP) {
+        constexpr int f = r - NFRAG;
+        psc[SET][f] = cb[psa + 16 * 32 * f + 2 * S8];
+      } else {
+        constexpr int j = r - NFRAG - XFP;
+        qsc[SET][j] = cb[qsa + 32 * j + 2 * S8 * XBQ];
+      }
+    }
+  };
+  auto scales = [&](auto seti) {
+    constexpr int SET = decltype(seti)::value;
+#pragma unroll
+    for (int i = 0; i < XFP; ++i) psc[SET][i] = sval[SET] ? psc[SET][i] : 0;
+#pragma unroll
+    for (int j = 0; j < XFQ; ++j) qsc[SET][j] = sval[SET] ? qsc[SET][j] : 0;
+  };
+
+  f32x16 acc[XFP][XFQ];
+#pragma unroll
+  for (int i = 0; i < XFP; ++i)
+#pragma unroll
+    for (int j = 0; j < XFQ; ++j) acc[i][j] = f32x16{};
+  auto mfma = [&](auto mi, auto seti) {
+    constexpr int m = decltype(mi)::value, SET = decltype(seti)::value;
+    constexpr int i = m / XFQ, j = m % XFQ;
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qf[SET][j], pf[SET][i], acc[i][j], kFQ, kFP, 0,
+                                                                 qsc[SET][j], 0, psc[SET][i]);
+  };
+  constexpr int NM = XFP * XFQ;
+  static_assert(TY == NM, "one stage load per MFMA of an odd half");
+
+  const int nh = (kend - kbeg + XBK - 1) / XBK;                 // 64-deep halves
+  const int npair = (nh + 1) / 2;
+  if (nh > 0) {
+    // Prologue: chunk 0 and stages 0 and 1 in flight, chunk 0 and stage 0
+    // landed and published, half 0's fragments read.
+    if (!pst->issued) {
+      issue_chunk(sc0, kbeg);
+      static_for<TY>([&](auto u) { issue(u, s0, kbeg); });
+      static_for<TY>([&](auto u) { issue(u, s1, kbeg + YBK); });
+      barrier_vm<TY>();
+    } else {
+      // Chunk 0 and stage 0 came before the previous tile's result stores.
+      static_for<TY>([&](auto u) { issue(u, s1, kbeg + YBK); });
+      barrier_vm<TY + kEpiStores>();
+    }
+    static_for<NREAD>([&](auto r) { read(r, IC<0>{}, IC<0>{}, IC<0>{}, s0, sc0, kbeg); });
+  }
+
+  // Half h = 2 jj + SS (H = h mod 16: stage buffer (H / 2) % 2, scale chunk
+  // (H / 8) % 2, chunk position H % 8).
+  auto half = [&](auto hi, int h) {
+    constexpr int H = decltype(hi)::value;
+    constexpr int SS = H % 2, CUR = H & 1, NXT = CUR ^ 1;
+    constexpr int S8 = H % 8, S8N = (H + 1) % 8;
+    uint8_t* const cur = stagebuf(IC<H / 2>{});
+    uint8_t* const nsb = stagebuf(IC<(H + 1) / 2>{});
+    const uint8_t* const cnxt = chunkbuf(IC<(H + 1) / 8>{});
+    const int k1 = kbeg + (h + 1) * XBK;
+    const int k2 = kbeg + (h + 3) * XBK;                         // stage jj + 2
+    if constexpr (SS == 1) {
+      barrier_vm<0>();
+      if constexpr (S8 == 3) issue_chunk(chunkbuf(IC<H / 8 + 1>{}), kbeg + (h + 5) * XBK);
+    }
+    scales(IC<CUR>{});
+    static_for<NM>([&](auto mi) {
+      constexpr int m = decltype(mi)::value;
+      mfma(mi, IC<CUR>{});
+      if constexpr (SS == 1) issue(mi, cur, k2);
+      static_for<NREAD>([&](auto ri) {
+        if constexpr (decltype(ri)::value * NM / NREAD == m) read(ri, IC<NXT>{}, IC<SS ^ 1>{}, IC<S8N>{}, nsb, cnxt, k1);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+  for (int jt = 0; jt < npair; jt += 8) {
+    static_for<16>([&](auto hi) {
+      constexpr int H = decltype(hi)::value;
+      if (jt + H / 2 < npair) half(hi, 2 * jt + H);
+    });
+  }
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  // The next tile's first scale chunk and stage 0, then this tile's results.
+  bool issued = false;
+  if (pst->next < p.ntiles) {
+    const Tile tn = select_tile<XCfg, false>(p, pst->ends, pst->next, true, &pst->hint);
+    if (tn.valid && tn.kend > tn.kbeg) {
+      const uint8_t* const npc = p.P.codes + (int64_t)tn.p0 * ldp;
+      const int64_t nprow = (int64_t)(tn.pend - tn.p0) * ldp;
+      const uint8_t* const nqc = p.Q.codes + (int64_t)tn.g * p.Q.code_batch;
+      const Rsrc nps_r = make_rsrc(p.P.scales + (int64_t)tn.p0 * sldp, (int64_t)(tn.pend - tn.p0) * sldp);
+      const Rsrc nqs_r = make_rsrc(p.Q.scales + (int64_t)tn.g * p.Q.scale_batch, p.Q.scale_bytes);
+      const int32_t nq_base = (32 * wave + lane / 16) * ldq + tn.q0;
+      const int k0 = tn.kbeg;
+      dma<16>(nps_r, (lds_void*)(sc0 + 1024 * wave), (64 * wave + lane) * sldp, k0 >> 5);
+      dma<16>(nqs_r, (lds_void*)(sc0 + XBP * 16 + 1024 * wave), (4 * wave + lane / 16) * sldq + tn.q0 + 16 * (lane & 15),
+              (k0 >> 5) * sldq);
+      static_for<8>([&](auto ui) {
+        constexpr int u = decltype(ui)::value;
+        const Rsrc r = make_rsrc(npc + k0, nprow - k0);
+        const bool out = k0 + 16 * ((u & 1) ? pl_odd : pl_even) >= tn.kend;
+        dma<16>(r, (lds_void*)(s0 + 1024 * (8 * wave + u)), out ? kOOB : ((u & 1) ? p_off_odd : p_off_even),
+                8 * u * ldp);
+      });
+      static_for<8>([&](auto vi) {
+        constexpr int v = decltype(vi)::value;
+        const Rsrc r = make_rsrc(nqc + (int64_t)k0 * ldq, (int64_t)(tn.kend - k0) * ldq);
+        dma<16>(r, (lds_void*)(s0 + kYPBytes + 1024 * (8 * wave + v)), nq_base + 16 * ((v & 1) ? (qc0 ^ 8) : qc0),
+                4 * v * ldq);
+      });
+      issued = true;
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // Results through buffer 1: four passes of 32 rows per wave, 8 KiB each,
+  // every wave issuing exactly kEpiStores stores (masked ones out of range).
+  // (Two passes of 64 rows measured the same.)
+  constexpr int ROWB = XWQ * 2;
+  int el = lane;
+  asm volatile("" : "+v"(el));
+  uint8_t* const stg = s1 + wave * (ROWB * kEpiRows);
+  const int row0 = t.p0 + wp * XWP, col0 = t.q0 + wq * XWQ;
+  const Rsrc orsrc = make_rsrc(p.C + (int64_t)row0 * p.ldc + col0, ((int64_t)(M - row0) * p.ldc - col0) * 2);
+  const int c16 = el & 15;
+  const bool col_ok = col0 + 8 * c16 < p.Qtot;
+#pragma unroll
+  for (int i = 0; i < XFP; ++i) {
+    __builtin_amdgcn_sched_barrier(0);
+    const int r = el & 31;
+#pragma unroll
+    for (int j = 0; j < XFQ; ++j) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int sl = (j * 32 + 8 * r4 + 4 * (el >> 5)) / 4;
+        const u32x2 v = {pack_bf16x2(acc[i][j][4 * r4], acc[i][j][4 * r4 + 1]),
+                         pack_bf16x2(acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3])};
+        *reinterpret_cast<u32x2*>(stg + r * ROWB + 8 * (sl ^ (r & 15))) = v;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);                          // lgkmcnt(0): the pass is staged
+#pragma unroll
+    for (int it = 0; it < kEpiRows / 4; ++it) {
+      const int rr = it * 4 + el / 16;
+      const uint8_t* src = stg + rr * ROWB;
+      const u32x2 lo = *reinterpret_cast<const u32x2*>(src + 8 * ((2 * c16) ^ (rr & 15)));
+      const u32x2 hi = *reinterpret_cast<const u32x2*>(src + 8 * ((2 * c16 + 1) ^ (rr & 15)));
+      const int32_t off = (row0 + i * kEpiRows + rr < t.pend && col_ok) ? ((i * kEpiRows + rr) * p.ldc + 8 * c16) * 2
+                                                                        : kOOB;
+      __builtin_amdgcn_raw_buffer_store_b128(u32x4{lo[0], lo[1], hi[0], hi[1]}, orsrc, off, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);                          // read back before the next pass overwrites
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  return issued ? kDoneNextIssued : kDone;
+}
+
 // Persistent grad_X (MXFP8, chunk mode): one workgroup per compute unit
 // walks the tile list.  Workgroup b runs on XCD b % 8 (the hardware deals
 // workgroups to the XCDs in turn); at each step the 32 workgroups of an XCD
@@ -556,8 +750,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 // with an empty contraction issue no loads; the next tile then issues its
 // own prologue.
 template <int kFP = 0, int kFQ = 0>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void fp8_mfma_persistent(Params p) {
-  LP_MX_LDS(kChunkMode);
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void fp8_mfma_paired(Params p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t s0[kYStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t s1[kYStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t sc0[kChunkBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sc1[kChunkBytes];
   __shared__ int32_t s_ends[kMaxGroups];
   const int nwg = gridDim.x, xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
   Persist ps{s_ends, 0, false, GroupHit{0, 0, 0, 0, false}};
@@ -567,7 +764,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   }
   for (int l = xcd * (nwg / 8) + slot; l < p.ntiles; l += nwg) {
     ps.next = l + nwg;
-    const int r = mx_tile<false, kChunkMode, kFP, kFQ, true>(p, l, st0, st1, st2, st3, sc0, sc1, &ps);
+    const int r = mx_tile_pair<kFP, kFQ>(p, l, s0, s1, sc0, sc1, &ps);
     if (r == kNoTile) break;
     ps.issued = r == kDoneNextIssued;
   }
