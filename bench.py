@@ -6,7 +6,7 @@ A step is one pass of the workload's whole backward path over one batch of
 synthetic input already resident in HBM:
   mxfp8_deferred  lp_mx_quant(grad, -1) + lp_grouped_dx_deferred: grouped dX over 64 experts
                   against the bf16 weight quantized to MXFP8 along its reduction axis, inside
-                  the product for experts of at most 512 tokens (default: the largest
+                  the product for experts of at most 1536 tokens (default: the largest
                   workload, 962 GFLOP per step; --unfused: lp_mx_quant(W, -2) then
                   lp_grouped_bwd)
   fp8_frozen      lp_dequant of a frozen FP8 128x128-block weight to bf16, then
@@ -67,12 +67,13 @@ PEAK_FP4_TFLOPS = 10100.0      # MI355X dense fp4 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 ROTATE_BYTES = 1 << 30
 UNFUSED = False                # mxfp8_deferred: the three-call step instead of lp_grouped_dx_deferred
-# mxfp8_deferred: experts of at most this many tokens (two 256-row tiles)
-# quantize their weight inside the product.  Interleaved steady-state sweep
-# of the whole call: 0 (every weight quantized first) 1046 us, 256 897-901,
-# 384 878, 512 873-879, 640 884, 768 904, 1024 898, 2048 908, every expert
-# 896.
-FUSE_ROWS = 512
+# mxfp8_deferred: experts of at most this many tokens (six 256-row tiles)
+# quantize their weight inside the product.  Interleaved steady-state sweeps
+# of the whole call, with each weight column's row tiles listed together:
+# 512 836-839 us, 768 827, 1024 831-835, 1536 805-809, 2048 811-820, every
+# expert 845 (with row tiles listed row by row: 0 1046, 256 897-901, 512
+# 873-879, every expert 896).
+FUSE_ROWS = 1536
 
 
 # ------------------------------------------------------------------ input preparation (torch, GPU)

@@ -344,7 +344,7 @@ def lp_linear_bwd_noalloc(grad_out: QTensor, x: Optional[QTensor], w: Optional[Q
     return (grad_x if need_dx else None), (grad_w if need_dw else None)
 
 
-def lp_grouped_dx_deferred(grad_out: QTensor, w: torch.Tensor, offsets: torch.Tensor, fuse_rows: int = 512,
+def lp_grouped_dx_deferred(grad_out: QTensor, w: torch.Tensor, offsets: torch.Tensor, fuse_rows: int = 1536,
                            grad_x: Optional[torch.Tensor] = None, w_codes: Optional[torch.Tensor] = None,
                            w_scales: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """grad_X of the deferred MXFP8 recipe: grad_out (MXFP8 along -1) times

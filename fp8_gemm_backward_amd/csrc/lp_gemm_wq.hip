@@ -104,11 +104,12 @@ __global__ __launch_bounds__(NT8) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __syncthreads();
 
   // The listed tiles (groups of 1 .. fuse_rows rows, ceil(rows / 256) row
-  // tiles each, nq column tiles per row tile), in order of group, row tile,
-  // column tile.  XCD x (workgroups b with b % 8 == x) takes the x-th
-  // eighth of the list and its workgroups deal it out in turn, so that the
-  // tiles one XCD runs together are neighbours: column tiles of the same
-  // rows, whose gradient rows its L2 then serves.
+  // tiles each, nq column tiles per row tile), in order of group, then
+  // column tile, then row tile.  XCD x (workgroups b with b % 8 == x) takes
+  // the x-th eighth of the list and its workgroups deal it out in turn, so
+  // that the tiles one XCD runs together are neighbours: column tiles of the
+  // same rows, whose gradient rows its L2 then serves, and the row tiles of
+  // one weight slice, which its L2 then streams once.
   auto listed = [&](int n) { return n <= p.fuse_rows; };
   const int nlist = find_row_tile<WBP>(s_ends, p.groups, M, INT32_MAX, listed).seen * p.nq;
   const int nslot = gridDim.x / 8, xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
@@ -122,13 +123,17 @@ __global__ __launch_bounds__(NT8) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     WTile t{0, 0, 0, 0, false};
     if (i >= mine) return t;
     const int l = first + i * nslot;
-    const int pidx = l / p.nq;
-    t.q0 = (l - pidx * p.nq) * WBQ;
-    const GroupHit h = find_row_tile<WBP>(s_ends, p.groups, M, pidx, listed, &hint);
+    // A group's n row tiles hold entries [seen nq, (seen + n) nq) of the
+    // list, so l / nq names a row tile of l's group.
+    const GroupHit h = find_row_tile<WBP>(s_ends, p.groups, M, l / p.nq, listed, &hint);
     if (h.found) {
       hint = h;
+      const int n = (h.end - h.start + WBP - 1) / WBP;
+      const int local = l - h.seen * p.nq;
+      const int col = local / n;
+      t.q0 = col * WBQ;
       t.g = h.g;
-      t.p0 = h.start + (pidx - h.seen) * WBP;
+      t.p0 = h.start + (local - col * n) * WBP;
       t.pend = h.end;
       t.valid = true;
     }

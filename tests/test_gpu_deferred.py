@@ -114,8 +114,8 @@ def test_deferred_full_size(lp):
     gq = lp.lp_mx_quant(Gt, -1, "mxfp8")
     gq.shape = (1, w.M, w.N)
     ref = _two_calls(lp, gq, Wt, offs, torch.empty((w.M, w.K), dtype=torch.bfloat16, device="cuda"))
-    # the benchmark's threshold (512: experts of up to two row tiles fused) and 256
-    for fr in (512, 256):
+    # the benchmark's threshold (1536: experts of up to six row tiles fused) and 256
+    for fr in (1536, 256):
         dx = lp.lp_grouped_dx_deferred(gq, Wt, offs, fuse_rows=fr)
         torch.cuda.synchronize()
         assert torch.equal(dx.view(torch.int16), ref.view(torch.int16)), f"fused call (fuse_rows {fr}) differs"
