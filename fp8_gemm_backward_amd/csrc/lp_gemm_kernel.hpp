@@ -696,9 +696,14 @@ __device__ __forceinline__ Tile select_tile(const Params& p, int32_t* s_ends, in
     }
     __syncthreads();
     t.g = *pick;
+    // Inside a group the P-tile index runs fastest, so that the tiles one
+    // XCD receives (every eighth) share their gradient columns (P tiles
+    // p, p + 8, ...) rather than each XCD reading every gradient block of
+    // the group; per is np nq.
     const int r = pos - rank * per;
-    t.p0 = (r / p.nq) * C::BP;
-    t.q0 = (r % p.nq) * C::BQ;
+    const int np = per / p.nq;
+    t.p0 = (r % np) * C::BP;
+    t.q0 = (r / np) * C::BQ;
     t.pend = p.Ptot;
     t.kbeg = t.g ? ends[t.g - 1] : 0;
     t.kend = ends[t.g];
