@@ -18,6 +18,8 @@ namespace lp {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kMaxQuantGroups = 1024;          // groups of a grouped weight (the API's limit)
+constexpr uint32_t kRowsGroupsGrid = 2048;     // workgroups of the filtered-group quantizer
 
 // Axis -1: the work unit is eight consecutive elements (16 bytes of bf16);
 // the four lanes of a quad hold one 32-element block and take its amax
@@ -265,50 +267,57 @@ __global__ __launch_bounds__(kThreads) void mx_quant_tile(const uint16_t* __rest
   quant_tile32<kFp4, kDual>(src, codes_c, scales_c, codes_r, scales_r, tile, tiles_per_row, cols);
 }
 
-// Rows of group g from int32 cumulative ends, with the kernels' clamping:
-// end_g = min(max(0, o_0 .. o_g), M).  Called by a whole wave (lane-parallel
-// loads, then a maximum across the wave); every lane gets the result.
-__device__ __forceinline__ int group_rows(const int32_t* __restrict__ offsets, int g, int M) {
-  const int lane = threadIdx.x & 63;
-  int hi = 0, lo = 0;                                    // max over o_0..o_g, and over o_0..o_{g-1}
-  for (int j = lane; j <= g; j += 64) {
-    const int o = offsets[j];
-    hi = o > hi ? o : hi;
-    if (j < g) lo = o > lo ? o : lo;
-  }
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int h = __shfl_xor(hi, d), l = __shfl_xor(lo, d);
-    hi = h > hi ? h : hi;
-    lo = l > lo ? l : lo;
-  }
-  hi = hi < M ? hi : M;
-  lo = lo < M ? lo : M;
-  return g > 0 ? hi - lo : hi;
-}
-
 // MXFP8 quantization along the rows (-2) of a grouped weight [G][N][K], for
 // the groups with more than min_rows rows only (the others quantize their
-// weight inside the grad_X product).  Workgroup (x, g) takes tiles
-// 16 x .. 16 x + 15 of group g.
+// weight inside the grad_X product).  The first wave lists those groups in
+// LDS from the int32 cumulative ends, with the kernels' clamping
+// (end_g = min(max(0, o_0 .. o_g), M)); the workgroups then stride over the
+// listed groups' tiles, 16 tiles (one per 16 lanes) per step.  A grid that
+// covered every group's tiles and let the unlisted ones exit spent most of
+// its time dispatching workgroups that do nothing.
 __global__ __launch_bounds__(kThreads) void mx_quant_rows_groups(const uint16_t* __restrict__ src,
                                                                  uint8_t* __restrict__ codes,
                                                                  uint8_t* __restrict__ scales,
                                                                  const int32_t* __restrict__ offsets, int32_t M,
-                                                                 int32_t min_rows, uint32_t tiles_per_group,
-                                                                 FastDiv tiles_per_row, uint32_t cols) {
-  __shared__ int s_rows;
-  const int g = blockIdx.y;
+                                                                 int32_t groups, int32_t min_rows,
+                                                                 uint32_t tiles_per_group, FastDiv tiles_per_row,
+                                                                 uint32_t cols) {
+  __shared__ int32_t s_list[kMaxQuantGroups];
+  __shared__ int32_t s_n;
   if (threadIdx.x < 64) {
-    const int rows = group_rows(offsets, g, M);
-    if (threadIdx.x == 0) s_rows = rows;
+    const int lane = threadIdx.x;
+    int carry = 0, n = 0;                                  // end of the previous chunk's last group; listed so far
+    for (int base = 0; base < groups; base += 64) {
+      const int j = base + lane;
+      int m = j < groups ? offsets[j] : 0;
+      m = m > 0 ? m : 0;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {                   // inclusive running maximum across the lanes
+        const int up = __shfl_up(m, d);
+        if (lane >= d) m = up > m ? up : m;
+      }
+      int end = m > carry ? m : carry;
+      end = end < M ? end : M;
+      int prev = __shfl_up(end, 1);
+      if (lane == 0) prev = carry < M ? carry : M;
+      const bool listed = j < groups && end - prev > min_rows;
+      const uint64_t mask = __ballot(listed);
+      if (listed) s_list[n + __popcll(mask & ((1ull << lane) - 1))] = j;
+      n += __popcll(mask);
+      carry = __shfl(end, 63);
+    }
+    if (lane == 0) s_n = n;
   }
   __syncthreads();
-  if (s_rows <= min_rows) return;
-  const uint32_t t = blockIdx.x * (kThreads / 16) + (threadIdx.x >> 4);
-  if (t >= tiles_per_group) return;
-  quant_tile32<false, false>(src, nullptr, nullptr, codes, scales, (uint32_t)g * tiles_per_group + t, tiles_per_row,
-                             cols);
+  const uint32_t steps = (tiles_per_group + kThreads / 16 - 1) / (kThreads / 16);   // steps per group
+  const uint32_t total = (uint32_t)s_n * steps;
+  for (uint32_t c = blockIdx.x; c < total; c += gridDim.x) {
+    const uint32_t li = c / steps;
+    const uint32_t t = (c - li * steps) * (kThreads / 16) + (threadIdx.x >> 4);
+    if (t < tiles_per_group)
+      quant_tile32<false, false>(src, nullptr, nullptr, codes, scales, (uint32_t)s_list[li] * tiles_per_group + t,
+                                 tiles_per_row, cols);
+  }
 }
 
 }  // namespace
@@ -319,10 +328,14 @@ hipError_t launch_mx_quant_rows_groups(const void* src, int64_t groups, int64_t 
   if (groups * rows * cols == 0) return hipSuccess;
   const uint32_t tpr = (uint32_t)(cols / 32);
   const uint32_t tpg = (uint32_t)(rows / 32) * tpr;
-  const dim3 grid((tpg + kThreads / 16 - 1) / (kThreads / 16), (uint32_t)groups), block(kThreads);
+  // Enough workgroups to keep every compute unit streaming; each strides
+  // over the listed groups' tiles.
+  const uint64_t steps = (uint64_t)groups * ((tpg + kThreads / 16 - 1) / (kThreads / 16));
+  const dim3 grid((uint32_t)(steps < kRowsGroupsGrid ? steps : kRowsGroupsGrid)), block(kThreads);
   mx_quant_rows_groups<<<grid, block, 0, stream>>>(static_cast<const uint16_t*>(src), static_cast<uint8_t*>(codes),
                                                    static_cast<uint8_t*>(scales), offsets, (int32_t)M,
-                                                   (int32_t)min_rows, tpg, make_fastdiv(tpr), (uint32_t)cols);
+                                                   (int32_t)groups, (int32_t)min_rows, tpg, make_fastdiv(tpr),
+                                                   (uint32_t)cols);
   return hipGetLastError();
 }
 
