@@ -88,6 +88,39 @@ def test_deferred_matches_quantize_then_product(lp, fuse_rows):
                  exp[:end][sel], f"fuse_rows={fuse_rows} vs oracle")
 
 
+def test_deferred_many_groups(lp):
+    """150 groups, most small, with groups above the threshold at indices
+    past 64 and 128 (the quantize-first pass lists its groups 64 at a time,
+    carrying the running end across), an empty group among them, and rows
+    past the last offset: dX bit for bit equal to quantize-then-product, the
+    weight copy written for exactly the large groups."""
+    N, K, G = 512, 64, 150
+    rng = W.rng(72, "route")
+    sizes = rng.integers(0, 60, size=G)
+    for gi, n in ((3, 700), (70, 300), (64, 257), (129, 513), (149, 400), (100, 0)):
+        sizes[gi] = n
+    M = int(sizes.sum()) + 37
+    g, gd, wbits, offsets = _case(lp, 72, M, N, K, sizes.tolist())
+    w = bf16_dev(wbits)
+    offs = torch.from_numpy(offsets).cuda()
+    ref = _two_calls(lp, g, w, offs, _sentinel((M, K)))
+    codes = torch.full((G, N, K), 0xA5, dtype=torch.uint8, device="cuda")
+    scales = torch.full((G, N // 32, K), 0x5A, dtype=torch.uint8, device="cuda")
+    dx = lp.lp_grouped_dx_deferred(g, w, offs, fuse_rows=256, grad_x=_sentinel((M, K)), w_codes=codes,
+                                   w_scales=scales)
+    torch.cuda.synchronize()
+    assert_bits_equal(bits_host(dx), bits_host(ref), "150 groups vs quantize-then-product")
+    wc, ws = F.mx_quant(wbits, -2, "e4m3")
+    got_c, got_s = codes.cpu().numpy(), scales.cpu().numpy()
+    large = [gi for gi, (s0, e0) in enumerate(O.group_bounds(offsets)) if e0 - s0 > 256]
+    assert large == [3, 64, 70, 129, 149]
+    for gi in range(G):
+        if gi in large:
+            assert np.array_equal(got_c[gi], wc[gi]) and np.array_equal(got_s[gi], ws[gi]), f"group {gi} codes"
+        else:
+            assert np.all(got_c[gi] == 0xA5) and np.all(got_s[gi] == 0x5A), f"group {gi} copy was written"
+
+
 @pytest.mark.parametrize("N,K", [(800, 272), (1024, 400)])
 def test_deferred_other_widths_fall_back(lp, N, K):
     """N % 512 != 0 or K % 32 != 0: every weight is quantized first; the
