@@ -585,3 +585,55 @@ def test_mxfp8_dense_full_size(lp):
     xc, xs = F.mx_quant(xcol[None], -2, "e4m3")
     ref = O.linear_dw(F.dequant("mxfp8", gq, gs, axis=-2)[0], F.dequant("mxfp8", xc, xs, axis=-2)[0])
     assert_close(dw[torch.from_numpy(nrows).cuda()][:, ic], ref, "mxfp8 dense dW")
+
+
+def test_mxfp8_persistent_partial_tiles(lp):
+    """The persistent block-scaled grad_X (more output tiles than compute
+    units: 17 x 17 = 289 here) with a ragged last row tile (M = 4133) and a
+    partial last column tile (K = 4160, 64 columns past 16 tiles of 256),
+    dense and grouped (five groups with ragged ends, an empty one, sentinel
+    rows past the last offset), on sampled rows and every column of the
+    partial tile against the oracle."""
+    M, N, K = 4133, 1024, 4160
+    Gt = W.torch_normal_bf16((M, N), 1.0, seed=6106, device="cuda")
+    Wt = W.torch_normal_bf16((3, N, K), 0.02, seed=6107, device="cuda")
+    gc = lp.lp_mx_quant(Gt, -1, "mxfp8")
+    gc.shape = (1, M, N)
+    wq = lp.lp_mx_quant(Wt, -2, "mxfp8")
+
+    def host(t):
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    rows = np.unique(np.concatenate([_sample_rows(M, 12, 60), [M - 1, 4095, 4096]]))
+    cols = np.unique(np.concatenate([_sample_rows(K, 24, 61), np.arange(4096, K)]))
+    ic = torch.from_numpy(cols).cuda()
+    g = host(Gt[torch.from_numpy(rows).cuda()])
+    gq, gs = F.mx_quant(g[None], -1, "e4m3")
+    gd = F.dequant("mxfp8", gq, gs, axis=-1)[0]
+    wd = []
+    for e in range(3):
+        wc, ws = F.mx_quant(host(Wt[e][:, ic])[None], -2, "e4m3")
+        wd.append(F.dequant("mxfp8", wc, ws, axis=-2)[0])
+
+    w1 = lp.QTensor("mxfp8", wq.codes[:1], wq.scales[:1], shape=(1, N, K), axis=-2)
+    dx, _ = lp.lp_linear_bwd(gc, None, w1, need_dw=False)
+    torch.cuda.synchronize()
+    assert_close(dx[torch.from_numpy(rows).cuda()][:, ic], O.linear_dx(gd, wd[0]), "dense persistent dX")
+
+    # four groups; group 3 reuses expert 0's weight (a copy)
+    sizes = [1500, 0, 1201, 900]
+    ends = W.cumulative_ends(sizes)
+    wq4 = lp.QTensor("mxfp8", torch.cat([wq.codes, wq.codes[:1]]), torch.cat([wq.scales, wq.scales[:1]]),
+                     shape=(4, N, K), axis=-2)
+    sent = torch.full((M, K), -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    dxg, _ = lp.lp_grouped_bwd(gc, None, wq4, dev(ends), need_dw=False, grad_x=sent)
+    torch.cuda.synchronize()
+    for gi, (s0, e0) in enumerate(O.group_bounds(ends)):
+        sel = (rows >= s0) & (rows < e0)
+        if not sel.any():
+            continue
+        ref = O.linear_dx(gd[sel], wd[gi if gi < 3 else 0])
+        r = torch.from_numpy(rows[sel]).cuda()
+        assert_close(dxg[r][:, ic], ref, f"grouped persistent dX, group {gi}")
+    tail = rows[rows >= int(ends[-1])]
+    assert (host(dxg[torch.from_numpy(tail).cuda()]) == 0xFFFF).all(), "rows past the last offset were written"
