@@ -71,6 +71,32 @@ int64_t code_bytes2(int fmt) {
   return fmt == LP_BF16 ? 4 : (fmt == LP_MXFP4 || fmt == LP_NVFP4) ? 1 : 2;
 }
 
+// Grouped grad_X and forward on 256 x 256 tiles (prm.ntiles: the host's
+// bound on them) split by dispatch round: the whole rounds of kCUs tiles in
+// this launch, a short last round as 256 x 128 tiles in a second launch
+// (tail_params).  The group sizes live on the device, so the kernels count
+// the tiles and both launches reach the same split, or none (the second
+// launch then has no tile).  Returns whether to make the second launch.
+// Only for contractions of at least kTailMinSlabs slabs: measured in steady
+// state, the block-FP8 grouped forward (4096-long contraction, 544 tiles)
+// went from 342.5 to 316.3 us, while the MXFP4 grouped grad_X (2048-long,
+// 1088 tiles) went from 268.0 to 271.7 us; a short tile's fixed costs and
+// the second launch outweigh what its narrower last round saves.
+constexpr int kTailMinSlabs = 64;
+bool tile_split(Params& prm) {
+  if (prm.offsets == nullptr || prm.splits != 1 || prm.fuse_side != 0 || prm.ntiles < kCUs) return false;
+  if (prm.Ktot < kTailMinSlabs * BK) return false;
+  prm.tail = 1;
+  return true;
+}
+Params tail_params(const Params& big) {
+  Params t = big;
+  t.tail = 2;
+  t.nq = (int32_t)((t.Qtot + Narrow::BQ - 1) / Narrow::BQ);
+  t.ntiles = kCUs;
+  return t;
+}
+
 template <class C>
 hipError_t launch_cfg(const GemmCall& call, Params prm, hipStream_t stream) {
   prm.nq = (int32_t)((prm.Qtot + C::BQ - 1) / C::BQ);
@@ -81,8 +107,15 @@ hipError_t launch_cfg(const GemmCall& call, Params prm, hipStream_t stream) {
     const int64_t ptiles = call.offsets ? (call.M / C::BP + call.groups) : (call.M + C::BP - 1) / C::BP;
     prm.ntiles = (int32_t)(ptiles * prm.nq * prm.splits);
     const bool mx = call.grad->fmt == LP_MXFP8;
-    if constexpr (C::BQ == Big::BQ) return mx ? dx_big_mxfp8(*call.other, prm, stream) : dx_big_bf16(*call.other, prm, stream);
-    else return mx ? dx_narrow_mxfp8(*call.other, prm, stream) : dx_narrow_bf16(*call.other, prm, stream);
+    if constexpr (C::BQ == Big::BQ) {
+      const bool split = tile_split(prm);
+      const hipError_t e = mx ? dx_big_mxfp8(*call.other, prm, stream) : dx_big_bf16(*call.other, prm, stream);
+      if (e != hipSuccess || !split) return e;
+      const Params tail = tail_params(prm);
+      return mx ? dx_narrow_mxfp8(*call.other, tail, stream) : dx_narrow_bf16(*call.other, tail, stream);
+    } else {
+      return mx ? dx_narrow_mxfp8(*call.other, prm, stream) : dx_narrow_bf16(*call.other, prm, stream);
+    }
   }
   const int64_t np = (prm.Ptot + C::BP - 1) / C::BP;
   prm.ntiles = (int32_t)(np * prm.nq * call.groups * prm.splits);
@@ -90,7 +123,6 @@ hipError_t launch_cfg(const GemmCall& call, Params prm, hipStream_t stream) {
   else return dw_narrow(*call.other, prm, stream);
 }
 
-constexpr int kCUs = 256;
 constexpr int64_t kMinSplitSlabs = 16;     // contraction slabs per split, at least
 
 // Output tiles of the 256 x 256 configuration.
@@ -251,7 +283,11 @@ hipError_t launch_fwd(const lp_qtensor& x, const lp_qtensor& w, const int32_t* o
     prm.gm = tile_group(BP * code_bytes2(x.fmt), BQ * code_bytes2(w.fmt), (prm.Ptot + BP - 1) / BP);
   const int64_t ptiles = offsets ? (x.rows / BP + groups) : (x.rows + BP - 1) / BP;
   prm.ntiles = (int32_t)(ptiles * prm.nq);
-  return mx ? fwd_mx(prm, x.fmt == LP_MXFP4, stream) : fwd_dec(prm, x.fmt, w.fmt, stream);
+  if (mx) return fwd_mx(prm, x.fmt == LP_MXFP4, stream);
+  const bool split = BQ == Big::BQ && tile_split(prm);
+  const hipError_t e = fwd_dec(prm, x.fmt, w.fmt, false, stream);
+  if (e != hipSuccess || !split) return e;
+  return fwd_dec(tail_params(prm), x.fmt, w.fmt, true, stream);
 }
 
 hipError_t launch_grouped_dx_deferred(const lp_qtensor& grad, const void* w, int64_t K, const int32_t* offsets,

@@ -15,10 +15,16 @@
 namespace lp {
 namespace gk {
 
-hipError_t fwd_dec(const Params& prm, int fmt_x, int fmt_w, hipStream_t s) {
+// narrow: the 256 x 128 tiles of a split grouped call's last round (the
+// formats whose tiles are otherwise 256 x 256).
+hipError_t fwd_dec(const Params& prm, int fmt_x, int fmt_w, bool narrow, hipStream_t s) {
   if (fmt_x == LP_BF16 && fmt_w == LP_BF16) return run<Narrow, BF16, -1, BF16, -1, false, true>(prm, s);
-  if (fmt_x == LP_BF16 && fmt_w == LP_FP8_B128) return run<Big, BF16, -1, FP8_B128, -1, false, true>(prm, s);
-  if (fmt_x == LP_NVFP4 && fmt_w == LP_NVFP4) return run<Big, NVFP4, -1, NVFP4, -1, false, true>(prm, s);
+  if (fmt_x == LP_BF16 && fmt_w == LP_FP8_B128)
+    return narrow ? run<Narrow, BF16, -1, FP8_B128, -1, false, true>(prm, s)
+                  : run<Big, BF16, -1, FP8_B128, -1, false, true>(prm, s);
+  if (fmt_x == LP_NVFP4 && fmt_w == LP_NVFP4)
+    return narrow ? run<Narrow, NVFP4, -1, NVFP4, -1, false, true>(prm, s)
+                  : run<Big, NVFP4, -1, NVFP4, -1, false, true>(prm, s);
   return hipErrorInvalidValue;
 }
 

@@ -122,7 +122,16 @@ struct Params {
   // only, 0 lists every group.
   int32_t fuse_rows;
   int32_t fuse_side;
+  // Grouped grad_X and forward through bf16 tiles, split by dispatch round
+  // (tile_split): 1 takes the whole rounds of kCUs 256-wide tiles (all the
+  // tiles when there is no split), 2 the last partial round as 256 x 128
+  // tiles, in a second launch.  0: no split.
+  int32_t tail;
 };
+
+// Compute units of the GPU: one 256 x 256 (or 256 x 128) tile workgroup
+// each, since its LDS takes a whole CU.
+constexpr int kCUs = 256;
 
 template <int kBP, int kBQ>
 struct Cfg {
@@ -647,6 +656,28 @@ __device__ __forceinline__ Tile select_tile(const Params& p, int32_t* s_ends, in
         pidx = tile / p.nq;
         t.q0 = (tile % p.nq) * C::BQ;
         t.tile = tile;
+      } else if (p.tail != 0) {
+        // Split by dispatch round.  The ntb 256 x 256 tiles, one per CU at
+        // a time, run in rounds of kCUs; a last round of r <= kCUs / 2
+        // tiles would leave most CUs idle for a whole tile's time, so those
+        // tiles go to a second launch as 2r (at most) 256 x 128 tiles, each
+        // about half as long.  The row tiles (BP = 256) are the same in both
+        // launches and every tile sums its products in the same order, so
+        // the split changes no result bit.
+        const int nqb = (p.Qtot + 255) / 256;
+        const int rows = find_row_tile<C::BP>(s_ends, p.groups, p.Ptot, INT32_MAX, listed).seen;
+        const int ntb = rows * nqb, full = ntb / kCUs * kCUs, rest = ntb - full;
+        const bool split = full > 0 && rest > 0 && 2 * rest <= kCUs;
+        int nt = split ? full : ntb, base = 0;
+        if (p.tail == 2) {
+          // big tile `full` is row tile full / nqb, 256-column tile full % nqb
+          base = (full / nqb) * p.nq + 2 * (full % nqb);
+          nt = split ? rows * p.nq - base : 0;
+        }
+        tile = hw < nt ? base + xcd_remap(hw, nt) : rows * p.nq; // rows nq: past every tile
+        pidx = tile / p.nq;
+        t.q0 = (tile % p.nq) * C::BQ;
+        t.tile = tile;
       }
       const GroupHit h = find_row_tile<C::BP>(s_ends, p.groups, p.Ptot, pidx, listed, hint);
       if (hint != nullptr && h.found) *hint = h;
@@ -1142,8 +1173,9 @@ hipError_t dw_pt(const Params& prm, int fmt_p, int fmt_q, hipStream_t s);
 hipError_t fwd_mx(const Params& prm, bool fp4, hipStream_t s);
 // Forward y = x @ w^T through bf16 tiles (fused decode): bf16 x with a bf16
 // weight (256 x 128 tiles) or a block-FP8 weight, NVFP4 x with an NVFP4
-// weight (256 x 256 tiles).
-hipError_t fwd_dec(const Params& prm, int fmt_x, int fmt_w, hipStream_t s);
+// weight (256 x 256 tiles; 256 x 128 when narrow, the last round of a
+// split grouped call).
+hipError_t fwd_dec(const Params& prm, int fmt_x, int fmt_w, bool narrow, hipStream_t s);
 // Both of them in one launch (X and W in the same format fmt_q).
 hipError_t pt_pair(const Params& dx, const Params& dw, int fmt_p, int fmt_q, hipStream_t s);
 

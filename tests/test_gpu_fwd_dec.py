@@ -84,6 +84,41 @@ def test_grouped_fwd(lp, fx, fw, sizes):
     assert (y[end:].float() == 7.0).all(), "rows past the last end are not written"
 
 
+@pytest.mark.parametrize("fx,fw,N", [("bf16", "fp8_b128", 2048), ("bf16", "fp8_b128", 1936), ("nvfp4", "nvfp4", 2048)])
+def test_grouped_fwd_round_split(lp, fx, fw, N):
+    """A grouped forward over a 4096-long contraction with more 256 x 256
+    tiles than one round of the 256 CUs: 34 row tiles of 8 column tiles,
+    272 tiles, the last 16 run as 256 x 128 tiles in a second launch (N =
+    1936 ends on a single 128-wide tile).  Bit-identical to a linear forward
+    per group, within tolerance of the oracle on sampled rows of every group,
+    rows past the last end kept."""
+    sizes = [4000, 0, 4300, 1]
+    G, K = len(sizes), 4096
+    M = int(sum(sizes)) + 40
+    xq, xh, wq, wh = _operands(lp, fx, fw, 59, M, N, K, groups=G)
+    ends = W.cumulative_ends(sizes)
+    y = torch.full((M, N), 7.0, dtype=torch.bfloat16, device="cuda")
+    lp.lp_grouped_fwd(xq, wq, dev(ends), y=y)
+    per = []
+    for g, (s, e) in enumerate(O.group_bounds(ends)):
+        if e > s:
+            # copies, so that every pointer keeps the library's alignment
+            xsc = xq.scales.view(M, -1)[s:e].clone() if xq.scales is not None else None
+            xs = lp.QTensor(fx, xq.codes.view(M, -1)[s:e].clone(), xsc, xq.tensor_scale, shape=(1, e - s, K))
+            ws = wq.scales.view(G, -1)[g].clone() if wq.scales is not None else None
+            wg = lp.QTensor(fw, wq.codes.view(G, -1)[g].clone(), ws, wq.tensor_scale, shape=(1, N, K))
+            per.append((g, s, e, lp.lp_linear_fwd(xs, wg)))
+    torch.cuda.synchronize()
+    for g, s, e, yg in per:
+        assert np.array_equal(bits_host(y[s:e]), bits_host(yg)), f"group {g} differs from the linear forward"
+        rows = s + np.sort(W.rng(59 + g, "x").choice(e - s, size=min(24, e - s), replace=False))
+        xr = tuple(a[:, rows] if np.ndim(a) == 3 else a for a in xh)
+        wr = tuple(a[g:g + 1] if np.ndim(a) == 3 else a for a in wh)
+        assert_close(y[torch.from_numpy(rows).cuda()], _reference(fx, fw, xr, wr), f"{fx} x {fw} group {g}, N = {N}")
+    end = int(ends[-1])
+    assert (y[end:].float() == 7.0).all(), "rows past the last end are not written"
+
+
 @pytest.mark.parametrize("fx,fw", [("bf16", "fp8_b128"), ("nvfp4", "nvfp4")])
 def test_fused_decode_equals_decoded_copy(lp, fx, fw):
     """Decoding inside the contraction gives the same bits as decoding the

@@ -368,6 +368,48 @@ def test_grouped_one_group_equals_linear(lp):
     assert_bits_equal(bits_host(dw1)[0], bits_host(dw2), "dW")
 
 
+def _group_slice(lp, q, gi):
+    """Group gi of a grouped descriptor [G, R, C] as a [1, R, C] descriptor
+    (copies, so that every pointer keeps the library's alignment)."""
+    G, R, C = q.shape
+    scales = q.scales.view(G, -1)[gi].clone() if q.scales is not None else None
+    return lp.QTensor(q.fmt, q.codes.view(G, -1)[gi].clone(), scales, q.tensor_scale, shape=(1, R, C), axis=q.axis)
+
+
+@pytest.mark.parametrize("fmt,K,sizes", [("mxfp4", 2048, [4000, 0, 4300, 1]), ("fp8_b128", 1904, [4000, 0, 4300, 1]),
+                                         ("mxfp4", 2048, [7000, 0, 7800])])
+def test_grouped_round_split(lp, fmt, K, sizes):
+    """Grouped dX over a 4096-long contraction with more 256 x 256 tiles than
+    one round of the 256 CUs.  Sizes 4000, 0, 4300, 1: 34 row tiles of 8
+    column tiles, 272 tiles, 256 of them in whole rounds and the other 16 as
+    256 x 128 tiles of a second launch (K = 1904 ends on a single 128-wide
+    tile).  Sizes 7000, 0, 7800: 59 row tiles, 472 tiles, a last round of 216
+    tiles, too many to split.  Bit-identical to a linear call per group,
+    within the contraction tolerance of the oracle on sampled rows of every
+    group, rows past the last offset kept."""
+    N = 4096
+    G = len(sizes)
+    M = int(sum(sizes)) + 40
+    offsets = W.cumulative_ends(sizes)
+    g, gb = _grad(lp, 39, M, N)
+    w, wd = _operand(lp, 39, "w", (G, N, K), fmt, -1)
+    dx = lp.lp_grouped_bwd(g, None, w, torch.from_numpy(offsets).cuda(), need_dw=False,
+                           grad_x=_sentinel((M, K)))[0]
+    per = []
+    for gi, (s0, e0) in enumerate(O.group_bounds(offsets)):
+        if e0 > s0:
+            gq = lp.QTensor("bf16", g.codes.view(M, N)[s0:e0], shape=(1, e0 - s0, N))
+            per.append((gi, s0, e0, lp.lp_linear_bwd(gq, None, _group_slice(lp, w, gi), need_dw=False)[0]))
+    torch.cuda.synchronize()
+    for gi, s0, e0, d in per:
+        assert_bits_equal(bits_host(dx[s0:e0]), bits_host(d), f"{fmt} group {gi} vs the linear call")
+        rows = s0 + _sample_rows(e0 - s0, 24, 39 + gi)
+        sel = torch.from_numpy(rows).cuda()
+        assert_close(dx[sel], O.rows_dx(gb, wd[gi], rows), f"{fmt} group {gi}, sampled rows")
+    end = int(offsets[-1])
+    assert np.all(bits_host(dx[end:]) == 0xFFFF), "rows past the last offset were written"
+
+
 def test_grouped_bad_offsets_are_clamped(lp):
     """Offsets out of order or past M are clamped (end_g = clamp(o_g,
     end_{g-1}, M)): the kernels stay in bounds and compute those groups."""
