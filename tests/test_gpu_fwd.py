@@ -68,6 +68,43 @@ def test_grouped_fwd_one_group_equals_linear(lp):
 
 
 @pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8"])
+def test_more_tiles_than_cus(lp, fmt):
+    """More 256 x 256 tiles than compute units (a second dispatch round): a
+    grouped forward of 34 row tiles of 8 column tiles (272 tiles; an empty
+    group, a 1-row group, rows past the last end kept) bit-identical to a
+    linear forward per group and within tolerance of the oracle, and a dense
+    one with ragged last row and column tiles (M = 9000, N = 2000: 36 x 8 =
+    288 tiles)."""
+    sizes = [4000, 0, 4300, 1]
+    G, N, K = len(sizes), 2048, 256
+    M = int(sum(sizes)) + 40
+    xq, xd, wq, wd = _operands(lp, fmt, 47, M, N, K, groups=G)
+    ends = W.cumulative_ends(sizes)
+    y = torch.full((M, N), 7.0, dtype=torch.bfloat16, device="cuda")
+    lp.lp_grouped_fwd(xq, wq, dev(ends), y=y)
+    per = []
+    for g, (s, e) in enumerate(O.group_bounds(ends)):
+        if e > s:
+            # copies, so that every pointer keeps the library's alignment
+            xs = lp.QTensor(fmt, xq.codes.view(M, -1)[s:e].clone(), xq.scales.view(M, -1)[s:e].clone(),
+                            shape=(1, e - s, K))
+            wg = lp.QTensor(fmt, wq.codes.view(G, -1)[g].clone(), wq.scales.view(G, -1)[g].clone(), shape=(1, N, K))
+            per.append((g, s, e, lp.lp_linear_fwd(xs, wg)))
+    torch.cuda.synchronize()
+    for g, s, e, yg in per:
+        assert torch.equal(y[s:e].view(torch.int16), yg.view(torch.int16)), f"group {g} differs from the linear call"
+    end = int(ends[-1])
+    assert_close(y[:end], O.grouped_fwd(xd, wd, ends)[:end], f"{fmt} grouped forward, 272 tiles")
+    assert (y[end:].float() == 7.0).all(), "rows past the last end are not written"
+
+    Md, Nd = 9000, 2000
+    xq, xd, wq, wd = _operands(lp, fmt, 48, Md, Nd, K)
+    y = lp.lp_linear_fwd(xq, wq)
+    torch.cuda.synchronize()
+    assert_close(y, O.linear_fwd(xd, wd), f"{fmt} dense forward, 288 tiles")
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8"])
 def test_nan_scale_blocks(lp, fmt):
     """An E8M0 NaN scale (0xFF) makes its block NaN: the output column of a
     NaN weight block and the output row of a NaN input block are NaN, as in
