@@ -442,11 +442,11 @@ def time_standalone(lp, stream, q, reps=50):
 # ------------------------------------------------------------------ HBM traffic from committed counters
 
 def kernel_source_digest() -> str:
-    """Digest of every kernel source (the library's .hip and .hpp files)."""
+    """Digest of every kernel source (the library's .hip, .hpp and .inc files)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "fp8_gemm_backward_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".hpp")):
+        if f.endswith((".hip", ".hpp", ".inc")):
             h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 

@@ -97,8 +97,10 @@ Params tail_params(const Params& big) {
   return t;
 }
 
+// The tile counts and order of a call on C tiles (prm from base_params, with
+// any split plan already set).
 template <class C>
-hipError_t launch_cfg(const GemmCall& call, Params prm, hipStream_t stream) {
+Params cfg_params(const GemmCall& call, Params prm) {
   prm.nq = (int32_t)((prm.Qtot + C::BQ - 1) / C::BQ);
   if (call.offsets == nullptr && prm.splits == 1)
     prm.gm = tile_group(C::BP * code_bytes2(call.grad->fmt), C::BQ * code_bytes2(call.other->fmt),
@@ -106,6 +108,17 @@ hipError_t launch_cfg(const GemmCall& call, Params prm, hipStream_t stream) {
   if (!call.dw) {
     const int64_t ptiles = call.offsets ? (call.M / C::BP + call.groups) : (call.M + C::BP - 1) / C::BP;
     prm.ntiles = (int32_t)(ptiles * prm.nq * prm.splits);
+  } else {
+    const int64_t np = (prm.Ptot + C::BP - 1) / C::BP;
+    prm.ntiles = (int32_t)(np * prm.nq * call.groups * prm.splits);
+  }
+  return prm;
+}
+
+template <class C>
+hipError_t launch_cfg(const GemmCall& call, Params prm, hipStream_t stream) {
+  prm = cfg_params<C>(call, prm);
+  if (!call.dw) {
     const bool mx = call.grad->fmt == LP_MXFP8;
     if constexpr (C::BQ == Big::BQ) {
       const bool split = tile_split(prm);
@@ -117,8 +130,6 @@ hipError_t launch_cfg(const GemmCall& call, Params prm, hipStream_t stream) {
       return mx ? dx_narrow_mxfp8(*call.other, prm, stream) : dx_narrow_bf16(*call.other, prm, stream);
     }
   }
-  const int64_t np = (prm.Ptot + C::BP - 1) / C::BP;
-  prm.ntiles = (int32_t)(np * prm.nq * call.groups * prm.splits);
   if constexpr (C::BQ == Big::BQ) return dw_big(*call.other, prm, stream);
   else return dw_narrow(*call.other, prm, stream);
 }
@@ -334,6 +345,13 @@ hipError_t launch_grouped_dx_deferred(const lp_qtensor& grad, const void* w, int
 hipError_t launch_gemm_pair(const GemmCall& dx, const GemmCall& dw, hipStream_t stream) {
   if (native_pt(dx) && native_pt(dw) && dx.other->fmt == dw.other->fmt)
     return pt_pair(native_params(dx), native_params(dw), dx.grad->fmt, dx.other->fmt, stream);
+  // A grouped layer's grad_X and grad_W from a bf16 gradient and FP4 W and X
+  // (scaled along their last axis), both on 256 x 256 tiles: one launch.
+  const int fq = dx.other->fmt;
+  if (dx.offsets != nullptr && dx.grad->fmt == LP_BF16 && (fq == LP_MXFP4 || fq == LP_NVFP4) &&
+      dw.other->fmt == fq && dx.other->scale_axis == -1 && dw.other->scale_axis == -1 && dx.ws == nullptr &&
+      dw.ws == nullptr && big_tiles(dx) >= kCUs && big_tiles(dw) >= kCUs)
+    return dec_pair(cfg_params<Big>(dx, base_params(dx)), cfg_params<Big>(dw, base_params(dw)), fq, stream);
   const hipError_t e = launch_gemm(dx, stream);
   return e != hipSuccess ? e : launch_gemm(dw, stream);
 }

@@ -894,230 +894,52 @@ __device__ __forceinline__ void barrier_vm() {
 //
 // kFwd: the forward y = x @ W^T (P = x rows, Q = W[g] rows, both k-major,
 // the contraction running along K, the columns of both).
-template <class C, int PF, int PA, int QF, int QA, bool kDW, bool kFwd = false>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_kernel(Params p) {
+// Operand paths and LDS buffers of one instantiation.
+template <class C, int PF, int PA, int QF, int QA, bool kDW, bool kFwd>
+struct GemmShape {
   static_assert(!(kFwd && kDW), "the forward lists its tiles as grad_X does");
-  constexpr bool PK = !kDW;                                      // P k-major in dx and the forward, mn-major in dw
-  constexpr bool QK = kFwd;                                      // Q k-major in the forward only
-  constexpr bool PD = PF == BF16;                                // P loaded straight into LDS
+  static constexpr bool PK = !kDW;                               // P k-major in dx and the forward, mn-major in dw
+  static constexpr bool QK = kFwd;                               // Q k-major in the forward only
+  static constexpr bool PD = PF == BF16;                         // P loaded straight into LDS
   // Q straight into LDS too when both operands are bf16 and three Q stages fit.
-  constexpr bool QD = PD && QF == BF16 && 3 * Direct<PK, C::BP>::BUF_BYTES + 3 * Direct<QK, C::BQ>::BUF_BYTES <= kMaxLds;
+  static constexpr bool QD =
+      PD && QF == BF16 && 3 * Direct<PK, C::BP>::BUF_BYTES + 3 * Direct<QK, C::BQ>::BUF_BYTES <= kMaxLds;
   using LP = std::conditional_t<PD, Direct<PK, C::BP>, Decoded<PF, PA, PK, C::BP>>;
   // A decoded k-major Q tile drops its row padding when two padded buffers
   // would not fit beside P's.
-  constexpr bool QSWZ = QK && !QD && (PD ? 3 : 2) * LP::BUF_BYTES + 2 * C::BQ * (BK + 8) * 2 > kMaxLds;
+  static constexpr bool QSWZ = QK && !QD && (PD ? 3 : 2) * LP::BUF_BYTES + 2 * C::BQ * (BK + 8) * 2 > kMaxLds;
   using LQ = std::conditional_t<QD, Direct<QK, C::BQ>, Decoded<QF, QA, QK, C::BQ, QSWZ>>;
-  constexpr int PERIOD = PD ? 3 : 2;                             // slabs per iteration = register stages
-  constexpr int PBUF = LP::BUF_BYTES, QBUF = LQ::BUF_BYTES;
-  constexpr int SB = C::WP * C::WQ * 2;                          // epilogue staging bytes per wave
-  constexpr int QBUF0 = QD ? (QBUF > SB ? QBUF : SB) : 2 * QBUF; // Q buffer 0 (also wave 3's staging)
+  static constexpr int PBUF = LP::BUF_BYTES, QBUF = LQ::BUF_BYTES;
+  static constexpr int SB = C::WP * C::WQ * 2;                   // epilogue staging bytes per wave
+  static constexpr int QBUF0 = QD ? (QBUF > SB ? QBUF : SB) : 2 * QBUF;   // Q buffer 0 (also wave 3's staging)
+  // Bytes of the six LDS buffers sp0, sp1, sp2, sq0, sq1, sq2.
+  static constexpr int SP0 = PD ? PBUF : 2 * PBUF, SP1 = PD ? PBUF : 16, SP2 = PD ? PBUF : 16;
+  static constexpr int SQ0 = QBUF0, SQ1 = QD ? QBUF : 16, SQ2 = QD ? QBUF : 16;
   static_assert((PD ? 3 * PBUF : 2 * PBUF) + QBUF0 + (QD ? 2 * QBUF : 0) <= kMaxLds, "LDS budget");
   static_assert(kMaxGroups * 4 <= PBUF, "group ends alias P buffer 0");
-  __shared__ __attribute__((aligned(1024))) uint8_t sp0[PD ? PBUF : 2 * PBUF];
-  __shared__ __attribute__((aligned(1024))) uint8_t sp1[PD ? PBUF : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t sp2[PD ? PBUF : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t sq0[QBUF0];
-  __shared__ __attribute__((aligned(1024))) uint8_t sq1[QD ? QBUF : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t sq2[QD ? QBUF : 16];
+};
 
-  // Per slab, in issue order: direct loads (P, then Q), register loads (P,
-  // then Q).
-  constexpr int nDP = (PD ? LP::VMEM : 0) + (QD ? LQ::VMEM : 0);
-  constexpr int nL = (PD ? 0 : LP::VMEM) + (QD ? 0 : LQ::VMEM);
-  constexpr int NIS = LP::ITEMS + LQ::ITEMS;
-  constexpr int ND = LP::DECODES + LQ::DECODES;
-  constexpr int DS0 = C::FP * C::FQ / 2;                         // first decode slot
-  constexpr int FP = C::FP, FQ = C::FQ, NM = FP * FQ;
-  using FAP = FragAddr<PK, PD, C::BP, FP>;
-  using FAQ = FragAddr<QK, QK && (QD || QSWZ), C::BQ, FQ>;
-  constexpr int NRP = FAP::NREAD, NRQ = FAQ::NREAD, NR = FP * NRP + NRQ * FQ;
-  // The barrier of slab k needs this wave's direct loads of slab k+1 (issued
-  // in slab k-1, ahead of its register loads); vmcnt lets the loads issued
-  // after them stay outstanding (loads complete in order).
-  constexpr int NV_LOOP = PD ? nDP + 2 * nL : 63;
-  constexpr int NV_PRO = PD ? nDP + (PERIOD - 1) * nL : 63;
+// One output tile: hw is the workgroup's index among p.ntiles (see
+// select_tile); sp0 .. sq2 are the six LDS buffers of GemmShape, separate
+// variables of the calling kernel.
+template <class C, int PF, int PA, int QF, int QA, bool kDW, bool kFwd = false>
+__device__ __forceinline__ void gemm_tile(const Params& p, int hw, uint8_t* sp0, uint8_t* sp1, uint8_t* sp2,
+                                          uint8_t* sq0, uint8_t* sq1, uint8_t* sq2) {
+  using G = GemmShape<C, PF, PA, QF, QA, kDW, kFwd>;
+#include "lp_gemm_tile_body.inc"
+}
 
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wp = wave >> 1, wq = wave & 1;
-  const Tile t = select_tile<C, kDW>(p, reinterpret_cast<int32_t*>(sp0));
-  if (!t.valid) return;
-  __syncthreads();                                               // group ends read; buffer 0 reusable
-  const int kend = t.kend, kbeg = t.kbeg;
-
-  // dx: P = grad rows [p0, pend) (k-major), Q = W[g] columns from q0.
-  // dw: P = grad columns from p0, Q = X columns from q0, rows [kbeg, kend).
-  // forward: P = x rows [p0, pend), Q = W[g] rows from q0 (both k-major).
-  LP lp;
-  LQ lq;
-  if constexpr (PD) lp.init(p.P, 0, t.p0, kDW ? 0 : p.P.rows, wave, lane);
-  else lp.init(p.P, 0, t.p0, kDW ? 0 : p.P.rows, tid);
-  if constexpr (QD) lq.init(p.Q, kDW ? 0 : t.g, t.q0, QK ? p.Q.rows : 0, wave, lane);
-  else lq.init(p.Q, kDW ? 0 : t.g, t.q0, QK ? p.Q.rows : 0, tid);
-  FAP fap;
-  FAQ faq;
-  fap.init(wp * C::WP, lane);
-  faq.init(wq * C::WQ, lane);
-
-  // P buffer of slab k (B = k mod 3 when direct, else k's parity at run time).
-  auto pbuf = [&](auto bi, int k) -> uint8_t* {
-    constexpr int B = decltype(bi)::value % 3;
-    if constexpr (!PD) return sp0 + (k & 1) * PBUF;
-    else if constexpr (B == 0) return sp0;
-    else if constexpr (B == 1) return sp1;
-    else return sp2;
-  };
-  // Q buffer of slab k (B = k mod 3 when direct, else k's parity).
-  auto qbuf = [&](auto bi, int k) -> uint8_t* {
-    constexpr int B = decltype(bi)::value % 3;
-    if constexpr (!QD) return sq0 + (k & 1) * QBUF;
-    else if constexpr (B == 0) return sq0;
-    else if constexpr (B == 1) return sq1;
-    else return sq2;
-  };
-
-  f32x16 acc[FP][FQ];
-#pragma unroll
-  for (int i = 0; i < FP; ++i)
-#pragma unroll
-    for (int j = 0; j < FQ; ++j) acc[i][j] = f32x16{};
-
-  i16x8v fr[2][FP + FQ];             // two fragment sets: P fragments, then Q fragments
-  typename LP::Stage ps[PERIOD];
-  typename LQ::Stage qs[PERIOD];
-
-  // Load item n into register stage ST (direct items: into LDS buffers pb,
-  // qb; direct Q items take window qwd, register Q items window qw).
-  auto issue = [&](auto ni, auto sti, const typename LP::Win& pw, const typename LQ::Win& qwd,
-                   const typename LQ::Win& qw, uint8_t* pb, uint8_t* qb) {
-    constexpr int n = decltype(ni)::value, ST = decltype(sti)::value;
-    if constexpr (n < LP::ITEMS) {
-      if constexpr (PD) lp.template load<n>(pb, pw);
-      else lp.template load<n>(ps[ST], pw, p.P);
-    } else if constexpr (QD) {
-      lq.template load<n - LP::ITEMS>(qb, qwd);
-    } else {
-      lq.template load<n - LP::ITEMS>(qs[ST], qw, p.Q);
-    }
-  };
-  // Decode item n of register stage ST into LDS buffers pb / qb.
-  DecState dst;
-  auto decode = [&](auto ni, auto sti, uint8_t* pb, uint8_t* qb) {
-    constexpr int n = decltype(ni)::value, ST = decltype(sti)::value;
-    if constexpr (n < LP::DECODES) {
-      if constexpr (!PD) {
-        constexpr int QU = LP::QUARTERS, piece = n / QU;
-        lp.template decode<piece / LP::PIECES, piece % LP::PIECES, n % QU>(ps[ST], pb, dst);
-      }
-    } else if constexpr (!QD) {
-      constexpr int m = n - LP::DECODES, QU = LQ::QUARTERS, piece = m / QU;
-      lq.template decode<piece / LQ::PIECES, piece % LQ::PIECES, m % QU>(qs[ST], qb, dst);
-    }
-  };
-  // Fragment read r of substep S into fragment set SET, in the order the
-  // MFMAs consume them: P0, Q0 .. Q(FQ-1), P1 .. P(FP-1).
-  auto read = [&](auto ri, auto si, auto seti, const uint8_t* pb, const uint8_t* qb) {
-    constexpr int r = decltype(ri)::value, S = decltype(si)::value, SET = decltype(seti)::value;
-    if constexpr (r < NRP) {
-      fap.template read<S, r, 0>(pb, fr[SET][0]);
-    } else if constexpr (r < NRP + NRQ * FQ) {
-      constexpr int j = (r - NRP) / NRQ, h = (r - NRP) % NRQ;
-      faq.template read<S, h, j>(qb, fr[SET][FP + j]);
-    } else {
-      constexpr int i = 1 + (r - NRP - NRQ * FQ) / NRP, h = (r - NRP - NRQ * FQ) % NRP;
-      fap.template read<S, h, i>(pb, fr[SET][i]);
-    }
-  };
-  auto mfma = [&](auto mi, auto seti) {
-    constexpr int m = decltype(mi)::value, SET = decltype(seti)::value;
-    constexpr int i = m / FQ, j = m % FQ;
-    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fr[SET][FP + j]),
-                                                        __builtin_bit_cast(bf16x8, fr[SET][i]), acc[i][j], 0, 0, 0);
-  };
-
-  const int nk = (kend - kbeg + BK - 1) / BK;
-  if (nk > 0) {
-    // Prologue: register loads of slabs 0 .. PERIOD-1 and direct loads of
-    // slabs 0 and 1 issued; slab 0 decoded; substep-0 fragments read.  The
-    // order (register loads of slab s, then direct loads of slab s) repeats
-    // the loop's (direct loads of k+2, register loads of k+3), so that the
-    // compiler's wait counts agree on both ways into the loop.
-    static_for<PERIOD>([&](auto si) {
-      constexpr int s = decltype(si)::value;
-      const auto pw = lp.window(p.P, kbeg + s * BK, kend);
-      const auto qw = lq.window(p.Q, kbeg + s * BK, kend);
-      static_for<2>([&](auto pass) {                                 // register items, then direct items
-        static_for<NIS>([&](auto n) {
-          constexpr int item = decltype(n)::value;
-          constexpr bool dir = (PD && item < LP::ITEMS) || (QD && item >= LP::ITEMS);
-          if constexpr (dir == (decltype(pass)::value == 1) && !(dir && s >= 2))
-            issue(IC<item>{}, si, pw, qw, qw, pbuf(si, s), qbuf(si, s));
-        });
-      });
-    });
-    static_for<ND>([&](auto n) { decode(n, IC<0>{}, pbuf(IC<0>{}, 0), qbuf(IC<0>{}, 0)); });
-    barrier_vm<NV_PRO>();
-    static_for<NR>([&](auto r) { read(r, IC<0>{}, IC<0>{}, pbuf(IC<0>{}, 0), qbuf(IC<0>{}, 0)); });
-  }
-
-  // Slab k = kt + J: multiply P buffer (k) and Q buffer (k); issue the
-  // register loads of slab k + PERIOD into stage J and the direct loads of
-  // slab k + 2; decode slab k + 1 from stage (J + 1) % PERIOD.
-  auto slab = [&](auto ji, int k) {
-    constexpr int J = decltype(ji)::value;
-    constexpr int JN = (J + 1) % PERIOD;
-    const uint8_t* const pcur = pbuf(ji, k);
-    const uint8_t* const qcur = qbuf(ji, k);
-    uint8_t* const pnxt = pbuf(IC<J + 1>{}, k + 1);
-    uint8_t* const qnxt = qbuf(IC<J + 1>{}, k + 1);
-    uint8_t* const pdst = pbuf(IC<J + 2>{}, k + 2);
-    uint8_t* const qdst = qbuf(IC<J + 2>{}, k + 2);
-    const auto pw = lp.window(p.P, kbeg + (k + (PD ? 2 : PERIOD)) * BK, kend);
-    const auto qw = lq.window(p.Q, kbeg + (k + (QD ? 2 : PERIOD)) * BK, kend);
-
-    static_for<4>([&](auto si) {
-      constexpr int S = decltype(si)::value;
-      constexpr int CUR = S & 1, NXT = CUR ^ 1;
-      static_for<NM>([&](auto mi) {
-        constexpr int m = decltype(mi)::value;
-        mfma(mi, IC<CUR>{});
-        if constexpr (S == 3 && m == 0) barrier_vm<NV_LOOP>();
-        if constexpr (S < 3) {
-          static_for<NR>([&](auto ri) {                              // reads spread over the substep
-            if constexpr (decltype(ri)::value * NM / NR == m) read(ri, IC<S + 1>{}, IC<NXT>{}, pcur, qcur);
-          });
-        } else if constexpr (m > 0) {
-          static_for<NR>([&](auto ri) {                              // next slab's substep 0
-            if constexpr (1 + decltype(ri)::value * (NM - 1) / NR == m) read(ri, IC<0>{}, IC<0>{}, pnxt, qnxt);
-          });
-        }
-        if constexpr (S < 3) {                                       // loads spread over substeps 0-2
-          static_for<NIS>([&](auto ni) {
-            if constexpr (decltype(ni)::value * 3 * NM / NIS == S * NM + m) issue(ni, ji, pw, qw, qw, pdst, qdst);
-          });
-        }
-        if constexpr (S < 3) {                                       // decode from mid substep 0 on
-          static_for<ND>([&](auto di) {
-            if constexpr (DS0 + decltype(di)::value * (3 * NM - DS0) / ND == S * NM + m) decode(di, IC<JN>{}, pnxt, qnxt);
-          });
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      });
-    });
-  };
-
-  for (int kt = 0; kt < nk; kt += PERIOD) {
-    static_for<PERIOD>([&](auto ji) { slab(ji, kt + decltype(ji)::value); });
-  }
-  // No direct load may still be writing LDS when the workgroup ends, and no
-  // wave may still read a buffer the staging below overwrites.
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-  __syncthreads();
-  static_assert(PD ? (PBUF >= SB && QBUF0 >= SB) : (2 * PBUF >= 2 * SB && QBUF0 >= 2 * SB), "staging fits");
-  if (p.splits > 1 && !reduce_split<C>(p, t, acc, wave, lane, reinterpret_cast<uint32_t*>(sq0))) return;
-  uint8_t* stage = PD ? (wave == 0 ? sp0 : wave == 1 ? sp1 : wave == 2 ? sp2 : sq0)
-                      : (wave < 2 ? sp0 + wave * SB : sq0 + (wave - 2) * SB);
-  store_acc<C, kDW>(p, t, acc, wp, wq, lane, stage);
+template <class C, int PF, int PA, int QF, int QA, bool kDW, bool kFwd = false>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_kernel(Params p) {
+  using G = GemmShape<C, PF, PA, QF, QA, kDW, kFwd>;
+  __shared__ __attribute__((aligned(1024))) uint8_t sp0[G::SP0];
+  __shared__ __attribute__((aligned(1024))) uint8_t sp1[G::SP1];
+  __shared__ __attribute__((aligned(1024))) uint8_t sp2[G::SP2];
+  __shared__ __attribute__((aligned(1024))) uint8_t sq0[G::SQ0];
+  __shared__ __attribute__((aligned(1024))) uint8_t sq1[G::SQ1];
+  __shared__ __attribute__((aligned(1024))) uint8_t sq2[G::SQ2];
+  const int hw = blockIdx.x;
+#include "lp_gemm_tile_body.inc"
 }
 
 template <class C, int PF, int PA, int QF, int QA, bool kDW, bool kFwd = false>
@@ -1178,6 +1000,10 @@ hipError_t fwd_mx(const Params& prm, bool fp4, hipStream_t s);
 hipError_t fwd_dec(const Params& prm, int fmt_x, int fmt_w, bool narrow, hipStream_t s);
 // Both of them in one launch (X and W in the same format fmt_q).
 hipError_t pt_pair(const Params& dx, const Params& dw, int fmt_p, int fmt_q, hipStream_t s);
+// Grouped grad_X and grad_W of a bf16 gradient through 256 x 256 bf16 tiles
+// in one launch, grad_X's tiles first; W and X both LP_MXFP4 or both
+// LP_NVFP4 (fmt_q), scaled along their last axis.
+hipError_t dec_pair(const Params& dx, const Params& dw, int fmt_q, hipStream_t s);
 
 }  // namespace gk
 }  // namespace lp

@@ -410,6 +410,40 @@ def test_grouped_round_split(lp, fmt, K, sizes):
     assert np.all(bits_host(dx[end:]) == 0xFFFF), "rows past the last offset were written"
 
 
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+def test_grouped_pair_launch(lp, fmt):
+    """Grouped dX + dW with FP4 X and W and more 256 x 256 tiles than compute
+    units in both products (dX 34 row tiles x 8 column tiles, dW 4 groups x
+    8 x 8 tiles) run as one launch, grad_X's tiles first: both results equal
+    the dX-only and dW-only calls bit for bit (rows past the last offset
+    kept, an empty group's grad_W zero) and the oracle on sampled rows."""
+    sizes = [4000, 0, 4300, 1]
+    G, N, K = len(sizes), 2048, 2048
+    M = int(sum(sizes)) + 40
+    offsets = W.cumulative_ends(sizes)
+    off = torch.from_numpy(offsets).cuda()
+    g, gb = _grad(lp, 49, M, N)
+    x, xd = _operand(lp, 49, "x", (M, K), fmt, -1)
+    w, wd = _operand(lp, 49, "w", (G, N, K), fmt, -1)
+    dx, dw = lp.lp_grouped_bwd(g, x, w, off, grad_x=_sentinel((M, K)), grad_w=_sentinel((G, N, K)))
+    dx1 = lp.lp_grouped_bwd(g, None, w, off, need_dw=False, grad_x=_sentinel((M, K)))[0]
+    dw1 = lp.lp_grouped_bwd(g, x, None, off, need_dx=False, grad_w=_sentinel((G, N, K)))[1]
+    torch.cuda.synchronize()
+    assert_bits_equal(bits_host(dx), bits_host(dx1), f"{fmt} paired dX vs dX alone")
+    assert_bits_equal(bits_host(dw), bits_host(dw1), f"{fmt} paired dW vs dW alone")
+    end = int(offsets[-1])
+    assert np.all(bits_host(dx[end:]) == 0xFFFF), "rows past the last offset were written"
+    assert np.all(bits_host(dw[1]) == 0), "the empty group's dW is not zero"
+    for gi, (s0, e0) in enumerate(O.group_bounds(offsets)):
+        if e0 == s0:
+            continue
+        rows = s0 + _sample_rows(e0 - s0, 8, 49 + gi)
+        assert_close(dx[torch.from_numpy(rows).cuda()], O.rows_dx(gb, wd[gi], rows), f"{fmt} group {gi} dX rows")
+        nrows = _sample_rows(N, 8, 59 + gi)
+        assert_close(dw[gi][torch.from_numpy(nrows).cuda()], O.rows_dw(gb[s0:e0], xd[0][s0:e0], nrows),
+                     f"{fmt} group {gi} dW rows")
+
+
 def test_grouped_bad_offsets_are_clamped(lp):
     """Offsets out of order or past M are clamped (end_g = clamp(o_g,
     end_{g-1}, M)): the kernels stay in bounds and compute those groups."""
