@@ -197,7 +197,8 @@ def build(lp, name: str):
             dx = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
             dw = torch.empty((w.groups, N, K), dtype=torch.bfloat16, device="cuda")
             sets.append((lp.QTensor("bf16", g, shape=(1, M, N)), xq, wq, dx, dw))
-        phases.append(Phase("grouped_bwd", "gemm_kernel", flops=4.0 * M * N * K))
+        # dX and dW in one launch (grad_X tiles first)
+        phases.append(Phase("grouped_bwd", "gemm_pair_kernel", flops=4.0 * M * N * K))
 
         def step(i, stream):
             gq, xq, wq, dx, dw = sets[i % len(sets)]
