@@ -444,6 +444,44 @@ def test_grouped_pair_launch(lp, fmt):
                      f"{fmt} group {gi} dW rows")
 
 
+def test_grouped_pair_launch_many_groups(lp):
+    """The one-launch grouped dX + dW with 300 groups (more than grad_W ranks
+    by size, so its tiles are dealt round-robin), empty ones among them, and
+    258 grad_X / 600 grad_W tiles of 256 x 256: both results equal the
+    dX-only and dW-only calls bit for bit, and the oracle on sampled rows."""
+    rng = W.rng(50, "route")
+    sizes = rng.integers(0, 221, size=300)
+    sizes[rng.choice(300, size=25, replace=False)] = 0
+    M = int(sizes.sum())
+    if (M + 255) // 256 < 129:                                 # keep 129 row tiles: 258 dX tiles
+        sizes[0] += 129 * 256 - 255 - M
+        M = int(sizes.sum())
+    M += 20
+    G, N, K = len(sizes), 256, 512
+    offsets = W.cumulative_ends(sizes)
+    off = torch.from_numpy(offsets).cuda()
+    g, gb = _grad(lp, 50, M, N)
+    x, xd = _operand(lp, 50, "x", (M, K), "mxfp4", -1)
+    w, wd = _operand(lp, 50, "w", (G, N, K), "mxfp4", -1)
+    dx, dw = lp.lp_grouped_bwd(g, x, w, off)
+    dx1 = lp.lp_grouped_bwd(g, None, w, off, need_dw=False)[0]
+    dw1 = lp.lp_grouped_bwd(g, x, None, off, need_dx=False)[1]
+    torch.cuda.synchronize()
+    end = int(offsets[-1])
+    assert_bits_equal(bits_host(dx[:end]), bits_host(dx1[:end]), "paired dX vs dX alone")
+    assert_bits_equal(bits_host(dw), bits_host(dw1), "paired dW vs dW alone")
+    bounds = O.group_bounds(offsets)
+    for gi in [int(i) for i in np.flatnonzero(sizes)[::37]]:
+        s0, e0 = bounds[gi]
+        rows = s0 + _sample_rows(e0 - s0, 4, 60 + gi)
+        assert_close(dx[torch.from_numpy(rows).cuda()], O.rows_dx(gb, wd[gi], rows), f"group {gi} dX rows")
+        nrows = _sample_rows(N, 4, 70 + gi)
+        assert_close(dw[gi][torch.from_numpy(nrows).cuda()], O.rows_dw(gb[s0:e0], xd[0][s0:e0], nrows),
+                     f"group {gi} dW rows")
+    for gi in np.flatnonzero(sizes == 0)[:5]:
+        assert np.all(bits_host(dw[int(gi)]) == 0), f"empty group {gi}'s dW is not zero"
+
+
 def test_grouped_bad_offsets_are_clamped(lp):
     """Offsets out of order or past M are clamped (end_g = clamp(o_g,
     end_{g-1}, M)): the kernels stay in bounds and compute those groups."""
