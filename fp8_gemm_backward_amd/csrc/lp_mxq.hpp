@@ -62,6 +62,40 @@ __device__ __forceinline__ uint32_t to_e2m1x2(float a, float b) {
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a, b, 1.0f, 0) & 0xFFu;
 }
 
+// E4M3 codes of bf16 pairs by the scaled bf16 conversion, without fp32
+// arithmetic.  For a block scale byte b (not 0xFF) each magnitude is first
+// clamped to 448 * 2^(b - 127), the largest that stays in range (the
+// conversion does not saturate), on the bit patterns: a signed 16-bit min
+// clamps positive values and leaves negative ones, an unsigned min against
+// sign | threshold clamps negative ones.  The conversion then takes off the
+// power of two in its scale operand's exponent field (b) and rounds to
+// nearest even: the codes to_e4m3x2 gives for the elements times s.inv.
+struct E4M3Scale {
+  float sc;       // scale operand: exponent field b
+  uint32_t thr;   // bf16 bits of 448 * 2^(b - 127), in both halves
+};
+__device__ __forceinline__ E4M3Scale e4m3_scale(uint32_t byte) {
+  E4M3Scale q;
+  q.sc = __builtin_bit_cast(float, byte << 23);
+  q.thr = (((byte + 8u) << 7) | 0x60u) * 0x00010001u;   // b <= 246 for a finite block
+  return q;
+}
+// The pair w (low element first) clamped and converted into the high
+// (kHi) or low half of old (the other half kept).
+template <bool kHi>
+__device__ __forceinline__ uint32_t e4m3x2_scaled(uint32_t old, uint32_t w, const E4M3Scale& q) {
+  typedef short s16x2v __attribute__((ext_vector_type(2)));
+  typedef unsigned short u16x2v __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  const uint32_t pos = __builtin_bit_cast(
+      uint32_t, __builtin_elementwise_min(__builtin_bit_cast(s16x2v, w), __builtin_bit_cast(s16x2v, q.thr)));
+  const uint32_t c = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2v, pos),
+                                                                          __builtin_bit_cast(u16x2v, q.thr | 0x80008000u)));
+  const s16x2v r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(__builtin_bit_cast(s16x2v, old),
+                                                             __builtin_bit_cast(bf16x2v, c), q.sc, kHi);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
 // NaN codes of a bad block: E4M3 0x7F with each element's sign; E2M1 0.
 __device__ __forceinline__ uint32_t nan_e4m3x2(uint32_t w) {
   return 0x7F7Fu | ((w >> 8) & 0x80u) | ((w >> 16) & 0x8000u);

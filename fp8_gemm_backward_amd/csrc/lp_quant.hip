@@ -60,13 +60,13 @@ __global__ __launch_bounds__(kThreads) void mx_quant_cols(const u32x4* __restric
     const BlockScale s = block_scale<kFp4>(amax);
     if ((threadIdx.x & 3) == 0) scales[u >> 2] = (uint8_t)s.byte;
     if constexpr (!kFp4) {
+      const E4M3Scale q = e4m3_scale(s.byte);
       uint32_t o[2];
 #pragma unroll
       for (int k = 0; k < 4; k += 2) {
         const uint32_t w0 = v[j][k], w1 = v[j][k + 1];
-        const uint32_t lo = s.bad ? nan_e4m3x2(w0) : to_e4m3x2(bf16_lo(w0) * s.inv, bf16_hi(w0) * s.inv);
-        const uint32_t hi = s.bad ? nan_e4m3x2(w1) : to_e4m3x2(bf16_lo(w1) * s.inv, bf16_hi(w1) * s.inv);
-        o[k / 2] = lo | (hi << 16);
+        const uint32_t c = e4m3x2_scaled<true>(e4m3x2_scaled<false>(w0, w0, q), w1, q);
+        o[k / 2] = s.bad ? (nan_e4m3x2(w0) | (nan_e4m3x2(w1) << 16)) : c;
       }
       __builtin_nontemporal_store(u32x2{o[0], o[1]}, codes + u);
     } else {
@@ -194,24 +194,42 @@ __device__ __forceinline__ void quant_tile32(const uint16_t* __restrict__ src, u
   if (ri == 0) *reinterpret_cast<u32x2*>(scales_r + (size_t)rb * cols + c0) = u32x2{sbytes[0], sbytes[1]};
   const size_t row_bytes = kFp4 ? cols / 2 : cols;
   uint8_t* out_r = codes_r + row0 * row_bytes + (kFp4 ? c0 / 2 : c0);
+  if constexpr (!kFp4) {
+    // E4M3 along the rows, two rows at a time: column c's elements of rows
+    // r and r + 1 form one pair under column c's scale, so each conversion
+    // takes one scale; byte permutes then regroup the codes by row.  A block
+    // with a NaN or an infinity (any in the wave: a uniform branch) gets the
+    // NaN codes afterwards.
+    E4M3Scale q[8];
+    uint32_t badc = 0;
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    if constexpr (!kFp4) {
-      uint32_t o[2];
+    for (int c = 0; c < 8; ++c) {
+      q[c] = e4m3_scale(s[c].byte);
+      badc |= (s[c].bad ? 1u : 0u) << c;
+    }
+    const bool anybad = __builtin_amdgcn_ballot_w64(badc != 0) != 0;
 #pragma unroll
-      for (int k = 0; k < 4; k += 2) {
-        const uint32_t w0 = v[r][k], w1 = v[r][k + 1];
-        const int c = 2 * k;
-        const uint32_t p0 = to_e4m3x2(bf16_lo(w0) * s[c].inv, bf16_hi(w0) * s[c + 1].inv);
-        const uint32_t p1 = to_e4m3x2(bf16_lo(w1) * s[c + 2].inv, bf16_hi(w1) * s[c + 3].inv);
-        const uint32_t b0 = s[c].bad ? (0x7Fu | ((w0 >> 8) & 0x80u)) : (p0 & 0xFFu);
-        const uint32_t b1 = s[c + 1].bad ? (0x7Fu | ((w0 >> 24) & 0x80u)) : (p0 >> 8);
-        const uint32_t b2 = s[c + 2].bad ? (0x7Fu | ((w1 >> 8) & 0x80u)) : (p1 & 0xFFu);
-        const uint32_t b3 = s[c + 3].bad ? (0x7Fu | ((w1 >> 24) & 0x80u)) : (p1 >> 8);
-        o[k / 2] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+    for (int r = 0; r < 8; r += 2) {
+      uint32_t x[4];                      // x[k]: bytes (r, 2k), (r+1, 2k), (r, 2k+1), (r+1, 2k+1)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t pe = __builtin_amdgcn_perm(v[r + 1][k], v[r][k], 0x05040100u);   // column 2k, rows r, r+1
+        const uint32_t po = __builtin_amdgcn_perm(v[r + 1][k], v[r][k], 0x07060302u);   // column 2k+1
+        x[k] = e4m3x2_scaled<false>(pe, pe, q[2 * k]);
+        x[k] = e4m3x2_scaled<true>(x[k], po, q[2 * k + 1]);
+        if (__builtin_expect(anybad, false)) {
+          if ((badc >> (2 * k)) & 1u) x[k] = (x[k] & 0xFFFF0000u) | nan_e4m3x2(pe);
+          if ((badc >> (2 * k + 1)) & 1u) x[k] = (x[k] & 0xFFFFu) | (nan_e4m3x2(po) << 16);
+        }
       }
-      __builtin_nontemporal_store(u32x2{o[0], o[1]}, reinterpret_cast<u32x2*>(out_r + (size_t)r * row_bytes));
-    } else {
+      const u32x2 lo = {__builtin_amdgcn_perm(x[1], x[0], 0x06040200u), __builtin_amdgcn_perm(x[3], x[2], 0x06040200u)};
+      const u32x2 hi = {__builtin_amdgcn_perm(x[1], x[0], 0x07050301u), __builtin_amdgcn_perm(x[3], x[2], 0x07050301u)};
+      __builtin_nontemporal_store(lo, reinterpret_cast<u32x2*>(out_r + (size_t)r * row_bytes));
+      __builtin_nontemporal_store(hi, reinterpret_cast<u32x2*>(out_r + (size_t)(r + 1) * row_bytes));
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
       uint32_t o = 0;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -238,13 +256,14 @@ __device__ __forceinline__ void quant_tile32(const uint16_t* __restrict__ src, u
       const BlockScale sr = block_scale<kFp4>(quad_max(m));
       if (ci == (uint32_t)(r >> 1)) sc_c[(size_t)r * (cols / 32)] = (uint8_t)sr.byte;   // two rows per lane
       if constexpr (!kFp4) {
+        // E4M3 along the columns: the row's one scale for all eight values.
+        const E4M3Scale q = e4m3_scale(sr.byte);
         uint32_t o[2];
 #pragma unroll
         for (int k = 0; k < 4; k += 2) {
           const uint32_t w0 = v[r][k], w1 = v[r][k + 1];
-          const uint32_t lo = sr.bad ? nan_e4m3x2(w0) : to_e4m3x2(bf16_lo(w0) * sr.inv, bf16_hi(w0) * sr.inv);
-          const uint32_t hi = sr.bad ? nan_e4m3x2(w1) : to_e4m3x2(bf16_lo(w1) * sr.inv, bf16_hi(w1) * sr.inv);
-          o[k / 2] = lo | (hi << 16);
+          const uint32_t c = e4m3x2_scaled<true>(e4m3x2_scaled<false>(w0, w0, q), w1, q);
+          o[k / 2] = sr.bad ? (nan_e4m3x2(w0) | (nan_e4m3x2(w1) << 16)) : c;
         }
         __builtin_nontemporal_store(u32x2{o[0], o[1]}, reinterpret_cast<u32x2*>(out_c + (size_t)r * row_bytes));
       } else {
