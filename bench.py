@@ -18,8 +18,8 @@ synthetic input already resident in HBM:
                   + lp_linear_bwd dX, dW against E4M3 X and W (per-tensor scales)
   mxfp4_forward   lp_linear_fwd: y = X @ W^T, MXFP4 X 8192x4096 and W 4096x4096 (the forward
                   the FP4 backward pairs with, on the block-scaled FP4 MFMA)
-  nvfp4_forward   lp_linear_fwd: y = X @ W^T, NVFP4 X 8192x4096 and W 4096x4096, decoded to bf16
-                  inside the contraction
+  nvfp4_forward   lp_dequant of NVFP4 X 8192x4096 to bf16, then lp_linear_fwd: y = X @ W^T
+                  against the NVFP4 W 4096x4096, decoded inside the contraction
   fp8_grouped_forward  lp_grouped_fwd: bf16 X 16384x4096 against 8 block-FP8 experts
                   8x2048x4096 (the FP8-adapter page's grouped forward)
   mxfp4_tiny      lp_linear_bwd: dX and dW, 64 x 128 x 128
@@ -350,13 +350,23 @@ def build(lp, name: str):
             c, s, ts = nvfp4_quant_torch(_randn((N, K), w.w_sigma, 8400 + i))
             wq = lp.QTensor("nvfp4", c, s, ts, shape=(1, N, K))
             sets.append((xq, wq, torch.empty((M, N), dtype=torch.bfloat16, device="cuda")))
-        phases.append(Phase("linear_fwd", "gemm_kernel", flops=2.0 * M * N * K))
+        # X is decoded once per step into a bf16 copy (lp_dequant), then the
+        # forward contracts it with the NVFP4 weight, decoded inside the tiles.
+        # Decoding X inside the contraction instead repeats it in each of the
+        # 16 column tiles that read it; the results are bit-identical.
+        xbf = torch.empty((1, M, K), dtype=torch.bfloat16, device="cuda")
+        xbq = lp.QTensor("bf16", xbf, shape=(1, M, K))
+        phases.append(Phase("dequant X", "dequant_nvfp4", nbytes=M * K * (0.5 + 1 / 16 + 2)))
+        phases.append(Phase("linear_fwd (bf16 X)", "gemm_kernel", flops=2.0 * M * N * K))
 
         def step(i, stream):
             xq, wq, y = sets[i % len(sets)]
             ev = _events(stream)
-            lp.lp_linear_fwd(xq, wq, y=y, stream=stream)
-            return [ev.stop(stream)]
+            lp.lp_dequant(xq, xbf, stream=stream)
+            t0 = ev.stop(stream)
+            ev = _events(stream)
+            lp.lp_linear_fwd(xbq, wq, y=y, stream=stream)
+            return [t0, ev.stop(stream)]
         standalone = []
     elif name == "fp8_grouped_forward":
         offsets = torch.from_numpy(W.cumulative_ends(W.group_sizes(w))).cuda()

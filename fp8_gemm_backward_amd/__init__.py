@@ -419,7 +419,7 @@ def lp_grouped_bwd(grad_out: QTensor, x: Optional[QTensor], w: Optional[QTensor]
 
 def lp_linear_fwd(x: QTensor, w: QTensor, y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """y [M, N] = x @ w^T: both "mxfp4" or both "mxfp8" (scaled along k),
-    both "nvfp4", or a "bf16" x with a "bf16" or "fp8_b128" weight."""
+    both "nvfp4", or a "bf16" x with a "bf16", "fp8_b128" or "nvfp4" weight."""
     if y is None:
         y = torch.empty((x.rows, w.rows), dtype=torch.bfloat16, device=x.codes.device)
     _device(y, "y", 2 * x.rows * w.rows)

@@ -350,11 +350,12 @@ static lp_status check_fwd(const lp_qtensor* x, const lp_qtensor* w, void* y, in
   if ((st = check_tensor(w)) != LP_OK) return st;
   const bool mx = (x->fmt == LP_MXFP4 || x->fmt == LP_MXFP8) && w->fmt == x->fmt;
   const bool nv = x->fmt == LP_NVFP4 && w->fmt == LP_NVFP4;
-  const bool b16 = x->fmt == LP_BF16 && (w->fmt == LP_BF16 || w->fmt == LP_FP8_B128);
+  const bool b16 = x->fmt == LP_BF16 && (w->fmt == LP_BF16 || w->fmt == LP_FP8_B128 || w->fmt == LP_NVFP4);
   if (!mx && !nv && !b16) return LP_ERR_FORMAT;
   if ((mx || nv) && (x->scale_axis != -1 || w->scale_axis != -1)) return LP_ERR_FORMAT;
+  if (w->fmt == LP_NVFP4 && w->scale_axis != -1) return LP_ERR_FORMAT;
   if (x->batch != 1 || w->batch != (groups ? groups : 1) || w->cols != x->cols) return LP_ERR_SHAPE;
-  const int64_t kmul = x->fmt == LP_MXFP4 ? 128 : x->fmt == LP_MXFP8 ? 64 : nv ? 32 : 16;
+  const int64_t kmul = x->fmt == LP_MXFP4 ? 128 : x->fmt == LP_MXFP8 ? 64 : w->fmt == LP_NVFP4 ? 32 : 16;
   if (x->cols % kmul || w->rows % 16) return LP_ERR_SHAPE;
   if (x->rows >= kMaxProductRows || x->cols >= kMaxProductCols || w->rows >= kMaxProductCols) return LP_ERR_SHAPE;
   if (!tiles_ok(x->rows / 128 + (groups ? groups : 1) + 1, w->rows)) return LP_ERR_SHAPE;

@@ -9,7 +9,9 @@
 // unwritten).  "Add Autograd Backward Support for FP4 GEMM Custom Ops": the
 // f4f4bf16 forward ops multiply FP4 inputs by FP4 weights into BF16.  Each
 // quantized operand is decoded to bf16 inside the contraction, as the
-// backward decodes it, and contracted on the bf16 MFMA with fp32 sums.
+// backward decodes it, and contracted on the bf16 MFMA with fp32 sums.  A
+// bf16 x with an NVFP4 weight is the same product with x decoded
+// beforehand (lp_dequant), once rather than in every tile that reads it.
 #include "lp_gemm_kernel.hpp"
 
 namespace lp {
@@ -22,6 +24,9 @@ hipError_t fwd_dec(const Params& prm, int fmt_x, int fmt_w, bool narrow, hipStre
   if (fmt_x == LP_BF16 && fmt_w == LP_FP8_B128)
     return narrow ? run<Narrow, BF16, -1, FP8_B128, -1, false, true>(prm, s)
                   : run<Big, BF16, -1, FP8_B128, -1, false, true>(prm, s);
+  if (fmt_x == LP_BF16 && fmt_w == LP_NVFP4)
+    return narrow ? run<Narrow, BF16, -1, NVFP4, -1, false, true>(prm, s)
+                  : run<Big, BF16, -1, NVFP4, -1, false, true>(prm, s);
   if (fmt_x == LP_NVFP4 && fmt_w == LP_NVFP4)
     return narrow ? run<Narrow, NVFP4, -1, NVFP4, -1, false, true>(prm, s)
                   : run<Big, NVFP4, -1, NVFP4, -1, false, true>(prm, s);

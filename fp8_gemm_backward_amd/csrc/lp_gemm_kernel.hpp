@@ -994,8 +994,8 @@ hipError_t dw_pt(const Params& prm, int fmt_p, int fmt_q, hipStream_t s);
 // both MXFP8.
 hipError_t fwd_mx(const Params& prm, bool fp4, hipStream_t s);
 // Forward y = x @ w^T through bf16 tiles (fused decode): bf16 x with a bf16
-// weight (256 x 128 tiles) or a block-FP8 weight, NVFP4 x with an NVFP4
-// weight (256 x 256 tiles; 256 x 128 when narrow, the last round of a
+// weight (256 x 128 tiles) or a block-FP8 or NVFP4 weight, NVFP4 x with an
+// NVFP4 weight (256 x 256 tiles; 256 x 128 when narrow, the last round of a
 // split grouped call).
 hipError_t fwd_dec(const Params& prm, int fmt_x, int fmt_w, bool narrow, hipStream_t s);
 // Both of them in one launch (X and W in the same format fmt_q).

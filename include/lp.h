@@ -464,7 +464,9 @@ lp_status lp_grouped_dx_deferred(const lp_qtensor* grad_out, const void* w, int6
  *      K % 128 == 0 (LP_MXFP4) or K % 64 == 0 (LP_MXFP8);
  *    - both LP_NVFP4 (E4M3 scales per 16 along K, each its own tensor
  *      scale); K % 32 == 0;
- *    - x LP_BF16 and w LP_BF16 or LP_FP8_B128; K % 16 == 0.
+ *    - x LP_BF16 and w LP_BF16 or LP_FP8_B128 (K % 16 == 0) or LP_NVFP4
+ *      (scale_axis -1, K % 32 == 0): an NVFP4 x decoded first with
+ *      lp_dequant, which saves the per-tile decode of x.
  *    N % 16 == 0; M >= 0 arbitrary.
  * y  device bf16 [M][N].
  * MX operands: y[m][n] = sum_k dec(x)[m][k] * dec(w)[n][k] on the

@@ -148,7 +148,8 @@ def fwd(x, w, y=FAKE):
     (None, q("mxfp4", 64, 128), FAKE, NULL),
     (q("mxfp4", 64, 128), q("mxfp4", 32, 128), None, NULL),
     (q("mxfp4", 64, 128), q("mxfp8", 32, 128), FAKE, FORMAT),       # formats must agree
-    (q("bf16", 64, 128), q("mxfp4", 32, 128), FAKE, FORMAT),        # bf16 x: bf16 or block-FP8 weight
+    (q("bf16", 64, 128), q("mxfp4", 32, 128), FAKE, FORMAT),        # bf16 x: bf16, block-FP8 or NVFP4 weight
+    (q("bf16", 64, 48), q("nvfp4", 32, 48), FAKE, SHAPE),           # NVFP4 weight: K % 32
     (q("fp8_b128", 64, 128), q("bf16", 32, 128), FAKE, FORMAT),     # the block-FP8 operand is the weight
     (q("nvfp4", 64, 128), q("bf16", 32, 128), FAKE, FORMAT),        # NVFP4 x: NVFP4 weight
     (q("nvfp4", 64, 48), q("nvfp4", 32, 48), FAKE, SHAPE),          # NVFP4: K % 32

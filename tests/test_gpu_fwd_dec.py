@@ -1,5 +1,5 @@
 """Forward y = x @ W^T through bf16 tiles with both operands k-major (GPU):
-a bf16 input with a bf16 or block-FP8 weight ("Train adapters on top of FP8
+a bf16 input with a bf16, block-FP8 or NVFP4 weight ("Train adapters on top of FP8
 weights", FP8LinearFunction.forward and FP8GroupedMatmulFunction.forward)
 and NVFP4 operands on both sides ("Add Autograd Backward Support for FP4 GEMM
 Custom Ops", the f4f4bf16 forward ops), dense and grouped, against the
@@ -16,7 +16,7 @@ from oracle import gemm as O
 
 pytestmark = pytest.mark.gpu
 
-PAIRS = [("bf16", "bf16"), ("bf16", "fp8_b128"), ("nvfp4", "nvfp4")]
+PAIRS = [("bf16", "bf16"), ("bf16", "fp8_b128"), ("nvfp4", "nvfp4"), ("bf16", "nvfp4")]
 
 
 def _make(lp, fmt, v):
@@ -37,6 +37,9 @@ def _make(lp, fmt, v):
 def _reference(fx, fw, xh, wh, offsets=None):
     if fx == "nvfp4":
         return O.nvfp4_fwd(xh[0][0], xh[1][0], xh[2], wh[0], wh[1], wh[2], offsets)
+    if fw == "nvfp4":
+        wb = F.dequant("nvfp4", wh[0], wh[1], wh[2])
+        return O.linear_fwd(xh[0][0], wb[0]) if offsets is None else O.grouped_fwd(xh[0][0], wb, offsets)
     if fw == "fp8_b128":
         return O.fp8_block_fwd(xh[0][0], wh[0], wh[1], offsets)
     return O.linear_fwd(xh[0][0], wh[0][0]) if offsets is None else O.grouped_fwd(xh[0][0], wh[0], offsets)
@@ -50,16 +53,17 @@ def _operands(lp, fx, fw, number, M, N, K, groups=0):
     return xq, xh, wq, wh
 
 
-def _shapes(fx):
+def _shapes(fx, fw=None):
     # several tiles with ragged edges, one row, partial 128-blocks along N and
     # K, a contraction shorter than one 64-deep slab
     base = [(300, 272, 384), (1, 16, 32), (513, 528, 1024), (64, 1040, 256)]
-    return base + ([(200, 144, 352), (70, 48, 96)] if fx == "nvfp4" else [(200, 144, 336), (70, 48, 16)])
+    nv = "nvfp4" in (fx, fw)
+    return base + ([(200, 144, 352), (70, 48, 96)] if nv else [(200, 144, 336), (70, 48, 16)])
 
 
 @pytest.mark.parametrize("fx,fw", PAIRS)
 def test_linear_fwd(lp, fx, fw):
-    for i, (M, N, K) in enumerate(_shapes(fx)):
+    for i, (M, N, K) in enumerate(_shapes(fx, fw)):
         xq, xh, wq, wh = _operands(lp, fx, fw, 50 + i, M, N, K)
         y = lp.lp_linear_fwd(xq, wq)
         torch.cuda.synchronize()
@@ -84,7 +88,8 @@ def test_grouped_fwd(lp, fx, fw, sizes):
     assert (y[end:].float() == 7.0).all(), "rows past the last end are not written"
 
 
-@pytest.mark.parametrize("fx,fw,N", [("bf16", "fp8_b128", 2048), ("bf16", "fp8_b128", 1936), ("nvfp4", "nvfp4", 2048)])
+@pytest.mark.parametrize("fx,fw,N", [("bf16", "fp8_b128", 2048), ("bf16", "fp8_b128", 1936), ("nvfp4", "nvfp4", 2048),
+                                     ("bf16", "nvfp4", 2048)])
 def test_grouped_fwd_round_split(lp, fx, fw, N):
     """A grouped forward over a 4096-long contraction with more 256 x 256
     tiles than one round of the 256 CUs: 34 row tiles of 8 column tiles,
@@ -119,7 +124,7 @@ def test_grouped_fwd_round_split(lp, fx, fw, N):
     assert (y[end:].float() == 7.0).all(), "rows past the last end are not written"
 
 
-@pytest.mark.parametrize("fx,fw", [("bf16", "fp8_b128"), ("nvfp4", "nvfp4")])
+@pytest.mark.parametrize("fx,fw", [("bf16", "fp8_b128"), ("nvfp4", "nvfp4"), ("bf16", "nvfp4")])
 def test_fused_decode_equals_decoded_copy(lp, fx, fw):
     """Decoding inside the contraction gives the same bits as decoding the
     operands first (lp_dequant) and running the bf16 x bf16 forward: the
@@ -176,7 +181,9 @@ def test_rejects(lp):
 
 def test_nvfp4_forward_full_size(lp):
     """The NVFP4 forward workload (8192 x 4096 @ (4096 x 4096)^T, 1% outliers)
-    through the same call, on sampled output rows."""
+    through the fused call, on sampled output rows; the timed order (X
+    decoded once with lp_dequant, then the bf16 x NVFP4 forward) gives the
+    same bits."""
     w = W.WORKLOADS["nvfp4_forward"]
     x = W.with_outliers(W.normal_f32(w.number, "x", (w.M, w.K), w.x_sigma), w.number, "x")
     wt = W.with_outliers(W.normal_f32(w.number, "w", (w.N, w.K), w.w_sigma), w.number, "w")
@@ -187,6 +194,10 @@ def test_nvfp4_forward_full_size(lp):
     rows = np.unique(np.concatenate([np.arange(0, w.M, 67), [w.M - 1]]))
     ref = O.nvfp4_fwd(xh[0][0][rows], xh[1][0][rows], xh[2], wh[0], wh[1], wh[2])
     assert_close(y[torch.from_numpy(rows).cuda()], ref, "full-size NVFP4 forward rows")
+    xb = lp.lp_dequant(xq)
+    y2 = lp.lp_linear_fwd(lp.QTensor("bf16", xb, shape=(1, w.M, w.K)), wq)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), "decode-once forward differs"
 
 
 def test_fp8_grouped_forward_full_size(lp):
