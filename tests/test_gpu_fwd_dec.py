@@ -142,7 +142,8 @@ def test_fused_decode_equals_decoded_copy(lp, fx, fw):
 
 def test_nan_codes_and_scales(lp):
     """A NaN E4M3 weight code makes its output column NaN (block-FP8); a NaN
-    E4M3 block scale of x makes its output row NaN (NVFP4), as in the oracle."""
+    E4M3 block scale of x makes its output row NaN (NVFP4), and one of an
+    NVFP4 weight its output column (bf16 x), as in the oracle."""
     M, N, K = 96, 64, 256
     x = W.normal_f32(59, "x", (M, K), 1.0)
     w = W.normal_f32(59, "w", (N, K), 0.02)
@@ -163,6 +164,16 @@ def test_nan_codes_and_scales(lp):
     ref = O.nvfp4_fwd(xc[0], xs[0], xts, wc4, ws4, wts)
     got = y.float().cpu().numpy()
     assert np.isnan(ref[5]).all() and np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.linalg.norm(got[ok] - ref[ok]) / np.linalg.norm(ref[ok]) <= 5e-3
+    # bf16 x with an NVFP4 weight: a NaN block scale of W makes its output column NaN
+    ws4[0, 40, 2] = 0x7F
+    y = lp.lp_linear_fwd(qtensor(lp, "bf16", xb, shape=(1, M, K)),
+                         qtensor(lp, "nvfp4", wc4, ws4, float(wts), shape=(1, N, K)))
+    torch.cuda.synchronize()
+    ref = O.linear_fwd(xb[0], F.dequant("nvfp4", wc4, ws4, wts)[0])
+    got = y.float().cpu().numpy()
+    assert np.isnan(ref[:, 40]).all() and np.array_equal(np.isnan(got), np.isnan(ref))
     ok = ~np.isnan(ref)
     assert np.linalg.norm(got[ok] - ref[ok]) / np.linalg.norm(ref[ok]) <= 5e-3
 
